@@ -1,0 +1,51 @@
+"""The layer workloads: shapes, precision and the routing-skew recipe.
+
+Shapes follow the DeepSeek-V3-style MoE layer described in the
+Mixture-of-Kittens blog post ("Overlapping computation and communication in
+MoE"): one shared expert plus many routed experts, top-k routing.
+"""
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Dims:
+    name: str
+    T: int          # tokens
+    d: int          # model dimension
+    E: int          # routed experts
+    k: int          # experts per token
+    I: int          # routed-expert intermediate dimension
+    S: int          # shared experts
+    Is: int         # shared-expert intermediate dimension
+    prec: str       # "f32", "bf16" or "mxfp8" (routed-expert GEMMs)
+    zipf: float     # 0: no logit bias; else Zipf exponent of the expert-load skew
+    backward: bool = False
+    seed: int = 0
+
+    @property
+    def R(self):
+        return self.T * self.k
+
+    def fwd_flops(self):
+        """Algorithmic forward FLOPs: router + routed SwiGLU FFNs + shared FFNs."""
+        return (2 * self.T * self.d * self.E + 6 * self.T * self.k * self.d * self.I
+                + 6 * self.T * self.S * self.d * self.Is)
+
+
+CONFIGS = {
+    "c0": Dims("c0", 256, 128, 8, 2, 64, 1, 64, "f32", 0.0),
+    "c1": Dims("c1", 4096, 2048, 64, 6, 768, 1, 768, "bf16", 0.0),
+    "c2": Dims("c2", 8192, 4096, 128, 8, 1536, 0, 0, "bf16", 0.0),
+    "c3a": Dims("c3a", 8192, 7168, 256, 8, 2048, 1, 2048, "bf16", 1.2),
+    "c3b": Dims("c3b", 32768, 7168, 256, 8, 2048, 1, 2048, "bf16", 1.2),
+    "c4": Dims("c4", 16384, 7168, 256, 8, 2048, 1, 2048, "mxfp8", 1.2, backward=True),
+}
+
+
+def get_config(name, **over):
+    c = CONFIGS[name]
+    if not over:
+        return c
+    fields = dict(c.__dict__)
+    fields.update(over)
+    return Dims(**fields)

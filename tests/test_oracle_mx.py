@@ -1,0 +1,74 @@
+"""Pins of the oracle's MX (E4M3 + E8M0) quantizer: hand-worked cases, an
+exhaustive sweep over bf16 bit patterns against torch's float8_e4m3fn cast,
+and the decode table against torch."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+
+def block(vals):
+    v = np.zeros(32)
+    v[:len(vals)] = vals
+    return v
+
+
+def test_hand_cases():
+    # all-zero block: scale code 0, zero elements
+    c, s = O.mx_quantize(np.zeros((1, 32)))
+    assert s.tolist() == [[0]] and np.all(c == 0)
+    # amax 1.0: e_s = 0 - 8 -> code 119; 1.0 -> 256 = 2^8 (field 15, mant 0) = 0x78
+    c, s = O.mx_quantize(block([1.0, 0.5, -1.0])[None])
+    assert s[0, 0] == 119 and c[0, 0] == 0x78 and c[0, 1] == 0x70 and c[0, 2] == 0xF8
+    # 1.9375 * 256 = 496 saturates to 448 (0x7E); 1.8125 * 256 = 464 ties to 448 (even)
+    c, s = O.mx_quantize(block([1.9375, 1.8125, 1.0625])[None])
+    assert s[0, 0] == 119 and c[0, 0] == 0x7E and c[0, 1] == 0x7E
+    # 1.0625 * 256 = 272: halfway between 256 (m=0) and 288 (m=1) -> 256
+    assert c[0, 2] == 0x78
+    # subnormal: 2^-8 relative to 2^e_s -> 2 * 2^-9 -> code 0x02
+    c, s = O.mx_quantize(block([1.0, 2.0 ** -16])[None])
+    assert c[0, 1] == 0x02
+    # scale clamp at the bottom of E8M0
+    c, s = O.mx_quantize(block([2.0 ** -130])[None])
+    assert s[0, 0] == 0
+
+
+def test_exhaustive_bf16_against_torch_cast():
+    bits = np.arange(65536, dtype=np.uint32)
+    v = (bits << 16).view(np.float32).astype(np.float64)
+    v = v[np.isfinite(v)]
+    ours = O.e4m3_round(v)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    inr = np.abs(v) <= 464.0            # torch does not saturate beyond this
+    assert np.array_equal(ours[inr], ref[inr])
+    assert np.all(np.abs(ours[~inr]) == 448.0)
+    assert np.array_equal(np.signbit(ours[v != 0]), np.signbit(v[v != 0]))
+    enc = O.e4m3_encode(ours[inr])
+    ref_bits = torch.from_numpy(v[inr].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc, ref_bits)
+
+
+def test_decode_table_against_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_round_trip_error_bound(axis):
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-8, 8, size=(64, 96)))
+    v = v.astype(np.float32).astype(np.float64)
+    c, s = O.mx_quantize(v, axis=axis)
+    back = O.mx_dequantize(c, s, axis=axis)
+    sc = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=axis)
+    scaled = np.abs(v) / sc
+    _, ex = np.frexp(np.maximum(scaled, 2.0 ** -6))
+    half_q = np.ldexp(1.0, np.maximum(ex - 1, -6) - 4) * sc
+    sat = scaled > 448
+    assert np.all(np.abs(back - v)[~sat] <= half_q[~sat])
+    assert np.all(np.abs(back - v)[sat] <= 64 * sc[sat])
