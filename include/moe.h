@@ -1,0 +1,191 @@
+/* moe.h - C ABI of the MI355X (gfx950) MoE-layer library, libmoe.so.
+ *
+ * The operation is the DeepSeek-V3-style mixture-of-experts layer described
+ * in the Mixture-of-Kittens blog post ("Overlapping computation and
+ * communication in MoE"): a router projection chooses the top-k routed
+ * experts of every token with a weight each; every chosen expert runs a
+ * SwiGLU feed-forward network (gate and up projections, SwiGLU, down
+ * projection); the layer output is the router-weighted sum of the chosen
+ * experts' outputs plus the shared experts' outputs (weight 1).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named in a signature are DEVICE pointers unless stated, and
+ *    must be 16-byte aligned.  Matrices are row-major; weights use the
+ *    [out][in] layout, stacked per expert.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The library never allocates device memory, never synchronises
+ *    the host and never reads device data on the host.  Scratch memory comes
+ *    from the caller's workspace (size from moe_workspace_bytes).
+ *  - Arguments are validated on the host before anything is enqueued.  On
+ *    any error status nothing has been enqueued (MOE_EHIP: a launch failed,
+ *    earlier launches of the same call may have been enqueued) and outputs
+ *    are undefined.  No exception crosses this boundary.
+ *  - Inputs holding NaN or Inf are outside the contract.
+ *  - Results are deterministic: identical inputs give bitwise identical
+ *    outputs (no floating-point atomics anywhere).
+ *
+ * Precision modes (moe_prec)
+ *  - MOE_F32:   every tensor fp32.
+ *  - MOE_BF16:  activations, weights and outputs bf16; fp32 accumulation;
+ *               router logits and weights fp32.
+ *  - MOE_MXFP8: like MOE_BF16, but the routed-expert GEMMs take E4M3
+ *               operands with one E8M0 scale per 32 elements along K (OCP MX
+ *               v1.0); the shared expert and the router stay bf16 (blog post,
+ *               "Other features / MXFP8 support").
+ *
+ * Shape limits: 1 <= k <= min(E, 16), E <= 1024, T >= 0.  MOE_F32 accepts
+ * any d, I, I_s >= 1.  MOE_BF16 and MOE_MXFP8 need d, I and I_s multiples
+ * of 64.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* bad argument: dims, NULL or misaligned pointer */
+  MOE_EUNSUPPORTED = 2,  /* valid request that this build does not implement */
+  MOE_EWORKSPACE = 3,    /* workspace missing or smaller than required */
+  MOE_EHIP = 4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_prec;
+
+/* Layer dimensions (host struct).  T tokens, model dim d, E routed experts,
+ * top-k, routed intermediate dim I, n_shared shared experts of intermediate
+ * dim I_shared.  R = T*k routed rows. */
+typedef struct {
+  int64_t T;
+  int32_t d, E, k, I, n_shared, I_shared;
+} moe_dims;
+
+/* Weights (host struct of device pointers).  Element type: fp32 in MOE_F32,
+ * bf16 otherwise.  ws_* are NULL when n_shared == 0.  In MOE_MXFP8 the
+ * routed experts are read only from the pre-quantized copies q_* (produced
+ * by moe_quantize_mxfp8 along the GEMM's K axis, i.e. along d for gate/up
+ * and along I for down); w_gate/w_up/w_down may then be NULL. */
+typedef struct {
+  const void* w_router;                          /* [E][d] */
+  const void* w_gate;                            /* [E][I][d] */
+  const void* w_up;                              /* [E][I][d] */
+  const void* w_down;                            /* [E][d][I] */
+  const void* ws_gate;                           /* [S][I_s][d] */
+  const void* ws_up;                             /* [S][I_s][d] */
+  const void* ws_down;                           /* [S][d][I_s] */
+  const uint8_t *q_gate, *q_gate_scale;          /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
+  const uint8_t *q_up, *q_up_scale;              /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
+  const uint8_t *q_down, *q_down_scale;          /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
+} moe_weights;
+
+/* Routing state of one forward pass (host struct of caller-owned device
+ * pointers), kept for inspection or for a later backward.  Any field may be
+ * NULL in moe_layer_forward (then it lives in the workspace). */
+typedef struct {
+  float* logits;          /* [T][E] fp32 */
+  int32_t* topk_idx;      /* [T][k] ascending expert id */
+  float* topk_w;          /* [T][k] fp32 */
+  int32_t* expert_counts; /* [E] */
+  int32_t* expert_offsets;/* [E+1] */
+  int32_t* row_token;     /* [R] */
+  int32_t* token_row;     /* [T][k] */
+} moe_routing;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(moe_status s);
+
+/* Workspace needed by an entry point: which = 0 moe_layer_forward,
+ * 1 moe_permute, 2 moe_expert_ffn, 3 moe_shared_ffn.  Writes the byte count
+ * to *bytes (host pointer).  Pure host computation. */
+moe_status moe_workspace_bytes(const moe_dims* dims, moe_prec prec, int which, size_t* bytes);
+
+/* Router projection, top-k selection and normalized weights.
+ * Blog post, "Overlapping computation and communication in MoE" (router
+ * projection, top-k, a router weight per chosen expert); paper summary
+ * section 2.1 ("normalized router weights").
+ *   logits[t][e] = fp32(x_t . W_r[e]) + bias[e] (bias optional, fp32 [E]);
+ *   topk_idx[t]  = the k largest logits, ties to the smaller id, stored in
+ *                  ascending id order;
+ *   topk_w[t][j] = softmax of the selected logits.
+ * Selection is exact with respect to correctly rounded fp32 logits: tokens
+ * whose k-th/(k+1)-th logit gap is within the fp32 accumulation error bound
+ * have their boundary logits recomputed in fp64 before the selection.
+ * logits, topk_idx and topk_w are outputs owned by the caller. */
+moe_status moe_route(const moe_dims* dims, moe_prec prec, const void* x, const void* w_router,
+                     const float* logit_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream);
+
+/* Schedule and dispatch: histogram of routes per expert, exclusive prefix
+ * sum as region offsets, and the stable placement of every route into its
+ * expert's region (expert-major, token-ascending), then the gather
+ * x_perm[r] = x[row_token[r]].
+ * Blog post, "Choosing the right communication direction / Scheduling"
+ * (count per expert, prefix-sum offsets, re-walk the routes; tokens of an
+ * expert land in contiguous rows) and "MXFP8 support" (activation
+ * quantization fused into the dispatch).
+ *   expert_counts [E], expert_offsets [E+1], row_token [R], token_row [T][k]:
+ *   int32 outputs.  x_perm: [R][d] in the activation type, or E4M3 bytes in
+ *   MOE_MXFP8 with x_perm_scale E8M0 [R][d/32]; x_perm may be NULL
+ *   (schedule only).  ws: workspace of moe_workspace_bytes(which=1). */
+moe_status moe_permute(const moe_dims* dims, moe_prec prec, const int32_t* topk_idx, const void* x,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                       int32_t* token_row, void* x_perm, uint8_t* x_perm_scale, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Routed expert FFNs on the permuted rows, grouped by expert:
+ *   o_perm[r] = (SiLU(a W_g[e]^T) * (a W_u[e]^T)) W_d[e]^T,  a = x_perm[r],
+ * for r in [expert_offsets[e], expert_offsets[e+1]).
+ * Blog post, "Overlapping computation and communication in MoE" (gate and
+ * up projections, SwiGLU, down projection per expert).
+ * o_perm: [R][d] output in the activation type (bf16 in MOE_MXFP8).
+ * ws: workspace of moe_workspace_bytes(which=2). */
+moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_perm,
+                          const uint8_t* x_perm_scale, const int32_t* expert_offsets,
+                          const moe_weights* w, void* o_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Shared experts: y_shared[t] = sum_s FFN_s(x_t) in the activation type
+ * (bf16 in MOE_MXFP8; the shared expert stays bf16, blog post "MXFP8
+ * support").  With n_shared == 0 it writes zeros.
+ * ws: workspace of moe_workspace_bytes(which=3). */
+moe_status moe_shared_ffn(const moe_dims* dims, moe_prec prec, const void* x, const moe_weights* w,
+                          void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted sum back to token order (blog post footnote to "Overlapping
+ * computation and communication in MoE": the weighted sum is the last step):
+ *   y[t] = sum_{j ascending expert} topk_w[t][j] * o_perm[token_row[t][j]]
+ *          + y_shared[t]
+ * accumulated in fp32 in that fixed order, rounded once to the output type.
+ * y_shared may be NULL.  Tensors in the activation type (bf16 in MXFP8). */
+moe_status moe_combine(const moe_dims* dims, moe_prec prec, const void* o_perm, const int32_t* token_row,
+                       const float* topk_w, const void* y_shared, void* y, void* stream);
+
+/* The whole forward: route, schedule and dispatch, shared and routed expert
+ * FFNs, weighted sum.  y: [T][d] in the activation type.  routing: optional
+ * caller buffers that receive the routing state (NULL or any NULL field:
+ * kept in the workspace).  ws: workspace of moe_workspace_bytes(which=0). */
+moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x, const moe_weights* w,
+                             const float* logit_bias, void* y, const moe_routing* routing, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* MX quantization of a bf16 matrix src [rows][cols] (OCP MX v1.0; blog post
+ * "MXFP8 support": a quantization kernel pre-quantizes the weights).
+ * axis = 0: one block per 32 consecutive elements of a row (cols % 32 == 0):
+ *   dst [rows][cols] E4M3, scale [rows][cols/32] E8M0.
+ * axis = 1: one block per 32 consecutive rows of a column (rows % 32 == 0):
+ *   dst [rows][cols] E4M3, scale [rows/32][cols] E8M0.
+ * Per block: e = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for
+ * an all-zero block); element = v / 2^e rounded to nearest-even E4M3,
+ * saturating at +-448, sign kept; scale byte = e + 127. */
+moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t cols, int axis, uint8_t* dst,
+                              uint8_t* scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

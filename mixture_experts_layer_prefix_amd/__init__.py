@@ -1,0 +1,9 @@
+"""MI355X-native (gfx950) hot path of a DeepSeek-V3-style MoE layer.
+
+The compute runs in hand-written HIP kernels inside libmoe.so (C ABI in
+include/moe.h); this package only marshals torch tensors (device memory and
+the current stream) into those calls.
+"""
+from . import _lib  # noqa: F401
+from .ops import (Dims, Weights, route, permute, expert_ffn, shared_ffn, combine, layer_forward,  # noqa: F401
+                  quantize_mxfp8, workspace_bytes)

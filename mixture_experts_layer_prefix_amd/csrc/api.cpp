@@ -1,0 +1,380 @@
+// C ABI of libmoe.so: argument validation, workspace carving and the launch
+// sequence of each entry point.  See include/moe.h for the contract.
+#include <limits.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_bytes(moe_prec prec) { return prec == MOE_F32 ? 4 : 2; }
+
+moe_status check_dims(const moe_dims* D, moe_prec prec) {
+  if (!D) return MOE_EINVAL;
+  if (prec != MOE_F32 && prec != MOE_BF16 && prec != MOE_MXFP8) return MOE_EINVAL;
+  if (D->T < 0 || D->d < 1 || D->E < 1 || D->E > 1024 || D->k < 1 || D->k > 16 || D->k > D->E || D->I < 1 ||
+      D->n_shared < 0 || (D->n_shared > 0 && D->I_shared < 1))
+    return MOE_EINVAL;
+  if (D->T * (int64_t)D->k > INT32_MAX) return MOE_EUNSUPPORTED;
+  if (D->n_shared > 1) return MOE_EUNSUPPORTED;
+  if (prec == MOE_F32) {
+    if (D->d % 8) return MOE_EUNSUPPORTED;
+  } else {
+    if (D->d % 64 || D->I % 64 || (D->n_shared > 0 && D->I_shared % 64)) return MOE_EUNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+// Sequential carving of a caller workspace (or size computation when base is null).
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+struct FfnWs {
+  int32_t* prefix;
+  void* h;
+  uint8_t* h_scale;
+};
+
+FfnWs carve_ffn(Carver& c, const moe_dims* D, moe_prec prec) {
+  const int64_t R = D->T * D->k;
+  FfnWs w;
+  w.prefix = static_cast<int32_t*>(c.take((size_t)(D->E + 2) * sizeof(int32_t)));
+  if (prec == MOE_MXFP8) {
+    w.h = c.take((size_t)R * D->I);
+    w.h_scale = static_cast<uint8_t*>(c.take((size_t)R * (D->I / 32)));
+  } else {
+    w.h = c.take((size_t)R * D->I * act_bytes(prec));
+    w.h_scale = nullptr;
+  }
+  return w;
+}
+
+void* carve_shared(Carver& c, const moe_dims* D, moe_prec prec) {
+  return c.take((size_t)D->T * (D->n_shared ? D->I_shared : 0) * act_bytes(prec));
+}
+
+struct FwdWs {
+  float* logits;
+  int32_t *topk_idx, *counts, *offsets, *row_token, *token_row;
+  float* topk_w;
+  void* sched;
+  void* x_perm;
+  uint8_t* x_perm_scale;
+  FfnWs ffn;
+  void* o_perm;
+  void* y_shared;
+  void* hs;
+};
+
+FwdWs carve_forward(Carver& c, const moe_dims* D, moe_prec prec, const moe_routing* rt) {
+  const int64_t T = D->T, R = D->T * D->k;
+  FwdWs w;
+  auto pick = [&](void* user, size_t bytes) { return user ? (c.take(0), user) : c.take(bytes); };
+  w.logits = static_cast<float*>(pick(rt ? rt->logits : nullptr, (size_t)T * D->E * 4));
+  w.topk_idx = static_cast<int32_t*>(pick(rt ? rt->topk_idx : nullptr, (size_t)R * 4));
+  w.topk_w = static_cast<float*>(pick(rt ? rt->topk_w : nullptr, (size_t)R * 4));
+  w.counts = static_cast<int32_t*>(pick(rt ? rt->expert_counts : nullptr, (size_t)D->E * 4));
+  w.offsets = static_cast<int32_t*>(pick(rt ? rt->expert_offsets : nullptr, (size_t)(D->E + 1) * 4));
+  w.row_token = static_cast<int32_t*>(pick(rt ? rt->row_token : nullptr, (size_t)R * 4));
+  w.token_row = static_cast<int32_t*>(pick(rt ? rt->token_row : nullptr, (size_t)R * 4));
+  w.sched = c.take(permute_scratch_bytes(T, D->E));
+  if (prec == MOE_MXFP8) {
+    w.x_perm = c.take((size_t)R * D->d);
+    w.x_perm_scale = static_cast<uint8_t*>(c.take((size_t)R * (D->d / 32)));
+  } else {
+    w.x_perm = c.take((size_t)R * D->d * act_bytes(prec));
+    w.x_perm_scale = nullptr;
+  }
+  w.ffn = carve_ffn(c, D, prec);
+  w.o_perm = c.take((size_t)R * D->d * act_bytes(prec));
+  w.y_shared = D->n_shared ? c.take((size_t)T * D->d * act_bytes(prec)) : nullptr;
+  w.hs = carve_shared(c, D, prec);
+  return w;
+}
+
+size_t workspace_size(const moe_dims* D, moe_prec prec, int which) {
+  Carver c(nullptr);
+  switch (which) {
+    case 0: carve_forward(c, D, prec, nullptr); break;
+    case 1: c.take(permute_scratch_bytes(D->T, D->E)); break;
+    case 2: carve_ffn(c, D, prec); break;
+    case 3: carve_shared(c, D, prec); break;
+    default: return 0;
+  }
+  return c.used;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)                  \
+  do {                                 \
+    moe_status st_ = (expr);           \
+    if (st_ != MOE_OK) return st_;     \
+  } while (0)
+
+#define MOE_HIP(expr)                              \
+  do {                                             \
+    if ((expr) != hipSuccess) return MOE_EHIP;     \
+  } while (0)
+
+// ---- launch sequences (arguments already validated) ------------------------
+
+moe_status run_route(const moe_dims* D, moe_prec prec, const void* x, const void* wr, const float* bias,
+                     float* logits, int32_t* idx, float* w, hipStream_t s) {
+  const bool f32 = prec == MOE_F32;
+  MOE_HIP(launch_router_logits(f32, x, wr, bias, logits, D->T, D->d, D->E, s));
+  MOE_HIP(launch_topk(f32, logits, x, wr, bias, idx, w, D->T, D->d, D->E, D->k, s));
+  return MOE_OK;
+}
+
+moe_status run_permute(const moe_dims* D, moe_prec prec, const int32_t* idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* row_token, int32_t* token_row, void* x_perm, uint8_t* x_perm_scale,
+                       void* sched, hipStream_t s) {
+  const int64_t R = D->T * D->k;
+  MOE_HIP(launch_schedule(idx, D->T, D->E, D->k, counts, offsets, row_token, token_row, sched, s));
+  if (x_perm) {
+    if (prec == MOE_MXFP8)
+      MOE_HIP(launch_gather_quant_mx(static_cast<const bf16_t*>(x), row_token, static_cast<uint8_t*>(x_perm),
+                                     x_perm_scale, R, D->d, s));
+    else
+      MOE_HIP(launch_gather_rows(x, row_token, x_perm, R, D->d, (int)act_bytes(prec), s));
+  }
+  return MOE_OK;
+}
+
+// One SwiGLU FFN over grouped rows: gate/up (+SwiGLU) into h, then down.
+moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t lda, const int32_t* row_off,
+                           int64_t M, int G, const void* wg, const void* wu, const void* wd, int d, int I, void* h,
+                           void* out, int32_t* prefix, hipStream_t s) {
+  GemmProblem q = {};
+  q.mode = GEMM_GATEUP;
+  q.A = A;
+  q.a_rows = a_rows;
+  q.lda = lda;
+  q.row_off = row_off;
+  q.M = M;
+  q.G = G;
+  q.B0 = wg;
+  q.B1 = wu;
+  q.b_group_stride = (int64_t)I * d;
+  q.N = I;
+  q.K = d;
+  q.C = h;
+  q.ldc = I;
+  q.tile_prefix = prefix;
+  MOE_HIP(prec == MOE_F32 ? launch_gemm_f32(q, s) : launch_gemm_bf16(q, s));
+  GemmProblem r = {};
+  r.mode = GEMM_DOWN;
+  r.A = h;
+  r.lda = I;
+  r.row_off = row_off;
+  r.M = M;
+  r.G = G;
+  r.B0 = wd;
+  r.b_group_stride = (int64_t)d * I;
+  r.N = d;
+  r.K = I;
+  r.C = out;
+  r.ldc = d;
+  r.tile_prefix = prefix;
+  MOE_HIP(prec == MOE_F32 ? launch_gemm_f32(r, s) : launch_gemm_bf16(r, s));
+  return MOE_OK;
+}
+
+moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const int32_t* a_rows,
+                          const int32_t* offsets, const moe_weights* w, void* o_perm, const FfnWs& ws,
+                          hipStream_t s) {
+  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  return run_ffn_grouped(prec, A, a_rows, D->d, offsets, D->T * D->k, D->E, w->w_gate, w->w_up, w->w_down, D->d,
+                         D->I, ws.h, o_perm, ws.prefix, s);
+}
+
+moe_status run_shared_ffn(const moe_dims* D, moe_prec prec, const void* x, const moe_weights* w, void* y_shared,
+                          void* hs, hipStream_t s) {
+  if (D->T == 0) return MOE_OK;
+  if (D->n_shared == 0) {
+    MOE_HIP(launch_fill_zero(y_shared, (size_t)D->T * D->d * act_bytes(prec), s));
+    return MOE_OK;
+  }
+  const moe_prec p = prec == MOE_F32 ? MOE_F32 : MOE_BF16;  // shared expert stays bf16 under MXFP8
+  return run_ffn_grouped(p, x, nullptr, D->d, nullptr, D->T, 1, w->ws_gate, w->ws_up, w->ws_down, D->d,
+                         D->I_shared, hs, y_shared, nullptr, s);
+}
+
+moe_status check_weights(const moe_dims* D, moe_prec prec, const moe_weights* w, bool routed, bool shared,
+                         bool router) {
+  if (!w) return MOE_EINVAL;
+  if (router && (!w->w_router || !aligned16(w->w_router))) return MOE_EINVAL;
+  if (routed) {
+    if (prec == MOE_MXFP8) {
+      const void* q[] = {w->q_gate, w->q_gate_scale, w->q_up, w->q_up_scale, w->q_down, w->q_down_scale};
+      for (const void* p : q)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    } else {
+      const void* q[] = {w->w_gate, w->w_up, w->w_down};
+      for (const void* p : q)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    }
+  }
+  if (shared && D->n_shared > 0) {
+    const void* q[] = {w->ws_gate, w->ws_up, w->ws_down};
+    for (const void* p : q)
+      if (!p || !aligned16(p)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+bool ptr_ok(const void* p) { return p && aligned16(p); }
+bool opt_ok(const void* p) { return !p || aligned16(p); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape or mode not supported by this build";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_workspace_bytes(const moe_dims* dims, moe_prec prec, int which, size_t* bytes) {
+  MOE_TRY(check_dims(dims, prec));
+  if (!bytes || which < 0 || which > 3) return MOE_EINVAL;
+  *bytes = workspace_size(dims, prec, which);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_dims* dims, moe_prec prec, const void* x, const void* w_router, const float* logit_bias,
+                     float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  if (dims->T > 0 && (!ptr_ok(x) || !ptr_ok(w_router) || !ptr_ok(logits) || !ptr_ok(topk_idx) || !ptr_ok(topk_w)))
+    return MOE_EINVAL;
+  if (!opt_ok(logit_bias)) return MOE_EINVAL;
+  if (dims->T == 0) return MOE_OK;
+  return run_route(dims, prec, x, w_router, logit_bias, logits, topk_idx, topk_w, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_dims* dims, moe_prec prec, const int32_t* topk_idx, const void* x,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token, int32_t* token_row,
+                       void* x_perm, uint8_t* x_perm_scale, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  if (!ptr_ok(expert_counts) || !ptr_ok(expert_offsets)) return MOE_EINVAL;
+  if (dims->T > 0 && (!ptr_ok(topk_idx) || !ptr_ok(row_token) || !ptr_ok(token_row))) return MOE_EINVAL;
+  if (x_perm && (!aligned16(x_perm) || !ptr_ok(x) || (prec == MOE_MXFP8 && !ptr_ok(x_perm_scale)))) return MOE_EINVAL;
+  if (prec == MOE_MXFP8 && x_perm && dims->d % 32) return MOE_EUNSUPPORTED;
+  const size_t need = workspace_size(dims, prec, 1);
+  if (need && (!ws || ws_bytes < need)) return MOE_EWORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_EINVAL;
+  return run_permute(dims, prec, topk_idx, x, expert_counts, expert_offsets, row_token, token_row, x_perm,
+                     x_perm_scale, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_perm, const uint8_t* x_perm_scale,
+                          const int32_t* expert_offsets, const moe_weights* w, void* o_perm, void* ws, size_t ws_bytes,
+                          void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  MOE_TRY(check_weights(dims, prec, w, true, false, false));
+  if (!ptr_ok(expert_offsets)) return MOE_EINVAL;
+  if (dims->T > 0 && (!ptr_ok(x_perm) || !ptr_ok(o_perm))) return MOE_EINVAL;
+  if (prec == MOE_MXFP8 && dims->T > 0 && !ptr_ok(x_perm_scale)) return MOE_EINVAL;
+  const size_t need = workspace_size(dims, prec, 2);
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!aligned16(ws)) return MOE_EINVAL;
+  if (dims->T == 0) return MOE_OK;
+  Carver c(ws);
+  FfnWs f = carve_ffn(c, dims, prec);
+  return run_expert_ffn(dims, prec, x_perm, nullptr, expert_offsets, w, o_perm, f, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_shared_ffn(const moe_dims* dims, moe_prec prec, const void* x, const moe_weights* w, void* y_shared,
+                          void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  MOE_TRY(check_weights(dims, prec, w, false, true, false));
+  if (dims->T > 0 && (!ptr_ok(x) || !ptr_ok(y_shared))) return MOE_EINVAL;
+  const size_t need = workspace_size(dims, prec, 3);
+  if (need && (!ws || ws_bytes < need)) return MOE_EWORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_EINVAL;
+  Carver c(ws);
+  void* hs = carve_shared(c, dims, prec);
+  return run_shared_ffn(dims, prec, x, w, y_shared, hs, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_dims* dims, moe_prec prec, const void* o_perm, const int32_t* token_row,
+                       const float* topk_w, const void* y_shared, void* y, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  if (dims->T > 0 && (!ptr_ok(o_perm) || !ptr_ok(token_row) || !ptr_ok(topk_w) || !ptr_ok(y))) return MOE_EINVAL;
+  if (!opt_ok(y_shared)) return MOE_EINVAL;
+  MOE_HIP(launch_combine(prec == MOE_F32, o_perm, token_row, topk_w, y_shared, y, dims->T, dims->d, dims->k,
+                         static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x, const moe_weights* w,
+                             const float* logit_bias, void* y, const moe_routing* routing, void* ws, size_t ws_bytes,
+                             void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  MOE_TRY(check_weights(dims, prec, w, true, true, true));
+  if (dims->T > 0 && (!ptr_ok(x) || !ptr_ok(y))) return MOE_EINVAL;
+  if (!opt_ok(logit_bias)) return MOE_EINVAL;
+  if (routing) {
+    const void* f[] = {routing->logits, routing->topk_idx, routing->topk_w, routing->expert_counts,
+                       routing->expert_offsets, routing->row_token, routing->token_row};
+    for (const void* p : f)
+      if (!opt_ok(p)) return MOE_EINVAL;
+  }
+  const size_t need = workspace_size(dims, prec, 0);
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!aligned16(ws)) return MOE_EINVAL;
+  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  FwdWs f = carve_forward(c, dims, prec, routing);
+  if (dims->T == 0) {
+    MOE_HIP(launch_schedule(nullptr, 0, dims->E, dims->k, f.counts, f.offsets, nullptr, nullptr, f.sched, s));
+    return MOE_OK;
+  }
+  MOE_TRY(run_route(dims, prec, x, w->w_router, logit_bias, f.logits, f.topk_idx, f.topk_w, s));
+  MOE_TRY(run_permute(dims, prec, f.topk_idx, x, f.counts, f.offsets, f.row_token, f.token_row, f.x_perm,
+                      f.x_perm_scale, f.sched, s));
+  if (dims->n_shared > 0) MOE_TRY(run_shared_ffn(dims, prec, x, w, f.y_shared, f.hs, s));
+  MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
+  MOE_HIP(launch_combine(prec == MOE_F32, f.o_perm, f.token_row, f.topk_w, f.y_shared, y, dims->T, dims->d, dims->k,
+                         s));
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t cols, int axis, uint8_t* dst, uint8_t* scale,
+                              void* stream) {
+  if (rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return MOE_EINVAL;
+  if ((axis == 0 && cols % 32) || (axis == 1 && rows % 32)) return MOE_EINVAL;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!ptr_ok(src_bf16) || !ptr_ok(dst) || !scale) return MOE_EINVAL;
+  if (axis == 0 && cols > INT_MAX) return MOE_EUNSUPPORTED;
+  MOE_HIP(launch_quantize_mx(static_cast<const bf16_t*>(src_bf16), rows, cols, axis, dst, scale,
+                             static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // storage type of bf16 values (bit pattern)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (finite values).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (each returns hipGetLastError() of its launches)
+// ---------------------------------------------------------------------------
+
+// Router: logits (fp32) from x and W_r; top-k + weights (with fp64 refinement
+// of near-tie tokens).  act_f32: x and W_r are fp32 instead of bf16.
+hipError_t launch_router_logits(bool act_f32, const void* x, const void* w_router, const float* bias,
+                                float* logits, int64_t T, int d, int E, hipStream_t s);
+hipError_t launch_topk(bool act_f32, const float* logits, const void* x, const void* w_router,
+                       const float* bias, int32_t* topk_idx, float* topk_w, int64_t T, int d, int E,
+                       int k, hipStream_t s);
+
+// Schedule: per-block histograms -> scan -> stable scatter.
+int permute_num_blocks(int64_t T);
+size_t permute_scratch_bytes(int64_t T, int E);
+hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
+                           int32_t* offsets, int32_t* row_token, int32_t* token_row, void* scratch,
+                           hipStream_t s);
+// x_perm[r] = x[row_token[r]]; elem_bytes 2 or 4 (d elements per row).
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm, int64_t R, int d,
+                              int elem_bytes, hipStream_t s);
+// Gather + MX quantization along d.
+hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uint8_t* q, uint8_t* scale,
+                                  int64_t R, int d, hipStream_t s);
+hipError_t launch_quantize_mx(const bf16_t* src, int64_t rows, int64_t cols, int axis, uint8_t* dst,
+                              uint8_t* scale, hipStream_t s);
+
+// Zero-fill with a kernel (bytes % 16 == 0, 16-byte aligned); no memset
+// nodes, so the sequence stays safe to capture in a graph.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Combine (weighted sum).  act_f32: fp32 tensors, else bf16.
+hipError_t launch_combine(bool act_f32, const void* o_perm, const int32_t* token_row, const float* topk_w,
+                          const void* y_shared, void* y, int64_t T, int d, int k, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Grouped GEMMs.  A group g owns rows [row_off[g], row_off[g+1]) of the
+// routed rows; with row_off == nullptr there is one group of M rows.
+// ---------------------------------------------------------------------------
+enum GemmMode { GEMM_GATEUP = 0, GEMM_DOWN = 1, GEMM_PLAIN_F32OUT = 2 };
+
+struct GemmProblem {
+  int mode;
+  const void* A;            // [rows][K] (bf16 / fp32 / e4m3)
+  const uint8_t* A_scale;   // MX: [rows][K/32]
+  const int32_t* a_rows;    // optional row gather: row r reads A row a_rows[r]
+  int64_t lda;
+  const int32_t* row_off;   // [G+1] or nullptr
+  int64_t M;                // rows when row_off == nullptr
+  int G;
+  const void* B0;           // [G][N0][K]: W_gate / W_down / W_router
+  const void* B1;           // [G][N0][K]: W_up (gate/up mode)
+  const uint8_t* B0_scale;  // MX scales [G][N0][K/32]
+  const uint8_t* B1_scale;
+  int64_t b_group_stride;   // elements between groups in B0/B1
+  int N;                    // output columns (h columns in gate/up mode)
+  int K;
+  void* C;                  // [rows][N]
+  int64_t ldc;
+  const float* bias;        // [N] (plain mode)
+  int32_t* tile_prefix;     // scratch [G+1] (device), M-tile prefix per group
+};
+
+hipError_t launch_gemm_bf16(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_mxfp8(const GemmProblem& p, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,261 @@
+// Schedule and dispatch on one device, plus the MX (E4M3 + E8M0) quantizer.
+//
+// Mixture-of-Kittens blog post, "Choosing the right communication direction
+// / Scheduling": count the routes of every expert, take an exclusive prefix
+// sum of the counts as each expert's region offset, then walk the routes
+// again and give each its row, so that an expert's tokens land in
+// contiguous rows in token order.  With a single source rank the table
+// entry of a row is the token index.  The pages run this fully on the
+// device with no host round trip; so does this file.
+//
+// Three integer kernels, no floating point and no order-dependent atomics:
+//  1. block histograms: block b counts the routes of its kTokBlock tokens
+//     per expert (LDS integer atomics; counts do not depend on order);
+//  2. one workgroup scans them expert-major: offsets[e] = sum of earlier
+//     experts' totals and base[b][e] = offsets[e] + routes of e in blocks
+//     before b;
+//  3. block b re-walks its routes in (token, slot) order, 256 at a time; a
+//     route's row is base[b][e] plus the number of earlier routes of e in the
+//     block (rank among the 256 in flight plus a running LDS cursor).
+// The result is the unique expert-major, token-ascending layout.
+//
+// The gather copies rows with 16-byte loads and stores; the MXFP8 variant
+// quantizes every 32-element block of a row on the way (blog post, "MXFP8
+// support": activation quantization fused into the dispatch).
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTokBlock = 128;
+
+__global__ void __launch_bounds__(256) hist_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k,
+                                                   int32_t* __restrict__ block_counts) {
+  __shared__ int32_t h[1024];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * kTokBlock * k;
+  const int64_t r1 = min((int64_t)(blockIdx.x + 1) * kTokBlock, T) * k;
+  for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) {
+    const int e = topk_idx[r];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);  // ids outside [0, E) break the contract; skip them
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+__global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ block_counts, int nb, int E,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int32_t s[1024];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      int32_t c = block_counts[(int64_t)b * E + e];
+      block_counts[(int64_t)b * E + e] = total;
+      total += c;
+    }
+  }
+  s[e] = total;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int32_t v = e >= off ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int32_t excl = s[e] - total;
+    counts[e] = total;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = s[e];
+    for (int b = 0; b < nb; ++b) block_counts[(int64_t)b * E + e] += excl;
+  }
+}
+
+__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k,
+                                                      const int32_t* __restrict__ block_base,
+                                                      int32_t* __restrict__ row_token,
+                                                      int32_t* __restrict__ token_row) {
+  __shared__ int32_t cursor[1024];
+  __shared__ int32_t s_e[256];
+  for (int e = threadIdx.x; e < E; e += 256) cursor[e] = block_base[(int64_t)blockIdx.x * E + e];
+  const int64_t r0 = (int64_t)blockIdx.x * kTokBlock * k;
+  const int64_t r1 = min((int64_t)(blockIdx.x + 1) * kTokBlock, T) * k;
+  for (int64_t c0 = r0; c0 < r1; c0 += 256) {
+    const int64_t r = c0 + threadIdx.x;
+    const int n = (int)min((int64_t)256, r1 - c0);
+    int e = threadIdx.x < n ? topk_idx[r] : -1;
+    if ((unsigned)e >= (unsigned)E) {
+      if (threadIdx.x < n) token_row[r] = 0;  // invalid id: no row of its own (outside the contract)
+      e = -1;
+    }
+    s_e[threadIdx.x] = e;
+    __syncthreads();
+    int rank = 0, later = 0;
+    if (e >= 0) {
+      for (int i = 0; i < n; ++i) {
+        const int ei = s_e[i];
+        rank += (ei == e) & (i < (int)threadIdx.x);
+        later += (ei == e) & (i > (int)threadIdx.x);
+      }
+      const int32_t row = cursor[e] + rank;
+      row_token[row] = (int32_t)(r / k);
+      token_row[r] = row;
+    }
+    __syncthreads();
+    if (e >= 0 && later == 0) cursor[e] += rank + 1;
+    __syncthreads();
+  }
+}
+
+template <int EB>
+__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ row_token,
+                                                     uint8_t* __restrict__ xp, int64_t R, int64_t vpr) {
+  // vpr: 16-byte vectors per row
+  const int64_t nvec = R * vpr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+    const int64_t r = v / vpr, c = v - r * vpr;
+    const int64_t src = row_token[r];
+    const u32x4 val = *reinterpret_cast<const u32x4*>(x + (src * vpr + c) * 16);
+    *reinterpret_cast<u32x4*>(xp + (r * vpr + c) * 16) = val;
+  }
+}
+
+// |s| < 512 assumed (the block scale puts the block maximum below 2^9).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
+  const uint32_t bits = __float_as_uint(s);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(s);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;  // 448 itself, ties at 464 go to 448, larger values saturate
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
+    code = (u >> 20) - (120u << 3);     // rebias exponent 127 -> 7
+  }
+  return sign | code;
+}
+
+// Quantize 32 values in registers: returns the E8M0 byte, fills 8 packed words.
+__device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&packed)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = -127;
+  if (amax > 0.0f) {
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    e = max(ef - 127 - 8, -127);
+  }
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact (-e in [-119, 127])
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) p |= e4m3_rne_sat(v[4 * w + b] * inv) << (8 * b);
+    packed[w] = p;
+  }
+  return (uint32_t)(e + 127);
+}
+
+__global__ void __launch_bounds__(256) gather_quant_kernel(const bf16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ row_token,
+                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
+                                                           int64_t R, int d) {
+  const int bpr = d / 32;
+  const int64_t nblk = R * bpr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    const int64_t r = b / bpr, c = b - r * bpr;
+    const int64_t src = row_token ? (int64_t)row_token[r] : r;
+    const u32x4* in = reinterpret_cast<const u32x4*>(x + src * d + c * 32);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w = in[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    uint32_t packed[8];
+    const uint32_t sc = mx_quant32(v, packed);
+    u32x4* out = reinterpret_cast<u32x4*>(q + r * d + c * 32);
+    out[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    out[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+    scale[r * bpr + c] = (uint8_t)sc;
+  }
+}
+
+// Blocks of 32 consecutive rows of one column: thread per (row block, column).
+__global__ void __launch_bounds__(256) quant_cols_kernel(const bf16_t* __restrict__ src, int64_t rows, int64_t cols,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  const int64_t nwork = rows / 32 * cols;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwork; w += stride) {
+    const int64_t rb = w / cols, c = w - rb * cols;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(src[(rb * 32 + i) * cols + c]);
+    uint32_t packed[8];
+    const uint32_t sc = mx_quant32(v, packed);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) q[(rb * 32 + i) * cols + c] = (uint8_t)(packed[i >> 2] >> (8 * (i & 3)));
+    scale[rb * cols + c] = (uint8_t)sc;
+  }
+}
+
+unsigned stream_grid(int64_t work) {
+  int64_t g = (work + 255) / 256;
+  return (unsigned)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
+}
+
+}  // namespace
+
+int permute_num_blocks(int64_t T) { return (int)((T + kTokBlock - 1) / kTokBlock); }
+
+size_t permute_scratch_bytes(int64_t T, int E) { return (size_t)permute_num_blocks(T) * E * sizeof(int32_t); }
+
+hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
+                           int32_t* row_token, int32_t* token_row, void* scratch, hipStream_t s) {
+  const int nb = permute_num_blocks(T);
+  int32_t* bc = static_cast<int32_t*>(scratch);
+  if (nb > 0) hist_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc);
+  scan_kernel<<<1, 1024, 0, s>>>(bc, nb, E, counts, offsets);
+  if (nb > 0) scatter_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc, row_token, token_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm, int64_t R, int d, int elem_bytes,
+                              hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  const int64_t vpr = (int64_t)d * elem_bytes / 16;
+  gather_kernel<16><<<stream_grid(R * vpr), 256, 0, s>>>(static_cast<const uint8_t*>(x), row_token,
+                                                          static_cast<uint8_t*>(x_perm), R, vpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uint8_t* q, uint8_t* scale, int64_t R,
+                                  int d, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  gather_quant_kernel<<<stream_grid(R * (d / 32)), 256, 0, s>>>(x, row_token, q, scale, R, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const bf16_t* src, int64_t rows, int64_t cols, int axis, uint8_t* dst, uint8_t* scale,
+                              hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (axis == 0)
+    gather_quant_kernel<<<stream_grid(rows * (cols / 32)), 256, 0, s>>>(src, nullptr, dst, scale, rows, (int)cols);
+  else
+    quant_cols_kernel<<<stream_grid(rows / 32 * cols), 256, 0, s>>>(src, rows, cols, dst, scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe

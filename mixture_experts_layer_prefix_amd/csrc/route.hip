@@ -1,0 +1,171 @@
+// Router: projection logits, top-k selection with normalized weights.
+//
+// Mixture-of-Kittens blog post, "Overlapping computation and communication
+// in MoE": a router projection selects the top-k routed experts of a token
+// and a router weight for each; paper summary section 2.1: the weights are
+// normalized over the selected experts (softmax of the selected logits).
+//
+// The logits are an MFMA GEMM (fp32 accumulation) followed by the top-k
+// kernel: one wavefront per token, ceil(E/64) logits per lane, rounds of a
+// wave-wide arg-max (larger value, then smaller id).  The fp32 accumulation
+// order of the GEMM differs from a correctly rounded dot product by far less
+// than kBand.  When the k-th and (k+1)-th logits lie within kBand, every
+// expert whose logit is at least the (k+1)-th minus kBand gets its logit
+// recomputed as an fp64 dot product rounded once to fp32 (plus the fp32
+// bias), and the selection is redone on those values.  Experts further below
+// cannot enter the top-k, so the selected set is the one a selection on
+// correctly rounded logits makes.
+#include <math.h>
+
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr float kBand = 1.0f / 4096.0f;
+constexpr int kMaxK = 16;
+
+__device__ __forceinline__ void better(float& bv, int& bid, float ov, int oid) {
+  if (ov > bv || (ov == bv && oid < bid)) {
+    bv = ov;
+    bid = oid;
+  }
+}
+
+template <int PER_LANE>
+__device__ __forceinline__ void select_rounds(const float (&v)[PER_LANE], int E, int rounds, int lane, float (&sel_v)[kMaxK + 1],
+                                              int (&sel_id)[kMaxK + 1]) {
+  uint32_t taken = 0;
+#pragma unroll
+  for (int r = 0; r < kMaxK + 1; ++r) {
+    if (r >= rounds) break;
+    float bv = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u)) better(bv, bid, v[i], e);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oid = __shfl_xor(bid, off);
+      better(bv, bid, ov, oid);
+    }
+    sel_v[r] = bv;
+    sel_id[r] = bid;
+    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+  }
+}
+
+__device__ __forceinline__ double load_as_f64(const void* p, int64_t i, bool f32) {
+  return f32 ? (double)static_cast<const float*>(p)[i] : (double)bf16_to_f32(static_cast<const bf16_t*>(p)[i]);
+}
+
+template <int PER_LANE>
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, const void* __restrict__ x,
+                                                   const void* __restrict__ wr, const float* __restrict__ bias,
+                                                   bool act_f32, int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w, int64_t T, int d, int E, int k) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wavefront leaves; no block barrier below
+  float v[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    int e = lane + 64 * i;
+    v[i] = e < E ? logits[t * E + e] : -INFINITY;
+  }
+  const int rounds = k < E ? k + 1 : k;
+  float lv[kMaxK + 1];
+  int lid[kMaxK + 1];
+  select_rounds<PER_LANE>(v, E, rounds, lane, lv, lid);
+  if (k < E && lv[k - 1] - lv[k] <= kBand) {
+    // Near tie at the selection boundary: exact logits for the candidates.
+    const float thr = lv[k] - kBand;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      int e0 = 64 * i;
+      uint64_t mask = __ballot(lane + e0 < E && v[i] >= thr);
+      while (mask) {
+        int b = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        int e = e0 + b;
+        double acc = 0.0;
+        for (int c = lane; c < d; c += 64)
+          acc += load_as_f64(x, t * (int64_t)d + c, act_f32) * load_as_f64(wr, (int64_t)e * d + c, act_f32);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+        float ex = (float)acc;
+        if (bias) ex = ex + bias[e];
+        if (lane == b) v[i] = ex;
+      }
+    }
+    select_rounds<PER_LANE>(v, E, k, lane, lv, lid);
+  }
+  // Normalized weights over the selected logits, summed in selection order.
+  const float m = lv[0];
+  float ex[kMaxK];
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      ex[j] = expf(lv[j] - m);
+      sum += ex[j];
+    }
+  }
+  // Lane j writes the j-th selected expert at its ascending-id position.
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k && lane == j) {
+      int rank = 0;
+#pragma unroll
+      for (int q = 0; q < kMaxK; ++q)
+        if (q < k && lid[q] < lid[j]) ++rank;
+      topk_idx[t * k + rank] = lid[j];
+      topk_w[t * k + rank] = ex[j] / sum;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(bool act_f32, const void* x, const void* w_router, const float* bias,
+                                float* logits, int64_t T, int d, int E, hipStream_t s) {
+  GemmProblem q = {};
+  q.mode = act_f32 ? GEMM_DOWN : GEMM_PLAIN_F32OUT;
+  q.A = x;
+  q.lda = d;
+  q.M = T;
+  q.G = 1;
+  q.B0 = w_router;
+  q.N = E;
+  q.K = d;
+  q.C = logits;
+  q.ldc = E;
+  q.bias = bias;
+  if (T == 0) return hipSuccess;
+  return act_f32 ? launch_gemm_f32(q, s) : launch_gemm_bf16(q, s);
+}
+
+hipError_t launch_topk(bool act_f32, const float* logits, const void* x, const void* w_router, const float* bias,
+                       int32_t* topk_idx, float* topk_w, int64_t T, int d, int E, int k, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)((T + 3) / 4));
+  const int per_lane = (E + 63) / 64;
+#define MOE_TOPK(P)                                                                                         \
+  topk_kernel<P><<<grid, 256, 0, s>>>(logits, x, w_router, bias, act_f32, topk_idx, topk_w, T, d, E, k); \
+  break;
+  switch (per_lane) {
+    case 1: MOE_TOPK(1)
+    case 2: MOE_TOPK(2)
+    case 3: case 4: MOE_TOPK(4)
+    case 5: case 6: case 7: case 8: MOE_TOPK(8)
+    default: MOE_TOPK(16)
+  }
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,179 @@
+"""Torch-facing wrappers of the C ABI: allocate outputs and workspaces with
+torch (device memory only), pass raw pointers and the current HIP stream.
+No arithmetic of the layer happens here."""
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PREC, call, moe_dims, moe_routing, moe_weights
+
+
+@dataclass(frozen=True)
+class Dims:
+    T: int
+    d: int
+    E: int
+    k: int
+    I: int
+    S: int = 0
+    Is: int = 0
+
+    def c(self):
+        return moe_dims(self.T, self.d, self.E, self.k, self.I, self.S, self.Is if self.S else 0)
+
+    @property
+    def R(self):
+        return self.T * self.k
+
+
+@dataclass
+class Weights:
+    w_router: torch.Tensor
+    w_gate: Optional[torch.Tensor] = None
+    w_up: Optional[torch.Tensor] = None
+    w_down: Optional[torch.Tensor] = None
+    ws_gate: Optional[torch.Tensor] = None
+    ws_up: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None
+    q_gate: Optional[torch.Tensor] = None
+    q_gate_scale: Optional[torch.Tensor] = None
+    q_up: Optional[torch.Tensor] = None
+    q_up_scale: Optional[torch.Tensor] = None
+    q_down: Optional[torch.Tensor] = None
+    q_down_scale: Optional[torch.Tensor] = None
+
+    def c(self):
+        w = moe_weights()
+        for name, _ in moe_weights._fields_:
+            t = getattr(self, name)
+            setattr(w, name, t.data_ptr() if t is not None else None)
+        return w
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _act_dtype(prec):
+    return torch.float32 if prec == "f32" else torch.bfloat16
+
+
+def workspace_bytes(dims: Dims, prec: str, which: int) -> int:
+    n = ctypes.c_size_t(0)
+    call("moe_workspace_bytes", ctypes.byref(dims.c()), PREC[prec], which, ctypes.byref(n))
+    return n.value
+
+
+def _workspace(dims, prec, which, device):
+    n = workspace_bytes(dims, prec, which)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device), n
+
+
+def route(x, w_router, dims: Dims, prec: str, bias=None):
+    dev = x.device
+    logits = torch.empty(dims.T, dims.E, dtype=torch.float32, device=dev)
+    idx = torch.empty(dims.T, dims.k, dtype=torch.int32, device=dev)
+    w = torch.empty(dims.T, dims.k, dtype=torch.float32, device=dev)
+    call("moe_route", ctypes.byref(dims.c()), PREC[prec], _p(x), _p(w_router), _p(bias), _p(logits), _p(idx), _p(w),
+         _stream())
+    return logits, idx, w
+
+
+def permute(topk_idx, x, dims: Dims, prec: str, gather=True):
+    dev = topk_idx.device
+    counts = torch.empty(dims.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(dims.E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(max(dims.R, 1), dtype=torch.int32, device=dev)
+    token_row = torch.empty(dims.T, dims.k, dtype=torch.int32, device=dev)
+    x_perm = scale = None
+    if gather:
+        if prec == "mxfp8":
+            x_perm = torch.empty(dims.R, dims.d, dtype=torch.uint8, device=dev)
+            scale = torch.empty(dims.R, dims.d // 32, dtype=torch.uint8, device=dev)
+        else:
+            x_perm = torch.empty(dims.R, dims.d, dtype=_act_dtype(prec), device=dev)
+    ws, n = _workspace(dims, prec, 1, dev)
+    call("moe_permute", ctypes.byref(dims.c()), PREC[prec], _p(topk_idx), _p(x), _p(counts), _p(offsets),
+         _p(row_token), _p(token_row), _p(x_perm), _p(scale), _p(ws), n, _stream())
+    return counts, offsets, row_token[:dims.R], token_row, x_perm, scale
+
+
+def expert_ffn(x_perm, x_perm_scale, offsets, weights: Weights, dims: Dims, prec: str):
+    dev = offsets.device
+    o_perm = torch.empty(dims.R, dims.d, dtype=_act_dtype(prec), device=dev)
+    ws, n = _workspace(dims, prec, 2, dev)
+    w = weights.c()
+    call("moe_expert_ffn", ctypes.byref(dims.c()), PREC[prec], _p(x_perm), _p(x_perm_scale), _p(offsets),
+         ctypes.byref(w), _p(o_perm), _p(ws), n, _stream())
+    return o_perm
+
+
+def shared_ffn(x, weights: Weights, dims: Dims, prec: str):
+    y_shared = torch.empty(dims.T, dims.d, dtype=_act_dtype(prec), device=x.device)
+    ws, n = _workspace(dims, prec, 3, x.device)
+    w = weights.c()
+    call("moe_shared_ffn", ctypes.byref(dims.c()), PREC[prec], _p(x), ctypes.byref(w), _p(y_shared), _p(ws), n,
+         _stream())
+    return y_shared
+
+
+def combine(o_perm, token_row, topk_w, y_shared, dims: Dims, prec: str):
+    y = torch.empty(dims.T, dims.d, dtype=_act_dtype(prec), device=token_row.device)
+    call("moe_combine", ctypes.byref(dims.c()), PREC[prec], _p(o_perm), _p(token_row), _p(topk_w), _p(y_shared), _p(y),
+         _stream())
+    return y
+
+
+class ForwardPlan:
+    """Pre-allocated output, routing buffers and workspace of one forward
+    configuration, so that repeated calls allocate nothing."""
+
+    def __init__(self, dims: Dims, prec: str, device="cuda", keep_routing=True):
+        self.dims, self.prec = dims, prec
+        T, E, k = dims.T, dims.E, dims.k
+        self.y = torch.empty(T, dims.d, dtype=_act_dtype(prec), device=device)
+        self.routing = None
+        self.rt = None
+        if keep_routing:
+            self.routing = dict(
+                logits=torch.empty(T, E, dtype=torch.float32, device=device),
+                topk_idx=torch.empty(T, k, dtype=torch.int32, device=device),
+                topk_w=torch.empty(T, k, dtype=torch.float32, device=device),
+                expert_counts=torch.empty(E, dtype=torch.int32, device=device),
+                expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
+                row_token=torch.empty(max(dims.R, 1), dtype=torch.int32, device=device),
+                token_row=torch.empty(T, k, dtype=torch.int32, device=device))
+            self.rt = moe_routing(**{n: t.data_ptr() for n, t in self.routing.items()})
+        self.ws, self.ws_bytes = _workspace(dims, prec, 0, device)
+        self.cdims = dims.c()
+
+    def run(self, x, weights: Weights, bias=None):
+        w = weights.c()
+        call("moe_layer_forward", ctypes.byref(self.cdims), PREC[self.prec], _p(x), ctypes.byref(w), _p(bias),
+             _p(self.y), ctypes.byref(self.rt) if self.rt is not None else None, _p(self.ws), self.ws_bytes,
+             _stream())
+        return self.y
+
+
+def layer_forward(x, weights: Weights, dims: Dims, prec: str, bias=None, keep_routing=True):
+    plan = ForwardPlan(dims, prec, x.device, keep_routing)
+    y = plan.run(x, weights, bias)
+    return y, plan.routing
+
+
+def quantize_mxfp8(src, axis):
+    rows, cols = src.shape
+    dst = torch.empty(rows, cols, dtype=torch.uint8, device=src.device)
+    if axis == 0:
+        scale = torch.empty(rows, cols // 32, dtype=torch.uint8, device=src.device)
+    else:
+        scale = torch.empty(rows // 32, cols, dtype=torch.uint8, device=src.device)
+    call("moe_quantize_mxfp8", _p(src), rows, cols, axis, _p(dst), _p(scale), _stream())
+    return dst, scale

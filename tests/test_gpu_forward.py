@@ -1,0 +1,148 @@
+"""GPU parity of the forward hot path against the oracle, entry point by
+entry point and for the fused layer forward, through the C ABI.
+
+Bars: routing ids, expert counts, offsets and the permutation bit-exact;
+gathered rows bit-exact; float outputs within max|d|/max|ref| of 1e-4
+(fp32), 2e-2 (bf16); repeated runs bitwise identical."""
+import numpy as np
+import pytest
+
+import gen
+from oracle import moe_oracle as O
+from tests.moe_parity import TOL, HostProblem, boundary_gaps, device_problem, rel_err, rms_rel, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "c0_f32": gen.get_config("c0"),
+    "bf16_ragged": gen.Dims("bf16_ragged", 300, 256, 16, 4, 192, 1, 128, "bf16", 0.0),
+    "bf16_skew_noshared": gen.Dims("bf16_skew_noshared", 513, 192, 32, 8, 128, 0, 0, "bf16", 1.2),
+    "bf16_k1": gen.Dims("bf16_k1", 77, 64, 4, 1, 64, 1, 64, "bf16", 0.0),
+    "bf16_kE": gen.Dims("bf16_kE", 64, 128, 8, 8, 64, 0, 0, "bf16", 0.0),
+    "f32_skew": gen.Dims("f32_skew", 200, 96, 12, 3, 40, 1, 24, "f32", 1.2),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_routing(gpu_logits, gpu_idx, gpu_w, ref, k):
+    gaps = boundary_gaps(ref["logits"], k)
+    bad = np.nonzero(np.any(gpu_idx != ref["topk_idx"], axis=1))[0]
+    assert len(bad) == 0, "routing mismatch on tokens %s (oracle boundary gaps %s)" % (bad[:10], gaps[bad[:10]])
+    dl = np.max(np.abs(gpu_logits.astype(np.float64) - ref["logits"].astype(np.float64)))
+    assert dl <= 1e-4 * max(1.0, float(np.max(np.abs(ref["logits"])))), dl
+    assert np.max(np.abs(gpu_w.astype(np.float64) - ref["topk_w"])) <= 2e-6
+    return dl
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_every_entry_point(name):
+    import mixture_experts_layer_prefix_amd as M
+    D = SMALL[name]
+    say("[case]", name, D)
+    hp = HostProblem(D)
+    ref = hp.oracle_forward()
+    p, t, md, w = device_problem(D)
+    prec = D.prec
+    # route
+    logits, idx, tw = M.route(t["x"], t["w_router"], md, prec, bias=t["bias"])
+    check_routing(to_np(logits), to_np(idx), to_np(tw), ref, D.k)
+    # permute
+    counts, offsets, row_token, token_row, x_perm, _ = M.permute(idx, t["x"], md, prec)
+    for n, g in (("counts", counts), ("offsets", offsets), ("row_token", row_token), ("token_row", token_row)):
+        assert np.array_equal(to_np(g), ref[n]), n
+    assert torch.equal(x_perm, t["x"][row_token.long()])
+    # shared experts
+    y_sh = M.shared_ffn(t["x"], w, md, prec)
+    if D.S:
+        assert rel_err(to_np(y_sh), ref["y_shared"]) <= TOL[prec]
+    else:
+        assert torch.count_nonzero(y_sh) == 0
+    # routed experts
+    o_perm = M.expert_ffn(x_perm, None, offsets, w, md, prec)
+    e_o = rel_err(to_np(o_perm), ref["o_perm"])
+    assert e_o <= TOL[prec], e_o
+    # combine of the GPU's own expert outputs against a float64 weighted sum of them
+    y_c = M.combine(o_perm, token_row, tw, y_sh if D.S else None, md, prec)
+    y_c_ref = O.combine(to_np(o_perm), ref["token_row"], to_np(tw), to_np(y_sh) if D.S else None)
+    assert rel_err(to_np(y_c), y_c_ref) <= (1e-6 if prec == "f32" else 4e-3)
+    # fused forward
+    y, routing = M.layer_forward(t["x"], w, md, prec, bias=t["bias"])
+    e_y = rel_err(to_np(y), ref["y"])
+    say("   rel err y %.3e (rms %.3e), o_perm %.3e" % (e_y, rms_rel(to_np(y), ref["y"]), e_o))
+    assert e_y <= TOL[prec]
+    for n in ("topk_idx", "expert_counts", "expert_offsets", "token_row"):
+        r = ref[{"expert_counts": "counts", "expert_offsets": "offsets"}.get(n, n)]
+        assert np.array_equal(to_np(routing[n]), r), n
+    y2, _ = M.layer_forward(t["x"], w, md, prec, bias=t["bias"])
+    assert torch.equal(y, y2), "forward is not bitwise deterministic"
+
+
+def test_generator_device_matches_host():
+    for bf16 in (False, True):
+        D = gen.Dims("g", 64, 1000, 8, 2, 64, 0, 0, "bf16" if bf16 else "f32", 0.0)
+        p = gen.Problem(D)
+        dev = to_np(p.device("x"))
+        host = p.host("x")
+        assert np.array_equal(dev.astype(np.float64), host)
+
+
+def test_empty_batch():
+    import mixture_experts_layer_prefix_amd as M
+    D = M.Dims(0, 128, 8, 2, 64, 1, 64)
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    wts = M.Weights(*(torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in
+                      [(8, 128), (8, 64, 128), (8, 64, 128), (8, 128, 64), (1, 64, 128), (1, 64, 128), (1, 128, 64)]))
+    y, routing = M.layer_forward(x, wts, D, "bf16")
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128) and int(routing["expert_offsets"][-1]) == 0
+
+
+def test_c1_full_oracle():
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.get_config("c1")
+    say("[case] c1 full", D)
+    ref = HostProblem(D).oracle_forward()
+    p, t, md, w = device_problem(D)
+    y, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
+    check_routing(to_np(routing["logits"]), to_np(routing["topk_idx"]), to_np(routing["topk_w"]), ref, D.k)
+    for n, r in (("expert_counts", "counts"), ("expert_offsets", "offsets"), ("row_token", "row_token"),
+                 ("token_row", "token_row")):
+        assert np.array_equal(to_np(routing[n]), ref[r]), n
+    e = rel_err(to_np(y), ref["y"])
+    say("   c1 rel err y %.3e rms %.3e" % (e, rms_rel(to_np(y), ref["y"])))
+    assert e <= TOL[D.prec]
+
+
+@pytest.mark.parametrize("cfg,nsample", [("c2", 48), ("c3a", 24), ("c3b", 16)])
+def test_large_config_sampled(cfg, nsample):
+    """Full routing and permutation; outputs on a seeded token sample."""
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.get_config(cfg)
+    say("[case] sampled", cfg, D)
+    p, t, md, w = device_problem(D)
+    y, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
+    y2, _ = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
+    assert torch.equal(y, y2), "forward is not bitwise deterministic"
+    hp = HostProblem(D)
+    ref = hp.routing()
+    check_routing(to_np(routing["logits"]), to_np(routing["topk_idx"]), to_np(routing["topk_w"]), ref, D.k)
+    for n, r in (("expert_counts", "counts"), ("expert_offsets", "offsets"), ("row_token", "row_token"),
+                 ("token_row", "token_row")):
+        assert np.array_equal(to_np(routing[n]), ref[r]), n
+    rng = np.random.default_rng(1234)
+    tokens = sorted(rng.choice(D.T, size=nsample, replace=False).tolist())
+    # include every token of the smallest non-empty expert (ragged tail)
+    nz = np.nonzero(ref["counts"])[0]
+    e_small = int(nz[np.argmin(ref["counts"][nz])])
+    lo, hi = ref["offsets"][e_small], ref["offsets"][e_small + 1]
+    tokens = sorted(set(tokens) | set(ref["row_token"][lo:hi].tolist()))
+    ys = hp.sampled_forward(tokens, ref["topk_idx"], ref["topk_w"])
+    got = to_np(y[torch.tensor(tokens, device="cuda")])
+    e = rel_err(got, ys)
+    say("   %s sampled %d tokens: rel err %.3e rms %.3e; experts empty %d, max rows %d" % (
+        cfg, len(tokens), e, rms_rel(got, ys), int(np.sum(ref["counts"] == 0)), int(ref["counts"].max())))
+    assert e <= TOL[D.prec]
