@@ -148,6 +148,22 @@ moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_per
                           const uint8_t* x_perm_scale, const int32_t* expert_offsets,
                           const moe_weights* w, void* o_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of moe_expert_ffn, for callers that schedule or time them
+ * separately (same contract, same workspace which=2):
+ *   moe_expert_gate_up: h[r] = SiLU(a W_g[e]^T) * (a W_u[e]^T), h [R][I] in
+ *     the activation type (MOE_MXFP8: E4M3 [R][I] with h_scale E8M0
+ *     [R][I/32], quantized in the epilogue; blog post "MXFP8 support":
+ *     activation quantization fused into the SwiGLU);
+ *   moe_expert_down: o_perm[r] = h[r] W_d[e]^T.
+ * Blog post, "Scheduling the overlaps": up/gate projections with SwiGLU,
+ * then the down projection, per expert. */
+moe_status moe_expert_gate_up(const moe_dims* dims, moe_prec prec, const void* x_perm, const uint8_t* x_perm_scale,
+                              const int32_t* expert_offsets, const moe_weights* w, void* h, uint8_t* h_scale,
+                              void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_down(const moe_dims* dims, moe_prec prec, const void* h, const uint8_t* h_scale,
+                           const int32_t* expert_offsets, const moe_weights* w, void* o_perm, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* Shared experts: y_shared[t] = sum_s FFN_s(x_t) in the activation type
  * (bf16 in MOE_MXFP8; the shared expert stays bf16, blog post "MXFP8
  * support").  With n_shared == 0 it writes zeros.

@@ -5,5 +5,5 @@ include/moe.h); this package only marshals torch tensors (device memory and
 the current stream) into those calls.
 """
 from . import _lib  # noqa: F401
-from .ops import (Dims, Weights, route, permute, expert_ffn, shared_ffn, combine, layer_forward,  # noqa: F401
-                  quantize_mxfp8, workspace_bytes)
+from .ops import (Dims, Weights, ForwardPlan, route, permute, expert_ffn, expert_gate_up, expert_down,  # noqa: F401
+                  shared_ffn, combine, layer_forward, quantize_mxfp8, workspace_bytes)

@@ -46,6 +46,10 @@ _SIGS = {
     "moe_permute": ([_DIMS, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_expert_ffn": ([_DIMS, ctypes.c_int, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, ctypes.c_size_t, _P],
                        ctypes.c_int),
+    "moe_expert_gate_up": ([_DIMS, ctypes.c_int, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P,
+                            ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_expert_down": ([_DIMS, ctypes.c_int, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, ctypes.c_size_t, _P],
+                        ctypes.c_int),
     "moe_shared_ffn": ([_DIMS, ctypes.c_int, _P, ctypes.POINTER(moe_weights), _P, _P, ctypes.c_size_t, _P],
                        ctypes.c_int),
     "moe_combine": ([_DIMS, ctypes.c_int, _P, _P, _P, _P, _P, _P], ctypes.c_int),

@@ -55,7 +55,7 @@ struct FfnWs {
 FfnWs carve_ffn(Carver& c, const moe_dims* D, moe_prec prec) {
   const int64_t R = D->T * D->k;
   FfnWs w;
-  w.prefix = static_cast<int32_t*>(c.take((size_t)(D->E + 2) * sizeof(int32_t)));
+  w.prefix = static_cast<int32_t*>(c.take((size_t)2 * (D->E + 2) * sizeof(int32_t)));
   if (prec == MOE_MXFP8) {
     w.h = c.take((size_t)R * D->I);
     w.h_scale = static_cast<uint8_t*>(c.take((size_t)R * (D->I / 32)));
@@ -159,10 +159,10 @@ moe_status run_permute(const moe_dims* D, moe_prec prec, const int32_t* idx, con
   return MOE_OK;
 }
 
-// One SwiGLU FFN over grouped rows: gate/up (+SwiGLU) into h, then down.
-moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t lda, const int32_t* row_off,
-                           int64_t M, int G, const void* wg, const void* wu, const void* wd, int d, int I, void* h,
-                           void* out, int32_t* prefix, hipStream_t s) {
+// Grouped gate/up GEMM with the SwiGLU epilogue into h.
+moe_status run_gateup(moe_prec prec, const void* A, const int32_t* a_rows, int64_t lda, const int32_t* row_off,
+                      int64_t M, int G, const void* wg, const void* wu, int d, int I, void* h, int32_t* prefix,
+                      hipStream_t s) {
   GemmProblem q = {};
   q.mode = GEMM_GATEUP;
   q.A = A;
@@ -180,6 +180,12 @@ moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, 
   q.ldc = I;
   q.tile_prefix = prefix;
   MOE_HIP(prec == MOE_F32 ? launch_gemm_f32(q, s) : launch_gemm_bf16(q, s));
+  return MOE_OK;
+}
+
+// Grouped down GEMM from h.
+moe_status run_down(moe_prec prec, const int32_t* row_off, int64_t M, int G, const void* wd, int d, int I,
+                    const void* h, void* out, int32_t* prefix, hipStream_t s) {
   GemmProblem r = {};
   r.mode = GEMM_DOWN;
   r.A = h;
@@ -196,6 +202,14 @@ moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, 
   r.tile_prefix = prefix;
   MOE_HIP(prec == MOE_F32 ? launch_gemm_f32(r, s) : launch_gemm_bf16(r, s));
   return MOE_OK;
+}
+
+// One SwiGLU FFN over grouped rows: gate/up (+SwiGLU) into h, then down.
+moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t lda, const int32_t* row_off,
+                           int64_t M, int G, const void* wg, const void* wu, const void* wd, int d, int I, void* h,
+                           void* out, int32_t* prefix, hipStream_t s) {
+  MOE_TRY(run_gateup(prec, A, a_rows, lda, row_off, M, G, wg, wu, d, I, h, prefix, s));
+  return run_down(prec, row_off, M, G, wd, d, I, h, out, prefix, s);
 }
 
 moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const int32_t* a_rows,
@@ -306,6 +320,44 @@ moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_per
   Carver c(ws);
   FfnWs f = carve_ffn(c, dims, prec);
   return run_expert_ffn(dims, prec, x_perm, nullptr, expert_offsets, w, o_perm, f, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_gate_up(const moe_dims* dims, moe_prec prec, const void* x_perm, const uint8_t* x_perm_scale,
+                              const int32_t* expert_offsets, const moe_weights* w, void* h, uint8_t* h_scale, void* ws,
+                              size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  MOE_TRY(check_weights(dims, prec, w, true, false, false));
+  if (!ptr_ok(expert_offsets)) return MOE_EINVAL;
+  if (dims->T > 0 && (!ptr_ok(x_perm) || !ptr_ok(h))) return MOE_EINVAL;
+  if (prec == MOE_MXFP8 && dims->T > 0 && (!ptr_ok(x_perm_scale) || !ptr_ok(h_scale))) return MOE_EINVAL;
+  const size_t need = workspace_size(dims, prec, 2);
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!aligned16(ws)) return MOE_EINVAL;
+  if (dims->T == 0) return MOE_OK;
+  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  Carver c(ws);
+  FfnWs f = carve_ffn(c, dims, prec);
+  return run_gateup(prec, x_perm, nullptr, dims->d, expert_offsets, dims->T * dims->k, dims->E, w->w_gate, w->w_up,
+                    dims->d, dims->I, h, f.prefix, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_down(const moe_dims* dims, moe_prec prec, const void* h, const uint8_t* h_scale,
+                           const int32_t* expert_offsets, const moe_weights* w, void* o_perm, void* ws, size_t ws_bytes,
+                           void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  MOE_TRY(check_weights(dims, prec, w, true, false, false));
+  if (!ptr_ok(expert_offsets)) return MOE_EINVAL;
+  if (dims->T > 0 && (!ptr_ok(h) || !ptr_ok(o_perm))) return MOE_EINVAL;
+  if (prec == MOE_MXFP8 && dims->T > 0 && !ptr_ok(h_scale)) return MOE_EINVAL;
+  const size_t need = workspace_size(dims, prec, 2);
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!aligned16(ws)) return MOE_EINVAL;
+  if (dims->T == 0) return MOE_OK;
+  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  Carver c(ws);
+  FfnWs f = carve_ffn(c, dims, prec);
+  return run_down(prec, expert_offsets, dims->T * dims->k, dims->E, w->w_down, dims->d, dims->I, h, o_perm, f.prefix,
+                  static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_shared_ffn(const moe_dims* dims, moe_prec prec, const void* x, const moe_weights* w, void* y_shared,

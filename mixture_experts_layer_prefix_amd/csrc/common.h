@@ -75,6 +75,7 @@ struct GemmProblem {
   const void* A;            // [rows][K] (bf16 / fp32 / e4m3)
   const uint8_t* A_scale;   // MX: [rows][K/32]
   const int32_t* a_rows;    // optional row gather: row r reads A row a_rows[r]
+  int64_t a_bytes;          // size of A in bytes when a_rows is set
   int64_t lda;
   const int32_t* row_off;   // [G+1] or nullptr
   int64_t M;                // rows when row_off == nullptr

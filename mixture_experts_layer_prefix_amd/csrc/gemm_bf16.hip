@@ -7,58 +7,90 @@
 // "Scheduling": tokens of an expert land in contiguous rows so the
 // expert-grouped GEMMs start without reordering).
 //
-// Structure (one persistent grid, every workgroup loops over output tiles):
-//  * Tiles are BM x BN; 4 waves of 64 lanes split the tile 2 x 2, each wave
-//    owns (BM/2) x (BN/2) as a grid of 32x32 MFMA blocks.
-//  * K is consumed BK at a time through two LDS buffers; the next slab is
-//    fetched from global memory into registers while the MFMAs run on the
-//    current one (one barrier per slab).  LDS rows are padded by 16 bytes so
-//    the 16-byte fragment reads of 32 consecutive rows hit distinct banks.
-//  * Tile order: an M-tile prefix over the groups (experts) is computed on
-//    the device, so empty experts cost nothing and the host never learns the
-//    counts.  Logical tiles are handed out so that each XCD (workgroup id
-//    mod 8) owns a contiguous run, and runs walk GN N-tiles of one M-tile
-//    before the next M-tile: neighbouring workgroups of an XCD share A and B
-//    slabs in that XCD's L2.
-//  * Gate/up mode: the B tile interleaves 32-row blocks of W_gate and W_up
-//    for the same output columns, so a wave holds G and U of the same
-//    elements and applies SwiGLU, h = SiLU(G) * U, in registers (blog post,
-//    "Scheduling the overlaps": SwiGLU runs with the grouped GEMMs).
+// Tiles.  One persistent grid; every workgroup (4 waves, 2 x 2) loops over
+// output tiles of two kinds:
+//  * big tiles, 256 x 256: each wave owns 128 x 128 as 4 x 4 MFMA blocks, so
+//    a 16-byte LDS fragment feeds 4 MFMAs and LDS traffic stays at half the
+//    CU's LDS bandwidth while the matrix cores run;
+//  * small tiles, 64 x 256, for the last rows of an expert (a group of n
+//    rows gets floor(n / 256) big tiles, one more if the remainder exceeds
+//    128, and 64-row tiles for a smaller remainder).  Under skewed routing
+//    most experts hold a few rows: their cost is streaming the expert's
+//    weights, and a 64-row tile does that without 4x the wasted MFMA work.
+// K advances 64 at a time through two LDS buffers: the next slab is fetched
+// from global memory into registers while the MFMAs consume the current one
+// (one barrier per slab).  LDS rows are padded by 16 bytes, so 16-byte
+// fragment reads of consecutive rows fall in distinct banks.
+//
+// Order.  M-tile prefixes per group are built on the device (empty experts
+// cost nothing, the host never learns the counts).  Logical tiles are dealt
+// so each XCD (workgroup id mod 8) owns a contiguous run; within a run the
+// N-tiles of one M-tile come before the next M-tile, so the workgroups of an
+// XCD share A and B slabs in that XCD's L2.
+//
+// Gate/up mode: the B tile interleaves 32-row blocks of W_gate and W_up for
+// the same output columns, so each wave holds G and U of the same elements
+// and applies SwiGLU, h = SiLU(G) * U, in registers before the store (blog
+// post, "Scheduling the overlaps": SwiGLU runs with the grouped GEMMs).
 #include "common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kPad = 8;  // bf16 elements of padding per LDS row (16 bytes)
+constexpr int kPad = 8;     // bf16 elements of padding per LDS row (16 bytes)
+constexpr int kBK = 64;     // K slab
+constexpr int kLdsK = kBK + kPad;
+constexpr int kBigM = 256, kSmallM = 64, kBN = 256;
+constexpr int kWavesM = 2, kWavesN = 4;           // 8 waves: 2 per SIMD
+constexpr int kThreads = 64 * kWavesM * kWavesN;  // 512
+constexpr size_t kSmemBytes = 2ull * (kBigM + kBN) * kBK * sizeof(bf16_t);  // 131,072 B
 
-__global__ void __launch_bounds__(1024) tile_prefix_kernel(const int32_t* __restrict__ row_off, int64_t M, int G,
-                                                            int BM, int32_t* __restrict__ prefix) {
-  __shared__ int32_t s[1024];
-  __shared__ int32_t carry;
+// Tile counts of a group of `rows` rows.
+__host__ __device__ __forceinline__ void tiles_of(int64_t rows, int& nb, int& ns) {
+  int64_t b = rows / kBigM, r = rows - b * kBigM;
+  if (r > kBigM / 2) {
+    ++b;
+    r = 0;
+  }
+  nb = (int)b;
+  ns = (int)((r + kSmallM - 1) / kSmallM);
+}
+
+// Exclusive prefixes of the big and small M-tile counts over the groups.
+__global__ void __launch_bounds__(1024) tile_prefix_kernel(const int32_t* __restrict__ row_off, int G,
+                                                            int32_t* __restrict__ big, int32_t* __restrict__ small) {
+  __shared__ int32_t sb[1024], ss[1024];
+  __shared__ int32_t cb, cs;
   if (threadIdx.x == 0) {
-    carry = 0;
-    prefix[0] = 0;
+    cb = cs = 0;
+    big[0] = small[0] = 0;
   }
   __syncthreads();
   for (int base = 0; base < G; base += 1024) {
-    int g = base + threadIdx.x;
-    int n = 0;
-    if (g < G) {
-      int64_t rows = row_off ? (int64_t)(row_off[g + 1] - row_off[g]) : M;
-      n = (int)((rows + BM - 1) / BM);
-    }
-    s[threadIdx.x] = n;
+    const int g = base + threadIdx.x;
+    int nb = 0, ns = 0;
+    if (g < G) tiles_of((int64_t)(row_off[g + 1] - row_off[g]), nb, ns);
+    sb[threadIdx.x] = nb;
+    ss[threadIdx.x] = ns;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-      int v = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+      const int vb = threadIdx.x >= off ? sb[threadIdx.x - off] : 0;
+      const int vs = threadIdx.x >= off ? ss[threadIdx.x - off] : 0;
       __syncthreads();
-      s[threadIdx.x] += v;
+      sb[threadIdx.x] += vb;
+      ss[threadIdx.x] += vs;
       __syncthreads();
     }
-    if (g < G) prefix[g + 1] = carry + s[threadIdx.x];
+    if (g < G) {
+      big[g + 1] = cb + sb[threadIdx.x];
+      small[g + 1] = cs + ss[threadIdx.x];
+    }
     __syncthreads();
-    if (threadIdx.x == 1023) carry += s[1023];
+    if (threadIdx.x == 1023) {
+      cb += sb[1023];
+      cs += ss[1023];
+    }
     __syncthreads();
   }
 }
@@ -67,7 +99,7 @@ struct KArgs {
   const bf16_t* A;
   const int32_t* a_rows;
   int64_t lda;
-  const int32_t* row_off;
+  const int32_t* row_off;  // [G+1] or nullptr (one group of M rows)
   int64_t M;
   int G;
   const bf16_t* B0;
@@ -79,177 +111,336 @@ struct KArgs {
   void* C;
   int64_t ldc;
   const float* bias;
-  const int32_t* prefix;  // M-tile prefix per group, or nullptr: one group
-  int single_mt;          // M tiles of the single group when prefix == nullptr
+  uint32_t a_bytes;      // bytes of A when rows are gathered through a_rows
+  const int32_t* big;    // big M-tile prefix [G+1] (nullptr: single group)
+  const int32_t* small;  // small M-tile prefix [G+1]
+  int single_big, single_small;
 };
 
-template <int BM, int BN, int BK, int MODE, int GN>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(KArgs p) {
-  constexpr int NT = 256;
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int LDS_K = BK + kPad;
-  constexpr int KV = BK / 8;  // 16-byte vectors per row slab
-  constexpr int A_VECS = BM * KV / NT;
-  constexpr int B_VECS = BN * KV / NT;
-  static_assert(A_VECS * NT == BM * KV && B_VECS * NT == BN * KV, "tile/thread mismatch");
-  static_assert(MODE != GEMM_GATEUP || FN % 2 == 0, "gate/up needs G,U block pairs per wave");
+// LDS swizzle of a 128-byte row: chunk position = logical chunk ^ swz(row).
+// 16 consecutive rows then spread a 16-byte column read over 16 distinct
+// 16-byte bank groups of a 256-byte bank window (even and odd rows sit in
+// opposite halves), and any 8 consecutive rows over 8 distinct groups of a
+// 128-byte window.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM][LDS_K];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN][LDS_K];
+// A pointer the whole wave agrees on, kept in scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Largest g with prefix[g] <= mt (prefix non-decreasing, prefix[0] = 0).
+__device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// One BM x kBN output tile of group g: rows [m0, m0 + BM) of the group.
+//
+// Slabs of 64 K-elements go global -> LDS directly (buffer_load ... lds, no
+// register staging): one instruction moves 8 rows x 128 bytes for a wave.
+// Per-lane byte offsets are fixed for the whole tile, the K position rides
+// in the scalar offset, and the buffer descriptors bound every access to its
+// tensor.  LDS rows are dense 128-byte lines with the 16-byte chunks
+// XOR-swizzled per row (swz), realised by letting each lane fetch the chunk
+// that belongs at its LDS slot; the MFMA fragment reads of 8 consecutive rows
+// then hit 8 distinct bank groups.
+//
+// Per slab the four 16-deep K steps are software-pipelined: fragments of
+// step s+1 are read from LDS while the MFMAs of step s run (two register
+// sets).  The barrier sits before the last step's MFMAs, so the load of the
+// slab after next and the first fragments of the next slab overlap them.
+template <int BM, int MODE>
+__device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, int64_t row_begin, int64_t n_g,
+                                          int64_t m0, int ntile) {
+  constexpr int BN = kBN;
+  constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int RPR = kThreads / 8;          // rows per load round (8 rows per wave)
+  constexpr int AR = BM / RPR, BR = BN / RPR;
+  static_assert(AR * RPR == BM && BR * RPR == BN, "tile/thread mismatch");
+  static_assert(MODE != GEMM_GATEUP || FN % 2 == 0, "gate/up needs G,U block pairs per wave");
+  bf16_t* As = smem;                    // [2][BM][64]
+  bf16_t* Bs = smem + 2 * BM * kBK;     // [2][BN][64]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int lrow = wave * 8 + (lane >> 3);       // row inside a load round
+  // global 16-byte chunk for this lane's LDS slot: slot (lane & 7) of row r
+  // holds chunk slot ^ swz(r), r & 7 = lane >> 3 and (r >> 3) & 1 = wave & 1
+  const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  int K = p.K;
+  asm volatile("" : "+s"(K));  // keep per-tile address arithmetic inside the tile
 
-  const int total_m = p.prefix ? p.prefix[p.G] : p.single_mt;
-  const int total = total_m * p.ntiles;
-  const int nwg = gridDim.x;
-  const int per_xcd = nwg >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int KT = p.K / BK;
-
-  for (int it = 0;; ++it) {
-    const int L = it * nwg + xcd * per_xcd + slot;
-    if (L >= total) break;
-    // ---- decode the logical tile ----------------------------------------
-    const int ng = L / (total_m * GN);
-    const int r0 = L - ng * total_m * GN;
-    const int gn = min(GN, p.ntiles - ng * GN);
-    const int mt = r0 / gn;
-    const int ntile = ng * GN + (r0 - mt * gn);
-    int lo = 0, hi = p.G;  // largest g with prefix[g] <= mt
-    if (p.prefix) {
-      while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (p.prefix[mid] <= mt) lo = mid; else hi = mid;
-      }
-    }
-    const int g = lo;
-    const int64_t row_begin = p.prefix ? p.row_off[g] : 0;
-    const int64_t n_g = p.prefix ? (int64_t)(p.row_off[g + 1] - p.row_off[g]) : p.M;
-    const int64_t m0 = (int64_t)(mt - (p.prefix ? p.prefix[g] : 0)) * BM;
-
-    // ---- per-thread global source pointers --------------------------------
-    const bf16_t* pa[A_VECS];
-    const bf16_t* pb[B_VECS];
+  // A: rows of the group (or gathered token rows); descriptor over the
+  // group's rows, or over the whole gather source.
+  const bf16_t* abase = uniform_ptr(p.a_rows ? p.A : p.A + row_begin * p.lda);
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane(p.a_rows ? p.a_bytes : (uint32_t)(n_g * p.lda * 2));
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
+  uint32_t aoff[AR];
 #pragma unroll
-    for (int i = 0; i < A_VECS; ++i) {
-      int v = tid + i * NT;
-      int row = v / KV, kc = (v % KV) * 8;
-      int64_t lr = m0 + row;
-      int64_t grow = row_begin + (lr < n_g ? lr : 0);
-      int64_t src = p.a_rows ? (int64_t)p.a_rows[grow] : grow;
-      pa[i] = p.A + src * p.lda + kc;
+  for (int i = 0; i < AR; ++i) {
+    const int64_t lr0 = m0 + i * RPR + lrow;
+    const int64_t lr = lr0 < n_g ? lr0 : 0;
+    const int64_t src = p.a_rows ? (int64_t)p.a_rows[row_begin + lr] : lr;
+    aoff[i] = (uint32_t)(src * p.lda * 2) + chunk * 16;
+  }
+  // B: one expert's [N][K] matrix (two of them, gate and up, in gate/up mode).
+  // In gate/up mode the tile's B rows are 32-row blocks alternating W_gate
+  // and W_up for the same output columns; the rows a wave loads in one round
+  // lie in one block, so the matrix choice is wave-uniform.
+  const uint32_t bbytes = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)p.N * K * 2));
+  const bf16_t* bsel = MODE == GEMM_GATEUP && ((wave >> 2) & 1) ? p.B1 : p.B0;
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(bsel + (int64_t)g * p.b_group_stride), (short)0, (int)bbytes, 0x00020000);
+  const uint32_t boff = (uint32_t)((lane >> 3) * K * 2) + chunk * 16;
+
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto issue = [&](int buf, int k0) {
+#pragma unroll
+    for (int i = 0; i < AR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(As + (buf * BM + i * RPR + wave * 8) * kBK), 16,
+                                               aoff[i], k0 * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+      // first B row of this wave's 8 rows in round i
+      int row0 = MODE == GEMM_GATEUP ? ntile * (BN / 2) + i * (RPR / 2) + (wave & 3) * 8
+                                     : ntile * BN + i * RPR + wave * 8;
+      row0 = min(row0, p.N - 8);  // rows past N load valid rows; their outputs are not stored
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void*)(Bs + (buf * BN + i * RPR + wave * 8) * kBK), 16, boff,
+                                               (row0 * K + k0) * 2, 0, 0);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](int set, int buf, int kk) {
+    const bf16_t* Ab = As + buf * BM * kBK;
+    const bf16_t* Bb = Bs + buf * BN * kBK;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WM + i * 32 + (lane & 31);
+      fa[set][i] = *reinterpret_cast<const bf16x8*>(Ab + r * kBK + ((c ^ swz(r)) << 3));
     }
 #pragma unroll
-    for (int i = 0; i < B_VECS; ++i) {
-      int v = tid + i * NT;
-      int n = v / KV, kc = (v % KV) * 8;
-      const bf16_t* mat;
-      int srow;
-      if (MODE == GEMM_GATEUP) {
-        int blk = n >> 5;
-        mat = (blk & 1) ? p.B1 : p.B0;
-        srow = ntile * (BN / 2) + (blk >> 1) * 32 + (n & 31);
-      } else {
-        mat = p.B0;
-        srow = min(ntile * BN + n, p.N - 1);
-      }
-      pb[i] = mat + (int64_t)g * p.b_group_stride + (int64_t)srow * p.K + kc;
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WN + j * 32 + (lane & 31);
+      fb[set][j] = *reinterpret_cast<const bf16x8*>(Bb + r * kBK + ((c ^ swz(r)) << 3));
     }
-
-    f32x16 acc[FM][FN];
+  };
+  auto mma = [&](int set) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
 
-    u32x4 ra[A_VECS], rb[B_VECS];
-    auto load_global = [&](int k0) {
+  // Ask the scheduler to interleave the fragment reads of the next step with
+  // the MFMAs of the current one (one LDS read per MFMA_PER_READ MFMAs).
+  constexpr int NREAD = FM + FN, NMMA = FM * FN;
+  constexpr int MFMA_PER_READ = NMMA / NREAD > 0 ? NMMA / NREAD : 1;
+  auto interleave = [&]() {
 #pragma unroll
-      for (int i = 0; i < A_VECS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
-#pragma unroll
-      for (int i = 0; i < B_VECS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < A_VECS; ++i) {
-        int v = tid + i * NT;
-        *reinterpret_cast<u32x4*>(&As[buf][v / KV][(v % KV) * 8]) = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < B_VECS; ++i) {
-        int v = tid + i * NT;
-        *reinterpret_cast<u32x4*>(&Bs[buf][v / KV][(v % KV) * 8]) = rb[i];
-      }
-    };
-
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < KT) load_global((kt + 1) * BK);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[FM], bfr[FN];
-        const int kof = kk * 16 + (lane >> 5) * 8;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * WM + i * 32 + (lane & 31)][kof]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * WN + j * 32 + (lane & 31)][kof]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < KT) store_lds(buf ^ 1);
-      __syncthreads();
+    for (int i = 0; i < NREAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_READ, 0);  // MFMA
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NREAD * MFMA_PER_READ > 0 ? NMMA - NREAD * MFMA_PER_READ : 0,
+                                         0);
+  };
 
-    // ---- epilogue ----------------------------------------------------------
-    // 32x32 block layout: lane holds column (lane & 31) and rows
-    // 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
+  const int KT = K / kBK;
+  issue(0, 0);
+  if (KT > 1) issue(1, kBK);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_frags(0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    read_frags(1, buf, 1);
+    mma(0);
+    interleave();
+    read_frags(0, buf, 2);
+    mma(1);
+    interleave();
+    read_frags(1, buf, 3);
+    mma(0);
+    interleave();
+    // slab kt+1 must have landed (this wave's part, then everyone's); after
+    // the barrier every wave is done reading slab kt, so its buffer can take
+    // slab kt+2 while the last step's MFMAs run.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < KT) issue(buf, (kt + 2) * kBK);
+    if (kt + 1 < KT) read_frags(0, buf ^ 1, 0);
+    mma(1);
+    interleave();
+  }
+
+  // Epilogue.  32x32 block layout: lane holds column (lane & 31) and rows
+  // 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
+  int64_t ldc = p.ldc;
+  asm volatile("" : "+s"(ldc));
+  bf16_t* C = static_cast<bf16_t*>(p.C) + (row_begin + m0) * ldc;
+  const int rows_left = (int)min<int64_t>(n_g - m0, BM);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int64_t lr = m0 + rl;
-        if (lr >= n_g) continue;
-        const int64_t grow = row_begin + lr;
-        if (MODE == GEMM_GATEUP) {
-          bf16_t* C = static_cast<bf16_t*>(p.C);
+    for (int v = 0; v < 16; ++v) {
+      const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (rl >= rows_left) continue;
+      bf16_t* Crow = C + (int64_t)rl * ldc;
+      if (MODE == GEMM_GATEUP) {
 #pragma unroll
-          for (int q = 0; q < FN / 2; ++q) {
-            float gv = acc[i][2 * q][v], uv = acc[i][2 * q + 1][v];
-            int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
-            C[grow * p.ldc + col] = f32_to_bf16(silu_f32(gv) * uv);
-          }
-        } else if (MODE == GEMM_DOWN) {
-          bf16_t* C = static_cast<bf16_t*>(p.C);
+        for (int q = 0; q < FN / 2; ++q) {
+          const float gv = acc[i][2 * q][v], uv = acc[i][2 * q + 1][v];
+          const int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
+          if (col < p.N) Crow[col] = f32_to_bf16(silu_f32(gv) * uv);
+        }
+      } else {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
-            if (col < p.N) C[grow * p.ldc + col] = f32_to_bf16(acc[i][j][v]);
-          }
-        } else {
-          float* C = static_cast<float*>(p.C);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
-            if (col < p.N) C[grow * p.ldc + col] = acc[i][j][v] + (p.bias ? p.bias[col] : 0.0f);
-          }
+        for (int j = 0; j < FN; ++j) {
+          const int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
+          if (col < p.N) Crow[col] = f32_to_bf16(acc[i][j][v]);
         }
       }
     }
+  }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  const bool single = p.big == nullptr;
+  const int nbig = single ? p.single_big : p.big[p.G];
+  const int nsmall = single ? p.single_small : p.small[p.G];
+  const int tb = nbig * p.ntiles;
+  const int total = tb + nsmall * p.ntiles;
+  const int nwg = gridDim.x;
+  const int per_xcd = nwg >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  constexpr int GN = 4;  // N-tiles of one M-tile visited before the next M-tile
+
+  for (int it = 0;; ++it) {
+    int L = it * nwg + xcd * per_xcd + slot;
+    if (L >= total) break;
+    const bool is_big = L < tb;
+    const int nm = is_big ? nbig : nsmall;
+    if (!is_big) L -= tb;
+    const int ng = L / (nm * GN);
+    const int r0 = L - ng * nm * GN;
+    const int gn = min(GN, p.ntiles - ng * GN);
+    const int mt = r0 / gn;
+    const int ntile = ng * GN + (r0 - mt * gn);
+    int g = 0;
+    int64_t row_begin = 0, n_g = p.M, m0;
+    if (single) {
+      m0 = is_big ? (int64_t)mt * kBigM : (int64_t)p.single_big * kBigM + (int64_t)mt * kSmallM;
+    } else {
+      const int32_t* pre = is_big ? p.big : p.small;
+      g = find_group(pre, p.G, mt);
+      row_begin = p.row_off[g];
+      n_g = p.row_off[g + 1] - p.row_off[g];
+      const int nb_g = p.big[g + 1] - p.big[g];
+      m0 = is_big ? (int64_t)(mt - pre[g]) * kBigM : (int64_t)nb_g * kBigM + (int64_t)(mt - pre[g]) * kSmallM;
+    }
+    g = __builtin_amdgcn_readfirstlane(g);
+    row_begin = uniform_i64(row_begin);
+    n_g = uniform_i64(n_g);
+    m0 = uniform_i64(m0);
+    if (is_big) gemm_tile<kBigM, MODE>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    else gemm_tile<kSmallM, MODE>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    __syncthreads();
+  }
+}
+
+// Router-sized GEMM with fp32 output and bias: 64 x 64 tiles (the output has
+// only E columns, so big tiles would leave most CUs idle).
+__global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
+  constexpr int BM = 64, BN = 64, WM = 32, WN = 32;
+  constexpr int KV = kBK / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM][kLdsK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN][kLdsK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int ntile = blockIdx.y;
+  const bf16_t* pa[2];
+  const bf16_t* pb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = tid + i * 256, row = v / KV, kc = (v % KV) * 8;
+    const int64_t r = min(m0 + row, p.M - 1);
+    pa[i] = p.A + r * p.lda + kc;
+    pb[i] = p.B0 + (int64_t)min(ntile * BN + row, p.N - 1) * p.K + kc;
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  u32x4 ra[2], rb[2];
+  const int KT = p.K / kBK;
+  auto ld = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+      rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+    }
+  };
+  auto st = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + i * 256;
+      *reinterpret_cast<u32x4*>(&As[b][v / KV][(v % KV) * 8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[b][v / KV][(v % KV) * 8]) = rb[i];
+    }
+  };
+  ld(0);
+  st(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int b = kt & 1;
+    if (kt + 1 < KT) ld((kt + 1) * kBK);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int kof = kk * 16 + (lane >> 5) * 8;
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[b][wm * WM + (lane & 31)][kof]);
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[b][wn * WN + (lane & 31)][kof]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+    }
+    if (kt + 1 < KT) st(b ^ 1);
+    __syncthreads();
+  }
+  float* C = static_cast<float*>(p.C);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = m0 + wm * WM + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const int col = ntile * BN + wn * WN + (lane & 31);
+    if (row < p.M && col < p.N) C[row * p.ldc + col] = acc[v] + (p.bias ? p.bias[col] : 0.0f);
   }
 }
 
@@ -265,9 +456,16 @@ int num_cus() {
   return cus;
 }
 
-template <int BM, int BN, int BK, int MODE, int GN>
-hipError_t run(const GemmProblem& q, int occupancy, hipStream_t s) {
-  KArgs a;
+template <int MODE>
+hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<MODE>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  KArgs a = {};
   a.A = static_cast<const bf16_t*>(q.A);
   a.a_rows = q.a_rows;
   a.lda = q.lda;
@@ -279,38 +477,53 @@ hipError_t run(const GemmProblem& q, int occupancy, hipStream_t s) {
   a.b_group_stride = q.b_group_stride;
   a.N = q.N;
   a.K = q.K;
-  a.ntiles = MODE == GEMM_GATEUP ? q.N / (BN / 2) : (q.N + BN - 1) / BN;
+  a.ntiles = MODE == GEMM_GATEUP ? (q.N + kBN / 2 - 1) / (kBN / 2) : (q.N + kBN - 1) / kBN;
   a.C = q.C;
   a.ldc = q.ldc;
   a.bias = q.bias;
+  a.a_bytes = (uint32_t)q.a_bytes;
   if (q.row_off) {
-    a.prefix = q.tile_prefix;
-    a.single_mt = 0;
-    tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.M, q.G, BM, q.tile_prefix);
+    a.big = q.tile_prefix;
+    a.small = q.tile_prefix + (q.G + 1);
+    tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.G, q.tile_prefix, q.tile_prefix + (q.G + 1));
   } else {
-    a.prefix = nullptr;
+    a.big = a.small = nullptr;
     a.G = 1;
-    a.single_mt = (int)((q.M + BM - 1) / BM);
+    tiles_of(q.M, a.single_big, a.single_small);
   }
-  int64_t wg = (int64_t)num_cus() * occupancy;
+  int wg = num_cus();
   wg = (wg + 7) / 8 * 8;
-  gemm_bf16_kernel<BM, BN, BK, MODE, GN><<<(unsigned)wg, 256, 0, s>>>(a);
+  gemm_bf16_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
-  if (q.K % 64 != 0) return hipErrorInvalidValue;
+  if (q.K % kBK != 0) return hipErrorInvalidValue;
   switch (q.mode) {
     case GEMM_GATEUP:
-      if (q.N % 64 != 0) return hipErrorInvalidValue;
-      return run<128, 128, 64, GEMM_GATEUP, 4>(q, 2, s);
+      if (q.N % 8 != 0) return hipErrorInvalidValue;
+      return run_grouped<GEMM_GATEUP>(q, s);
     case GEMM_DOWN:
       if (q.N % 8 != 0) return hipErrorInvalidValue;
-      return run<128, 128, 64, GEMM_DOWN, 4>(q, 2, s);
-    default:
-      return run<64, 64, 64, GEMM_PLAIN_F32OUT, 4>(q, 4, s);
+      return run_grouped<GEMM_DOWN>(q, s);
+    default: {
+      if (q.row_off) return hipErrorInvalidValue;
+      KArgs a = {};
+      a.A = static_cast<const bf16_t*>(q.A);
+      a.lda = q.lda;
+      a.M = q.M;
+      a.B0 = static_cast<const bf16_t*>(q.B0);
+      a.N = q.N;
+      a.K = q.K;
+      a.C = q.C;
+      a.ldc = q.ldc;
+      a.bias = q.bias;
+      const dim3 grid((unsigned)((q.M + 63) / 64), (unsigned)((q.N + 63) / 64));
+      gemm_bf16_small_n_kernel<<<grid, 256, 0, s>>>(a);
+      return hipGetLastError();
+    }
   }
 }
 

@@ -59,8 +59,24 @@ __device__ __forceinline__ void select_rounds(const float (&v)[PER_LANE], int E,
   }
 }
 
-__device__ __forceinline__ double load_as_f64(const void* p, int64_t i, bool f32) {
-  return f32 ? (double)static_cast<const float*>(p)[i] : (double)bf16_to_f32(static_cast<const bf16_t*>(p)[i]);
+// Eight consecutive elements starting at i (i a multiple of 8), widened to fp64.
+__device__ __forceinline__ void load8_f64(const void* p, int64_t i, bool f32, double (&v)[8]) {
+  if (f32) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    f32x4 a = q[0], b = q[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
+  } else {
+    u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
 }
 
 template <int PER_LANE>
@@ -93,8 +109,16 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         mask &= mask - 1;
         int e = e0 + b;
         double acc = 0.0;
-        for (int c = lane; c < d; c += 64)
-          acc += load_as_f64(x, t * (int64_t)d + c, act_f32) * load_as_f64(wr, (int64_t)e * d + c, act_f32);
+        // 8 consecutive elements per lane per step (d is a multiple of 8), so
+        // the row streams with wide loads and many requests in flight.
+#pragma unroll 4
+        for (int c = lane * 8; c < d; c += 512) {
+          double xv[8], wv[8];
+          load8_f64(x, t * (int64_t)d + c, act_f32, xv);
+          load8_f64(wr, (int64_t)e * d + c, act_f32, wv);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc += xv[q] * wv[q];
+        }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
         float ex = (float)acc;

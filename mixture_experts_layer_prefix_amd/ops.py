@@ -115,6 +115,37 @@ def expert_ffn(x_perm, x_perm_scale, offsets, weights: Weights, dims: Dims, prec
     return o_perm
 
 
+def expert_gate_up(x_perm, x_perm_scale, offsets, weights: Weights, dims: Dims, prec: str, ws=None):
+    dev = offsets.device
+    if prec == "mxfp8":
+        h = torch.empty(dims.R, dims.I, dtype=torch.uint8, device=dev)
+        h_scale = torch.empty(dims.R, dims.I // 32, dtype=torch.uint8, device=dev)
+    else:
+        h = torch.empty(dims.R, dims.I, dtype=_act_dtype(prec), device=dev)
+        h_scale = None
+    if ws is None:
+        ws, n = _workspace(dims, prec, 2, dev)
+    else:
+        n = ws.numel()
+    w = weights.c()
+    call("moe_expert_gate_up", ctypes.byref(dims.c()), PREC[prec], _p(x_perm), _p(x_perm_scale), _p(offsets),
+         ctypes.byref(w), _p(h), _p(h_scale), _p(ws), n, _stream())
+    return h, h_scale
+
+
+def expert_down(h, h_scale, offsets, weights: Weights, dims: Dims, prec: str, ws=None):
+    dev = offsets.device
+    o_perm = torch.empty(dims.R, dims.d, dtype=_act_dtype(prec), device=dev)
+    if ws is None:
+        ws, n = _workspace(dims, prec, 2, dev)
+    else:
+        n = ws.numel()
+    w = weights.c()
+    call("moe_expert_down", ctypes.byref(dims.c()), PREC[prec], _p(h), _p(h_scale), _p(offsets), ctypes.byref(w),
+         _p(o_perm), _p(ws), n, _stream())
+    return o_perm
+
+
 def shared_ffn(x, weights: Weights, dims: Dims, prec: str):
     y_shared = torch.empty(dims.T, dims.d, dtype=_act_dtype(prec), device=x.device)
     ws, n = _workspace(dims, prec, 3, x.device)
