@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3a", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--cpu-sample", type=int, default=768, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--stage-reps", type=int, default=5, help="repetitions per stage timing (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:

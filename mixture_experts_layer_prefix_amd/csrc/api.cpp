@@ -25,6 +25,11 @@ moe_status check_dims(const moe_dims* D, moe_prec prec) {
       D->n_shared < 0 || (D->n_shared > 0 && D->I_shared < 1))
     return MOE_EINVAL;
   if (D->T * (int64_t)D->k > INT32_MAX) return MOE_EUNSUPPORTED;
+  // GEMM operands are addressed with 32-bit byte offsets from a per-expert
+  // (or per-tensor, for gathered token rows) base.
+  const int64_t inter = D->n_shared > 0 && D->I_shared > D->I ? D->I_shared : D->I;
+  if (D->T * (int64_t)D->d * 4 > UINT32_MAX || D->T * inter * 4 > UINT32_MAX || inter * (int64_t)D->d * 4 > UINT32_MAX)
+    return MOE_EUNSUPPORTED;
   if (D->n_shared > 1) return MOE_EUNSUPPORTED;
   if (prec == MOE_F32) {
     if (D->d % 8) return MOE_EUNSUPPORTED;
@@ -160,13 +165,14 @@ moe_status run_permute(const moe_dims* D, moe_prec prec, const int32_t* idx, con
 }
 
 // Grouped gate/up GEMM with the SwiGLU epilogue into h.
-moe_status run_gateup(moe_prec prec, const void* A, const int32_t* a_rows, int64_t lda, const int32_t* row_off,
-                      int64_t M, int G, const void* wg, const void* wu, int d, int I, void* h, int32_t* prefix,
-                      hipStream_t s) {
+moe_status run_gateup(moe_prec prec, const void* A, const int32_t* a_rows, int64_t a_bytes, int64_t lda,
+                      const int32_t* row_off, int64_t M, int G, const void* wg, const void* wu, int d, int I, void* h,
+                      int32_t* prefix, hipStream_t s) {
   GemmProblem q = {};
   q.mode = GEMM_GATEUP;
   q.A = A;
   q.a_rows = a_rows;
+  q.a_bytes = a_bytes;
   q.lda = lda;
   q.row_off = row_off;
   q.M = M;
@@ -205,10 +211,10 @@ moe_status run_down(moe_prec prec, const int32_t* row_off, int64_t M, int G, con
 }
 
 // One SwiGLU FFN over grouped rows: gate/up (+SwiGLU) into h, then down.
-moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t lda, const int32_t* row_off,
-                           int64_t M, int G, const void* wg, const void* wu, const void* wd, int d, int I, void* h,
-                           void* out, int32_t* prefix, hipStream_t s) {
-  MOE_TRY(run_gateup(prec, A, a_rows, lda, row_off, M, G, wg, wu, d, I, h, prefix, s));
+moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t a_bytes, int64_t lda,
+                           const int32_t* row_off, int64_t M, int G, const void* wg, const void* wu, const void* wd,
+                           int d, int I, void* h, void* out, int32_t* prefix, hipStream_t s) {
+  MOE_TRY(run_gateup(prec, A, a_rows, a_bytes, lda, row_off, M, G, wg, wu, d, I, h, prefix, s));
   return run_down(prec, row_off, M, G, wd, d, I, h, out, prefix, s);
 }
 
@@ -216,8 +222,9 @@ moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const
                           const int32_t* offsets, const moe_weights* w, void* o_perm, const FfnWs& ws,
                           hipStream_t s) {
   if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
-  return run_ffn_grouped(prec, A, a_rows, D->d, offsets, D->T * D->k, D->E, w->w_gate, w->w_up, w->w_down, D->d,
-                         D->I, ws.h, o_perm, ws.prefix, s);
+  const int64_t a_bytes = a_rows ? D->T * (int64_t)D->d * (int64_t)act_bytes(prec) : 0;
+  return run_ffn_grouped(prec, A, a_rows, a_bytes, D->d, offsets, D->T * D->k, D->E, w->w_gate, w->w_up, w->w_down,
+                         D->d, D->I, ws.h, o_perm, ws.prefix, s);
 }
 
 moe_status run_shared_ffn(const moe_dims* D, moe_prec prec, const void* x, const moe_weights* w, void* y_shared,
@@ -228,7 +235,7 @@ moe_status run_shared_ffn(const moe_dims* D, moe_prec prec, const void* x, const
     return MOE_OK;
   }
   const moe_prec p = prec == MOE_F32 ? MOE_F32 : MOE_BF16;  // shared expert stays bf16 under MXFP8
-  return run_ffn_grouped(p, x, nullptr, D->d, nullptr, D->T, 1, w->ws_gate, w->ws_up, w->ws_down, D->d,
+  return run_ffn_grouped(p, x, nullptr, 0, D->d, nullptr, D->T, 1, w->ws_gate, w->ws_up, w->ws_down, D->d,
                          D->I_shared, hs, y_shared, nullptr, s);
 }
 
@@ -337,8 +344,8 @@ moe_status moe_expert_gate_up(const moe_dims* dims, moe_prec prec, const void* x
   if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
   Carver c(ws);
   FfnWs f = carve_ffn(c, dims, prec);
-  return run_gateup(prec, x_perm, nullptr, dims->d, expert_offsets, dims->T * dims->k, dims->E, w->w_gate, w->w_up,
-                    dims->d, dims->I, h, f.prefix, static_cast<hipStream_t>(stream));
+  return run_gateup(prec, x_perm, nullptr, 0, dims->d, expert_offsets, dims->T * dims->k, dims->E, w->w_gate,
+                    w->w_up, dims->d, dims->I, h, f.prefix, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_down(const moe_dims* dims, moe_prec prec, const void* h, const uint8_t* h_scale,
@@ -408,10 +415,17 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
     return MOE_OK;
   }
   MOE_TRY(run_route(dims, prec, x, w->w_router, logit_bias, f.logits, f.topk_idx, f.topk_w, s));
-  MOE_TRY(run_permute(dims, prec, f.topk_idx, x, f.counts, f.offsets, f.row_token, f.token_row, f.x_perm,
-                      f.x_perm_scale, f.sched, s));
+  // Dispatch: the schedule places every route; in bf16 the grouped gate/up
+  // GEMM then reads its A rows straight from x through row_token (the gather
+  // rides in the GEMM's loads and x_perm is never written).
+  const bool fused_gather = prec == MOE_BF16;
+  MOE_TRY(run_permute(dims, prec, f.topk_idx, x, f.counts, f.offsets, f.row_token, f.token_row,
+                      fused_gather ? nullptr : f.x_perm, f.x_perm_scale, f.sched, s));
   if (dims->n_shared > 0) MOE_TRY(run_shared_ffn(dims, prec, x, w, f.y_shared, f.hs, s));
-  MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
+  if (fused_gather)
+    MOE_TRY(run_expert_ffn(dims, prec, x, f.row_token, f.offsets, w, f.o_perm, f.ffn, s));
+  else
+    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
   MOE_HIP(launch_combine(prec == MOE_F32, f.o_perm, f.token_row, f.topk_w, f.y_shared, y, dims->T, dims->d, dims->k,
                          s));
   return MOE_OK;

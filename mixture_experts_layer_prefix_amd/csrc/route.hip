@@ -9,11 +9,12 @@
 // kernel: one wavefront per token, ceil(E/64) logits per lane, rounds of a
 // wave-wide arg-max (larger value, then smaller id).  The fp32 accumulation
 // order of the GEMM differs from a correctly rounded dot product by far less
-// than kBand.  When the k-th and (k+1)-th logits lie within kBand, every
-// expert whose logit is at least the (k+1)-th minus kBand gets its logit
-// recomputed as an fp64 dot product rounded once to fp32 (plus the fp32
-// bias), and the selection is redone on those values.  Experts further below
-// cannot enter the top-k, so the selected set is the one a selection on
+// than kBand.  When the k-th and (k+1)-th logits lie within kBand, the
+// experts whose logits lie between the (k+1)-th minus kBand and the k-th
+// plus kBand/2 get their logits recomputed as fp64 dot products rounded once
+// to fp32 (plus the fp32 bias), and the selection is redone.  Experts above
+// that window are in the top-k and experts below it are out under any
+// rounding of that size, so the selected set is the one a selection on
 // correctly rounded logits makes.
 #include <math.h>
 
@@ -98,12 +99,15 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   int lid[kMaxK + 1];
   select_rounds<PER_LANE>(v, E, rounds, lane, lv, lid);
   if (k < E && lv[k - 1] - lv[k] <= kBand) {
-    // Near tie at the selection boundary: exact logits for the candidates.
-    const float thr = lv[k] - kBand;
+    // Near tie at the selection boundary.  Experts above hi are in the top-k
+    // whatever the rounding (fewer than k logits exceed the k-th largest);
+    // experts below lo are out (at least k+1 logits lie above them).  Only
+    // the ones in between get exact logits before the selection is redone.
+    const float lo = lv[k] - kBand, hi = lv[k - 1] + 0.5f * kBand;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
       int e0 = 64 * i;
-      uint64_t mask = __ballot(lane + e0 < E && v[i] >= thr);
+      uint64_t mask = __ballot(lane + e0 < E && v[i] >= lo && v[i] <= hi);
       while (mask) {
         int b = __ffsll((unsigned long long)mask) - 1;
         mask &= mask - 1;
