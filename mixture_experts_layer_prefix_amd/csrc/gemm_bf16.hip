@@ -17,6 +17,10 @@
 //    128, and 64-row tiles for a smaller remainder).  Under skewed routing
 //    most experts hold a few rows: their cost is streaming the expert's
 //    weights, and a 64-row tile does that without 4x the wasted MFMA work.
+//    Small tiles keep three slabs in LDS (two in flight) since they are
+//    bound by memory latency.  In the down projection they are spread
+//    evenly through the tile order so they stream weights while other CUs
+//    run big tiles.
 // K advances 64 at a time through two LDS buffers: the next slab is fetched
 // from global memory into registers while the MFMAs consume the current one
 // (one barrier per slab).  LDS rows are padded by 16 bytes, so 16-byte
@@ -115,6 +119,7 @@ struct KArgs {
   const int32_t* big;    // big M-tile prefix [G+1] (nullptr: single group)
   const int32_t* small;  // small M-tile prefix [G+1]
   int single_big, single_small;
+  int spread_small;      // interleave small tiles among big ones (else big first)
 };
 
 // LDS swizzle of a 128-byte row: chunk position = logical chunk ^ swz(row).
@@ -164,7 +169,13 @@ __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) 
 // step s+1 are read from LDS while the MFMAs of step s run (two register
 // sets).  The barrier sits before the last step's MFMAs, so the load of the
 // slab after next and the first fragments of the next slab overlap them.
-template <int BM, int MODE>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int MODE, int NS>
 __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, int64_t row_begin, int64_t n_g,
                                           int64_t m0, int ntile) {
   constexpr int BN = kBN;
@@ -174,8 +185,9 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   constexpr int AR = BM / RPR, BR = BN / RPR;
   static_assert(AR * RPR == BM && BR * RPR == BN, "tile/thread mismatch");
   static_assert(MODE != GEMM_GATEUP || FN % 2 == 0, "gate/up needs G,U block pairs per wave");
-  bf16_t* As = smem;                    // [2][BM][64]
-  bf16_t* Bs = smem + 2 * BM * kBK;     // [2][BN][64]
+  bf16_t* As = smem;                    // [NS][BM][64]
+  bf16_t* Bs = smem + NS * BM * kBK;    // [NS][BN][64]
+  constexpr int LPS = AR + BR;          // loads per slab per thread
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,13 +287,19 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   };
 
   const int KT = K / kBK;
-  issue(0, 0);
-  if (KT > 1) issue(1, kBK);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // NS-slab ring in LDS: slabs 0..NS-1 go out first; after the barrier of
+  // iteration kt slab kt's buffer is free and takes slab kt+NS.  Before the
+  // barrier only slab kt+1 must have landed, so vmcnt may leave the younger
+  // slabs (LPS loads each) in flight.
+  wait_vmcnt<0>();  // earlier stores of this wave drained: counts below are exact
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0)
+    if (s0 < KT) issue(s0, s0 * kBK);
+  if (KT >= NS) wait_vmcnt<(NS - 1) * LPS>(); else wait_vmcnt<0>();
   __syncthreads();
   read_frags(0, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
+    const int buf = kt % NS;
     read_frags(1, buf, 1);
     mma(0);
     interleave();
@@ -291,13 +309,10 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
     read_frags(1, buf, 3);
     mma(0);
     interleave();
-    // slab kt+1 must have landed (this wave's part, then everyone's); after
-    // the barrier every wave is done reading slab kt, so its buffer can take
-    // slab kt+2 while the last step's MFMAs run.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPS>(); else wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 2 < KT) issue(buf, (kt + 2) * kBK);
-    if (kt + 1 < KT) read_frags(0, buf ^ 1, 0);
+    if (kt + NS < KT) issue(buf, (kt + NS) * kBK);
+    if (kt + 1 < KT) read_frags(0, (kt + 1) % NS, 0);
     mma(1);
     interleave();
   }
@@ -346,12 +361,24 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   constexpr int GN = 4;  // N-tiles of one M-tile visited before the next M-tile
 
+  const int ts = total - tb;
   for (int it = 0;; ++it) {
-    int L = it * nwg + xcd * per_xcd + slot;
-    if (L >= total) break;
-    const bool is_big = L < tb;
+    const int P = it * nwg + xcd * per_xcd + slot;
+    if (P >= total) break;
+    // Small tiles (weight streaming, HBM-bound) are spread evenly among the
+    // big ones (MFMA-bound), so both kinds run side by side on different CUs:
+    // position P is small when the running share of small tiles steps up.
+    bool is_big;
+    int L;
+    if (p.spread_small) {
+      const int s_before = (int)((int64_t)P * ts / total);
+      is_big = (int)((int64_t)(P + 1) * ts / total) == s_before;
+      L = is_big ? P - s_before : s_before;
+    } else {
+      is_big = P < tb;
+      L = is_big ? P : P - tb;
+    }
     const int nm = is_big ? nbig : nsmall;
-    if (!is_big) L -= tb;
     const int ng = L / (nm * GN);
     const int r0 = L - ng * nm * GN;
     const int gn = min(GN, p.ntiles - ng * GN);
@@ -373,8 +400,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
     row_begin = uniform_i64(row_begin);
     n_g = uniform_i64(n_g);
     m0 = uniform_i64(m0);
-    if (is_big) gemm_tile<kBigM, MODE>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
-    else gemm_tile<kSmallM, MODE>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    if (is_big) gemm_tile<kBigM, MODE, 2>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    else gemm_tile<kSmallM, MODE, 3>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
     __syncthreads();
   }
 }
@@ -482,6 +509,10 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   a.ldc = q.ldc;
   a.bias = q.bias;
   a.a_bytes = (uint32_t)q.a_bytes;
+  // Interleaving helps the short-K down projection (small tiles overlap the
+  // big ones); for the long-K gate/up GEMM the big tiles are latency-bound
+  // and lose more from the shared memory traffic than the overlap gains.
+  a.spread_small = MODE == GEMM_DOWN ? 1 : 0;
   if (q.row_off) {
     a.big = q.tile_prefix;
     a.small = q.tile_prefix + (q.G + 1);
