@@ -35,6 +35,7 @@ moe_status check_dims(const moe_dims* D, moe_prec prec) {
     if (D->d % 8) return MOE_EUNSUPPORTED;
   } else {
     if (D->d % 64 || D->I % 64 || (D->n_shared > 0 && D->I_shared % 64)) return MOE_EUNSUPPORTED;
+    if (prec == MOE_MXFP8 && (D->d % 128 || D->I % 128)) return MOE_EUNSUPPORTED;
   }
   return MOE_OK;
 }
@@ -100,9 +101,9 @@ FwdWs carve_forward(Carver& c, const moe_dims* D, moe_prec prec, const moe_routi
   w.row_token = static_cast<int32_t*>(pick(rt ? rt->row_token : nullptr, (size_t)R * 4));
   w.token_row = static_cast<int32_t*>(pick(rt ? rt->token_row : nullptr, (size_t)R * 4));
   w.sched = c.take(permute_scratch_bytes(T, D->E));
-  if (prec == MOE_MXFP8) {
-    w.x_perm = c.take((size_t)R * D->d);
-    w.x_perm_scale = static_cast<uint8_t*>(c.take((size_t)R * (D->d / 32)));
+  if (prec == MOE_MXFP8) {  // quantized tokens [T][d] (+ scales); rows are gathered by the GEMM
+    w.x_perm = c.take((size_t)T * D->d);
+    w.x_perm_scale = static_cast<uint8_t*>(c.take((size_t)T * (D->d / 32)));
   } else {
     w.x_perm = c.take((size_t)R * D->d * act_bytes(prec));
     w.x_perm_scale = nullptr;
@@ -210,6 +211,57 @@ moe_status run_down(moe_prec prec, const int32_t* row_off, int64_t M, int G, con
   return MOE_OK;
 }
 
+// MXFP8 grouped gate/up (h quantized along I in the epilogue) and down.
+moe_status run_gateup_mx(const moe_dims* D, const uint8_t* A, const uint8_t* A_scale, const int32_t* a_rows,
+                         const int32_t* offsets, const moe_weights* w, uint8_t* h, uint8_t* h_scale, int32_t* prefix,
+                         hipStream_t s) {
+  GemmProblem q = {};
+  q.mode = GEMM_GATEUP;
+  q.A = A;
+  q.A_scale = A_scale;
+  q.a_rows = a_rows;
+  q.a_bytes = a_rows ? D->T * (int64_t)D->d : 0;
+  q.lda = D->d;
+  q.row_off = offsets;
+  q.M = D->T * D->k;
+  q.G = D->E;
+  q.B0 = w->q_gate;
+  q.B1 = w->q_up;
+  q.B0_scale = w->q_gate_scale;
+  q.B1_scale = w->q_up_scale;
+  q.b_group_stride = (int64_t)D->I * D->d;
+  q.N = D->I;
+  q.K = D->d;
+  q.C = h;
+  q.C_scale = h_scale;
+  q.ldc = D->I;
+  q.tile_prefix = prefix;
+  MOE_HIP(launch_gemm_mxfp8(q, s));
+  return MOE_OK;
+}
+
+moe_status run_down_mx(const moe_dims* D, const uint8_t* h, const uint8_t* h_scale, const int32_t* offsets,
+                       const moe_weights* w, void* o_perm, int32_t* prefix, hipStream_t s) {
+  GemmProblem r = {};
+  r.mode = GEMM_DOWN;
+  r.A = h;
+  r.A_scale = h_scale;
+  r.lda = D->I;
+  r.row_off = offsets;
+  r.M = D->T * D->k;
+  r.G = D->E;
+  r.B0 = w->q_down;
+  r.B0_scale = w->q_down_scale;
+  r.b_group_stride = (int64_t)D->d * D->I;
+  r.N = D->d;
+  r.K = D->I;
+  r.C = o_perm;
+  r.ldc = D->d;
+  r.tile_prefix = prefix;
+  MOE_HIP(launch_gemm_mxfp8(r, s));
+  return MOE_OK;
+}
+
 // One SwiGLU FFN over grouped rows: gate/up (+SwiGLU) into h, then down.
 moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t a_bytes, int64_t lda,
                            const int32_t* row_off, int64_t M, int G, const void* wg, const void* wu, const void* wd,
@@ -218,10 +270,14 @@ moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, 
   return run_down(prec, row_off, M, G, wd, d, I, h, out, prefix, s);
 }
 
-moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const int32_t* a_rows,
-                          const int32_t* offsets, const moe_weights* w, void* o_perm, const FfnWs& ws,
-                          hipStream_t s) {
-  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
+moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const uint8_t* A_scale,
+                          const int32_t* a_rows, const int32_t* offsets, const moe_weights* w, void* o_perm,
+                          const FfnWs& ws, hipStream_t s) {
+  if (prec == MOE_MXFP8) {
+    MOE_TRY(run_gateup_mx(D, static_cast<const uint8_t*>(A), A_scale, a_rows, offsets, w,
+                          static_cast<uint8_t*>(ws.h), ws.h_scale, ws.prefix, s));
+    return run_down_mx(D, static_cast<const uint8_t*>(ws.h), ws.h_scale, offsets, w, o_perm, ws.prefix, s);
+  }
   const int64_t a_bytes = a_rows ? D->T * (int64_t)D->d * (int64_t)act_bytes(prec) : 0;
   return run_ffn_grouped(prec, A, a_rows, a_bytes, D->d, offsets, D->T * D->k, D->E, w->w_gate, w->w_up, w->w_down,
                          D->d, D->I, ws.h, o_perm, ws.prefix, s);
@@ -326,7 +382,8 @@ moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_per
   if (dims->T == 0) return MOE_OK;
   Carver c(ws);
   FfnWs f = carve_ffn(c, dims, prec);
-  return run_expert_ffn(dims, prec, x_perm, nullptr, expert_offsets, w, o_perm, f, static_cast<hipStream_t>(stream));
+  return run_expert_ffn(dims, prec, x_perm, x_perm_scale, nullptr, expert_offsets, w, o_perm, f,
+                        static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_gate_up(const moe_dims* dims, moe_prec prec, const void* x_perm, const uint8_t* x_perm_scale,
@@ -341,9 +398,11 @@ moe_status moe_expert_gate_up(const moe_dims* dims, moe_prec prec, const void* x
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
   if (!aligned16(ws)) return MOE_EINVAL;
   if (dims->T == 0) return MOE_OK;
-  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
   Carver c(ws);
   FfnWs f = carve_ffn(c, dims, prec);
+  if (prec == MOE_MXFP8)
+    return run_gateup_mx(dims, static_cast<const uint8_t*>(x_perm), x_perm_scale, nullptr, expert_offsets, w,
+                         static_cast<uint8_t*>(h), h_scale, f.prefix, static_cast<hipStream_t>(stream));
   return run_gateup(prec, x_perm, nullptr, 0, dims->d, expert_offsets, dims->T * dims->k, dims->E, w->w_gate,
                     w->w_up, dims->d, dims->I, h, f.prefix, static_cast<hipStream_t>(stream));
 }
@@ -360,9 +419,11 @@ moe_status moe_expert_down(const moe_dims* dims, moe_prec prec, const void* h, c
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
   if (!aligned16(ws)) return MOE_EINVAL;
   if (dims->T == 0) return MOE_OK;
-  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
   Carver c(ws);
   FfnWs f = carve_ffn(c, dims, prec);
+  if (prec == MOE_MXFP8)
+    return run_down_mx(dims, static_cast<const uint8_t*>(h), h_scale, expert_offsets, w, o_perm, f.prefix,
+                       static_cast<hipStream_t>(stream));
   return run_down(prec, expert_offsets, dims->T * dims->k, dims->E, w->w_down, dims->d, dims->I, h, o_perm, f.prefix,
                   static_cast<hipStream_t>(stream));
 }
@@ -406,7 +467,6 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
   const size_t need = workspace_size(dims, prec, 0);
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
   if (!aligned16(ws)) return MOE_EINVAL;
-  if (prec == MOE_MXFP8) return MOE_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver c(ws);
   FwdWs f = carve_forward(c, dims, prec, routing);
@@ -418,14 +478,21 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
   // Dispatch: the schedule places every route; in bf16 the grouped gate/up
   // GEMM then reads its A rows straight from x through row_token (the gather
   // rides in the GEMM's loads and x_perm is never written).
-  const bool fused_gather = prec == MOE_BF16;
+  // In MXFP8 the tokens are quantized once along d (row-wise, so it commutes
+  // with the permutation) and the gate/up GEMM gathers the quantized rows.
+  const bool fused_gather = prec != MOE_F32;
   MOE_TRY(run_permute(dims, prec, f.topk_idx, x, f.counts, f.offsets, f.row_token, f.token_row,
                       fused_gather ? nullptr : f.x_perm, f.x_perm_scale, f.sched, s));
+  if (prec == MOE_MXFP8)
+    MOE_HIP(launch_quantize_mx(static_cast<const bf16_t*>(x), dims->T, dims->d, 0, static_cast<uint8_t*>(f.x_perm),
+                               f.x_perm_scale, s));
   if (dims->n_shared > 0) MOE_TRY(run_shared_ffn(dims, prec, x, w, f.y_shared, f.hs, s));
-  if (fused_gather)
-    MOE_TRY(run_expert_ffn(dims, prec, x, f.row_token, f.offsets, w, f.o_perm, f.ffn, s));
+  if (prec == MOE_MXFP8)
+    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, f.x_perm_scale, f.row_token, f.offsets, w, f.o_perm, f.ffn, s));
+  else if (fused_gather)
+    MOE_TRY(run_expert_ffn(dims, prec, x, nullptr, f.row_token, f.offsets, w, f.o_perm, f.ffn, s));
   else
-    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
+    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
   MOE_HIP(launch_combine(prec == MOE_F32, f.o_perm, f.token_row, f.topk_w, f.y_shared, y, dims->T, dims->d, dims->k,
                          s));
   return MOE_OK;

@@ -30,6 +30,57 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------
+// MX (OCP MX v1.0) E4M3 elements with one E8M0 scale per 32 values: the block
+// exponent is floor(log2 max|v|) - 8 clamped to [-127, 127] (-127 for an
+// all-zero block); elements are v / 2^e rounded to nearest-even E4M3,
+// saturating at +-448, sign kept.
+// ---------------------------------------------------------------------------
+// |s| < 512 assumed (the block scale puts the block maximum below 2^9).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
+  const uint32_t bits = __float_as_uint(s);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(s);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;  // 448 itself, ties at 464 go to 448, larger values saturate
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
+    code = (u >> 20) - (120u << 3);     // rebias exponent 127 -> 7
+  }
+  return sign | code;
+}
+
+// Block exponent (unbiased) of a 32-value block from its max magnitude.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  return max(ef - 127 - 8, -127);
+}
+
+// 2^-e as an fp32 (exact for e in [-127, 126]).
+__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// Quantize 32 values in registers: returns the E8M0 byte, fills 8 packed words.
+__device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&packed)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_block_exp(amax);
+  const float inv = mx_inv_scale(e);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) p |= e4m3_rne_sat(v[4 * w + b] * inv) << (8 * b);
+    packed[w] = p;
+  }
+  return (uint32_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
 // Kernel launchers (each returns hipGetLastError() of its launches)
 // ---------------------------------------------------------------------------
 
@@ -88,6 +139,7 @@ struct GemmProblem {
   int N;                    // output columns (h columns in gate/up mode)
   int K;
   void* C;                  // [rows][N]
+  uint8_t* C_scale;         // MX output scales [rows][N/32] (MXFP8 gate/up)
   int64_t ldc;
   const float* bias;        // [N] (plain mode)
   int32_t* tile_prefix;     // scratch [G+1] (device), M-tile prefix per group

@@ -1,0 +1,456 @@
+// Expert-grouped MXFP8 GEMMs on gfx950 scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 operands, E8M0 block scales).
+//
+// Mixture-of-Kittens blog post, "Other features / MXFP8 support": routed
+// experts run in MXFP8 (the shared expert stays BF16), weights are
+// pre-quantized, and activation quantization is fused into the dispatch, the
+// grouped GEMMs and the SwiGLU.  Block format: OCP MX v1.0 (the MX paper
+// cited by the pages): 32 E4M3 values along K share one E8M0 scale.
+//
+// C[rows of g] = A[rows of g] . B[g]^T with both operands stored K-major as
+// bytes plus a [rows][K/32] scale array.  The structure follows the bf16
+// kernel (csrc/gemm_bf16.hip): a persistent grid with device-built lists of
+// 256 x 256 and 64 x 256 tiles, 8 waves of 128 x 64 (4 x 2 MFMA blocks),
+// direct buffer -> LDS slabs with the same conflict-free swizzle.  A slab is
+// 128 K-elements = 128 bytes per row, so one 32x32x64 MFMA consumes half a
+// slab row: each lane holds 32 bytes of one row (two 16-byte LDS reads, see
+// read_frags for the operand layout) and the E8M0 scale of its lane group's
+// 32-element block.  Scales travel through LDS with the data (one dword,
+// four blocks, per row and slab).
+//
+// Gate/up mode writes h = SiLU(G) * U quantized along I (the down GEMM's K):
+// the 32 values of one 32-column block of a row sit in 32 lanes of a wave, so
+// the block maximum is a 5-step lane reduction, then each lane encodes its
+// element (blog post, "MXFP8 support": quantization fused into the SwiGLU).
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBKB = 128;  // K elements (bytes) per slab
+constexpr int kBigM = 256, kSmallM = 64, kBN = 256;
+constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kThreads = 64 * kWavesM * kWavesN;
+constexpr int stage_bytes(int bm) { return bm * kBKB + kBN * kBKB + bm * 4 + kBN * 4; }
+constexpr size_t kSmemBytes = 2 * stage_bytes(kBigM) > 3 * stage_bytes(kSmallM) ? 2 * stage_bytes(kBigM)
+                                                                                 : 3 * stage_bytes(kSmallM);
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void tiles_of(int64_t rows, int& nb, int& ns) {
+  int64_t b = rows / kBigM, r = rows - b * kBigM;
+  if (r > kBigM / 2) {
+    ++b;
+    r = 0;
+  }
+  nb = (int)b;
+  ns = (int)((r + kSmallM - 1) / kSmallM);
+}
+
+__global__ void __launch_bounds__(1024) mx_tile_prefix_kernel(const int32_t* __restrict__ row_off, int G,
+                                                               int32_t* __restrict__ big, int32_t* __restrict__ small) {
+  __shared__ int32_t sb[1024], ss[1024];
+  __shared__ int32_t cb, cs;
+  if (threadIdx.x == 0) {
+    cb = cs = 0;
+    big[0] = small[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < G; base += 1024) {
+    const int g = base + threadIdx.x;
+    int nb = 0, ns = 0;
+    if (g < G) tiles_of((int64_t)(row_off[g + 1] - row_off[g]), nb, ns);
+    sb[threadIdx.x] = nb;
+    ss[threadIdx.x] = ns;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int vb = threadIdx.x >= off ? sb[threadIdx.x - off] : 0;
+      const int vs = threadIdx.x >= off ? ss[threadIdx.x - off] : 0;
+      __syncthreads();
+      sb[threadIdx.x] += vb;
+      ss[threadIdx.x] += vs;
+      __syncthreads();
+    }
+    if (g < G) {
+      big[g + 1] = cb + sb[threadIdx.x];
+      small[g + 1] = cs + ss[threadIdx.x];
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) {
+      cb += sb[1023];
+      cs += ss[1023];
+    }
+    __syncthreads();
+  }
+}
+
+struct MxArgs {
+  const uint8_t* A;
+  const uint8_t* As;        // A scales [rows][K/32]
+  const int32_t* a_rows;    // optional gather of A rows (and their scales)
+  uint32_t a_bytes, as_bytes;  // sizes of A and its scales when gathered
+  int64_t lda;              // bytes per A row (= K)
+  const int32_t* row_off;
+  int64_t M;
+  int G;
+  const uint8_t* B0;
+  const uint8_t* B1;
+  const uint8_t* B0s;
+  const uint8_t* B1s;
+  int64_t b_stride, bs_stride;  // bytes between experts in B and in its scales
+  int N, K, ntiles;
+  void* C;                  // gate/up: E4M3 h [rows][N]; down: bf16 [rows][N]
+  uint8_t* Cs;              // gate/up: h scales [rows][N/32]
+  int64_t ldc;
+  const int32_t* big;
+  const int32_t* small;
+  int spread_small;
+};
+
+__device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int BM, int MODE, int NS>
+__device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, int64_t row_begin, int64_t n_g,
+                                        int64_t m0, int ntile) {
+  constexpr int BN = kBN;
+  constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int RPR = kThreads / 8;  // rows per data load round
+  constexpr int AR = BM / RPR, BR = BN / RPR;
+  constexpr int STG = stage_bytes(BM);
+  constexpr int LPS = AR + BR;       // data loads per slab per thread (+1 scale load on most waves)
+  static_assert(FN == 2 && (MODE != GEMM_GATEUP || FN % 2 == 0), "wave tile");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int lrow = wave * 8 + (lane >> 3);
+  const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  int K = p.K;
+  asm volatile("" : "+s"(K));
+  const int KS = K / 32;  // scale bytes per row
+
+  // A data and scales (rows of the group, or gathered token rows).
+  const bool gath = p.a_rows != nullptr;
+  const uint8_t* abase = uniform_ptr(gath ? p.A : p.A + row_begin * p.lda);
+  const uint8_t* asbase = uniform_ptr(gath ? p.As : p.As + row_begin * KS);
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(n_g * p.lda));
+  const uint32_t asbytes = __builtin_amdgcn_readfirstlane(gath ? p.as_bytes : (uint32_t)(n_g * KS));
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t asr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
+  uint32_t aoff[AR];
+#pragma unroll
+  for (int i = 0; i < AR; ++i) {
+    const int64_t lr0 = m0 + i * RPR + lrow;
+    const int64_t lr = lr0 < n_g ? lr0 : 0;
+    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + lr] : lr;
+    aoff[i] = (uint32_t)(src * p.lda) + chunk * 16;
+  }
+  // Scale loads: waves 0..BM/64-1 fetch 64 A-scale rows each, waves 4..7 fetch
+  // 64 B-scale rows each (for gate/up: G rows 0-63, 64-127, then U rows).
+  constexpr int ASW = BM / 64;
+  const bool a_sc = wave < ASW;
+  const bool b_sc = wave >= 4;
+  uint32_t scoff = 0;
+  if (a_sc) {
+    const int64_t lr0 = m0 + wave * 64 + lane;
+    const int64_t lr = lr0 < n_g ? lr0 : 0;
+    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + lr] : lr;
+    scoff = (uint32_t)(src * KS);
+  }
+  const int bi = wave - 4;  // B-scale round of this wave
+  const uint8_t* bsbase;
+  if (MODE == GEMM_GATEUP) {
+    bsbase = (bi >= 2) ? p.B1s : p.B0s;
+    if (b_sc) scoff = (uint32_t)(min(ntile * (BN / 2) + (bi & 1) * 64 + lane, p.N - 1) * KS);
+  } else {
+    bsbase = p.B0s;
+    if (b_sc) scoff = (uint32_t)(min(ntile * BN + bi * 64 + lane, p.N - 1) * KS);
+  }
+  const __amdgpu_buffer_rsrc_t bsr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(bsbase + (int64_t)g * p.bs_stride), (short)0, (int)((int64_t)p.N * KS), 0x00020000);
+  // B data
+  const uint8_t* bsel = MODE == GEMM_GATEUP && ((wave >> 2) & 1) ? p.B1 : p.B0;
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(bsel + (int64_t)g * p.b_stride), (short)0, (int)((int64_t)p.N * K), 0x00020000);
+  const uint32_t boff = (uint32_t)((lane >> 3) * K) + chunk * 16;
+
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto issue = [&](int st, int k0) {
+    uint8_t* S = smem + st * STG;
+#pragma unroll
+    for (int i = 0; i < AR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(S + (i * RPR + wave * 8) * kBKB), 16, aoff[i], k0, 0,
+                                               0);
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+      int row0 = MODE == GEMM_GATEUP ? ntile * (BN / 2) + i * (RPR / 2) + (wave & 3) * 8
+                                     : ntile * BN + i * RPR + wave * 8;
+      row0 = min(row0, p.N - 8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, boff,
+                                               row0 * K + k0, 0, 0);
+    }
+    if (a_sc)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, scoff,
+                                               k0 / 32, 0, 0);
+    if (b_sc)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bsr, (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + bi * 256), 4, scoff,
+                                               k0 / 32, 0, 0);
+  };
+  const bool any_sc = a_sc || b_sc;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  i32x8 fa[FM], fb[FN];
+  int sa[FM], sb[FN];
+  auto read_frags = [&](int st, int kk) {
+    const uint8_t* S = smem + st * STG;
+    // Operand layout of the 32x32x64 MFMA: lane group g = lane / 32 holds
+    // K[16g, 16g+16) in its low 16 bytes and K[32+16g, 32+16g+16) in its high
+    // 16 bytes; the scale of group g covers K[32g, 32g+32).
+    const int c0 = kk * 4 + (lane >> 5), c1 = c0 + 2;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WM + i * 32 + (lane & 31);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(S + r * kBKB + ((c0 ^ swz(r)) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(S + r * kBKB + ((c1 ^ swz(r)) << 4));
+      fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WN + j * 32 + (lane & 31);
+      const uint8_t* Bb = S + BM * kBKB;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(Bb + r * kBKB + ((c0 ^ swz(r)) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(Bb + r * kBKB + ((c1 ^ swz(r)) << 4));
+      fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  };
+  auto read_scales = [&](int st) {
+    const uint8_t* S = smem + st * STG + (BM + BN) * kBKB;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[i] = *reinterpret_cast<const int*>(S + (wm * WM + i * 32 + (lane & 31)) * 4);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = MODE == GEMM_GATEUP ? (j ? 128 : 0) + wn * 32 + (lane & 31) : wn * WN + j * 32 + (lane & 31);
+      sb[j] = *reinterpret_cast<const int*>(S + BM * 4 + r * 4);
+    }
+  };
+  auto mma = [&](int kk) {
+    const int sh = 8 * (kk * 2 + (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
+                                                                    (sa[i] >> sh) & 0xFF, 0, (sb[j] >> sh) & 0xFF);
+  };
+
+  const int KT = K / kBKB;
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0)
+    if (s0 < KT) issue(s0, s0 * kBKB);
+  if (KT >= NS) {
+    if (any_sc) wait_vmcnt<(NS - 1) * (LPS + 1)>(); else wait_vmcnt<(NS - 1) * LPS>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % NS;
+    read_scales(st);
+    read_frags(st, 0);
+    mma(0);
+    read_frags(st, 1);
+    mma(1);
+    if (kt + NS - 1 < KT) {
+      if (any_sc) wait_vmcnt<(NS - 2) * (LPS + 1)>(); else wait_vmcnt<(NS - 2) * LPS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (kt + NS < KT) issue(st, (kt + NS) * kBKB);
+  }
+
+  // Epilogue (32x32 block layout: column lane & 31, rows 8*(v/4) + 4*(lane/32) + v%4).
+  int64_t ldc = p.ldc;
+  asm volatile("" : "+s"(ldc));
+  const int rows_left = (int)min<int64_t>(n_g - m0, BM);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int64_t grow = row_begin + m0 + rl;
+      if (MODE == GEMM_GATEUP) {
+        // h = SiLU(G) * U for column block wn of this tile, quantized per row
+        // over its 32 columns (lanes 0-31 or 32-63 of the wave).
+        const float h = silu_f32(acc[i][0][v]) * acc[i][1][v];
+        float amax = fabsf(h);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const int e = mx_block_exp(amax);
+        const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
+        if (rl < rows_left && col < p.N) {
+          uint8_t* C = static_cast<uint8_t*>(p.C);
+          C[grow * ldc + col] = (uint8_t)e4m3_rne_sat(h * mx_inv_scale(e));
+          if ((lane & 31) == 0) p.Cs[grow * (ldc / 32) + col / 32] = (uint8_t)(e + 127);
+        }
+      } else {
+        if (rl >= rows_left) continue;
+        bf16_t* C = static_cast<bf16_t*>(p.C) + grow * ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
+          if (col < p.N) C[col] = f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_mx[];
+  const int nbig = p.big[p.G];
+  const int nsmall = p.small[p.G];
+  const int tb = nbig * p.ntiles;
+  const int total = tb + nsmall * p.ntiles;
+  const int ts = total - tb;
+  const int nwg = gridDim.x;
+  const int per_xcd = nwg >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  constexpr int GN = 4;
+  for (int it = 0;; ++it) {
+    const int P = it * nwg + xcd * per_xcd + slot;
+    if (P >= total) break;
+    bool is_big;
+    int L;
+    if (p.spread_small) {
+      const int s_before = (int)((int64_t)P * ts / total);
+      is_big = (int)((int64_t)(P + 1) * ts / total) == s_before;
+      L = is_big ? P - s_before : s_before;
+    } else {
+      is_big = P < tb;
+      L = is_big ? P : P - tb;
+    }
+    const int nm = is_big ? nbig : nsmall;
+    const int ng = L / (nm * GN);
+    const int r0 = L - ng * nm * GN;
+    const int gn = min(GN, p.ntiles - ng * GN);
+    const int mt = r0 / gn;
+    const int ntile = ng * GN + (r0 - mt * gn);
+    const int32_t* pre = is_big ? p.big : p.small;
+    const int g = __builtin_amdgcn_readfirstlane(find_group(pre, p.G, mt));
+    const int64_t row_begin = uniform_i64(p.row_off[g]);
+    const int64_t n_g = uniform_i64(p.row_off[g + 1] - p.row_off[g]);
+    const int nb_g = p.big[g + 1] - p.big[g];
+    const int64_t m0 = uniform_i64(is_big ? (int64_t)(mt - pre[g]) * kBigM
+                                          : (int64_t)nb_g * kBigM + (int64_t)(mt - pre[g]) * kSmallM);
+    if (is_big) mx_tile<kBigM, MODE, 2>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    else mx_tile<kSmallM, MODE, 3>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    __syncthreads();
+  }
+}
+
+int num_cus_mx() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      cus = prop.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  return cus;
+}
+
+template <int MODE>
+hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mxfp8_kernel<MODE>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  MxArgs a = {};
+  a.A = static_cast<const uint8_t*>(q.A);
+  a.As = q.A_scale;
+  a.a_rows = q.a_rows;
+  a.a_bytes = (uint32_t)q.a_bytes;
+  a.as_bytes = (uint32_t)(q.a_bytes / 32);
+  a.lda = q.lda;
+  a.row_off = q.row_off;
+  a.M = q.M;
+  a.G = q.G;
+  a.B0 = static_cast<const uint8_t*>(q.B0);
+  a.B1 = static_cast<const uint8_t*>(q.B1);
+  a.B0s = q.B0_scale;
+  a.B1s = q.B1_scale;
+  a.b_stride = q.b_group_stride;
+  a.bs_stride = q.b_group_stride / 32;
+  a.N = q.N;
+  a.K = q.K;
+  a.ntiles = MODE == GEMM_GATEUP ? (q.N + kBN / 2 - 1) / (kBN / 2) : (q.N + kBN - 1) / kBN;
+  a.C = q.C;
+  a.Cs = q.C_scale;
+  a.ldc = q.ldc;
+  a.big = q.tile_prefix;
+  a.small = q.tile_prefix + (q.G + 1);
+  a.spread_small = MODE == GEMM_DOWN ? 1 : 0;
+  mx_tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.G, q.tile_prefix, q.tile_prefix + (q.G + 1));
+  int wg = num_cus_mx();
+  wg = (wg + 7) / 8 * 8;
+  gemm_mxfp8_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Grouped MXFP8 GEMM: row_off and tile_prefix are required (grouped mode);
+// N and K must be multiples of 128 (K: whole slabs; N: whole scale blocks).
+hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
+  if (!q.row_off || q.K % kBKB != 0 || q.N % 64 != 0) return hipErrorInvalidValue;
+  if (q.mode == GEMM_GATEUP) return run_mx<GEMM_GATEUP>(q, s);
+  if (q.mode == GEMM_DOWN) return run_mx<GEMM_DOWN>(q, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -124,45 +124,6 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
   }
 }
 
-// |s| < 512 assumed (the block scale puts the block maximum below 2^9).
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
-  const uint32_t bits = __float_as_uint(s);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(s);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7Eu;  // 448 itself, ties at 464 go to 448, larger values saturate
-  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
-    code = (u >> 20) - (120u << 3);     // rebias exponent 127 -> 7
-  }
-  return sign | code;
-}
-
-// Quantize 32 values in registers: returns the E8M0 byte, fills 8 packed words.
-__device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&packed)[8]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int e = -127;
-  if (amax > 0.0f) {
-    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-    e = max(ef - 127 - 8, -127);
-  }
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact (-e in [-119, 127])
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) p |= e4m3_rne_sat(v[4 * w + b] * inv) << (8 * b);
-    packed[w] = p;
-  }
-  return (uint32_t)(e + 127);
-}
-
 __global__ void __launch_bounds__(256) gather_quant_kernel(const bf16_t* __restrict__ x,
                                                            const int32_t* __restrict__ row_token,
                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
