@@ -31,6 +31,14 @@ class Dims:
         return (2 * self.T * self.d * self.E + 6 * self.T * self.k * self.d * self.I
                 + 6 * self.T * self.S * self.d * self.Is)
 
+    def bwd_flops(self):
+        """Algorithmic backward FLOPs: three input-gradient and three
+        weight-gradient GEMMs per FFN (twice the forward's), plus the router's
+        weight and input gradients.  A recompute of the gate/up projections is
+        not counted."""
+        return (12 * self.T * self.k * self.d * self.I + 12 * self.T * self.S * self.d * self.Is
+                + 4 * self.T * self.d * self.E)
+
 
 CONFIGS = {
     "c0": Dims("c0", 256, 128, 8, 2, 64, 1, 64, "f32", 0.0),

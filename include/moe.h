@@ -33,9 +33,9 @@
  *               v1.0); the shared expert and the router stay bf16 (blog post,
  *               "Other features / MXFP8 support").
  *
- * Shape limits: 1 <= k <= min(E, 16), E <= 1024, T >= 0.  MOE_F32 accepts
- * any d, I, I_s >= 1.  MOE_BF16 and MOE_MXFP8 need d, I and I_s multiples
- * of 64.
+ * Shape limits: 1 <= k <= min(E, 16), E <= 1024, T >= 0, at most one
+ * shared expert.  MOE_F32 needs d % 8 == 0.  MOE_BF16 needs d, I and I_s
+ * multiples of 64; MOE_MXFP8 in addition d and I multiples of 128.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -81,7 +81,30 @@ typedef struct {
   const uint8_t *q_gate, *q_gate_scale;          /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
   const uint8_t *q_up, *q_up_scale;              /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
   const uint8_t *q_down, *q_down_scale;          /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
+  /* Backward only: transposed copies for the input-gradient GEMMs, made
+   * once per weight update with moe_transpose_weights (bf16). */
+  const void* wt_gate;                           /* [E][d][I] = W_gate[e]^T */
+  const void* wt_up;                             /* [E][d][I] = W_up[e]^T */
+  const void* wt_down;                           /* [E][I][d] = W_down[e]^T */
+  const void* wst_gate;                          /* [S][d][I_s] */
+  const void* wst_up;                            /* [S][d][I_s] */
+  const void* wst_down;                          /* [S][I_s][d] */
 } moe_weights;
+
+/* Gradients written by moe_layer_backward (host struct of caller-owned device
+ * pointers).  Weight gradients are bf16 in the weights' layouts; the shared
+ * ones are NULL when n_shared == 0.  dw_router NULL skips the router chain
+ * (then dx has no router term). */
+typedef struct {
+  void* dw_gate;          /* [E][I][d] */
+  void* dw_up;            /* [E][I][d] */
+  void* dw_down;          /* [E][d][I] */
+  void* dws_gate;         /* [S][I_s][d] */
+  void* dws_up;           /* [S][I_s][d] */
+  void* dws_down;         /* [S][d][I_s] */
+  float* dtopk_w;         /* [T][k] fp32: dL/d topk_w, aligned with topk_idx */
+  float* dw_router;       /* [E][d] fp32, or NULL */
+} moe_grads;
 
 /* Routing state of one forward pass (host struct of caller-owned device
  * pointers), kept for inspection or for a later backward.  Any field may be
@@ -100,8 +123,8 @@ typedef struct {
 const char* moe_status_str(moe_status s);
 
 /* Workspace needed by an entry point: which = 0 moe_layer_forward,
- * 1 moe_permute, 2 moe_expert_ffn, 3 moe_shared_ffn.  Writes the byte count
- * to *bytes (host pointer).  Pure host computation. */
+ * 1 moe_permute, 2 moe_expert_ffn, 3 moe_shared_ffn, 4 moe_layer_backward.
+ * Writes the byte count to *bytes (host pointer).  Pure host computation. */
 moe_status moe_workspace_bytes(const moe_dims* dims, moe_prec prec, int which, size_t* bytes);
 
 /* Router projection, top-k selection and normalized weights.
@@ -187,6 +210,34 @@ moe_status moe_combine(const moe_dims* dims, moe_prec prec, const void* o_perm, 
 moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x, const moe_weights* w,
                              const float* logit_bias, void* y, const moe_routing* routing, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* Backward of the layer for an output gradient dy [T][d] (bf16), given the
+ * forward's input x, weights (including the transposed copies wt_* and
+ * wst_*) and its routing state (every field of `routing` except logits is
+ * required: topk_idx, topk_w, expert_counts, expert_offsets, row_token,
+ * token_row).  Writes dx [T][d] bf16 and the gradients in `g`.
+ * Blog post, "Scheduling the overlaps" (backward: gather the output
+ * gradient to the expert rows, the input-gradient GEMMs with the SwiGLU
+ * backward, return the input gradients to token order, then the weight
+ * gradients over each expert's whole token range) and "Router weight
+ * gradient computation" (dL/dg of a route = <h, dY W_d>, fused into the
+ * SwiGLU backward).  G and U are recomputed from x (the forward replay of
+ * the blog post's "Reversed ring order" section).  Router chain, with the
+ * selection held fixed: dl_j = g_j (dg_j - sum_i g_i dg_i) for the selected
+ * experts, dW_router = dl^T x, dx += dl W_router.
+ * Precision: MOE_BF16 (bf16 operands, fp32 accumulation); MOE_F32 and
+ * MOE_MXFP8 return MOE_EUNSUPPORTED.  Every reduction runs in a fixed order
+ * (results are bitwise reproducible); experts without rows get exact zero
+ * weight gradients.  ws: workspace of moe_workspace_bytes(which=4). */
+moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* dy, const void* x,
+                              const moe_weights* w, const moe_routing* routing, void* dx, const moe_grads* g,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* dst[b][c][r] = src[b][r][c] for bf16 src [batch][rows][cols]: the
+ * transposed weight copies of the backward (W_gate^T, W_up^T, W_down^T),
+ * made once per weight update.  src and dst must not overlap. */
+moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, int64_t cols, void* dst,
+                                 void* stream);
 
 /* MX quantization of a bf16 matrix src [rows][cols] (OCP MX v1.0; blog post
  * "MXFP8 support": a quantization kernel pre-quantizes the weights).

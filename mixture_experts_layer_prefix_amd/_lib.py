@@ -29,7 +29,13 @@ class moe_dims(ctypes.Structure):
 class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
-        "q_gate", "q_gate_scale", "q_up", "q_up_scale", "q_down", "q_down_scale")]
+        "q_gate", "q_gate_scale", "q_up", "q_up_scale", "q_down", "q_down_scale",
+        "wt_gate", "wt_up", "wt_down", "wst_gate", "wst_up", "wst_down")]
+
+
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down", "dtopk_w", "dw_router")]
 
 
 class moe_routing(ctypes.Structure):
@@ -55,6 +61,9 @@ _SIGS = {
     "moe_combine": ([_DIMS, ctypes.c_int, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_layer_forward": ([_DIMS, ctypes.c_int, _P, ctypes.POINTER(moe_weights), _P, _P,
                            ctypes.POINTER(moe_routing), _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_layer_backward": ([_DIMS, ctypes.c_int, _P, _P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing),
+                            _P, ctypes.POINTER(moe_grads), _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_transpose_weights": ([_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P], ctypes.c_int),
     "moe_quantize_mxfp8": ([_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P], ctypes.c_int),
 }
 

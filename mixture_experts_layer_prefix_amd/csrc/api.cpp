@@ -115,6 +115,53 @@ FwdWs carve_forward(Carver& c, const moe_dims* D, moe_prec prec, const moe_routi
   return w;
 }
 
+// Backward scratch.  Rp: K capacity of the expert-padded transposed operands
+// of the weight-gradient GEMMs (every expert's rows rounded up to 64).
+struct BwdWs {
+  int64_t Rp, Tp;
+  int32_t* prefix;   // [2(E+2)] GEMM tile prefixes
+  int32_t* pad_off;  // [E+1]
+  int32_t* single;   // [4] {0, Tp, 0, T}: one-group K range and segment
+  float *w_row, *dl, *dl_row;
+  void *gu, *dgu, *gh, *da;
+  float* dg_part;
+  void *xT, *dyT, *ghT, *dguT;
+  float* router_partial;
+  void *gus, *dgus, *hs, *dxs, *xTs, *dyTs, *hsT, *dgusT;
+};
+
+BwdWs carve_backward(Carver& c, const moe_dims* D) {
+  const int64_t T = D->T, R = D->T * D->k, d = D->d, I = D->I, Is = D->n_shared ? D->I_shared : 0;
+  BwdWs w;
+  w.Rp = bwd_padded_rows(R, D->E);
+  w.Tp = (T + 63) / 64 * 64;
+  w.prefix = static_cast<int32_t*>(c.take((size_t)2 * (D->E + 2) * 4));
+  w.pad_off = static_cast<int32_t*>(c.take((size_t)(D->E + 1) * 4));
+  w.single = static_cast<int32_t*>(c.take(16));
+  w.w_row = static_cast<float*>(c.take((size_t)R * 4));
+  w.dl = static_cast<float*>(c.take((size_t)R * 4));
+  w.dl_row = static_cast<float*>(c.take((size_t)R * 4));
+  w.gu = c.take((size_t)R * 2 * I * 2);
+  w.dgu = c.take((size_t)R * 2 * I * 2);
+  w.gh = c.take((size_t)R * I * 2);
+  w.da = c.take((size_t)R * d * 2);
+  w.dg_part = static_cast<float*>(c.take((size_t)R * (I / 32) * 4));
+  w.xT = c.take((size_t)d * w.Rp * 2);
+  w.dyT = c.take((size_t)d * w.Rp * 2);
+  w.ghT = c.take((size_t)I * w.Rp * 2);
+  w.dguT = c.take((size_t)2 * I * w.Rp * 2);
+  w.router_partial = static_cast<float*>(c.take((size_t)(w.Rp / 64) * d * 4));
+  w.gus = c.take((size_t)T * 2 * Is * 2);
+  w.dgus = c.take((size_t)T * 2 * Is * 2);
+  w.hs = c.take((size_t)T * Is * 2);
+  w.dxs = c.take(Is ? (size_t)T * d * 2 : 0);
+  w.xTs = c.take(Is ? (size_t)d * w.Tp * 2 : 0);
+  w.dyTs = c.take(Is ? (size_t)d * w.Tp * 2 : 0);
+  w.hsT = c.take((size_t)Is * w.Tp * 2);
+  w.dgusT = c.take((size_t)2 * Is * w.Tp * 2);
+  return w;
+}
+
 size_t workspace_size(const moe_dims* D, moe_prec prec, int which) {
   Carver c(nullptr);
   switch (which) {
@@ -122,6 +169,7 @@ size_t workspace_size(const moe_dims* D, moe_prec prec, int which) {
     case 1: c.take(permute_scratch_bytes(D->T, D->E)); break;
     case 2: carve_ffn(c, D, prec); break;
     case 3: carve_shared(c, D, prec); break;
+    case 4: carve_backward(c, D); break;
     default: return 0;
   }
   return c.used;
@@ -321,6 +369,137 @@ moe_status check_weights(const moe_dims* D, moe_prec prec, const moe_weights* w,
 bool ptr_ok(const void* p) { return p && aligned16(p); }
 bool opt_ok(const void* p) { return !p || aligned16(p); }
 
+// ---- backward ---------------------------------------------------------------
+
+// GEMM descriptor with the fields every backward GEMM sets.
+GemmProblem gemm(int mode, const void* A, int64_t lda, const int32_t* row_off, int64_t M, int G, const void* B0,
+                 const void* B1, int64_t b_group_stride, int N, int K, void* C, int64_t ldc, int32_t* prefix) {
+  GemmProblem q = {};
+  q.mode = mode;
+  q.A = A;
+  q.lda = lda;
+  q.row_off = row_off;
+  q.M = M;
+  q.G = G;
+  q.B0 = B0;
+  q.B1 = B1;
+  q.b_group_stride = b_group_stride;
+  q.N = N;
+  q.K = K;
+  q.C = C;
+  q.ldc = ldc;
+  q.tile_prefix = prefix;
+  return q;
+}
+
+// Weight gradients C_g = A[:, K_g] B[:, K_g]^T of every group from the
+// transposed operands A [M][ldk], B [N][ldk] over the K ranges k_off.
+moe_status run_wgrad(const void* A, int64_t M, const void* B, int N, int64_t ldk, const int32_t* k_off, int G,
+                     void* C, hipStream_t s) {
+  GemmProblem q = gemm(GEMM_WGRAD, A, ldk, nullptr, M, G, B, nullptr, 0, N, 64, C, N, nullptr);
+  q.ldb = ldk;
+  q.k_off = k_off;
+  q.c_group_stride = M * N;
+  MOE_HIP(launch_gemm_bf16(q, s));
+  return MOE_OK;
+}
+
+moe_status check_backward_weights(const moe_dims* D, const moe_weights* w, bool router) {
+  if (!w) return MOE_EINVAL;
+  const void* r[] = {w->w_gate, w->w_up, w->wt_gate, w->wt_up, w->wt_down};
+  for (const void* p : r)
+    if (!ptr_ok(p)) return MOE_EINVAL;
+  if (D->n_shared > 0) {
+    const void* q[] = {w->ws_gate, w->ws_up, w->wst_gate, w->wst_up, w->wst_down};
+    for (const void* p : q)
+      if (!ptr_ok(p)) return MOE_EINVAL;
+  }
+  if (router && !ptr_ok(w->w_router)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, const moe_weights* w,
+                        const moe_routing* rt, bf16_t* dx, const moe_grads* g, const BwdWs& b, hipStream_t s) {
+  const int64_t T = D->T, R = T * D->k;
+  const int d = D->d, I = D->I, E = D->E, k = D->k;
+  const bool router = g->dw_router != nullptr;
+  MOE_HIP(launch_pad_offsets(rt->expert_counts, E, T, b.pad_off, b.single, s));
+  MOE_HIP(launch_row_weight(rt->token_row, rt->topk_w, R, b.w_row, s));
+
+  // Forward replay up to the SwiGLU input: [G | U] of every routed row.
+  GemmProblem q = gemm(GEMM_GU, x, d, rt->expert_offsets, R, E, w->w_gate, w->w_up, (int64_t)I * d, I, d, b.gu,
+                       2 * I, b.prefix);
+  q.a_rows = rt->row_token;
+  q.a_bytes = T * (int64_t)d * 2;
+  MOE_HIP(launch_gemm_bf16(q, s));
+  // Reverse combine + down-projection input gradient dH' = dY_perm W_d with
+  // the SwiGLU backward and the router-weight partials in the epilogue.
+  q = gemm(GEMM_SWIGLU_BWD, dy, d, rt->expert_offsets, R, E, w->wt_down, nullptr, (int64_t)I * d, I, d, b.dgu, 2 * I,
+           b.prefix);
+  q.a_rows = rt->row_token;
+  q.a_bytes = T * (int64_t)d * 2;
+  q.gu = b.gu;
+  q.w_row = b.w_row;
+  q.dgu = b.dgu;
+  q.h_out = b.gh;
+  q.dg_part = b.dg_part;
+  MOE_HIP(launch_gemm_bf16(q, s));
+  MOE_HIP(launch_dg(b.dg_part, I / 32, rt->token_row, rt->topk_w, T, k, g->dtopk_w, router ? b.dl : nullptr,
+                    b.dl_row, s));
+  // Gate/up input gradient dA = dG W_g + dU W_u (K = 2I over two matrices).
+  q = gemm(GEMM_DUALK, b.dgu, 2 * I, rt->expert_offsets, R, E, w->wt_gate, w->wt_up, (int64_t)d * I, d, 2 * I, b.da,
+           d, b.prefix);
+  MOE_HIP(launch_gemm_bf16(q, s));
+
+  const int Is = D->n_shared ? D->I_shared : 0;
+  if (Is) {
+    q = gemm(GEMM_GU, x, d, nullptr, T, 1, w->ws_gate, w->ws_up, 0, Is, d, b.gus, 2 * Is, nullptr);
+    MOE_HIP(launch_gemm_bf16(q, s));
+    q = gemm(GEMM_SWIGLU_BWD, dy, d, nullptr, T, 1, w->wst_down, nullptr, 0, Is, d, b.dgus, 2 * Is, nullptr);
+    q.gu = b.gus;
+    q.dgu = b.dgus;
+    q.h_out = b.hs;
+    MOE_HIP(launch_gemm_bf16(q, s));
+    q = gemm(GEMM_DUALK, b.dgus, 2 * Is, nullptr, T, 1, w->wst_gate, w->wst_up, 0, d, 2 * Is, b.dxs, d, nullptr);
+    MOE_HIP(launch_gemm_bf16(q, s));
+  }
+  // Reverse dispatch: token-order sum in ascending expert order.
+  MOE_HIP(launch_dx(static_cast<const bf16_t*>(b.da), rt->token_row, rt->topk_idx, router ? b.dl : nullptr,
+                    static_cast<const bf16_t*>(w->w_router), Is ? static_cast<const bf16_t*>(b.dxs) : nullptr, dx, T,
+                    d, k, s));
+
+  // Deferred weight gradients over each expert's whole (64-padded) row range.
+  MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, rt->expert_offsets, b.pad_off, E, b.Rp,
+                                static_cast<bf16_t*>(b.xT), b.Rp, s));
+  MOE_HIP(launch_transpose_rows(dy, d, d, rt->row_token, rt->expert_offsets, b.pad_off, E, b.Rp,
+                                static_cast<bf16_t*>(b.dyT), b.Rp, s));
+  MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.gh), I, I, nullptr, rt->expert_offsets, b.pad_off, E,
+                                b.Rp, static_cast<bf16_t*>(b.ghT), b.Rp, s));
+  MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.dgu), 2 * I, 2 * I, nullptr, rt->expert_offsets,
+                                b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT), b.Rp, s));
+  const bf16_t* dguT = static_cast<const bf16_t*>(b.dguT);
+  MOE_TRY(run_wgrad(b.dyT, d, b.ghT, I, b.Rp, b.pad_off, E, g->dw_down, s));
+  MOE_TRY(run_wgrad(dguT, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_gate, s));
+  MOE_TRY(run_wgrad(dguT + (int64_t)I * b.Rp, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_up, s));
+  if (Is) {
+    const int32_t* seg = b.single + 2;
+    MOE_HIP(launch_transpose_rows(x, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.xTs), b.Tp, s));
+    MOE_HIP(launch_transpose_rows(dy, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.dyTs), b.Tp, s));
+    MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.hs), Is, Is, nullptr, seg, b.single, 1, b.Tp,
+                                  static_cast<bf16_t*>(b.hsT), b.Tp, s));
+    MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.dgus), 2 * Is, 2 * Is, nullptr, seg, b.single, 1, b.Tp,
+                                  static_cast<bf16_t*>(b.dgusT), b.Tp, s));
+    const bf16_t* dgusT = static_cast<const bf16_t*>(b.dgusT);
+    MOE_TRY(run_wgrad(b.dyTs, d, b.hsT, Is, b.Tp, b.single, 1, g->dws_down, s));
+    MOE_TRY(run_wgrad(dgusT, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_gate, s));
+    MOE_TRY(run_wgrad(dgusT + (int64_t)Is * b.Tp, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_up, s));
+  }
+  if (router)
+    MOE_HIP(launch_router_wgrad(x, rt->row_token, b.dl_row, rt->expert_offsets, b.pad_off, E, d, b.Rp,
+                                b.router_partial, g->dw_router, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,7 +517,7 @@ const char* moe_status_str(moe_status s) {
 
 moe_status moe_workspace_bytes(const moe_dims* dims, moe_prec prec, int which, size_t* bytes) {
   MOE_TRY(check_dims(dims, prec));
-  if (!bytes || which < 0 || which > 3) return MOE_EINVAL;
+  if (!bytes || which < 0 || which > 4) return MOE_EINVAL;
   *bytes = workspace_size(dims, prec, which);
   return MOE_OK;
 }
@@ -495,6 +674,56 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
     MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
   MOE_HIP(launch_combine(prec == MOE_F32, f.o_perm, f.token_row, f.topk_w, f.y_shared, y, dims->T, dims->d, dims->k,
                          s));
+  return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* dy, const void* x,
+                              const moe_weights* w, const moe_routing* routing, void* dx, const moe_grads* g, void* ws,
+                              size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  if (prec != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (!g || !routing) return MOE_EINVAL;
+  MOE_TRY(check_backward_weights(dims, w, g->dw_router != nullptr));
+  if (!ptr_ok(g->dw_gate) || !ptr_ok(g->dw_up) || !ptr_ok(g->dw_down) || !opt_ok(g->dw_router)) return MOE_EINVAL;
+  if (dims->n_shared > 0 && (!ptr_ok(g->dws_gate) || !ptr_ok(g->dws_up) || !ptr_ok(g->dws_down))) return MOE_EINVAL;
+  if (!ptr_ok(routing->expert_counts) || !ptr_ok(routing->expert_offsets)) return MOE_EINVAL;
+  if (dims->T > 0) {
+    const void* f[] = {dy, x, dx, g->dtopk_w, routing->topk_idx, routing->topk_w, routing->row_token,
+                       routing->token_row};
+    for (const void* p : f)
+      if (!ptr_ok(p)) return MOE_EINVAL;
+  }
+  const size_t need = workspace_size(dims, prec, 4);
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!aligned16(ws)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t E = dims->E, d = dims->d, I = dims->I, Is = dims->n_shared ? dims->I_shared : 0;
+  if (dims->T == 0) {  // no tokens: every weight gradient is zero
+    MOE_HIP(launch_fill_zero(g->dw_gate, (size_t)(E * I * d * 2), s));
+    MOE_HIP(launch_fill_zero(g->dw_up, (size_t)(E * I * d * 2), s));
+    MOE_HIP(launch_fill_zero(g->dw_down, (size_t)(E * I * d * 2), s));
+    if (Is) {
+      MOE_HIP(launch_fill_zero(g->dws_gate, (size_t)(Is * d * 2), s));
+      MOE_HIP(launch_fill_zero(g->dws_up, (size_t)(Is * d * 2), s));
+      MOE_HIP(launch_fill_zero(g->dws_down, (size_t)(Is * d * 2), s));
+    }
+    if (g->dw_router) MOE_HIP(launch_fill_zero(g->dw_router, (size_t)(E * d * 4), s));
+    return MOE_OK;
+  }
+  Carver c(ws);
+  BwdWs b = carve_backward(c, dims);
+  return run_backward(dims, static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(x), w, routing,
+                      static_cast<bf16_t*>(dx), g, b, s);
+}
+
+moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, int64_t cols, void* dst,
+                                 void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0) return MOE_EINVAL;
+  if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
+  if (!ptr_ok(src) || !ptr_ok(dst)) return MOE_EINVAL;
+  if (batch > 65535 || (rows + 63) / 64 > INT_MAX || (cols + 63) / 64 > 65535) return MOE_EUNSUPPORTED;
+  MOE_HIP(launch_transpose_batched(static_cast<const bf16_t*>(src), batch, rows, cols, static_cast<bf16_t*>(dst),
+                                   static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 

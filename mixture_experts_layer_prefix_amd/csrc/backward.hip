@@ -1,0 +1,349 @@
+// Memory-bound kernels of the layer backward.
+//
+// Mixture-of-Kittens blog post, "Scheduling overlap" (backward ordering):
+// the output gradient is gathered back to the expert rows (reverse combine),
+// the input-gradient GEMMs and the SwiGLU backward run per expert, the input
+// gradients return to token order (reverse dispatch), and the weight
+// gradients run last, each accumulated over an expert's whole token range.
+// Blog post, "Router weight gradient computation": the gradient of a route's
+// router weight is the inner product of the SwiGLU activation with the down
+// projection's input gradient, taken inside the SwiGLU backward (the GEMM
+// epilogue writes per-32-column partials; dg_kernel sums them).
+//
+// Kernels here:
+//  - pad_offsets_kernel: expert K ranges of the weight-gradient GEMMs, each
+//    expert's rows rounded up to a multiple of 64 (zero padded);
+//  - row_weight_kernel: router weight of every routed row;
+//  - dg_kernel: router-weight gradients, and the logit gradients through the
+//    renormalized softmax when the router gradient is requested;
+//  - transpose_rows_kernel: [rows][cols] -> [cols][padded rows], optionally
+//    gathering rows (dispatch), in expert-padded column order;
+//  - transpose_batched_kernel: weight transposes (prepared once per update);
+//  - dx_kernel: token-order sum of the routed input gradients in ascending
+//    expert order, plus the shared expert's and the router's terms;
+//  - router_partial_kernel / router_reduce_kernel: W_router gradient as a
+//    fixed-order two-level sum over each expert's rows.
+// Every reduction has a fixed order: results do not depend on scheduling.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMaxK = 16;
+constexpr int kPadRows = 64;
+
+__global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __restrict__ counts, int E, int64_t T,
+                                                           int32_t* __restrict__ pad_off,
+                                                           int32_t* __restrict__ single_off) {
+  __shared__ int32_t s[1024];
+  const int e = threadIdx.x;
+  const int32_t c = e < E ? (counts[e] + kPadRows - 1) / kPadRows * kPadRows : 0;
+  s[e] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = e >= off ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) pad_off[e + 1] = s[e];
+  if (e == 0) {
+    pad_off[0] = 0;
+    single_off[0] = 0;
+    single_off[1] = (int32_t)((T + kPadRows - 1) / kPadRows * kPadRows);
+    single_off[2] = 0;
+    single_off[3] = (int32_t)T;
+  }
+}
+
+__global__ void __launch_bounds__(256) row_weight_kernel(const int32_t* __restrict__ token_row,
+                                                         const float* __restrict__ topk_w, int64_t R,
+                                                         float* __restrict__ w_row) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < R) w_row[token_row[i]] = topk_w[i];
+}
+
+// One wave per token.  dg[t][j] = sum over the 32-column partials of the
+// token's j-th row (lanes read partials, a fixed butterfly sums them).
+// With the router gradient: dl_j = g_j (dg_j - sum_i g_i dg_i).
+__global__ void __launch_bounds__(256) dg_kernel(const float* __restrict__ dg_part, int nparts,
+                                                 const int32_t* __restrict__ token_row, const float* __restrict__ topk_w,
+                                                 int64_t T, int k, float* __restrict__ dtopk_w, float* __restrict__ dl,
+                                                 float* __restrict__ dl_row) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  float dg[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    dg[j] = 0.0f;
+    if (j < k) {
+      const int64_t row = token_row[t * k + j];
+      float v = 0.0f;
+      for (int c = lane; c < nparts; c += 64) v += dg_part[row * nparts + c];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      dg[j] = v;
+    }
+  }
+  if (lane == 0) {
+    float inner = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) {
+        dtopk_w[t * k + j] = dg[j];
+        inner = fmaf(topk_w[t * k + j], dg[j], inner);
+      }
+    if (dl) {
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k) {
+          const float v = topk_w[t * k + j] * (dg[j] - inner);
+          dl[t * k + j] = v;
+          dl_row[token_row[t * k + j]] = v;
+        }
+    }
+  }
+}
+
+// Expert segment of padded column p0 (pad_off nondecreasing, p0 < pad_off[nseg]).
+__device__ __forceinline__ int find_segment(const int32_t* pad_off, int nseg, int64_t p0) {
+  int lo = 0, hi = nseg;  // invariant: pad_off[lo] <= p0 < pad_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pad_off[mid] <= p0) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// dst[c][p] = src[row(p)][c] for the 64x64 tile (p0.., c0..), where padded
+// column p of segment e is row seg_off[e] + (p - pad_off[e]) (zero past the
+// segment's rows) and row r reads source row gather[r] (or r).
+__global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __restrict__ src, int64_t ld_src, int cols,
+                                                             const int32_t* __restrict__ gather,
+                                                             const int32_t* __restrict__ seg_off,
+                                                             const int32_t* __restrict__ pad_off, int nseg,
+                                                             bf16_t* __restrict__ dst, int64_t ld_dst) {
+  __shared__ bf16_t tile[64][66];
+  const int64_t p0 = (int64_t)blockIdx.x * 64;
+  if (p0 >= pad_off[nseg]) return;
+  const int c0 = blockIdx.y * 64;
+  const int e = find_segment(pad_off, nseg, p0);
+  const int64_t r0 = seg_off[e] + (p0 - pad_off[e]);
+  const int64_t r_end = seg_off[e + 1];
+  const int tid = threadIdx.x;
+  const int ch = tid & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = (tid >> 3) + 32 * h;
+    const int64_t r = r0 + i;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (r < r_end && c0 + ch * 8 < cols) {
+      const int64_t srow = gather ? (int64_t)gather[r] : r;
+      v = *reinterpret_cast<const u32x4*>(src + srow * ld_src + c0 + ch * 8);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[i][ch * 8 + 2 * q] = (bf16_t)(v[q] & 0xFFFFu);
+      tile[i][ch * 8 + 2 * q + 1] = (bf16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = (tid >> 3) + 32 * h;
+    if (c0 + c >= cols) continue;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)tile[ch * 8 + 2 * q][c] | ((uint32_t)tile[ch * 8 + 2 * q + 1][c] << 16);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + c) * ld_dst + p0 + ch * 8) = o;
+  }
+}
+
+// dst[b][c][r] = src[b][r][c], element-wise bounds (any rows, cols).
+__global__ void __launch_bounds__(256) transpose_batched_kernel(const bf16_t* __restrict__ src, int64_t rows,
+                                                                int64_t cols, bf16_t* __restrict__ dst) {
+  __shared__ bf16_t tile[64][65];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const bf16_t* s = src + b * rows * cols;
+  bf16_t* d = dst + b * rows * cols;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = s[r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) d[c * rows + r] = tile[tx][i];
+  }
+}
+
+// dx[t] = sum_j (dA_perm[token_row[t][j]] + dl[t][j] W_r[idx[t][j]]) + dx_shared[t]
+// (j ascending = ascending expert id), fp32 accumulation, one bf16 rounding.
+__global__ void __launch_bounds__(256) dx_kernel(const bf16_t* __restrict__ da_perm, const int32_t* __restrict__ token_row,
+                                                 const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
+                                                 const bf16_t* __restrict__ w_router,
+                                                 const bf16_t* __restrict__ dx_shared, bf16_t* __restrict__ dx,
+                                                 int64_t T, int d, int k) {
+  const int vpr = d / 8;
+  const int64_t nvec = T * vpr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+    const int64_t t = v / vpr;
+    const int c = (int)(v - t * vpr) * 8;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int64_t row = token_row[t * k + j];
+      const u32x4 w = *reinterpret_cast<const u32x4*>(da_perm + row * d + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += __uint_as_float(w[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+      if (dl) {
+        const float g = dl[t * k + j];
+        const u32x4 r = *reinterpret_cast<const u32x4*>(w_router + (int64_t)topk_idx[t * k + j] * d + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(g, __uint_as_float(r[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(g, __uint_as_float(r[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+      }
+    }
+    if (dx_shared) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(dx_shared + t * d + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += __uint_as_float(w[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(dx + t * d + c) = o;
+  }
+}
+
+// partial[q][c] = sum over the rows of padded chunk q (64 positions inside
+// one expert's padded range) of dl_row[r] * x[row_token[r]][c], rows ascending.
+__global__ void __launch_bounds__(256) router_partial_kernel(const bf16_t* __restrict__ x,
+                                                             const int32_t* __restrict__ row_token,
+                                                             const float* __restrict__ dl_row,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ pad_off, int E, int d,
+                                                             float* __restrict__ partial) {
+  const int64_t q = blockIdx.x;
+  const int64_t p0 = q * kPadRows;
+  if (p0 >= pad_off[E]) return;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= d) return;
+  const int e = find_segment(pad_off, E, p0);
+  const int64_t r0 = offsets[e] + (p0 - pad_off[e]);
+  const int64_t r1 = min(r0 + kPadRows, (int64_t)offsets[e + 1]);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int64_t r = r0; r < r1; ++r) {
+    const float g = dl_row[r];
+    const u32x4 w = *reinterpret_cast<const u32x4*>(x + (int64_t)row_token[r] * d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+  }
+  f32x4* out = reinterpret_cast<f32x4*>(partial + q * d + c);
+  out[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  out[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+// dW_router[e][c] = sum of expert e's chunk partials in chunk order (0 when empty).
+__global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restrict__ partial,
+                                                            const int32_t* __restrict__ pad_off, int E, int d,
+                                                            float* __restrict__ dw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)E * d) return;
+  const int e = (int)(i / d), c = (int)(i - (int64_t)e * d);
+  float acc = 0.0f;
+  for (int q = pad_off[e] / kPadRows; q < pad_off[e + 1] / kPadRows; ++q) acc += partial[(int64_t)q * d + c];
+  dw[i] = acc;
+}
+
+unsigned grid_for(int64_t work, int64_t cap) {
+  int64_t g = (work + 255) / 256;
+  return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+}  // namespace
+
+int64_t bwd_padded_rows(int64_t rows, int groups) {
+  return (rows + kPadRows - 1) / kPadRows * kPadRows + (int64_t)kPadRows * groups;
+}
+
+hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int32_t* pad_off, int32_t* single_off,
+                              hipStream_t s) {
+  pad_offsets_kernel<<<1, 1024, 0, s>>>(counts, E, T, pad_off, single_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_weight(const int32_t* token_row, const float* topk_w, int64_t R, float* w_row, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  row_weight_kernel<<<(unsigned)((R + 255) / 256), 256, 0, s>>>(token_row, topk_w, R, w_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_dg(const float* dg_part, int nparts, const int32_t* token_row, const float* topk_w, int64_t T, int k,
+                     float* dtopk_w, float* dl, float* dl_row, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dg_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(dg_part, nparts, token_row, topk_w, T, k, dtopk_w, dl, dl_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_rows(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
+                                 const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap, bf16_t* dst,
+                                 int64_t ld_dst, hipStream_t s) {
+  if (p_cap == 0 || cols == 0) return hipSuccess;
+  if (p_cap % 64 || ld_dst % 8 || ld_src % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 63) / 64));
+  transpose_rows_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_batched(const bf16_t* src, int64_t batch, int64_t rows, int64_t cols, bf16_t* dst,
+                                    hipStream_t s) {
+  if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)batch);
+  transpose_batched_kernel<<<grid, 256, 0, s>>>(src, rows, cols, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx(const bf16_t* da_perm, const int32_t* token_row, const int32_t* topk_idx, const float* dl,
+                     const bf16_t* w_router, const bf16_t* dx_shared, bf16_t* dx, int64_t T, int d, int k,
+                     hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dx_kernel<<<grid_for(T * (d / 8), 16384), 256, 0, s>>>(da_perm, token_row, topk_idx, dl, w_router, dx_shared, dx, T,
+                                                         d, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const bf16_t* x, const int32_t* row_token, const float* dl_row, const int32_t* offsets,
+                               const int32_t* pad_off, int E, int d, int64_t p_cap, float* partial, float* dw,
+                               hipStream_t s) {
+  if (p_cap > 0) {
+    const dim3 grid((unsigned)(p_cap / kPadRows), (unsigned)((d / 8 + 255) / 256));
+    router_partial_kernel<<<grid, 256, 0, s>>>(x, row_token, dl_row, offsets, pad_off, E, d, partial);
+  }
+  router_reduce_kernel<<<grid_for((int64_t)E * d, 1 << 30), 256, 0, s>>>(partial, pad_off, E, d, dw);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -115,11 +115,40 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_combine(bool act_f32, const void* o_perm, const int32_t* token_row, const float* topk_w,
                           const void* y_shared, void* y, int64_t T, int d, int k, hipStream_t s);
 
+// Backward helpers.  Padded row capacity of a K-grouped operand: every
+// group's rows rounded up to 64.
+int64_t bwd_padded_rows(int64_t rows, int groups);
+// pad_off[E+1]: padded prefix of counts; single[4] = {0, round_up(T, 64), 0, T}.
+hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int32_t* pad_off, int32_t* single,
+                              hipStream_t s);
+hipError_t launch_row_weight(const int32_t* token_row, const float* topk_w, int64_t R, float* w_row, hipStream_t s);
+hipError_t launch_dg(const float* dg_part, int nparts, const int32_t* token_row, const float* topk_w, int64_t T, int k,
+                     float* dtopk_w, float* dl, float* dl_row, hipStream_t s);
+hipError_t launch_transpose_rows(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
+                                 const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap, bf16_t* dst,
+                                 int64_t ld_dst, hipStream_t s);
+hipError_t launch_transpose_batched(const bf16_t* src, int64_t batch, int64_t rows, int64_t cols, bf16_t* dst,
+                                    hipStream_t s);
+hipError_t launch_dx(const bf16_t* da_perm, const int32_t* token_row, const int32_t* topk_idx, const float* dl,
+                     const bf16_t* w_router, const bf16_t* dx_shared, bf16_t* dx, int64_t T, int d, int k,
+                     hipStream_t s);
+hipError_t launch_router_wgrad(const bf16_t* x, const int32_t* row_token, const float* dl_row, const int32_t* offsets,
+                               const int32_t* pad_off, int E, int d, int64_t p_cap, float* partial, float* dw,
+                               hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Grouped GEMMs.  A group g owns rows [row_off[g], row_off[g+1]) of the
 // routed rows; with row_off == nullptr there is one group of M rows.
 // ---------------------------------------------------------------------------
-enum GemmMode { GEMM_GATEUP = 0, GEMM_DOWN = 1, GEMM_PLAIN_F32OUT = 2 };
+enum GemmMode {
+  GEMM_GATEUP = 0,       // h = SiLU(A Wg^T) * (A Wu^T)
+  GEMM_DOWN = 1,         // C = A B^T (bf16 out)
+  GEMM_PLAIN_F32OUT = 2, // C = A B^T + bias (fp32 out, single group)
+  GEMM_GU = 3,           // [G | U] = [A Wg^T | A Wu^T] (bf16, ldc = 2N)
+  GEMM_SWIGLU_BWD = 4,   // dH' = A B^T, then SwiGLU backward and router-weight partials
+  GEMM_DUALK = 5,        // C = A [B0 | B1]^T with K split in halves over two matrices
+  GEMM_WGRAD = 6         // per group g: C_g = A[:, K_g] B[:, K_g]^T over the group's K range
+};
 
 struct GemmProblem {
   int mode;
@@ -142,7 +171,17 @@ struct GemmProblem {
   uint8_t* C_scale;         // MX output scales [rows][N/32] (MXFP8 gate/up)
   int64_t ldc;
   const float* bias;        // [N] (plain mode)
-  int32_t* tile_prefix;     // scratch [G+1] (device), M-tile prefix per group
+  int32_t* tile_prefix;     // scratch [2(G+1)] (device), M-tile prefixes per group
+  int64_t ldb;              // B row stride in elements (0: K; DUALK: K/2 each)
+  // SwiGLU backward epilogue
+  const void* gu;           // [rows][2N] saved/recomputed G | U
+  const float* w_row;       // [rows] router weight per routed row (nullptr: 1)
+  void* dgu;                // [rows][2N] out: dG | dU
+  void* h_out;              // [rows][N] out: w_row * h (nullptr: skip)
+  float* dg_part;           // [rows][N/32] out: partial <dH', h> per 32 columns (nullptr: skip)
+  // K-grouped (weight gradient) mode
+  const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups
+  int64_t c_group_stride;   // elements between group outputs
 };
 
 hipError_t launch_gemm_bf16(const GemmProblem& p, hipStream_t s);

@@ -120,6 +120,15 @@ struct KArgs {
   const int32_t* small;  // small M-tile prefix [G+1]
   int single_big, single_small;
   int spread_small;      // interleave small tiles among big ones (else big first)
+  int64_t ldb;           // B row stride (elements)
+  int k_half;            // DUALK: K of the first matrix
+  const bf16_t* gu;
+  const float* w_row;
+  bf16_t* dgu;
+  bf16_t* h_out;
+  float* dg_part;
+  const int32_t* k_off;
+  int64_t c_group_stride;
 };
 
 // LDS swizzle of a 128-byte row: chunk position = logical chunk ^ swz(row).
@@ -177,14 +186,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int BM, int MODE, int NS>
 __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, int64_t row_begin, int64_t n_g,
-                                          int64_t m0, int ntile) {
+                                          int64_t m0, int ntile, int k_begin, int KT) {
   constexpr int BN = kBN;
   constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int RPR = kThreads / 8;          // rows per load round (8 rows per wave)
   constexpr int AR = BM / RPR, BR = BN / RPR;
+  constexpr bool PAIRED = MODE == GEMM_GATEUP || MODE == GEMM_GU;  // B rows interleave two matrices
   static_assert(AR * RPR == BM && BR * RPR == BN, "tile/thread mismatch");
-  static_assert(MODE != GEMM_GATEUP || FN % 2 == 0, "gate/up needs G,U block pairs per wave");
+  static_assert(!PAIRED || FN % 2 == 0, "gate/up needs G,U block pairs per wave");
   bf16_t* As = smem;                    // [NS][BM][64]
   bf16_t* Bs = smem + NS * BM * kBK;    // [NS][BN][64]
   constexpr int LPS = AR + BR;          // loads per slab per thread
@@ -197,46 +207,60 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   // global 16-byte chunk for this lane's LDS slot: slot (lane & 7) of row r
   // holds chunk slot ^ swz(r), r & 7 = lane >> 3 and (r >> 3) & 1 = wave & 1
   const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-  int K = p.K;
-  asm volatile("" : "+s"(K));  // keep per-tile address arithmetic inside the tile
+  int64_t ldb = p.ldb;
+  asm volatile("" : "+s"(ldb));  // keep per-tile address arithmetic inside the tile
 
-  // A: rows of the group (or gathered token rows); descriptor over the
-  // group's rows, or over the whole gather source.
-  const bf16_t* abase = uniform_ptr(p.a_rows ? p.A : p.A + row_begin * p.lda);
-  const uint32_t abytes = __builtin_amdgcn_readfirstlane(p.a_rows ? p.a_bytes : (uint32_t)(n_g * p.lda * 2));
+  // A: this tile's rows of the group (or gathered token rows); descriptor over
+  // the tile's rows, or over the whole gather source.
+  const bool gath = p.a_rows != nullptr;
+  const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
+  const bf16_t* abase = uniform_ptr(gath ? p.A : p.A + (row_begin + m0) * p.lda);
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * p.lda * 2));
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
   uint32_t aoff[AR];
 #pragma unroll
   for (int i = 0; i < AR; ++i) {
-    const int64_t lr0 = m0 + i * RPR + lrow;
-    const int64_t lr = lr0 < n_g ? lr0 : 0;
-    const int64_t src = p.a_rows ? (int64_t)p.a_rows[row_begin + lr] : lr;
+    const int64_t lr0 = i * RPR + lrow;           // row within the tile
+    const int64_t lr = lr0 < tile_rows ? lr0 : 0;
+    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
     aoff[i] = (uint32_t)(src * p.lda * 2) + chunk * 16;
   }
-  // B: one expert's [N][K] matrix (two of them, gate and up, in gate/up mode).
-  // In gate/up mode the tile's B rows are 32-row blocks alternating W_gate
-  // and W_up for the same output columns; the rows a wave loads in one round
-  // lie in one block, so the matrix choice is wave-uniform.
-  const uint32_t bbytes = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)p.N * K * 2));
-  const bf16_t* bsel = MODE == GEMM_GATEUP && ((wave >> 2) & 1) ? p.B1 : p.B0;
-  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(bsel + (int64_t)g * p.b_group_stride), (short)0, (int)bbytes, 0x00020000);
-  const uint32_t boff = (uint32_t)((lane >> 3) * K * 2) + chunk * 16;
+  // B: the group's [N][ldb] matrix, rebased at the first row this N-tile
+  // reads.  Paired modes interleave 32-row blocks of two matrices (W_gate,
+  // W_up) for the same output columns; the rows a wave loads in one round lie
+  // in one block, so the matrix choice is wave-uniform.  DUALK switches
+  // matrix halfway along K (uniform per slab).
+  const int span = PAIRED ? BN / 2 : BN;          // B rows one N-tile covers per matrix
+  const int first_row = ntile * span;
+  const uint32_t bbytes =
+      __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)min(span, p.N - first_row) * ldb * 2));
+  const bf16_t* b0 = p.B0 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb;
+  const bf16_t* b1 = (PAIRED || MODE == GEMM_DUALK) ? p.B1 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb
+                                                    : b0;
+  const __amdgpu_buffer_rsrc_t br0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(PAIRED && ((wave >> 2) & 1) ? b1 : b0), (short)0, (int)bbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t br1 = MODE == GEMM_DUALK
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b1), (short)0, (int)bbytes, 0x00020000)
+      : br0;
+  const uint32_t boff = (uint32_t)((lane >> 3) * ldb * 2) + chunk * 16;
 
   typedef __attribute__((address_space(3))) void lds_void;
   auto issue = [&](int buf, int k0) {
+    const int ka = k_begin + k0;
 #pragma unroll
     for (int i = 0; i < AR; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(As + (buf * BM + i * RPR + wave * 8) * kBK), 16,
-                                               aoff[i], k0 * 2, 0, 0);
+                                               aoff[i], ka * 2, 0, 0);
+    const bool second = MODE == GEMM_DUALK && k0 >= p.k_half;
+    const int kb = MODE == GEMM_DUALK ? (second ? k0 - p.k_half : k0) : ka;
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
-      // first B row of this wave's 8 rows in round i
-      int row0 = MODE == GEMM_GATEUP ? ntile * (BN / 2) + i * (RPR / 2) + (wave & 3) * 8
-                                     : ntile * BN + i * RPR + wave * 8;
-      row0 = min(row0, p.N - 8);  // rows past N load valid rows; their outputs are not stored
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void*)(Bs + (buf * BN + i * RPR + wave * 8) * kBK), 16, boff,
-                                               (row0 * K + k0) * 2, 0, 0);
+      // first B row (within this N-tile) of this wave's 8 rows in round i
+      int r0 = PAIRED ? i * (RPR / 2) + (wave & 3) * 8 : i * RPR + wave * 8;
+      r0 = min(r0, p.N - first_row - 8);  // rows past N load valid rows; their outputs are not stored
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? br1 : br0,
+                                               (lds_void*)(Bs + (buf * BN + i * RPR + wave * 8) * kBK), 16, boff,
+                                               (uint32_t)((r0 * ldb + kb) * 2), 0, 0);
     }
   };
 
@@ -286,7 +310,6 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
                                          0);
   };
 
-  const int KT = K / kBK;
   // NS-slab ring in LDS: slabs 0..NS-1 go out first; after the barrier of
   // iteration kt slab kt's buffer is free and takes slab kt+NS.  Before the
   // barrier only slab kt+1 must have landed, so vmcnt may leave the younger
@@ -321,8 +344,49 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   // 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
   int64_t ldc = p.ldc;
   asm volatile("" : "+s"(ldc));
-  bf16_t* C = static_cast<bf16_t*>(p.C) + (row_begin + m0) * ldc;
-  const int rows_left = (int)min<int64_t>(n_g - m0, BM);
+  const int64_t row0 = row_begin + m0;
+  bf16_t* C = static_cast<bf16_t*>(p.C) + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) + row0 * ldc;
+  const int rows_left = (int)tile_rows;
+  if constexpr (MODE == GEMM_SWIGLU_BWD) {
+    // dH' (unscaled by the router weight w) -> dG, dU, w h (the down
+    // projection's weight-gradient operand) and the partial router-weight
+    // gradient <dH', h> over these 32 columns (all lanes take part in the
+    // reduction).
+    const int N = p.N;
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FM; ++i) {
+#pragma clang loop unroll(full)
+      for (int v = 0; v < 16; ++v) {
+        const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t grow = row0 + min(rl, rows_left - 1);
+        const float wr = p.w_row ? p.w_row[grow] : 1.0f;
+        const bf16_t* gurow = p.gu + grow * 2 * N;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
+          const int col = min(col0, N - 1);
+          const float gv = bf16_to_f32(gurow[col]);
+          const float uv = bf16_to_f32(gurow[N + col]);
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float sl = gv * sg;
+          const float h = sl * uv;
+          const float dhp = acc[i][j][v];
+          const float dh = wr * dhp;
+          float part = dhp * h;
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+          if (rl < rows_left && col0 < N) {
+            bf16_t* drow = p.dgu + grow * 2 * N;
+            drow[col] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
+            drow[N + col] = f32_to_bf16(dh * sl);
+            if (p.h_out) p.h_out[grow * N + col] = f32_to_bf16(wr * h);
+            if (p.dg_part && (lane & 31) == 0) p.dg_part[grow * (N / 32) + col / 32] = part;
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -336,6 +400,15 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
           const float gv = acc[i][2 * q][v], uv = acc[i][2 * q + 1][v];
           const int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
           if (col < p.N) Crow[col] = f32_to_bf16(silu_f32(gv) * uv);
+        }
+      } else if (MODE == GEMM_GU) {
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q) {
+          const int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
+          if (col < p.N) {
+            Crow[col] = f32_to_bf16(acc[i][2 * q][v]);
+            Crow[p.N + col] = f32_to_bf16(acc[i][2 * q + 1][v]);
+          }
         }
       } else {
 #pragma unroll
@@ -361,7 +434,27 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   constexpr int GN = 4;  // N-tiles of one M-tile visited before the next M-tile
 
+  if (MODE == GEMM_WGRAD) {
+    // One output per group, all of it in big tiles; K range from k_off.
+    const int mtl = (int)((p.M + kBigM - 1) / kBigM);
+    const int per_g = mtl * p.ntiles;
+    const int tot = p.G * per_g;
+    for (int it = 0;; ++it) {
+      const int P = it * nwg + xcd * per_xcd + slot;
+      if (P >= tot) break;
+      const int g = __builtin_amdgcn_readfirstlane(P / per_g);
+      const int r = P - g * per_g;
+      const int mt = r / p.ntiles, nt = r - mt * p.ntiles;
+      const int kb = __builtin_amdgcn_readfirstlane(p.k_off[g]);
+      const int kt = __builtin_amdgcn_readfirstlane((p.k_off[g + 1] - kb) / kBK);
+      gemm_tile<kBigM, MODE, 2>(p, smem, g, 0, p.M, uniform_i64((int64_t)mt * kBigM),
+                                __builtin_amdgcn_readfirstlane(nt), kb, kt);
+      __syncthreads();
+    }
+    return;
+  }
   const int ts = total - tb;
+  const int KT = p.K / kBK;
   for (int it = 0;; ++it) {
     const int P = it * nwg + xcd * per_xcd + slot;
     if (P >= total) break;
@@ -400,8 +493,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
     row_begin = uniform_i64(row_begin);
     n_g = uniform_i64(n_g);
     m0 = uniform_i64(m0);
-    if (is_big) gemm_tile<kBigM, MODE, 2>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
-    else gemm_tile<kSmallM, MODE, 3>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    if (is_big) gemm_tile<kBigM, MODE, 2>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile), 0, KT);
+    else gemm_tile<kSmallM, MODE, 3>(p, smem, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile), 0, KT);
     __syncthreads();
   }
 }
@@ -504,7 +597,17 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   a.b_group_stride = q.b_group_stride;
   a.N = q.N;
   a.K = q.K;
-  a.ntiles = MODE == GEMM_GATEUP ? (q.N + kBN / 2 - 1) / (kBN / 2) : (q.N + kBN - 1) / kBN;
+  constexpr bool paired = MODE == GEMM_GATEUP || MODE == GEMM_GU;
+  a.ntiles = paired ? (q.N + kBN / 2 - 1) / (kBN / 2) : (q.N + kBN - 1) / kBN;
+  a.ldb = q.ldb ? q.ldb : (MODE == GEMM_DUALK ? q.K / 2 : q.K);
+  a.k_half = q.K / 2;
+  a.gu = static_cast<const bf16_t*>(q.gu);
+  a.w_row = q.w_row;
+  a.dgu = static_cast<bf16_t*>(q.dgu);
+  a.h_out = static_cast<bf16_t*>(q.h_out);
+  a.dg_part = q.dg_part;
+  a.k_off = q.k_off;
+  a.c_group_stride = q.c_group_stride;
   a.C = q.C;
   a.ldc = q.ldc;
   a.bias = q.bias;
@@ -513,7 +616,9 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   // big ones); for the long-K gate/up GEMM the big tiles are latency-bound
   // and lose more from the shared memory traffic than the overlap gains.
   a.spread_small = MODE == GEMM_DOWN ? 1 : 0;
-  if (q.row_off) {
+  if (MODE == GEMM_WGRAD) {
+    a.big = a.small = nullptr;
+  } else if (q.row_off) {
     a.big = q.tile_prefix;
     a.small = q.tile_prefix + (q.G + 1);
     tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.G, q.tile_prefix, q.tile_prefix + (q.G + 1));
@@ -539,6 +644,18 @@ hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
     case GEMM_DOWN:
       if (q.N % 8 != 0) return hipErrorInvalidValue;
       return run_grouped<GEMM_DOWN>(q, s);
+    case GEMM_GU:
+      if (q.N % 32 != 0) return hipErrorInvalidValue;
+      return run_grouped<GEMM_GU>(q, s);
+    case GEMM_SWIGLU_BWD:
+      if (q.N % 32 != 0 || !q.gu || !q.dgu) return hipErrorInvalidValue;
+      return run_grouped<GEMM_SWIGLU_BWD>(q, s);
+    case GEMM_DUALK:
+      if (q.N % 8 != 0 || (q.K / 2) % kBK != 0) return hipErrorInvalidValue;
+      return run_grouped<GEMM_DUALK>(q, s);
+    case GEMM_WGRAD:
+      if (q.N % 8 != 0 || !q.k_off || q.G < 1) return hipErrorInvalidValue;
+      return run_grouped<GEMM_WGRAD>(q, s);
     default: {
       if (q.row_off) return hipErrorInvalidValue;
       KArgs a = {};

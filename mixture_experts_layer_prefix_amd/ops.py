@@ -8,7 +8,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PREC, call, moe_dims, moe_routing, moe_weights
+from ._lib import PREC, call, moe_dims, moe_grads, moe_routing, moe_weights
 
 
 @dataclass(frozen=True)
@@ -44,6 +44,12 @@ class Weights:
     q_up_scale: Optional[torch.Tensor] = None
     q_down: Optional[torch.Tensor] = None
     q_down_scale: Optional[torch.Tensor] = None
+    wt_gate: Optional[torch.Tensor] = None
+    wt_up: Optional[torch.Tensor] = None
+    wt_down: Optional[torch.Tensor] = None
+    wst_gate: Optional[torch.Tensor] = None
+    wst_up: Optional[torch.Tensor] = None
+    wst_down: Optional[torch.Tensor] = None
 
     def c(self):
         w = moe_weights()
@@ -220,3 +226,56 @@ def prepare_mxfp8(weights: Weights, dims: Dims) -> Weights:
     return Weights(w_router=weights.w_router, w_gate=weights.w_gate, w_up=weights.w_up, w_down=weights.w_down,
                    ws_gate=weights.ws_gate, ws_up=weights.ws_up, ws_down=weights.ws_down,
                    q_gate=qg, q_gate_scale=sg, q_up=qu, q_up_scale=su, q_down=qd, q_down_scale=sd)
+
+
+def transpose_weights(w):
+    """[batch][rows][cols] bf16 -> [batch][cols][rows] (moe_transpose_weights)."""
+    b, r, c = w.shape
+    out = torch.empty(b, c, r, dtype=w.dtype, device=w.device)
+    call("moe_transpose_weights", _p(w), b, r, c, _p(out), _stream())
+    return out
+
+
+def prepare_backward(weights: Weights) -> Weights:
+    """Weights with the transposed copies the backward's input-gradient GEMMs
+    read (made once per weight update)."""
+    import dataclasses
+    t = {"wt_gate": weights.w_gate, "wt_up": weights.w_up, "wt_down": weights.w_down,
+         "wst_gate": weights.ws_gate, "wst_up": weights.ws_up, "wst_down": weights.ws_down}
+    return dataclasses.replace(weights, **{n: (transpose_weights(v) if v is not None else None) for n, v in t.items()})
+
+
+class BackwardPlan:
+    """Pre-allocated gradients and workspace of one backward configuration."""
+
+    def __init__(self, dims: Dims, prec: str, device="cuda", router_grad=True):
+        self.dims, self.prec = dims, prec
+        T, d, E, k, I = dims.T, dims.d, dims.E, dims.k, dims.I
+        bf = torch.bfloat16
+        self.dx = torch.empty(T, d, dtype=bf, device=device)
+        self.grads = dict(
+            dw_gate=torch.empty(E, I, d, dtype=bf, device=device),
+            dw_up=torch.empty(E, I, d, dtype=bf, device=device),
+            dw_down=torch.empty(E, d, I, dtype=bf, device=device),
+            dtopk_w=torch.empty(T, k, dtype=torch.float32, device=device))
+        if dims.S:
+            self.grads.update(dws_gate=torch.empty(dims.S, dims.Is, d, dtype=bf, device=device),
+                              dws_up=torch.empty(dims.S, dims.Is, d, dtype=bf, device=device),
+                              dws_down=torch.empty(dims.S, d, dims.Is, dtype=bf, device=device))
+        if router_grad:
+            self.grads["dw_router"] = torch.empty(E, d, dtype=torch.float32, device=device)
+        self.g = moe_grads(**{n: t.data_ptr() for n, t in self.grads.items()})
+        self.ws, self.ws_bytes = _workspace(dims, prec, 4, device)
+        self.cdims = dims.c()
+
+    def run(self, dy, x, weights: Weights, routing):
+        w = weights.c()
+        rt = moe_routing(**{n: t.data_ptr() for n, t in routing.items()})
+        call("moe_layer_backward", ctypes.byref(self.cdims), PREC[self.prec], _p(dy), _p(x), ctypes.byref(w),
+             ctypes.byref(rt), _p(self.dx), ctypes.byref(self.g), _p(self.ws), self.ws_bytes, _stream())
+        return self.dx, self.grads
+
+
+def layer_backward(dy, x, weights: Weights, routing, dims: Dims, prec: str, router_grad=True):
+    plan = BackwardPlan(dims, prec, dy.device, router_grad)
+    return plan.run(dy, x, weights, routing)

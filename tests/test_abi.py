@@ -77,3 +77,42 @@ def test_entry_points_reject_null_and_small_workspace_before_device_work():
     assert st == L.MOE_EINVAL
     st = lib.moe_quantize_mxfp8(fake, 10, 33, 0, fake, fake, None)
     assert st == L.MOE_EINVAL
+
+
+def test_backward_validation_before_device_work():
+    lib = L.lib()
+    d = dims()
+    fake = 1 << 20
+    w = M.Weights(w_router=None).c()
+    g = L.moe_grads()
+    rt = L.moe_routing()
+    # fp32 and MXFP8 backward are not built
+    for prec in (L.MOE_F32, L.MOE_MXFP8):
+        st = lib.moe_layer_backward(ctypes.byref(d.c()), prec, fake, fake, ctypes.byref(w), ctypes.byref(rt), fake,
+                                    ctypes.byref(g), fake, 1 << 40, None)
+        assert st == L.MOE_EUNSUPPORTED
+    # missing transposed weights / gradients / routing
+    st = lib.moe_layer_backward(ctypes.byref(d.c()), L.MOE_BF16, fake, fake, ctypes.byref(w), ctypes.byref(rt), fake,
+                                ctypes.byref(g), fake, 1 << 40, None)
+    assert st == L.MOE_EINVAL
+    st = lib.moe_layer_backward(ctypes.byref(d.c()), L.MOE_BF16, fake, fake, ctypes.byref(w), None, fake, None, fake,
+                                1 << 40, None)
+    assert st == L.MOE_EINVAL
+    # complete arguments but a small workspace
+    names = [n for n, _ in L.moe_weights._fields_]
+    w_full = L.moe_weights(**{n: fake for n in names})
+    g_full = L.moe_grads(**{n: fake for n, _ in L.moe_grads._fields_})
+    rt_full = L.moe_routing(**{n: fake for n, _ in L.moe_routing._fields_})
+    st = lib.moe_layer_backward(ctypes.byref(d.c()), L.MOE_BF16, fake, fake, ctypes.byref(w_full),
+                                ctypes.byref(rt_full), fake, ctypes.byref(g_full), fake, 64, None)
+    assert st == L.MOE_EWORKSPACE
+    # misaligned gradient pointer
+    g_bad = L.moe_grads(**{n: fake for n, _ in L.moe_grads._fields_})
+    g_bad.dw_up = fake + 2
+    st = lib.moe_layer_backward(ctypes.byref(d.c()), L.MOE_BF16, fake, fake, ctypes.byref(w_full),
+                                ctypes.byref(rt_full), fake, ctypes.byref(g_bad), fake, 1 << 40, None)
+    assert st == L.MOE_EINVAL
+    assert ws_status(d, "bf16", 4)[0] == L.MOE_OK and ws_status(d, "bf16", 4)[1] > 0
+    assert lib.moe_transpose_weights(fake, -1, 4, 4, fake, None) == L.MOE_EINVAL
+    assert lib.moe_transpose_weights(None, 1, 4, 4, fake, None) == L.MOE_EINVAL
+    assert lib.moe_transpose_weights(None, 0, 4, 4, None, None) == L.MOE_OK
