@@ -89,6 +89,12 @@ typedef struct {
   const void* wst_gate;                          /* [S][d][I_s] */
   const void* wst_up;                            /* [S][d][I_s] */
   const void* wst_down;                          /* [S][I_s][d] */
+  /* Backward in MOE_MXFP8 only: the transposed routed copies quantized along
+   * their rows (the input-gradient GEMMs' K): moe_quantize_mxfp8(axis 0) of
+   * wt_gate, wt_up (blocks along I) and wt_down (blocks along d). */
+  const uint8_t *qt_gate, *qt_gate_scale;        /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
+  const uint8_t *qt_up, *qt_up_scale;            /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
+  const uint8_t *qt_down, *qt_down_scale;        /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
 } moe_weights;
 
 /* Gradients written by moe_layer_backward (host struct of caller-owned device
@@ -225,10 +231,16 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
  * the blog post's "Reversed ring order" section).  Router chain, with the
  * selection held fixed: dl_j = g_j (dg_j - sum_i g_i dg_i) for the selected
  * experts, dW_router = dl^T x, dx += dl W_router.
- * Precision: MOE_BF16 (bf16 operands, fp32 accumulation); MOE_F32 and
- * MOE_MXFP8 return MOE_EUNSUPPORTED.  Every reduction runs in a fixed order
- * (results are bitwise reproducible); experts without rows get exact zero
- * weight gradients.  ws: workspace of moe_workspace_bytes(which=4). */
+ * Precision: MOE_BF16 (bf16 operands, fp32 accumulation) and MOE_MXFP8:
+ * every routed-expert GEMM takes E4M3 operands with E8M0 scales along its
+ * own K (blog post, "MXFP8 support"): dY and x along d, the weights as the
+ * q_* (forward replay) and qt_* copies, dG and dU along I (quantized in the
+ * SwiGLU-backward epilogue), and the weight-gradient operands along the
+ * routed-row axis in blocks of 32 rows of one expert (each expert's rows
+ * zero-padded to a multiple of 128); the shared expert and the router stay
+ * bf16.  MOE_F32 returns MOE_EUNSUPPORTED.  Every reduction runs in a fixed
+ * order (results are bitwise reproducible); experts without rows get exact
+ * zero weight gradients.  ws: workspace of moe_workspace_bytes(which=4). */
 moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* dy, const void* x,
                               const moe_weights* w, const moe_routing* routing, void* dx, const moe_grads* g,
                               void* ws, size_t ws_bytes, void* stream);

@@ -30,7 +30,8 @@ class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
         "q_gate", "q_gate_scale", "q_up", "q_up_scale", "q_down", "q_down_scale",
-        "wt_gate", "wt_up", "wt_down", "wst_gate", "wst_up", "wst_down")]
+        "wt_gate", "wt_up", "wt_down", "wst_gate", "wst_up", "wst_down",
+        "qt_gate", "qt_gate_scale", "qt_up", "qt_up_scale", "qt_down", "qt_down_scale")]
 
 
 class moe_grads(ctypes.Structure):

@@ -116,8 +116,10 @@ FwdWs carve_forward(Carver& c, const moe_dims* D, moe_prec prec, const moe_routi
 }
 
 // Backward scratch.  Rp: K capacity of the expert-padded transposed operands
-// of the weight-gradient GEMMs (every expert's rows rounded up to 64).
+// of the weight-gradient GEMMs (every expert's rows rounded up to `pad`: 64
+// for the bf16 GEMM's K slabs, 128 for the MXFP8 ones).
 struct BwdWs {
+  int pad;
   int64_t Rp, Tp;
   int32_t* prefix;   // [2(E+2)] GEMM tile prefixes
   int32_t* pad_off;  // [E+1]
@@ -125,16 +127,23 @@ struct BwdWs {
   float *w_row, *dl, *dl_row;
   void *gu, *dgu, *gh, *da;
   float* dg_part;
-  void *xT, *dyT, *ghT, *dguT;
   float* router_partial;
+  void *xT, *dyT, *ghT, *dguT;  // bf16 transposed operands
+  // MXFP8: quantized tokens and output gradients (along d), dG|dU along I, and
+  // the transposed operands quantized along the routed-row axis.
+  uint8_t *xq, *xqs, *dyq, *dyqs, *dguq, *dguqs;
+  uint8_t *xTq, *xTqs, *dyTq, *dyTqs, *ghTq, *ghTqs, *dguTq, *dguTqs;
   void *gus, *dgus, *hs, *dxs, *xTs, *dyTs, *hsT, *dgusT;
 };
 
-BwdWs carve_backward(Carver& c, const moe_dims* D) {
+BwdWs carve_backward(Carver& c, const moe_dims* D, moe_prec prec) {
   const int64_t T = D->T, R = D->T * D->k, d = D->d, I = D->I, Is = D->n_shared ? D->I_shared : 0;
-  BwdWs w;
-  w.Rp = bwd_padded_rows(R, D->E);
-  w.Tp = (T + 63) / 64 * 64;
+  const bool mx = prec == MOE_MXFP8;
+  BwdWs w = {};
+  w.pad = mx ? 128 : 64;
+  w.Rp = bwd_padded_rows(R, D->E, w.pad);
+  w.Tp = (T + w.pad - 1) / w.pad * w.pad;
+  auto u8 = [&](size_t n) { return static_cast<uint8_t*>(c.take(n)); };
   w.prefix = static_cast<int32_t*>(c.take((size_t)2 * (D->E + 2) * 4));
   w.pad_off = static_cast<int32_t*>(c.take((size_t)(D->E + 1) * 4));
   w.single = static_cast<int32_t*>(c.take(16));
@@ -146,11 +155,28 @@ BwdWs carve_backward(Carver& c, const moe_dims* D) {
   w.gh = c.take((size_t)R * I * 2);
   w.da = c.take((size_t)R * d * 2);
   w.dg_part = static_cast<float*>(c.take((size_t)R * (I / 32) * 4));
-  w.xT = c.take((size_t)d * w.Rp * 2);
-  w.dyT = c.take((size_t)d * w.Rp * 2);
-  w.ghT = c.take((size_t)I * w.Rp * 2);
-  w.dguT = c.take((size_t)2 * I * w.Rp * 2);
   w.router_partial = static_cast<float*>(c.take((size_t)(w.Rp / 64) * d * 4));
+  if (mx) {
+    w.xq = u8((size_t)T * d);
+    w.xqs = u8((size_t)T * d / 32);
+    w.dyq = u8((size_t)T * d);
+    w.dyqs = u8((size_t)T * d / 32);
+    w.dguq = u8((size_t)R * 2 * I);
+    w.dguqs = u8((size_t)R * 2 * I / 32);
+    w.xTq = u8((size_t)d * w.Rp);
+    w.xTqs = u8((size_t)d * w.Rp / 32);
+    w.dyTq = u8((size_t)d * w.Rp);
+    w.dyTqs = u8((size_t)d * w.Rp / 32);
+    w.ghTq = u8((size_t)I * w.Rp);
+    w.ghTqs = u8((size_t)I * w.Rp / 32);
+    w.dguTq = u8((size_t)2 * I * w.Rp);
+    w.dguTqs = u8((size_t)2 * I * w.Rp / 32);
+  } else {
+    w.xT = c.take((size_t)d * w.Rp * 2);
+    w.dyT = c.take((size_t)d * w.Rp * 2);
+    w.ghT = c.take((size_t)I * w.Rp * 2);
+    w.dguT = c.take((size_t)2 * I * w.Rp * 2);
+  }
   w.gus = c.take((size_t)T * 2 * Is * 2);
   w.dgus = c.take((size_t)T * 2 * Is * 2);
   w.hs = c.take((size_t)T * Is * 2);
@@ -169,7 +195,7 @@ size_t workspace_size(const moe_dims* D, moe_prec prec, int which) {
     case 1: c.take(permute_scratch_bytes(D->T, D->E)); break;
     case 2: carve_ffn(c, D, prec); break;
     case 3: carve_shared(c, D, prec); break;
-    case 4: carve_backward(c, D); break;
+    case 4: carve_backward(c, D, prec); break;
     default: return 0;
   }
   return c.used;
@@ -404,11 +430,32 @@ moe_status run_wgrad(const void* A, int64_t M, const void* B, int N, int64_t ldk
   return MOE_OK;
 }
 
-moe_status check_backward_weights(const moe_dims* D, const moe_weights* w, bool router) {
+// MXFP8 weight gradients from the quantized transposed operands
+// (A [M][ldk] + scales [M][ldk/32], B [N][ldk] + scales).
+moe_status run_wgrad_mx(const uint8_t* A, const uint8_t* As, int64_t M, const uint8_t* B, const uint8_t* Bs, int N,
+                        int64_t ldk, const int32_t* k_off, int G, void* C, hipStream_t s) {
+  GemmProblem q = gemm(GEMM_WGRAD, A, ldk, nullptr, M, G, B, nullptr, 0, N, 128, C, N, nullptr);
+  q.A_scale = As;
+  q.B0_scale = Bs;
+  q.ldb = ldk;
+  q.k_off = k_off;
+  q.c_group_stride = M * N;
+  MOE_HIP(launch_gemm_mxfp8(q, s));
+  return MOE_OK;
+}
+
+moe_status check_backward_weights(const moe_dims* D, moe_prec prec, const moe_weights* w, bool router) {
   if (!w) return MOE_EINVAL;
-  const void* r[] = {w->w_gate, w->w_up, w->wt_gate, w->wt_up, w->wt_down};
-  for (const void* p : r)
-    if (!ptr_ok(p)) return MOE_EINVAL;
+  if (prec == MOE_MXFP8) {
+    const void* r[] = {w->q_gate, w->q_gate_scale, w->q_up, w->q_up_scale, w->qt_gate, w->qt_gate_scale,
+                       w->qt_up, w->qt_up_scale, w->qt_down, w->qt_down_scale};
+    for (const void* p : r)
+      if (!ptr_ok(p)) return MOE_EINVAL;
+  } else {
+    const void* r[] = {w->w_gate, w->w_up, w->wt_gate, w->wt_up, w->wt_down};
+    for (const void* p : r)
+      if (!ptr_ok(p)) return MOE_EINVAL;
+  }
   if (D->n_shared > 0) {
     const void* q[] = {w->ws_gate, w->ws_up, w->wst_gate, w->wst_up, w->wst_down};
     for (const void* p : q)
@@ -423,33 +470,56 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   const int64_t T = D->T, R = T * D->k;
   const int d = D->d, I = D->I, E = D->E, k = D->k;
   const bool router = g->dw_router != nullptr;
-  MOE_HIP(launch_pad_offsets(rt->expert_counts, E, T, b.pad_off, b.single, s));
+  const bool mx = b.pad == 128;
+  MOE_HIP(launch_pad_offsets(rt->expert_counts, E, T, b.pad, b.pad_off, b.single, s));
   MOE_HIP(launch_row_weight(rt->token_row, rt->topk_w, R, b.w_row, s));
+  if (mx) {  // tokens and output gradients quantized once along d (row-wise: commutes with the gather)
+    MOE_HIP(launch_quantize_mx(x, T, d, 0, b.xq, b.xqs, s));
+    MOE_HIP(launch_quantize_mx(dy, T, d, 0, b.dyq, b.dyqs, s));
+  }
 
   // Forward replay up to the SwiGLU input: [G | U] of every routed row.
-  GemmProblem q = gemm(GEMM_GU, x, d, rt->expert_offsets, R, E, w->w_gate, w->w_up, (int64_t)I * d, I, d, b.gu,
-                       2 * I, b.prefix);
+  GemmProblem q = gemm(GEMM_GU, mx ? (const void*)b.xq : x, d, rt->expert_offsets, R, E,
+                       mx ? (const void*)w->q_gate : w->w_gate, mx ? (const void*)w->q_up : w->w_up, (int64_t)I * d,
+                       I, d, b.gu, 2 * I, b.prefix);
   q.a_rows = rt->row_token;
-  q.a_bytes = T * (int64_t)d * 2;
-  MOE_HIP(launch_gemm_bf16(q, s));
+  q.a_bytes = T * (int64_t)d * (mx ? 1 : 2);
+  if (mx) {
+    q.A_scale = b.xqs;
+    q.B0_scale = w->q_gate_scale;
+    q.B1_scale = w->q_up_scale;
+  }
+  MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
   // Reverse combine + down-projection input gradient dH' = dY_perm W_d with
   // the SwiGLU backward and the router-weight partials in the epilogue.
-  q = gemm(GEMM_SWIGLU_BWD, dy, d, rt->expert_offsets, R, E, w->wt_down, nullptr, (int64_t)I * d, I, d, b.dgu, 2 * I,
-           b.prefix);
+  q = gemm(GEMM_SWIGLU_BWD, mx ? (const void*)b.dyq : dy, d, rt->expert_offsets, R, E,
+           mx ? (const void*)w->qt_down : w->wt_down, nullptr, (int64_t)I * d, I, d, b.dgu, 2 * I, b.prefix);
   q.a_rows = rt->row_token;
-  q.a_bytes = T * (int64_t)d * 2;
+  q.a_bytes = T * (int64_t)d * (mx ? 1 : 2);
   q.gu = b.gu;
   q.w_row = b.w_row;
   q.dgu = b.dgu;
   q.h_out = b.gh;
   q.dg_part = b.dg_part;
-  MOE_HIP(launch_gemm_bf16(q, s));
+  if (mx) {
+    q.A_scale = b.dyqs;
+    q.B0_scale = w->qt_down_scale;
+    q.dgu_q = b.dguq;
+    q.dgu_scale = b.dguqs;
+  }
+  MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
   MOE_HIP(launch_dg(b.dg_part, I / 32, rt->token_row, rt->topk_w, T, k, g->dtopk_w, router ? b.dl : nullptr,
                     b.dl_row, s));
   // Gate/up input gradient dA = dG W_g + dU W_u (K = 2I over two matrices).
-  q = gemm(GEMM_DUALK, b.dgu, 2 * I, rt->expert_offsets, R, E, w->wt_gate, w->wt_up, (int64_t)d * I, d, 2 * I, b.da,
-           d, b.prefix);
-  MOE_HIP(launch_gemm_bf16(q, s));
+  q = gemm(GEMM_DUALK, mx ? (const void*)b.dguq : b.dgu, 2 * I, rt->expert_offsets, R, E,
+           mx ? (const void*)w->qt_gate : w->wt_gate, mx ? (const void*)w->qt_up : w->wt_up, (int64_t)d * I, d, 2 * I,
+           b.da, d, b.prefix);
+  if (mx) {
+    q.A_scale = b.dguqs;
+    q.B0_scale = w->qt_gate_scale;
+    q.B1_scale = w->qt_up_scale;
+  }
+  MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
 
   const int Is = D->n_shared ? D->I_shared : 0;
   if (Is) {
@@ -468,19 +538,33 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
                     static_cast<const bf16_t*>(w->w_router), Is ? static_cast<const bf16_t*>(b.dxs) : nullptr, dx, T,
                     d, k, s));
 
-  // Deferred weight gradients over each expert's whole (64-padded) row range.
-  MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, rt->expert_offsets, b.pad_off, E, b.Rp,
-                                static_cast<bf16_t*>(b.xT), b.Rp, s));
-  MOE_HIP(launch_transpose_rows(dy, d, d, rt->row_token, rt->expert_offsets, b.pad_off, E, b.Rp,
-                                static_cast<bf16_t*>(b.dyT), b.Rp, s));
-  MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.gh), I, I, nullptr, rt->expert_offsets, b.pad_off, E,
-                                b.Rp, static_cast<bf16_t*>(b.ghT), b.Rp, s));
-  MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.dgu), 2 * I, 2 * I, nullptr, rt->expert_offsets,
-                                b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT), b.Rp, s));
-  const bf16_t* dguT = static_cast<const bf16_t*>(b.dguT);
-  MOE_TRY(run_wgrad(b.dyT, d, b.ghT, I, b.Rp, b.pad_off, E, g->dw_down, s));
-  MOE_TRY(run_wgrad(dguT, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_gate, s));
-  MOE_TRY(run_wgrad(dguT + (int64_t)I * b.Rp, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_up, s));
+  // Deferred weight gradients over each expert's whole (padded) row range.
+  const bf16_t* gh = static_cast<const bf16_t*>(b.gh);
+  const bf16_t* dgu = static_cast<const bf16_t*>(b.dgu);
+  const int32_t* off = rt->expert_offsets;
+  if (mx) {
+    const int64_t Rp = b.Rp, Rs = b.Rp / 32;
+    MOE_HIP(launch_transpose_quant(x, d, d, rt->row_token, off, b.pad_off, E, Rp, b.xTq, b.xTqs, Rp, s));
+    MOE_HIP(launch_transpose_quant(dy, d, d, rt->row_token, off, b.pad_off, E, Rp, b.dyTq, b.dyTqs, Rp, s));
+    MOE_HIP(launch_transpose_quant(gh, I, I, nullptr, off, b.pad_off, E, Rp, b.ghTq, b.ghTqs, Rp, s));
+    MOE_HIP(launch_transpose_quant(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, Rp, b.dguTq, b.dguTqs, Rp, s));
+    MOE_TRY(run_wgrad_mx(b.dyTq, b.dyTqs, d, b.ghTq, b.ghTqs, I, Rp, b.pad_off, E, g->dw_down, s));
+    MOE_TRY(run_wgrad_mx(b.dguTq, b.dguTqs, I, b.xTq, b.xTqs, d, Rp, b.pad_off, E, g->dw_gate, s));
+    MOE_TRY(run_wgrad_mx(b.dguTq + (int64_t)I * Rp, b.dguTqs + (int64_t)I * Rs, I, b.xTq, b.xTqs, d, Rp, b.pad_off, E,
+                         g->dw_up, s));
+  } else {
+    MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.xT), b.Rp,
+                                  s));
+    MOE_HIP(launch_transpose_rows(dy, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dyT), b.Rp,
+                                  s));
+    MOE_HIP(launch_transpose_rows(gh, I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.ghT), b.Rp, s));
+    MOE_HIP(launch_transpose_rows(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT),
+                                  b.Rp, s));
+    const bf16_t* dguT = static_cast<const bf16_t*>(b.dguT);
+    MOE_TRY(run_wgrad(b.dyT, d, b.ghT, I, b.Rp, b.pad_off, E, g->dw_down, s));
+    MOE_TRY(run_wgrad(dguT, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_gate, s));
+    MOE_TRY(run_wgrad(dguT + (int64_t)I * b.Rp, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_up, s));
+  }
   if (Is) {
     const int32_t* seg = b.single + 2;
     MOE_HIP(launch_transpose_rows(x, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.xTs), b.Tp, s));
@@ -681,9 +765,9 @@ moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* d
                               const moe_weights* w, const moe_routing* routing, void* dx, const moe_grads* g, void* ws,
                               size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(dims, prec));
-  if (prec != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (prec == MOE_F32) return MOE_EUNSUPPORTED;
   if (!g || !routing) return MOE_EINVAL;
-  MOE_TRY(check_backward_weights(dims, w, g->dw_router != nullptr));
+  MOE_TRY(check_backward_weights(dims, prec, w, g->dw_router != nullptr));
   if (!ptr_ok(g->dw_gate) || !ptr_ok(g->dw_up) || !ptr_ok(g->dw_down) || !opt_ok(g->dw_router)) return MOE_EINVAL;
   if (dims->n_shared > 0 && (!ptr_ok(g->dws_gate) || !ptr_ok(g->dws_up) || !ptr_ok(g->dws_down))) return MOE_EINVAL;
   if (!ptr_ok(routing->expert_counts) || !ptr_ok(routing->expert_offsets)) return MOE_EINVAL;
@@ -711,7 +795,7 @@ moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* d
     return MOE_OK;
   }
   Carver c(ws);
-  BwdWs b = carve_backward(c, dims);
+  BwdWs b = carve_backward(c, dims, prec);
   return run_backward(dims, static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(x), w, routing,
                       static_cast<bf16_t*>(dx), g, b, s);
 }

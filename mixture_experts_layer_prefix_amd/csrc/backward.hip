@@ -23,6 +23,8 @@
 //    expert order, plus the shared expert's and the router's terms;
 //  - router_partial_kernel / router_reduce_kernel: W_router gradient as a
 //    fixed-order two-level sum over each expert's rows.
+//  - transpose_quant_kernel: the same transpose, quantized to MX along the
+//    routed-row axis (the K axis of the MXFP8 weight-gradient GEMMs);
 // Every reduction has a fixed order: results do not depend on scheduling.
 #include "common.h"
 
@@ -34,11 +36,11 @@ constexpr int kMaxK = 16;
 constexpr int kPadRows = 64;
 
 __global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __restrict__ counts, int E, int64_t T,
-                                                           int32_t* __restrict__ pad_off,
+                                                           int pad, int32_t* __restrict__ pad_off,
                                                            int32_t* __restrict__ single_off) {
   __shared__ int32_t s[1024];
   const int e = threadIdx.x;
-  const int32_t c = e < E ? (counts[e] + kPadRows - 1) / kPadRows * kPadRows : 0;
+  const int32_t c = e < E ? (counts[e] + pad - 1) / pad * pad : 0;
   s[e] = c;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -51,7 +53,7 @@ __global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __rest
   if (e == 0) {
     pad_off[0] = 0;
     single_off[0] = 0;
-    single_off[1] = (int32_t)((T + kPadRows - 1) / kPadRows * kPadRows);
+    single_off[1] = (int32_t)((T + pad - 1) / pad * pad);
     single_off[2] = 0;
     single_off[3] = (int32_t)T;
   }
@@ -159,6 +161,70 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
     for (int q = 0; q < 4; ++q)
       o[q] = (uint32_t)tile[ch * 8 + 2 * q][c] | ((uint32_t)tile[ch * 8 + 2 * q + 1][c] << 16);
     *reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + c) * ld_dst + p0 + ch * 8) = o;
+  }
+}
+
+// As transpose_rows_kernel, with the output quantized to MX E4M3 along its
+// rows (blocks of 32 consecutive padded positions p, i.e. 32 consecutive
+// routed rows of one expert; zero padding quantizes to zero codes): dst
+// [cols][ld_dst] bytes, dst_scale [cols][ld_dst/32].  The four threads of a
+// block combine their maxima with lane shuffles.
+__global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __restrict__ src, int64_t ld_src, int cols,
+                                                              const int32_t* __restrict__ gather,
+                                                              const int32_t* __restrict__ seg_off,
+                                                              const int32_t* __restrict__ pad_off, int nseg,
+                                                              uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_scale,
+                                                              int64_t ld_dst) {
+  __shared__ bf16_t tile[64][66];
+  const int64_t p0 = (int64_t)blockIdx.x * 64;
+  if (p0 >= pad_off[nseg]) return;
+  const int c0 = blockIdx.y * 64;
+  const int e = find_segment(pad_off, nseg, p0);
+  const int64_t r0 = seg_off[e] + (p0 - pad_off[e]);
+  const int64_t r_end = seg_off[e + 1];
+  const int tid = threadIdx.x;
+  const int ch = tid & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = (tid >> 3) + 32 * h;
+    const int64_t r = r0 + i;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (r < r_end && c0 + ch * 8 < cols) {
+      const int64_t srow = gather ? (int64_t)gather[r] : r;
+      v = *reinterpret_cast<const u32x4*>(src + srow * ld_src + c0 + ch * 8);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[i][ch * 8 + 2 * q] = (bf16_t)(v[q] & 0xFFFFu);
+      tile[i][ch * 8 + 2 * q + 1] = (bf16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = (tid >> 3) + 32 * h;
+    float v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      v[q] = bf16_to_f32(tile[ch * 8 + q][c]);
+      amax = fmaxf(amax, fabsf(v[q]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int ex = mx_block_exp(amax);
+    const float inv = mx_inv_scale(ex);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w0 |= e4m3_rne_sat(v[q] * inv) << (8 * q);
+      w1 |= e4m3_rne_sat(v[4 + q] * inv) << (8 * q);
+    }
+    if (c0 + c < cols) {
+      const int64_t row = c0 + c;
+      *reinterpret_cast<uint2*>(dst + row * ld_dst + p0 + ch * 8) = uint2{w0, w1};
+      if ((ch & 3) == 0) dst_scale[row * (ld_dst / 32) + (p0 + ch * 8) / 32] = (uint8_t)(ex + 127);
+    }
   }
 }
 
@@ -285,13 +351,25 @@ unsigned grid_for(int64_t work, int64_t cap) {
 
 }  // namespace
 
-int64_t bwd_padded_rows(int64_t rows, int groups) {
-  return (rows + kPadRows - 1) / kPadRows * kPadRows + (int64_t)kPadRows * groups;
+int64_t bwd_padded_rows(int64_t rows, int groups, int pad) {
+  return (rows + pad - 1) / pad * pad + (int64_t)pad * groups;
 }
 
-hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int32_t* pad_off, int32_t* single_off,
+hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int pad, int32_t* pad_off, int32_t* single_off,
                               hipStream_t s) {
-  pad_offsets_kernel<<<1, 1024, 0, s>>>(counts, E, T, pad_off, single_off);
+  if (pad % kPadRows) return hipErrorInvalidValue;
+  pad_offsets_kernel<<<1, 1024, 0, s>>>(counts, E, T, pad, pad_off, single_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
+                                  const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
+                                  uint8_t* dst, uint8_t* dst_scale, int64_t ld_dst, hipStream_t s) {
+  if (p_cap == 0 || cols == 0) return hipSuccess;
+  if (p_cap % 64 || ld_dst % 32 || ld_src % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 63) / 64));
+  transpose_quant_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, dst_scale,
+                                              ld_dst);
   return hipGetLastError();
 }
 

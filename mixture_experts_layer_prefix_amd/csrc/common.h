@@ -116,11 +116,14 @@ hipError_t launch_combine(bool act_f32, const void* o_perm, const int32_t* token
                           const void* y_shared, void* y, int64_t T, int d, int k, hipStream_t s);
 
 // Backward helpers.  Padded row capacity of a K-grouped operand: every
-// group's rows rounded up to 64.
-int64_t bwd_padded_rows(int64_t rows, int groups);
-// pad_off[E+1]: padded prefix of counts; single[4] = {0, round_up(T, 64), 0, T}.
-hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int32_t* pad_off, int32_t* single,
+// group's rows rounded up to `pad` (a multiple of 64).
+int64_t bwd_padded_rows(int64_t rows, int groups, int pad);
+// pad_off[E+1]: padded prefix of counts; single[4] = {0, round_up(T, pad), 0, T}.
+hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int pad, int32_t* pad_off, int32_t* single,
                               hipStream_t s);
+hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
+                                  const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
+                                  uint8_t* dst, uint8_t* dst_scale, int64_t ld_dst, hipStream_t s);
 hipError_t launch_row_weight(const int32_t* token_row, const float* topk_w, int64_t R, float* w_row, hipStream_t s);
 hipError_t launch_dg(const float* dg_part, int nparts, const int32_t* token_row, const float* topk_w, int64_t T, int k,
                      float* dtopk_w, float* dl, float* dl_row, hipStream_t s);
@@ -179,6 +182,8 @@ struct GemmProblem {
   void* dgu;                // [rows][2N] out: dG | dU
   void* h_out;              // [rows][N] out: w_row * h (nullptr: skip)
   float* dg_part;           // [rows][N/32] out: partial <dH', h> per 32 columns (nullptr: skip)
+  uint8_t* dgu_q;           // MX: [rows][2N] dG | dU quantized along the columns
+  uint8_t* dgu_scale;       // MX: [rows][2N/32]
   // K-grouped (weight gradient) mode
   const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups
   int64_t c_group_stride;   // elements between group outputs

@@ -314,7 +314,9 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   // iteration kt slab kt's buffer is free and takes slab kt+NS.  Before the
   // barrier only slab kt+1 must have landed, so vmcnt may leave the younger
   // slabs (LPS loads each) in flight.
-  wait_vmcnt<0>();  // earlier stores of this wave drained: counts below are exact
+  // Stores of the previous tile may still be in flight: they are older than
+  // this tile's loads, and loads return in order, so a wait for "at most n
+  // outstanding" still guarantees that every load but the youngest n landed.
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0)
     if (s0 < KT) issue(s0, s0 * kBK);
@@ -421,6 +423,19 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   }
 }
 
+// Zero rows [m0, m0 + 256) x columns [n0, n0 + 256) of one group's output
+// (a weight gradient of an expert without rows) with 16-byte stores.
+__device__ __forceinline__ void zero_tile(const KArgs& p, int g, int64_t m0, int n0) {
+  bf16_t* C = static_cast<bf16_t*>(p.C) + (int64_t)g * p.c_group_stride;
+  const int rows = (int)min<int64_t>(kBigM, p.M - m0);
+  const int cols = min(kBN, p.N - n0);
+  const int cpr = cols / 8;  // 16-byte chunks per row
+  for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
+    const int r = c / cpr, q = c - r * cpr;
+    *reinterpret_cast<u32x4*>(C + (m0 + r) * p.ldc + n0 + q * 8) = u32x4{0, 0, 0, 0};
+  }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
@@ -447,6 +462,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
       const int mt = r / p.ntiles, nt = r - mt * p.ntiles;
       const int kb = __builtin_amdgcn_readfirstlane(p.k_off[g]);
       const int kt = __builtin_amdgcn_readfirstlane((p.k_off[g + 1] - kb) / kBK);
+      if (kt == 0) {
+        zero_tile(p, g, (int64_t)mt * kBigM, nt * kBN);
+        continue;
+      }
       gemm_tile<kBigM, MODE, 2>(p, smem, g, 0, p.M, uniform_i64((int64_t)mt * kBigM),
                                 __builtin_amdgcn_readfirstlane(nt), kb, kt);
       __syncthreads();

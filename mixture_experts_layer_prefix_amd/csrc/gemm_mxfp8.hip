@@ -107,10 +107,10 @@ __global__ void __launch_bounds__(1024) mx_tile_prefix_kernel(const int32_t* __r
 
 struct MxArgs {
   const uint8_t* A;
-  const uint8_t* As;        // A scales [rows][K/32]
+  const uint8_t* As;        // A scales [rows][lda/32]
   const int32_t* a_rows;    // optional gather of A rows (and their scales)
   uint32_t a_bytes, as_bytes;  // sizes of A and its scales when gathered
-  int64_t lda;              // bytes per A row (= K)
+  int64_t lda;              // bytes per A row
   const int32_t* row_off;
   int64_t M;
   int G;
@@ -119,13 +119,26 @@ struct MxArgs {
   const uint8_t* B0s;
   const uint8_t* B1s;
   int64_t b_stride, bs_stride;  // bytes between experts in B and in its scales
+  int64_t ldb;              // bytes per B row
   int N, K, ntiles;
-  void* C;                  // gate/up: E4M3 h [rows][N]; down: bf16 [rows][N]
+  int k_half;               // DUALK: K of the first matrix
+  void* C;                  // gate/up: E4M3 h [rows][N]; others: bf16 [rows][N] (G|U: [rows][2N])
   uint8_t* Cs;              // gate/up: h scales [rows][N/32]
   int64_t ldc;
   const int32_t* big;
   const int32_t* small;
   int spread_small;
+  // SwiGLU backward epilogue
+  const bf16_t* gu;         // [rows][2N] G | U
+  const float* w_row;       // [rows] router weight (nullptr: 1)
+  bf16_t* dgu;              // [rows][2N] dG | dU (bf16)
+  uint8_t* dguq;            // [rows][2N] dG | dU quantized along the columns
+  uint8_t* dgus;            // [rows][2N/32] their scales
+  bf16_t* h_out;            // [rows][N] w h
+  float* dg_part;           // [rows][N/32]
+  // K-grouped weight-gradient mode
+  const int32_t* k_off;
+  int64_t c_group_stride;
 };
 
 __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) {
@@ -137,9 +150,21 @@ __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) 
   return lo;
 }
 
+// Quantize the 32 values of one row's 32-column block held by lanes
+// (lane & 31) of a lane half: returns the E4M3 code of this lane's value and
+// the block's E8M0 byte in *scale (all lanes take part).
+__device__ __forceinline__ uint32_t mx_lane_quant(float v, uint32_t* scale) {
+  float amax = fabsf(v);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = mx_block_exp(amax);
+  *scale = (uint32_t)(e + 127);
+  return e4m3_rne_sat(v * mx_inv_scale(e));
+}
+
 template <int BM, int MODE, int NS>
 __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, int64_t row_begin, int64_t n_g,
-                                        int64_t m0, int ntile) {
+                                        int64_t m0, int ntile, int k_begin, int KT) {
   constexpr int BN = kBN;
   constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -147,7 +172,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
   constexpr int AR = BM / RPR, BR = BN / RPR;
   constexpr int STG = stage_bytes(BM);
   constexpr int LPS = AR + BR;       // data loads per slab per thread (+1 scale load on most waves)
-  static_assert(FN == 2 && (MODE != GEMM_GATEUP || FN % 2 == 0), "wave tile");
+  constexpr bool PAIRED = MODE == GEMM_GATEUP || MODE == GEMM_GU;
+  constexpr bool DUAL = MODE == GEMM_DUALK;
+  static_assert(FN == 2, "wave tile");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,77 +182,91 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int lrow = wave * 8 + (lane >> 3);
   const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-  int K = p.K;
-  asm volatile("" : "+s"(K));
-  const int KS = K / 32;  // scale bytes per row
+  int64_t ldb = p.ldb;
+  asm volatile("" : "+s"(ldb));
+  const int64_t ldas = p.lda / 32, ldbs = ldb / 32;  // scale bytes per A / B row
 
-  // A data and scales (rows of the group, or gathered token rows).
+  // A data and scales: the tile's rows (or gathered token rows; then the
+  // descriptors span the whole gather source).
   const bool gath = p.a_rows != nullptr;
-  const uint8_t* abase = uniform_ptr(gath ? p.A : p.A + row_begin * p.lda);
-  const uint8_t* asbase = uniform_ptr(gath ? p.As : p.As + row_begin * KS);
-  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(n_g * p.lda));
-  const uint32_t asbytes = __builtin_amdgcn_readfirstlane(gath ? p.as_bytes : (uint32_t)(n_g * KS));
+  const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
+  const uint8_t* abase = uniform_ptr(gath ? p.A : p.A + (row_begin + m0) * p.lda);
+  const uint8_t* asbase = uniform_ptr(gath ? p.As : p.As + (row_begin + m0) * ldas);
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * p.lda));
+  const uint32_t asbytes = __builtin_amdgcn_readfirstlane(gath ? p.as_bytes : (uint32_t)(tile_rows * ldas));
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t asr =
       __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
   uint32_t aoff[AR];
 #pragma unroll
   for (int i = 0; i < AR; ++i) {
-    const int64_t lr0 = m0 + i * RPR + lrow;
-    const int64_t lr = lr0 < n_g ? lr0 : 0;
-    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + lr] : lr;
+    const int64_t lr0 = i * RPR + lrow;
+    const int64_t lr = lr0 < tile_rows ? lr0 : 0;
+    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
     aoff[i] = (uint32_t)(src * p.lda) + chunk * 16;
   }
   // Scale loads: waves 0..BM/64-1 fetch 64 A-scale rows each, waves 4..7 fetch
-  // 64 B-scale rows each (for gate/up: G rows 0-63, 64-127, then U rows).
+  // 64 B-scale rows each (paired modes: G rows 0-63, 64-127, then U rows).
   constexpr int ASW = BM / 64;
   const bool a_sc = wave < ASW;
   const bool b_sc = wave >= 4;
   uint32_t scoff = 0;
   if (a_sc) {
-    const int64_t lr0 = m0 + wave * 64 + lane;
-    const int64_t lr = lr0 < n_g ? lr0 : 0;
-    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + lr] : lr;
-    scoff = (uint32_t)(src * KS);
+    const int64_t lr0 = wave * 64 + lane;
+    const int64_t lr = lr0 < tile_rows ? lr0 : 0;
+    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
+    scoff = (uint32_t)(src * ldas);
   }
   const int bi = wave - 4;  // B-scale round of this wave
-  const uint8_t* bsbase;
-  if (MODE == GEMM_GATEUP) {
-    bsbase = (bi >= 2) ? p.B1s : p.B0s;
-    if (b_sc) scoff = (uint32_t)(min(ntile * (BN / 2) + (bi & 1) * 64 + lane, p.N - 1) * KS);
-  } else {
-    bsbase = p.B0s;
-    if (b_sc) scoff = (uint32_t)(min(ntile * BN + bi * 64 + lane, p.N - 1) * KS);
+  const int span = PAIRED ? BN / 2 : BN;
+  const int first_row = ntile * span;          // first B row of this N-tile
+  const int brows = min(span, p.N - first_row);
+  if (b_sc) {
+    const int r = PAIRED ? (bi & 1) * 64 + lane : bi * 64 + lane;
+    scoff = (uint32_t)(min(r, brows - 1) * ldbs);
   }
-  const __amdgpu_buffer_rsrc_t bsr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(bsbase + (int64_t)g * p.bs_stride), (short)0, (int)((int64_t)p.N * KS), 0x00020000);
+  const uint8_t* bs0 = p.B0s + (int64_t)g * p.bs_stride + first_row * ldbs;
+  const uint8_t* bs1 = (PAIRED || DUAL) ? p.B1s + (int64_t)g * p.bs_stride + first_row * ldbs : bs0;
+  const uint32_t bsbytes = __builtin_amdgcn_readfirstlane((uint32_t)(brows * ldbs));
+  const __amdgpu_buffer_rsrc_t bsr0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(PAIRED && bi >= 2 ? bs1 : bs0), (short)0, (int)bsbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t bsr1 =
+      DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(bs1), (short)0, (int)bsbytes, 0x00020000) : bsr0;
   // B data
-  const uint8_t* bsel = MODE == GEMM_GATEUP && ((wave >> 2) & 1) ? p.B1 : p.B0;
-  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(bsel + (int64_t)g * p.b_stride), (short)0, (int)((int64_t)p.N * K), 0x00020000);
-  const uint32_t boff = (uint32_t)((lane >> 3) * K) + chunk * 16;
+  const uint8_t* b0 = p.B0 + (int64_t)g * p.b_stride + first_row * ldb;
+  const uint8_t* b1 = (PAIRED || DUAL) ? p.B1 + (int64_t)g * p.b_stride + first_row * ldb : b0;
+  const uint32_t bbytes = __builtin_amdgcn_readfirstlane((uint32_t)(brows * ldb));
+  const __amdgpu_buffer_rsrc_t br0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(PAIRED && ((wave >> 2) & 1) ? b1 : b0), (short)0, (int)bbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t br1 =
+      DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b1), (short)0, (int)bbytes, 0x00020000) : br0;
+  const uint32_t boff = (uint32_t)((lane >> 3) * ldb) + chunk * 16;
 
   typedef __attribute__((address_space(3))) void lds_void;
   auto issue = [&](int st, int k0) {
     uint8_t* S = smem + st * STG;
+    const int ka = k_begin + k0;
 #pragma unroll
     for (int i = 0; i < AR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(S + (i * RPR + wave * 8) * kBKB), 16, aoff[i], k0, 0,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(S + (i * RPR + wave * 8) * kBKB), 16, aoff[i], ka, 0,
                                                0);
+    const bool second = DUAL && k0 >= p.k_half;
+    const int kb = DUAL ? (second ? k0 - p.k_half : k0) : ka;
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
-      int row0 = MODE == GEMM_GATEUP ? ntile * (BN / 2) + i * (RPR / 2) + (wave & 3) * 8
-                                     : ntile * BN + i * RPR + wave * 8;
-      row0 = min(row0, p.N - 8);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, boff,
-                                               row0 * K + k0, 0, 0);
+      int r0 = PAIRED ? i * (RPR / 2) + (wave & 3) * 8 : i * RPR + wave * 8;
+      r0 = min(r0, brows - 8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? br1 : br0,
+                                               (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, boff,
+                                               (uint32_t)(r0 * ldb + kb), 0, 0);
     }
     if (a_sc)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, scoff,
-                                               k0 / 32, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, scoff, ka / 32,
+                                               0, 0);
     if (b_sc)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bsr, (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + bi * 256), 4, scoff,
-                                               k0 / 32, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? bsr1 : bsr0,
+                                               (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + bi * 256), 4, scoff,
+                                               kb / 32, 0, 0);
   };
   const bool any_sc = a_sc || b_sc;
 
@@ -267,7 +308,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
     for (int i = 0; i < FM; ++i) sa[i] = *reinterpret_cast<const int*>(S + (wm * WM + i * 32 + (lane & 31)) * 4);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int r = MODE == GEMM_GATEUP ? (j ? 128 : 0) + wn * 32 + (lane & 31) : wn * WN + j * 32 + (lane & 31);
+      const int r = PAIRED ? (j ? 128 : 0) + wn * 32 + (lane & 31) : wn * WN + j * 32 + (lane & 31);
       sb[j] = *reinterpret_cast<const int*>(S + BM * 4 + r * 4);
     }
   };
@@ -281,7 +322,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
                                                                     (sa[i] >> sh) & 0xFF, 0, (sb[j] >> sh) & 0xFF);
   };
 
-  const int KT = K / kBKB;
   wait_vmcnt<0>();
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0)
@@ -311,51 +351,135 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
   // Epilogue (32x32 block layout: column lane & 31, rows 8*(v/4) + 4*(lane/32) + v%4).
   int64_t ldc = p.ldc;
   asm volatile("" : "+s"(ldc));
-  const int rows_left = (int)min<int64_t>(n_g - m0, BM);
-#pragma unroll
+  const int rows_left = (int)tile_rows;
+  const int N = p.N;
+#pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int v = 0; v < 16; ++v) {
       const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const int64_t grow = row_begin + m0 + rl;
-      if (MODE == GEMM_GATEUP) {
+      const bool row_ok = rl < rows_left;
+      const int64_t grow = row_begin + m0 + (row_ok ? rl : rows_left - 1);
+      if constexpr (MODE == GEMM_GATEUP) {
         // h = SiLU(G) * U for column block wn of this tile, quantized per row
         // over its 32 columns (lanes 0-31 or 32-63 of the wave).
         const float h = silu_f32(acc[i][0][v]) * acc[i][1][v];
-        float amax = fabsf(h);
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        const int e = mx_block_exp(amax);
+        uint32_t sc;
+        const uint32_t code = mx_lane_quant(h, &sc);
         const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
-        if (rl < rows_left && col < p.N) {
+        if (row_ok && col < N) {
           uint8_t* C = static_cast<uint8_t*>(p.C);
-          C[grow * ldc + col] = (uint8_t)e4m3_rne_sat(h * mx_inv_scale(e));
-          if ((lane & 31) == 0) p.Cs[grow * (ldc / 32) + col / 32] = (uint8_t)(e + 127);
+          C[grow * ldc + col] = (uint8_t)code;
+          if ((lane & 31) == 0) p.Cs[grow * (ldc / 32) + col / 32] = (uint8_t)sc;
+        }
+      } else if constexpr (MODE == GEMM_GU) {
+        const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
+        if (row_ok && col < N) {
+          bf16_t* C = static_cast<bf16_t*>(p.C) + grow * ldc;
+          C[col] = f32_to_bf16(acc[i][0][v]);
+          C[N + col] = f32_to_bf16(acc[i][1][v]);
+        }
+      } else if constexpr (MODE == GEMM_SWIGLU_BWD) {
+        // dH' -> dG, dU (bf16 and quantized along the columns), w h and the
+        // partial router-weight gradient <dH', h> per 32-column block.
+        const float wr = p.w_row ? p.w_row[grow] : 1.0f;
+        const bf16_t* gurow = p.gu + grow * 2 * N;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
+          const int col = min(col0, N - 1);
+          const float gv = bf16_to_f32(gurow[col]);
+          const float uv = bf16_to_f32(gurow[N + col]);
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float sl = gv * sg;
+          const float h = sl * uv;
+          const float dhp = acc[i][j][v];
+          const float dh = wr * dhp;
+          const float dgv = dh * uv * sg * (1.0f + gv * (1.0f - sg));
+          const float duv = dh * sl;
+          float part = dhp * h;
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+          uint32_t sg_sc, su_sc;
+          const uint32_t cg = mx_lane_quant(dgv, &sg_sc);
+          const uint32_t cu = mx_lane_quant(duv, &su_sc);
+          if (row_ok && col0 < N) {
+            bf16_t* drow = p.dgu + grow * 2 * N;
+            drow[col] = f32_to_bf16(dgv);
+            drow[N + col] = f32_to_bf16(duv);
+            uint8_t* qrow = p.dguq + grow * 2 * N;
+            qrow[col] = (uint8_t)cg;
+            qrow[N + col] = (uint8_t)cu;
+            p.h_out[grow * N + col] = f32_to_bf16(wr * h);
+            if ((lane & 31) == 0) {
+              uint8_t* srow = p.dgus + grow * (2 * N / 32);
+              srow[col / 32] = (uint8_t)sg_sc;
+              srow[(N + col) / 32] = (uint8_t)su_sc;
+              if (p.dg_part) p.dg_part[grow * (N / 32) + col / 32] = part;
+            }
+          }
         }
       } else {
-        if (rl >= rows_left) continue;
-        bf16_t* C = static_cast<bf16_t*>(p.C) + grow * ldc;
+        if (!row_ok) continue;
+        bf16_t* C = static_cast<bf16_t*>(p.C) + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) + grow * ldc;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
-          if (col < p.N) C[col] = f32_to_bf16(acc[i][j][v]);
+          if (col < N) C[col] = f32_to_bf16(acc[i][j][v]);
         }
       }
     }
   }
 }
 
+// Zero one 256 x 256 output tile of group g (weight gradient of an expert
+// without rows) with 16-byte stores.
+__device__ __forceinline__ void mx_zero_tile(const MxArgs& p, int g, int64_t m0, int n0) {
+  bf16_t* C = static_cast<bf16_t*>(p.C) + (int64_t)g * p.c_group_stride;
+  const int rows = (int)min<int64_t>(kBigM, p.M - m0);
+  const int cols = min(kBN, p.N - n0);
+  const int cpr = cols / 8;
+  for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
+    const int r = c / cpr, q = c - r * cpr;
+    *reinterpret_cast<u32x4*>(C + (m0 + r) * p.ldc + n0 + q * 8) = u32x4{0, 0, 0, 0};
+  }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_mx[];
+  const int nwg = gridDim.x;
+  const int per_xcd = nwg >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  if constexpr (MODE == GEMM_WGRAD) {
+    // One output per group, all in big tiles; K range of group g from k_off.
+    const int mtl = (int)((p.M + kBigM - 1) / kBigM);
+    const int per_g = mtl * p.ntiles;
+    const int tot = p.G * per_g;
+    for (int it = 0;; ++it) {
+      const int P = it * nwg + xcd * per_xcd + slot;
+      if (P >= tot) break;
+      const int g = __builtin_amdgcn_readfirstlane(P / per_g);
+      const int r = P - g * per_g;
+      const int mt = r / p.ntiles, nt = r - mt * p.ntiles;
+      const int kb = __builtin_amdgcn_readfirstlane(p.k_off[g]);
+      const int kt = __builtin_amdgcn_readfirstlane((p.k_off[g + 1] - kb) / kBKB);
+      if (kt == 0) {
+        mx_zero_tile(p, g, (int64_t)mt * kBigM, nt * kBN);
+        continue;
+      }
+      mx_tile<kBigM, MODE, 2>(p, smem_mx, g, 0, p.M, uniform_i64((int64_t)mt * kBigM),
+                              __builtin_amdgcn_readfirstlane(nt), kb, kt);
+      __syncthreads();
+    }
+    return;
+  }
   const int nbig = p.big[p.G];
   const int nsmall = p.small[p.G];
   const int tb = nbig * p.ntiles;
   const int total = tb + nsmall * p.ntiles;
   const int ts = total - tb;
-  const int nwg = gridDim.x;
-  const int per_xcd = nwg >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int KT = p.K / kBKB;
   constexpr int GN = 4;
   for (int it = 0;; ++it) {
     const int P = it * nwg + xcd * per_xcd + slot;
@@ -383,8 +507,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
     const int nb_g = p.big[g + 1] - p.big[g];
     const int64_t m0 = uniform_i64(is_big ? (int64_t)(mt - pre[g]) * kBigM
                                           : (int64_t)nb_g * kBigM + (int64_t)(mt - pre[g]) * kSmallM);
-    if (is_big) mx_tile<kBigM, MODE, 2>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
-    else mx_tile<kSmallM, MODE, 3>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile));
+    if (is_big)
+      mx_tile<kBigM, MODE, 2>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile), 0, KT);
+    else
+      mx_tile<kSmallM, MODE, 3>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile), 0, KT);
     __syncthreads();
   }
 }
@@ -428,14 +554,30 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.bs_stride = q.b_group_stride / 32;
   a.N = q.N;
   a.K = q.K;
-  a.ntiles = MODE == GEMM_GATEUP ? (q.N + kBN / 2 - 1) / (kBN / 2) : (q.N + kBN - 1) / kBN;
+  constexpr bool paired = MODE == GEMM_GATEUP || MODE == GEMM_GU;
+  a.ntiles = paired ? (q.N + kBN / 2 - 1) / (kBN / 2) : (q.N + kBN - 1) / kBN;
+  a.ldb = q.ldb ? q.ldb : (MODE == GEMM_DUALK ? q.K / 2 : q.K);
+  a.k_half = q.K / 2;
   a.C = q.C;
   a.Cs = q.C_scale;
   a.ldc = q.ldc;
-  a.big = q.tile_prefix;
-  a.small = q.tile_prefix + (q.G + 1);
+  a.gu = static_cast<const bf16_t*>(q.gu);
+  a.w_row = q.w_row;
+  a.dgu = static_cast<bf16_t*>(q.dgu);
+  a.dguq = q.dgu_q;
+  a.dgus = q.dgu_scale;
+  a.h_out = static_cast<bf16_t*>(q.h_out);
+  a.dg_part = q.dg_part;
+  a.k_off = q.k_off;
+  a.c_group_stride = q.c_group_stride;
   a.spread_small = MODE == GEMM_DOWN ? 1 : 0;
-  mx_tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.G, q.tile_prefix, q.tile_prefix + (q.G + 1));
+  if (MODE == GEMM_WGRAD) {
+    a.big = a.small = nullptr;
+  } else {
+    a.big = q.tile_prefix;
+    a.small = q.tile_prefix + (q.G + 1);
+    mx_tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.G, q.tile_prefix, q.tile_prefix + (q.G + 1));
+  }
   int wg = num_cus_mx();
   wg = (wg + 7) / 8 * 8;
   gemm_mxfp8_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes, s>>>(a);
@@ -444,12 +586,27 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
 
 }  // namespace
 
-// Grouped MXFP8 GEMM: row_off and tile_prefix are required (grouped mode);
-// N and K must be multiples of 128 (K: whole slabs; N: whole scale blocks).
+// Grouped MXFP8 GEMM: row_off and tile_prefix are required except in the
+// K-grouped weight-gradient mode (k_off instead); K (each half in DUALK) must
+// be whole 128-byte slabs and N whole 64-column blocks.
 hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
-  if (!q.row_off || q.K % kBKB != 0 || q.N % 64 != 0) return hipErrorInvalidValue;
-  if (q.mode == GEMM_GATEUP) return run_mx<GEMM_GATEUP>(q, s);
-  if (q.mode == GEMM_DOWN) return run_mx<GEMM_DOWN>(q, s);
+  if (q.N % 64 != 0) return hipErrorInvalidValue;
+  if (q.mode == GEMM_WGRAD) {
+    if (!q.k_off || q.G < 1 || q.ldb % 128 || q.lda % 128) return hipErrorInvalidValue;
+    return run_mx<GEMM_WGRAD>(q, s);
+  }
+  if (!q.row_off || q.K % kBKB != 0) return hipErrorInvalidValue;
+  switch (q.mode) {
+    case GEMM_GATEUP: return run_mx<GEMM_GATEUP>(q, s);
+    case GEMM_DOWN: return run_mx<GEMM_DOWN>(q, s);
+    case GEMM_GU: return run_mx<GEMM_GU>(q, s);
+    case GEMM_SWIGLU_BWD:
+      if (!q.gu || !q.dgu || !q.dgu_q || !q.dgu_scale || !q.h_out) return hipErrorInvalidValue;
+      return run_mx<GEMM_SWIGLU_BWD>(q, s);
+    case GEMM_DUALK:
+      if ((q.K / 2) % kBKB != 0) return hipErrorInvalidValue;
+      return run_mx<GEMM_DUALK>(q, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -50,6 +50,12 @@ class Weights:
     wst_gate: Optional[torch.Tensor] = None
     wst_up: Optional[torch.Tensor] = None
     wst_down: Optional[torch.Tensor] = None
+    qt_gate: Optional[torch.Tensor] = None
+    qt_gate_scale: Optional[torch.Tensor] = None
+    qt_up: Optional[torch.Tensor] = None
+    qt_up_scale: Optional[torch.Tensor] = None
+    qt_down: Optional[torch.Tensor] = None
+    qt_down_scale: Optional[torch.Tensor] = None
 
     def c(self):
         w = moe_weights()
@@ -236,13 +242,24 @@ def transpose_weights(w):
     return out
 
 
-def prepare_backward(weights: Weights) -> Weights:
+def prepare_backward(weights: Weights, mxfp8=False) -> Weights:
     """Weights with the transposed copies the backward's input-gradient GEMMs
-    read (made once per weight update)."""
+    read (made once per weight update); with mxfp8 also their MX-quantized
+    forms (blocks along the rows of the transposed copies: I for W_gate^T and
+    W_up^T, d for W_down^T)."""
     import dataclasses
     t = {"wt_gate": weights.w_gate, "wt_up": weights.w_up, "wt_down": weights.w_down,
          "wst_gate": weights.ws_gate, "wst_up": weights.ws_up, "wst_down": weights.ws_down}
-    return dataclasses.replace(weights, **{n: (transpose_weights(v) if v is not None else None) for n, v in t.items()})
+    out = dataclasses.replace(weights, **{n: (transpose_weights(v) if v is not None else None) for n, v in t.items()})
+    if mxfp8:
+        q = {}
+        for n in ("gate", "up", "down"):
+            wt = getattr(out, "wt_" + n)
+            codes, scale = quantize_mxfp8(wt.reshape(-1, wt.shape[-1]), 0)
+            q["qt_" + n] = codes.reshape(wt.shape)
+            q["qt_%s_scale" % n] = scale
+        out = dataclasses.replace(out, **q)
+    return out
 
 
 class BackwardPlan:
@@ -251,7 +268,7 @@ class BackwardPlan:
     def __init__(self, dims: Dims, prec: str, device="cuda", router_grad=True):
         self.dims, self.prec = dims, prec
         T, d, E, k, I = dims.T, dims.d, dims.E, dims.k, dims.I
-        bf = torch.bfloat16
+        bf = torch.bfloat16  # gradients are bf16 in both bf16 and MXFP8 modes
         self.dx = torch.empty(T, d, dtype=bf, device=device)
         self.grads = dict(
             dw_gate=torch.empty(E, I, d, dtype=bf, device=device),

@@ -1,0 +1,246 @@
+"""GPU parity of the MXFP8 layer backward through the C ABI.
+
+Every routed-expert GEMM takes E4M3 operands with E8M0 scales along its K
+axis; the shared expert and the router stay bf16.  Two references:
+  * the float64 oracle of the unquantized layer (the authority);
+  * a quantization-aware float64 model built from the oracle's MX quantizer:
+    the same operands MX-rounded at the same points (x, dY and the weights
+    along each GEMM's K, dG and dU along I, the weight-gradient operands along
+    the routed-row axis in 32-row blocks of one expert) and the path's bf16
+    storage of G, U and of the weight-gradient operands, exact arithmetic
+    otherwise.
+Bars per tensor (max|d|/max|ref|): against the quantization-aware model
+3e-2; against the oracle the stated 6e-2 bound, or the format's own error
+(the quantization-aware model against the oracle) plus 1e-2 where MX
+rounding alone exceeds 6e-2 on a small shape.  Weight gradients of experts
+without rows are exactly zero and repeated runs are bitwise identical."""
+import numpy as np
+import pytest
+
+import gen
+from oracle import moe_oracle as O
+from tests.moe_parity import TOL, HostProblem, bf16r, device_problem, qd, qd_rows, rel_err, shared_weights, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_Q = 3e-2
+
+SMALL = {
+    "mxb_ragged": gen.Dims("mxb_ragged", 300, 256, 16, 4, 256, 1, 128, "mxfp8", 0.0, backward=True),
+    "mxb_skew_noshared": gen.Dims("mxb_skew_noshared", 513, 384, 32, 8, 128, 0, 0, "mxfp8", 1.2, backward=True),
+    "mxb_k1": gen.Dims("mxb_k1", 77, 128, 4, 1, 128, 1, 64, "mxfp8", 0.0, backward=True),
+    "mxb_tiles": gen.Dims("mxb_tiles", 1100, 512, 8, 2, 384, 1, 192, "mxfp8", 0.0, backward=True),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def token_grads_q(x, dy, gr, wg, wu, wd):
+    """Quantization-aware input gradients dA and router-weight gradients dg of
+    one expert's rows (x, dy rows, router weights gr)."""
+    G = bf16r(qd(x) @ qd(wg).T)
+    U = bf16r(qd(x) @ qd(wu).T)
+    dHp = qd(dy) @ qd(wd.T).T
+    h = O.silu(G) * U
+    dh = gr[:, None] * dHp
+    dG = dh * U * O.silu_grad(G)
+    dU = dh * O.silu(G)
+    return qd(dG) @ qd(wg.T).T + qd(dU) @ qd(wu.T).T, np.sum(dHp * h, axis=1)
+
+
+def expert_grads_q(x, dy, gr, wg, wu, wd, with_da=True):
+    """Quantization-aware gradients of one expert over its rows (x, dy rows,
+    router weights gr): dA rows (None unless with_da), dg per row, dW_gate,
+    dW_up, dW_down.  Without dA the weights may be restricted to a subset of
+    intermediate columns (every other step is per column)."""
+    G = bf16r(qd(x) @ qd(wg).T)
+    U = bf16r(qd(x) @ qd(wu).T)
+    dHp = qd(dy) @ qd(wd.T).T
+    h = O.silu(G) * U
+    dg = np.sum(dHp * h, axis=1)
+    dh = gr[:, None] * dHp
+    dG = dh * U * O.silu_grad(G)
+    dU = dh * O.silu(G)
+    dA = qd(dG) @ qd(wg.T).T + qd(dU) @ qd(wu.T).T if with_da else None
+    # the weight-gradient operands pass through bf16 storage before their
+    # token-axis quantization (w h, dG, dU; x and dY are bf16 already)
+    dWd = qd_rows(dy).T @ qd_rows(bf16r(gr[:, None] * h))
+    dWg = qd_rows(bf16r(dG)).T @ qd_rows(x)
+    dWu = qd_rows(bf16r(dU)).T @ qd_rows(x)
+    return dA, dg, dWg, dWu, dWd
+
+
+def backward_q(hp, fw):
+    """Quantization-aware model of the whole MXFP8 backward (small shapes)."""
+    D, p = hp.dims, hp.p
+    x, dy = p.host("x"), p.host("dy")
+    off, row_token, token_row = fw["offsets"], fw["row_token"], fw["token_row"]
+    g = fw["topk_w"].astype(np.float64)
+    g_row = np.zeros(D.R)
+    g_row[token_row.reshape(-1)] = g.reshape(-1)
+    dA = np.zeros((D.R, D.d))
+    dg_row = np.zeros(D.R)
+    out = {n: np.zeros(p.shape(n)) for n in ("w_gate", "w_up", "w_down")}
+    for e in range(D.E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        toks = row_token[lo:hi]
+        r = expert_grads_q(x[toks], dy[toks], g_row[lo:hi], *hp.expert(e))
+        dA[lo:hi], dg_row[lo:hi], out["w_gate"][e], out["w_up"][e], out["w_down"][e] = r
+    dx = np.zeros((D.T, D.d))
+    for j in range(D.k):
+        dx += dA[token_row[:, j]]
+    res = dict(dw_gate=out["w_gate"], dw_up=out["w_up"], dw_down=out["w_down"])
+    for s in range(D.S):
+        dAs, res["dws_gate"], res["dws_up"], res["dws_down"], _, _ = O.ffn_backward(x, *shared_weights(p, D, s), dy)
+        dx += dAs
+    dg = dg_row[token_row]
+    inner = np.sum(g * dg, axis=1, keepdims=True)
+    dsel = g * (dg - inner)
+    dl = np.zeros((D.T, D.E))
+    np.put_along_axis(dl, fw["topk_idx"].astype(np.int64), dsel, axis=1)
+    res["dx"] = dx + dl @ p.host("w_router")
+    res["dtopk_w"] = dg
+    res["dw_router"] = dl.T @ x
+    return res
+
+
+def sampled_backward_q(hp, tokens, idx, g):
+    """Quantization-aware dx (with the shared expert and router terms) and dg
+    of selected tokens given their routing; experts in parallel threads
+    (numpy releases the interpreter lock inside its kernels)."""
+    from concurrent.futures import ThreadPoolExecutor
+    D, p = hp.dims, hp.p
+    x, dy = p.host_rows("x", tokens), p.host_rows("dy", tokens)
+    pairs = {}
+    for i, t in enumerate(tokens):
+        for j in range(D.k):
+            pairs.setdefault(int(idx[t, j]), []).append((i, j, float(g[t, j])))
+
+    def one(e):
+        rows = [i for i, _, _ in pairs[e]]
+        gr = np.array([gg for _, _, gg in pairs[e]])
+        wts = tuple(p.host_expert(n, e) for n in ("w_gate", "w_up", "w_down"))
+        return e, token_grads_q(x[rows], dy[rows], gr, *wts)
+
+    dx = np.zeros((len(tokens), D.d))
+    dg = np.zeros((len(tokens), D.k))
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for e, (dA, dge) in ex.map(one, sorted(pairs)):
+            for q, (i, j, _) in enumerate(pairs[e]):
+                dx[i] += dA[q]
+                dg[i, j] = dge[q]
+    for s in range(D.S):
+        dx += O.ffn_backward(x, *shared_weights(p, D, s), dy)[0]
+    gt = np.asarray(g, np.float64)[tokens]
+    dl = gt * (dg - np.sum(gt * dg, axis=1, keepdims=True))
+    wr = p.host("w_router")
+    for i, t in enumerate(tokens):
+        for j in range(D.k):
+            dx[i] += dl[i, j] * wr[int(idx[t, j])]
+    return dx, dg
+
+
+def run_backward(D):
+    import mixture_experts_layer_prefix_amd as M
+    p, t, md, w = device_problem(D)
+    dy = p.device("dy")
+    wq = M.prepare_mxfp8(w, md)
+    wb = M.prepare_backward(wq, mxfp8=True)
+    _, routing = M.layer_forward(t["x"], wq, md, "mxfp8", bias=t["bias"])
+    plan = M.BackwardPlan(md, "mxfp8")
+    dx, grads = plan.run(dy, t["x"], wb, routing)
+    torch.cuda.synchronize()
+    out = {"dx": dx}
+    out.update(grads)
+    return out, (plan, dy, t, wb, routing)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_mxfp8_backward(name):
+    D = SMALL[name]
+    say("[case]", name, D)
+    hp = HostProblem(D)
+    a = hp.full()
+    exact = O.layer_backward(a["x"], a["w_router"], a["bias"], a["w_gate"], a["w_up"], a["w_down"], a["ws_gate"],
+                             a["ws_up"], a["ws_down"], D.k, hp.p.host("dy"), with_router=True)
+    qref = backward_q(hp, exact["fw"])
+    got, (plan, dy, t, wb, routing) = run_backward(D)
+    got = {n: to_np(v) for n, v in got.items()}
+    assert np.array_equal(to_np(routing["topk_idx"]), exact["fw"]["topk_idx"])
+    names = ["dx", "dtopk_w", "dw_gate", "dw_up", "dw_down", "dw_router"]
+    if D.S:
+        names += ["dws_gate", "dws_up", "dws_down"]
+    errs = {}
+    for n in names:
+        errs[n] = (rel_err(got[n], qref[n]), rel_err(got[n], exact[n]), rel_err(qref[n], exact[n]))
+        say("   %-9s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)" % ((n,) + errs[n]))
+    bad = [n for n, (e_q, e_x, e_fmt) in errs.items() if e_q > TOL_Q or e_x > max(TOL["mxfp8"], e_fmt + 1e-2)]
+    for n in bad:
+        if n.startswith("dw_") and n != "dw_router":
+            per = [(rel_err(got[n][e], qref[n][e]), e, int(exact["fw"]["counts"][e])) for e in range(D.E)]
+            say("   %s worst experts (err, id, rows):" % n, sorted(per, reverse=True)[:4])
+    assert not bad, bad
+    empty = np.nonzero(exact["fw"]["counts"] == 0)[0]
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert not np.any(got[n][empty]), n
+    dx2, grads2 = plan.run(dy, t["x"], wb, routing)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(dx2), got["dx"])
+    for n, v in grads2.items():
+        assert np.array_equal(to_np(v), got[n]), n
+
+
+def test_c4_backward_sampled():
+    """The DeepSeek-V3-shaped MXFP8 layer (T=16384, Zipf-skewed routing)."""
+    D = gen.get_config("c4")
+    say("[case] c4 backward sampled", D)
+    got, (plan, dy, t, wb, routing) = run_backward(D)
+    del plan, dy, t, wb
+    hp = HostProblem(D)
+    ref_rt = hp.routing()
+    idx, g = ref_rt["topk_idx"], ref_rt["topk_w"]
+    assert np.array_equal(to_np(routing["topk_idx"]), idx)
+    from tests.moe_parity import sampled_backward
+    rng = np.random.default_rng(12)
+    tokens = np.sort(rng.choice(D.T, size=6, replace=False))
+    dx_ref, dg_ref = sampled_backward(hp, tokens, idx, g)
+    tk = torch.as_tensor(tokens, device=got["dx"].device)
+    dx_got, dg_got = to_np(got["dx"][tk]), to_np(got["dtopk_w"][tk])
+    dx_q, dg_q = sampled_backward_q(hp, tokens, idx, g)
+    for n, gv, ex, qv in (("dx", dx_got, dx_ref, dx_q), ("dtopk_w", dg_got, dg_ref, dg_q)):
+        e_q, e_x, e_fmt = rel_err(gv, qv), rel_err(gv, ex), rel_err(qv, ex)
+        say("   sampled tokens %-8s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)" % (n, e_q, e_x, e_fmt))
+        assert e_q <= TOL_Q and e_x <= max(TOL["mxfp8"], e_fmt + 1e-2), n
+    counts, offsets, row_token = ref_rt["counts"], ref_rt["offsets"], ref_rt["row_token"]
+    nz = np.nonzero(counts)[0]
+    picks = sorted({int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
+                    int(nz[np.argsort(counts[nz])[len(nz) // 2]])})
+    p = hp.p
+    for e in picks:
+        rows = np.arange(offsets[e], offsets[e + 1])
+        toks = row_token[rows]
+        gr = np.array([g[tk][list(idx[tk]).index(e)] for tk in toks], np.float64)
+        cols = np.sort(rng.choice(D.I, size=16, replace=False))
+        x, dyr = p.host_rows("x", toks), p.host_rows("dy", toks)
+        wg, wu = p.host_expert_rows("w_gate", e, cols), p.host_expert_rows("w_up", e, cols)
+        wd = p.host_expert("w_down", e)[:, cols]
+        # the FFN restricted to these intermediate columns has exactly these
+        # columns' weight gradients
+        _, dWg, dWu, dWd, _, _ = O.ffn_backward(x, wg, wu, wd, gr[:, None] * dyr)
+        _, _, qWg, qWu, qWd = expert_grads_q(x, dyr, gr, wg, wu, wd, with_da=False)
+        c = torch.as_tensor(cols, device=got["dx"].device)
+        for n, gv, ex, qv in (("dw_gate", to_np(got["dw_gate"][e][c]), dWg, qWg),
+                              ("dw_up", to_np(got["dw_up"][e][c]), dWu, qWu),
+                              ("dw_down", to_np(got["dw_down"][e][:, c]), dWd, qWd)):
+            e_q, e_x, e_fmt = rel_err(gv, qv), rel_err(gv, ex), rel_err(qv, ex)
+            say("   expert %d (%d rows) %-8s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)"
+                % (e, len(rows), n, e_q, e_x, e_fmt))
+            assert e_q <= TOL_Q and e_x <= max(TOL["mxfp8"], e_fmt + 1e-2), (e, n)
+    empty = np.nonzero(counts == 0)[0]
+    if len(empty):
+        assert torch.count_nonzero(got["dw_down"][int(empty[0])]) == 0

@@ -72,3 +72,15 @@ def test_round_trip_error_bound(axis):
     sat = scaled > 448
     assert np.all(np.abs(back - v)[~sat] <= half_q[~sat])
     assert np.all(np.abs(back - v)[sat] <= 64 * sc[sat])
+
+
+def test_round_trip_from_primitives_matches_codes():
+    """The parity tests' fast MX round trip (block exponent + E4M3 rounding,
+    no bit encoding) gives exactly dequantize(quantize(v))."""
+    from tests.moe_parity import qd
+    rng = np.random.default_rng(5)
+    for shape, axis in (((64, 96), -1), ((96, 40), 0), ((3, 32, 64), 1)):
+        v = (rng.standard_normal(shape) * rng.choice([1e-3, 1.0, 300.0])).astype(np.float32).astype(np.float64)
+        v.flat[::17] = 0.0
+        q, s = O.mx_quantize(v, axis=axis)
+        assert np.array_equal(qd(v, axis), O.mx_dequantize(q, s, axis=axis))
