@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
-"""Benchmark of the MoE layer forward on one MI355X (gfx950).
+"""Benchmark of the MoE layer hot path on one MI355X (gfx950).
 
-One step = one full forward of the layer (router, top-k, schedule and
-dispatch, shared and routed SwiGLU expert FFNs, weighted sum) over one batch
-of seeded synthetic tokens already resident in HBM.  Default workload: the
-DeepSeek-V3-shaped layer (T=8192, d=7168, 256 routed experts top-8, I=2048,
-one shared expert, Zipf(1.2)-skewed router) in bf16.
+One step = one full forward and backward of the DeepSeek-V3-shaped layer in
+MXFP8 (T=16384 tokens, d=7168, 256 routed experts top-8, I=2048, one bf16
+shared expert I=2048, Zipf(1.2)-skewed router, dY ~ N(0,1)): routing, schedule,
+quantized dispatch, shared and routed SwiGLU FFNs, weighted combine, then the
+backward (forward replay of G/U, dgrads with the fused SwiGLU backward and
+router-weight gradients, dX, deferred weight gradients, router gradient).
+Inputs are seeded synthetic tensors already resident in HBM.
 
-Prints ONE JSON line with the whole-job throughput, the roofline of the
-dominant kernel (the grouped gate/up GEMM with its SwiGLU epilogue) measured
-with HIP events on the stream it runs on, per-stage timings, and the CPU
-oracle timed on a bounded token sample of the same workload.
+Also measured in the same run: the bf16 DeepSeek-V3 layer (T=8192) forward and
+backward, standalone permute and combine bandwidth, and the CPU oracle on a
+bounded sample of the headline workload.
+
+Prints ONE JSON line.  Stage times come from HIP events that the library
+records on its stream at fixed stage boundaries during the timed steps; the
+roofline object describes the dominant kernel of the step.
 """
 import argparse
 import json
@@ -22,185 +27,269 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd/bwd tokens/sec + MFMA TFLOPS (% peak), DSV3 shape, bf16 & MXFP8"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK = {"bf16": 2500.0, "mxfp8": 5000.0}   # MI355X dense MFMA TFLOP/s
+PEAK_HBM_GBS = 8000.0
 
-WORKLOAD_NAMES = {
-    "c3a": "DSV3-shaped MoE layer forward, bf16, T=8192 tokens, d=7168, 256 routed experts top-8, I=2048, "
-           "1 shared expert I=2048, router logits biased by Zipf(1.2) over a seeded expert permutation",
-    "c3b": "DSV3-shaped MoE layer forward, bf16, T=32768 tokens, d=7168, 256 routed experts top-8, I=2048, "
-           "1 shared expert I=2048, router logits biased by Zipf(1.2) over a seeded expert permutation",
-    "c2": "Qwen3-235B-shaped MoE layer forward, bf16, T=8192 tokens, d=4096, 128 routed experts top-8, I=1536, "
-          "no shared expert",
-    "c1": "Mid MoE layer forward, bf16, T=4096 tokens, d=2048, 64 routed experts top-6, I=768, 1 shared expert",
-}
+WORKLOAD = ("DSV3-shaped MoE layer forward+backward, MXFP8 routed experts (E4M3, E8M0 per 32 along K) with bf16 "
+            "shared expert and router: T=16384 tokens, d=7168, 256 routed experts top-8, I=2048, 1 shared expert "
+            "I=2048, router logits biased by Zipf(1.2) over a seeded expert permutation, dY ~ N(0,1)")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_stream(fn, reps, torch):
-    """Average duration (s) of fn() over reps calls, HIP events on the current stream."""
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fn()
-    s.record()
-    for _ in range(reps):
-        fn()
-    e.record()
-    e.synchronize()
-    return s.elapsed_time(e) / 1e3 / reps
+def gemm_flops(D):
+    """Algorithmic FLOPs of each single-kernel GEMM stage (routed rows R)."""
+    r = 2.0 * D.R * D.d * D.I
+    return {"gate_up": 2 * r, "down": r, "replay_gate_up": 2 * r, "down_dgrad_swiglu": r, "gate_up_dgrad": 2 * r,
+            "wgrad_down": r, "wgrad_gate": r, "wgrad_up": r}
 
 
-def cpu_baseline(D, n_tokens):
-    """The oracle, as it stands, on a seeded sample of the workload's tokens:
-    routing of the sampled tokens plus their expert and shared FFNs and the
-    weighted sum.  Only the oracle's own arithmetic is timed; regenerating
-    the inputs on the host is not."""
+def split_flops(D):
+    """(routed, bf16-side) FLOPs of one forward+backward step."""
+    routed = 18.0 * D.R * D.d * D.I
+    other = 18.0 * D.T * D.S * D.d * D.Is + 6.0 * D.T * D.d * D.E
+    return routed, other
+
+
+def timed_steps(run, steps, torch):
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        run(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return max(wall, ev0.elapsed_time(ev1) / 1e3)
+
+
+def roofline_of(stages, flops, peak, label):
+    name = max(flops, key=lambda n: stages.get(n, 0.0))
+    ms = stages[name]
+    achieved = flops[name] / (ms / 1e3) / 1e12
+    return dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s", frac=round(achieved / peak, 4),
+                traffic=None, kernel="%s stage: %s" % (label, name), flops_per_launch=flops[name],
+                launch_ms=round(ms, 4))
+
+
+def cpu_baseline(D, rows_hot=8192, tokens=2048):
+    """The oracle, as it stands, on a bounded sample of the headline workload,
+    scaled to tokens/s.  A token's forward+backward costs its router
+    projection and softmax top-k, k routed-expert FFN forward+backward
+    evaluations on one row each, and one shared-expert forward+backward.  Timed
+    on the host (input regeneration untimed): the oracle FFN forward and
+    backward on `rows_hot` rows of the hottest expert plus every row of a
+    median-load expert (per-row cost), the shared expert and the router on
+    `tokens` tokens (per-token cost)."""
     import numpy as np
     import gen
     from oracle import moe_oracle as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: report the affinity mask
+    except Exception:
         threads = len(os.sched_getaffinity(0))
     p = gen.Problem(D)
     rng = np.random.default_rng(7)
-    tokens = np.sort(rng.choice(D.T, size=min(n_tokens, D.T), replace=False))
-    x = p.host_rows("x", tokens)
-    wr = p.host("w_router")
-    bias = p.logit_bias()
-    spent = 0.0
+    sample = np.sort(rng.choice(D.T, size=tokens, replace=False))
+    x = p.host_rows("x", sample)
+    dy = p.host_rows("dy", sample)
     t0 = time.perf_counter()
-    logits = O.router_logits(x, wr, bias)
+    logits = O.router_logits(x, p.host("w_router"), p.logit_bias())
     idx = O.topk_route(logits, D.k)
     g = O.renormalized_weights(logits, idx)
-    spent += time.perf_counter() - t0
-    y = np.zeros((len(tokens), D.d))
-    for e in range(D.E):
-        rows = np.nonzero(np.any(idx == e, axis=1))[0]
-        if len(rows) == 0:
-            continue
-        wg, wu, wd = (p.host_expert(n, e) for n in ("w_gate", "w_up", "w_down"))
+    t_router = (time.perf_counter() - t0) / tokens
+    # expert loads of the sample's routing stand in for the full histogram shape
+    counts = np.bincount(idx.reshape(-1), minlength=D.E)
+    hot = int(np.argmax(counts))
+    nz = np.nonzero(counts)[0]
+    med = int(nz[np.argsort(counts[nz])[len(nz) // 2]])
+    spent_rows, nrows = 0.0, 0
+    for e, n in ((hot, rows_hot), (med, max(int(counts[med]), 1))):
+        wg, wu, wd = (p.host_expert(nm, e) for nm in ("w_gate", "w_up", "w_down"))
+        xr = p.host_rows("x", rng.choice(D.T, size=n, replace=False))
+        dyr = p.host_rows("dy", rng.choice(D.T, size=n, replace=False))
         t0 = time.perf_counter()
-        out = O.swiglu_ffn(x[rows], wg, wu, wd)[0]
-        gw = g[rows][idx[rows] == e].astype(np.float64)
-        y[rows] += gw[:, None] * out
-        spent += time.perf_counter() - t0
-    if D.S:
-        ws = [p.host(n)[0] for n in ("ws_gate", "ws_up", "ws_down")]
-        t0 = time.perf_counter()
-        y += O.swiglu_ffn(x, *ws)[0]
-        spent += time.perf_counter() - t0
-    return dict(value=len(tokens) / spent, unit="tokens/s", cores=threads, kind="oracle",
-                sample="%d seeded tokens of the same workload (routing, all their routed and shared expert FFNs and "
-                       "the weighted sum, float64 numpy); %.1f s of oracle compute, input regeneration untimed"
-                       % (len(tokens), spent))
+        O.swiglu_ffn(xr, wg, wu, wd)
+        O.ffn_backward(xr, wg, wu, wd, 0.3 * dyr)
+        spent_rows += time.perf_counter() - t0
+        nrows += n
+    t_row = spent_rows / nrows
+    ws = [p.host(n)[0] for n in ("ws_gate", "ws_up", "ws_down")]
+    t0 = time.perf_counter()
+    O.swiglu_ffn(x, *ws)
+    O.ffn_backward(x, *ws, dy)
+    t_shared = (time.perf_counter() - t0) / tokens
+    per_token = t_router + D.k * t_row + t_shared
+    return dict(value=round(1.0 / per_token, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample="float64 numpy oracle: router + top-k on %d seeded tokens, routed-expert FFN forward+backward "
+                       "on %d rows (hottest expert %d rows, median expert %d rows), shared-expert forward+backward on "
+                       "the %d tokens; tokens/s = 1 / (router + k x per-row + shared) per-token cost; %.1f s of "
+                       "oracle compute, input regeneration untimed"
+                       % (tokens, nrows, rows_hot, nrows - rows_hot, tokens,
+                          t_router * tokens + spent_rows + t_shared * tokens))
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3a", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens for the CPU oracle baseline (0: skip)")
-    ap.add_argument("--stage-reps", type=int, default=5, help="repetitions per stage timing (0: skip)")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the CPU oracle sample (0: skip)")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 DeepSeek-V3 (T=8192) measurements")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
     import torch
     import gen
     import mixture_experts_layer_prefix_amd as M
-    D = gen.get_config(args.config)
+
+    D = gen.get_config("c4")
     log("[bench] workload", D)
     p = gen.Problem(D)
-    names = ("w_router", "w_gate", "w_up", "w_down") + (("ws_gate", "ws_up", "ws_down") if D.S else ())
+    names = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
     w = M.Weights(**{n: p.device(n) for n in names})
-    x, bias = p.device("x"), p.device_bias()
+    x, dy, bias = p.device("x"), p.device("dy"), p.device_bias()
     md = M.Dims(D.T, D.d, D.E, D.k, D.I, D.S, D.Is)
-    plan = M.ForwardPlan(md, D.prec, keep_routing=True)
+    wq = M.prepare_mxfp8(w, md)
+    wb = M.prepare_backward(wq, mxfp8=True)
+    fplan = M.ForwardPlan(md, "mxfp8")
+    bplan = M.BackwardPlan(md, "mxfp8")
     for _ in range(args.warmup):
-        plan.run(x, w, bias)
+        fplan.run(x, wq, bias)
+        bplan.run(dy, x, wb, fplan.routing)
     torch.cuda.synchronize()
     log("[bench] warmup done")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        plan.run(x, w, bias)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_s = ev0.elapsed_time(ev1) / 1e3
-    elapsed = max(wall, gpu_s)
+    tf, tb = M.StageTimer(0, args.steps), M.StageTimer(1, args.steps)
+
+    def step(i):
+        tf.arm(i)
+        fplan.run(x, wq, bias)
+        tb.arm(i)
+        bplan.run(dy, x, wb, fplan.routing)
+
+    elapsed = timed_steps(step, args.steps, torch)
+    tf.disarm()
+    tb.disarm()
     ms = elapsed / args.steps * 1e3
     tokens_s = D.T * args.steps / elapsed
-    tflops = D.fwd_flops() * args.steps / elapsed / 1e12
-    log("[bench] timed %d steps: %.3f ms/step, %.0f tokens/s, %.1f TFLOP/s" % (args.steps, ms, tokens_s, tflops))
-
-    # ---- stages, each through its own entry point, on the current stream ----
-    stages = {}
-    roofline = None
-    if args.stage_reps > 0:
-        r = plan.routing
-        reps = args.stage_reps
-        counts = r["expert_counts"]
-        stages["route"] = time_stream(lambda: M.route(x, w.w_router, md, D.prec, bias=bias), reps, torch)
-        perm = M.permute(r["topk_idx"], x, md, D.prec)
-        stages["permute"] = time_stream(lambda: M.permute(r["topk_idx"], x, md, D.prec), reps, torch)
-        x_perm, offsets, token_row = perm[4], perm[1], perm[3]
-        if D.S:
-            stages["shared_ffn"] = time_stream(lambda: M.shared_ffn(x, w, md, D.prec), reps, torch)
-        ws = torch.empty(max(M.workspace_bytes(md, D.prec, 2), 16), dtype=torch.uint8, device="cuda")
-        h, _ = M.expert_gate_up(x_perm, None, offsets, w, md, D.prec, ws=ws)
-        stages["gate_up"] = time_stream(lambda: M.expert_gate_up(x_perm, None, offsets, w, md, D.prec, ws=ws),
-                                        reps, torch)
-        o_perm = M.expert_down(h, None, offsets, w, md, D.prec, ws=ws)
-        stages["down"] = time_stream(lambda: M.expert_down(h, None, offsets, w, md, D.prec, ws=ws), reps, torch)
-        y_sh = M.shared_ffn(x, w, md, D.prec) if D.S else None
-        stages["combine"] = time_stream(lambda: M.combine(o_perm, token_row, r["topk_w"], y_sh, md, D.prec), reps,
-                                        torch)
-        R = D.T * D.k
-        gu_flops = 4.0 * R * D.d * D.I
-        achieved = gu_flops / stages["gate_up"] / 1e12
-        roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None,
-                        kernel="grouped gate/up GEMM + SwiGLU epilogue (gemm_bf16_kernel, gate/up mode)",
-                        flops_per_launch=gu_flops)
-        eb = 2
-        perm_bytes = D.T * D.d * eb + R * D.d * eb + R * 4
-        comb_bytes = R * D.d * eb + 2 * D.T * D.d * eb * (1 if D.S else 0.5) + R * 8
-        hbm = dict(permute_GBs=round(perm_bytes / stages["permute"] / 1e9, 1),
-                   combine_GBs=round(comb_bytes / stages["combine"] / 1e9, 1))
-        hbm["permute_frac"] = round(hbm["permute_GBs"] / PEAK_HBM_GBS, 4)
-        hbm["combine_frac"] = round(hbm["combine_GBs"] / PEAK_HBM_GBS, 4)
-        hc = counts.cpu()
-        skew = dict(max_rows=int(hc.max()), empty_experts=int((hc == 0).sum()), under_32=int((hc < 32).sum()))
-        log("[bench] stages ms:", {k: round(v * 1e3, 3) for k, v in stages.items()})
-    cpu = None
-    if args.cpu_sample > 0:
-        log("[bench] cpu baseline on %d tokens" % args.cpu_sample)
-        cpu = cpu_baseline(D, args.cpu_sample)
-        log("[bench] cpu baseline %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+    fwd_st, bwd_st = tf.mean_ms(), tb.mean_ms()
+    routed, other = split_flops(D)
+    tflops = (routed + other) / (ms / 1e3) / 1e12
+    t_roof = routed / (PEAK["mxfp8"] * 1e12) + other / (PEAK["bf16"] * 1e12)
+    stages = {"fwd_" + k: v for k, v in fwd_st.items()}
+    stages.update({"bwd_" + k: v for k, v in bwd_st.items()})
+    flops = {("fwd_" if n in ("gate_up", "down") else "bwd_") + n: f for n, f in gemm_flops(D).items()}
+    roofline = roofline_of(stages, flops, PEAK["mxfp8"], "MXFP8 grouped GEMM (gemm_mxfp8_kernel)")
+    log("[bench] timed %d steps: %.3f ms/step (fwd %.3f, bwd %.3f), %.0f tokens/s, %.1f TFLOP/s"
+        % (args.steps, ms, sum(fwd_st.values()), sum(bwd_st.values()), tokens_s, tflops))
+    log("[bench] stages ms:", {k: round(v, 3) for k, v in stages.items()})
+    del fplan, bplan, wb, wq
+    torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": D.prec, "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "T": D.T, "d": D.d, "E": D.E, "k": D.k, "I": D.I,
-                   "n_shared": D.S, "I_shared": D.Is, "precision": D.prec, "parallelism": "1 GPU"},
-        "tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "cpu_baseline": cpu,
+        "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "T": D.T, "d": D.d, "E": D.E, "k": D.k, "I": D.I, "n_shared": D.S,
+                   "I_shared": D.Is, "precision": "mxfp8 routed experts, bf16 shared expert and router",
+                   "pass": "forward+backward", "parallelism": "1 GPU"},
+        "tflops": round(tflops, 2), "roofline_step_frac": round(t_roof / (ms / 1e3), 4),
+        "roofline": roofline, "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
-    if stages:
-        out["stages_ms"] = {k: round(v * 1e3, 4) for k, v in stages.items()}
-        out["hbm"] = hbm
-        out["routing_skew"] = skew
+
+    if not args.no_bf16:
+        D3 = gen.get_config("c3a")
+        assert (D3.d, D3.E, D3.I, D3.S, D3.Is, D3.seed) == (D.d, D.E, D.I, D.S, D.Is, D.seed)  # same weights
+        p3 = gen.Problem(D3)
+        x3, dy3, bias3 = p3.device("x"), p3.device("dy"), p3.device_bias()
+        md3 = M.Dims(D3.T, D3.d, D3.E, D3.k, D3.I, D3.S, D3.Is)
+        wb3 = M.prepare_backward(w)
+        f3, b3 = M.ForwardPlan(md3, "bf16"), M.BackwardPlan(md3, "bf16")
+        for _ in range(args.warmup):
+            f3.run(x3, w, bias3)
+            b3.run(dy3, x3, wb3, f3.routing)
+        t3f, t3b = M.StageTimer(0, args.steps), M.StageTimer(1, args.steps)
+
+        def fstep(i):
+            t3f.arm(i)
+            f3.run(x3, w, bias3)
+
+        def bstep(i):
+            t3b.arm(i)
+            b3.run(dy3, x3, wb3, f3.routing)
+
+        ef = timed_steps(fstep, args.steps, torch)
+        eb = timed_steps(bstep, args.steps, torch)
+        t3f.disarm()
+        t3b.disarm()
+        fms, bms = ef / args.steps * 1e3, eb / args.steps * 1e3
+        fst, bst = t3f.mean_ms(), t3b.mean_ms()
+        ffl, bfl = D3.fwd_flops(), D3.bwd_flops()
+        st3 = {"fwd_" + k: v for k, v in fst.items()}
+        st3.update({"bwd_" + k: v for k, v in bst.items()})
+        fl3 = {("fwd_" if n in ("gate_up", "down") else "bwd_") + n: f for n, f in gemm_flops(D3).items()}
+        out["bf16_dsv3_t8192"] = {
+            "forward": {"ms": round(fms, 4), "tokens_s": round(D3.T / (fms / 1e3), 1),
+                        "tflops": round(ffl / (fms / 1e3) / 1e12, 2),
+                        "mfma_peak_frac": round(ffl / (fms / 1e3) / 1e12 / PEAK["bf16"], 4),
+                        "roofline": roofline_of({k: v for k, v in st3.items() if k.startswith("fwd_")},
+                                                {k: v for k, v in fl3.items() if k.startswith("fwd_")},
+                                                PEAK["bf16"], "bf16 grouped GEMM (gemm_bf16_kernel)")},
+            "backward": {"ms": round(bms, 4), "tokens_s": round(D3.T / (bms / 1e3), 1),
+                         "tflops": round(bfl / (bms / 1e3) / 1e12, 2),
+                         "mfma_peak_frac": round(bfl / (bms / 1e3) / 1e12 / PEAK["bf16"], 4),
+                         "roofline": roofline_of({k: v for k, v in st3.items() if k.startswith("bwd_")},
+                                                 {k: v for k, v in fl3.items() if k.startswith("bwd_")},
+                                                 PEAK["bf16"], "bf16 grouped GEMM (gemm_bf16_kernel)")},
+            "stages_ms": {k: round(v, 4) for k, v in st3.items()},
+        }
+        log("[bench] bf16 T=8192: fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)"
+            % (fms, ffl / (fms / 1e3) / 1e12, bms, bfl / (bms / 1e3) / 1e12))
+        # standalone dispatch gather and weighted sum (algorithmic bytes)
+        r = f3.routing
+        perm = M.permute(r["topk_idx"], x3, md3, "bf16")
+        o_perm = torch.empty(D3.R, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
+        y_sh = torch.empty(D3.T, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
+        reps = 5
+
+        def one(fn):
+            fn()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            e.synchronize()
+            return s.elapsed_time(e) / 1e3 / reps
+
+        t_perm = one(lambda: M.permute(r["topk_idx"], x3, md3, "bf16"))
+        t_comb = one(lambda: M.combine(o_perm, perm[3], r["topk_w"], y_sh, md3, "bf16"))
+        perm_bytes = D3.T * D3.d * 2 + D3.R * D3.d * 2 + D3.R * 4 * 3
+        comb_bytes = D3.R * D3.d * 2 + 2 * D3.T * D3.d * 2 + D3.R * 8
+        out["hbm"] = {"permute_GBs": round(perm_bytes / t_perm / 1e9, 1),
+                      "permute_frac": round(perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS, 4),
+                      "combine_GBs": round(comb_bytes / t_comb / 1e9, 1),
+                      "combine_frac": round(comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS, 4),
+                      "workload": "bf16, T=8192, d=7168, k=8 (standalone moe_permute with gather, moe_combine)"}
+        hc = r["expert_counts"].cpu()
+        out["routing_skew_t8192"] = dict(max_rows=int(hc.max()), empty_experts=int((hc == 0).sum()),
+                                         under_32=int((hc < 32).sum()))
+        del f3, b3, wb3
+
+    if args.cpu_sample > 0:
+        log("[bench] cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(D, rows_hot=4 * args.cpu_sample, tokens=args.cpu_sample)
+        log("[bench] cpu baseline %.2f tokens/s on %d threads" % (out["cpu_baseline"]["value"],
+                                                                  out["cpu_baseline"]["cores"]))
+    else:
+        out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
 
 

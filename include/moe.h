@@ -251,6 +251,22 @@ moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* d
 moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, int64_t cols, void* dst,
                                  void* stream);
 
+/* Stage-timing hook for profiling (host state of the library, not
+ * thread-safe).  events: n <= 32 caller-created hipEvent_t handles (host
+ * array); the fused entry points then record events[i] on their stream at
+ * stage boundary i, so that elapsed times between consecutive events give
+ * each stage's device time.  n = 0 disables.  Boundaries:
+ *   which = 0, moe_layer_forward: 0 start, 1 routed (router + top-k),
+ *     2 scheduled (+ MXFP8 token quantization), 3 shared FFN done,
+ *     4 routed gate/up done, 5 routed down done, 6 combine done;
+ *   which = 1, moe_layer_backward: 0 start, 1 prepared (padded offsets, row
+ *     weights, MXFP8 quantization of x and dY), 2 G|U replayed, 3 down dgrad
+ *     + SwiGLU backward done, 4 router-weight gradients done, 5 gate/up dgrad
+ *     done, 6 shared-expert input gradient done, 7 dx done, 8 transposes done,
+ *     9 dW_down done, 10 dW_gate done, 11 dW_up done, 12 shared weight
+ *     gradients done, 13 router gradient done. */
+moe_status moe_trace_events(int which, void* const* events, int n);
+
 /* MX quantization of a bf16 matrix src [rows][cols] (OCP MX v1.0; blog post
  * "MXFP8 support": a quantization kernel pre-quantizes the weights).
  * axis = 0: one block per 32 consecutive elements of a row (cols % 32 == 0):

@@ -12,6 +12,16 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+// Stage-timing hook (moe_trace_events): caller-created events recorded at
+// fixed stage boundaries of the fused forward (0) and backward (1).
+constexpr int kMaxTrace = 32;
+void* g_trace[2][kMaxTrace];
+int g_ntrace[2];
+
+void trace(int which, int i, hipStream_t s) {
+  if (i < g_ntrace[which] && g_trace[which][i]) (void)hipEventRecord(static_cast<hipEvent_t>(g_trace[which][i]), s);
+}
+
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -346,15 +356,19 @@ moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, 
 
 moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const uint8_t* A_scale,
                           const int32_t* a_rows, const int32_t* offsets, const moe_weights* w, void* o_perm,
-                          const FfnWs& ws, hipStream_t s) {
+                          const FfnWs& ws, hipStream_t s, bool traced = false) {
   if (prec == MOE_MXFP8) {
     MOE_TRY(run_gateup_mx(D, static_cast<const uint8_t*>(A), A_scale, a_rows, offsets, w,
                           static_cast<uint8_t*>(ws.h), ws.h_scale, ws.prefix, s));
+    if (traced) trace(0, 4, s);
     return run_down_mx(D, static_cast<const uint8_t*>(ws.h), ws.h_scale, offsets, w, o_perm, ws.prefix, s);
   }
   const int64_t a_bytes = a_rows ? D->T * (int64_t)D->d * (int64_t)act_bytes(prec) : 0;
-  return run_ffn_grouped(prec, A, a_rows, a_bytes, D->d, offsets, D->T * D->k, D->E, w->w_gate, w->w_up, w->w_down,
-                         D->d, D->I, ws.h, o_perm, ws.prefix, s);
+  const int64_t R = D->T * D->k;
+  MOE_TRY(run_gateup(prec, A, a_rows, a_bytes, D->d, offsets, R, D->E, w->w_gate, w->w_up, D->d, D->I, ws.h,
+                     ws.prefix, s));
+  if (traced) trace(0, 4, s);
+  return run_down(prec, offsets, R, D->E, w->w_down, D->d, D->I, ws.h, o_perm, ws.prefix, s);
 }
 
 moe_status run_shared_ffn(const moe_dims* D, moe_prec prec, const void* x, const moe_weights* w, void* y_shared,
@@ -471,12 +485,14 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   const int d = D->d, I = D->I, E = D->E, k = D->k;
   const bool router = g->dw_router != nullptr;
   const bool mx = b.pad == 128;
+  trace(1, 0, s);
   MOE_HIP(launch_pad_offsets(rt->expert_counts, E, T, b.pad, b.pad_off, b.single, s));
   MOE_HIP(launch_row_weight(rt->token_row, rt->topk_w, R, b.w_row, s));
   if (mx) {  // tokens and output gradients quantized once along d (row-wise: commutes with the gather)
     MOE_HIP(launch_quantize_mx(x, T, d, 0, b.xq, b.xqs, s));
     MOE_HIP(launch_quantize_mx(dy, T, d, 0, b.dyq, b.dyqs, s));
   }
+  trace(1, 1, s);
 
   // Forward replay up to the SwiGLU input: [G | U] of every routed row.
   GemmProblem q = gemm(GEMM_GU, mx ? (const void*)b.xq : x, d, rt->expert_offsets, R, E,
@@ -490,6 +506,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q.B1_scale = w->q_up_scale;
   }
   MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
+  trace(1, 2, s);
   // Reverse combine + down-projection input gradient dH' = dY_perm W_d with
   // the SwiGLU backward and the router-weight partials in the epilogue.
   q = gemm(GEMM_SWIGLU_BWD, mx ? (const void*)b.dyq : dy, d, rt->expert_offsets, R, E,
@@ -508,8 +525,10 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q.dgu_scale = b.dguqs;
   }
   MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
+  trace(1, 3, s);
   MOE_HIP(launch_dg(b.dg_part, I / 32, rt->token_row, rt->topk_w, T, k, g->dtopk_w, router ? b.dl : nullptr,
                     b.dl_row, s));
+  trace(1, 4, s);
   // Gate/up input gradient dA = dG W_g + dU W_u (K = 2I over two matrices).
   q = gemm(GEMM_DUALK, mx ? (const void*)b.dguq : b.dgu, 2 * I, rt->expert_offsets, R, E,
            mx ? (const void*)w->qt_gate : w->wt_gate, mx ? (const void*)w->qt_up : w->wt_up, (int64_t)d * I, d, 2 * I,
@@ -520,6 +539,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q.B1_scale = w->qt_up_scale;
   }
   MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
+  trace(1, 5, s);
 
   const int Is = D->n_shared ? D->I_shared : 0;
   if (Is) {
@@ -533,10 +553,12 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q = gemm(GEMM_DUALK, b.dgus, 2 * Is, nullptr, T, 1, w->wst_gate, w->wst_up, 0, d, 2 * Is, b.dxs, d, nullptr);
     MOE_HIP(launch_gemm_bf16(q, s));
   }
+  trace(1, 6, s);
   // Reverse dispatch: token-order sum in ascending expert order.
   MOE_HIP(launch_dx(static_cast<const bf16_t*>(b.da), rt->token_row, rt->topk_idx, router ? b.dl : nullptr,
                     static_cast<const bf16_t*>(w->w_router), Is ? static_cast<const bf16_t*>(b.dxs) : nullptr, dx, T,
                     d, k, s));
+  trace(1, 7, s);
 
   // Deferred weight gradients over each expert's whole (padded) row range.
   const bf16_t* gh = static_cast<const bf16_t*>(b.gh);
@@ -548,10 +570,14 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     MOE_HIP(launch_transpose_quant(dy, d, d, rt->row_token, off, b.pad_off, E, Rp, b.dyTq, b.dyTqs, Rp, s));
     MOE_HIP(launch_transpose_quant(gh, I, I, nullptr, off, b.pad_off, E, Rp, b.ghTq, b.ghTqs, Rp, s));
     MOE_HIP(launch_transpose_quant(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, Rp, b.dguTq, b.dguTqs, Rp, s));
+    trace(1, 8, s);
     MOE_TRY(run_wgrad_mx(b.dyTq, b.dyTqs, d, b.ghTq, b.ghTqs, I, Rp, b.pad_off, E, g->dw_down, s));
+    trace(1, 9, s);
     MOE_TRY(run_wgrad_mx(b.dguTq, b.dguTqs, I, b.xTq, b.xTqs, d, Rp, b.pad_off, E, g->dw_gate, s));
+    trace(1, 10, s);
     MOE_TRY(run_wgrad_mx(b.dguTq + (int64_t)I * Rp, b.dguTqs + (int64_t)I * Rs, I, b.xTq, b.xTqs, d, Rp, b.pad_off, E,
                          g->dw_up, s));
+    trace(1, 11, s);
   } else {
     MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.xT), b.Rp,
                                   s));
@@ -560,10 +586,14 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     MOE_HIP(launch_transpose_rows(gh, I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.ghT), b.Rp, s));
     MOE_HIP(launch_transpose_rows(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT),
                                   b.Rp, s));
+    trace(1, 8, s);
     const bf16_t* dguT = static_cast<const bf16_t*>(b.dguT);
     MOE_TRY(run_wgrad(b.dyT, d, b.ghT, I, b.Rp, b.pad_off, E, g->dw_down, s));
+    trace(1, 9, s);
     MOE_TRY(run_wgrad(dguT, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_gate, s));
+    trace(1, 10, s);
     MOE_TRY(run_wgrad(dguT + (int64_t)I * b.Rp, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_up, s));
+    trace(1, 11, s);
   }
   if (Is) {
     const int32_t* seg = b.single + 2;
@@ -578,9 +608,11 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     MOE_TRY(run_wgrad(dgusT, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_gate, s));
     MOE_TRY(run_wgrad(dgusT + (int64_t)Is * b.Tp, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_up, s));
   }
+  trace(1, 12, s);
   if (router)
     MOE_HIP(launch_router_wgrad(x, rt->row_token, b.dl_row, rt->expert_offsets, b.pad_off, E, d, b.Rp,
                                 b.router_partial, g->dw_router, s));
+  trace(1, 13, s);
   return MOE_OK;
 }
 
@@ -737,7 +769,9 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
     MOE_HIP(launch_schedule(nullptr, 0, dims->E, dims->k, f.counts, f.offsets, nullptr, nullptr, f.sched, s));
     return MOE_OK;
   }
+  trace(0, 0, s);
   MOE_TRY(run_route(dims, prec, x, w->w_router, logit_bias, f.logits, f.topk_idx, f.topk_w, s));
+  trace(0, 1, s);
   // Dispatch: the schedule places every route; in bf16 the grouped gate/up
   // GEMM then reads its A rows straight from x through row_token (the gather
   // rides in the GEMM's loads and x_perm is never written).
@@ -749,15 +783,19 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
   if (prec == MOE_MXFP8)
     MOE_HIP(launch_quantize_mx(static_cast<const bf16_t*>(x), dims->T, dims->d, 0, static_cast<uint8_t*>(f.x_perm),
                                f.x_perm_scale, s));
+  trace(0, 2, s);
   if (dims->n_shared > 0) MOE_TRY(run_shared_ffn(dims, prec, x, w, f.y_shared, f.hs, s));
+  trace(0, 3, s);
   if (prec == MOE_MXFP8)
-    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, f.x_perm_scale, f.row_token, f.offsets, w, f.o_perm, f.ffn, s));
+    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, f.x_perm_scale, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true));
   else if (fused_gather)
-    MOE_TRY(run_expert_ffn(dims, prec, x, nullptr, f.row_token, f.offsets, w, f.o_perm, f.ffn, s));
+    MOE_TRY(run_expert_ffn(dims, prec, x, nullptr, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true));
   else
-    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, nullptr, f.offsets, w, f.o_perm, f.ffn, s));
+    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, nullptr, f.offsets, w, f.o_perm, f.ffn, s, true));
+  trace(0, 5, s);
   MOE_HIP(launch_combine(prec == MOE_F32, f.o_perm, f.token_row, f.topk_w, f.y_shared, y, dims->T, dims->d, dims->k,
                          s));
+  trace(0, 6, s);
   return MOE_OK;
 }
 
@@ -798,6 +836,13 @@ moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* d
   BwdWs b = carve_backward(c, dims, prec);
   return run_backward(dims, static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(x), w, routing,
                       static_cast<bf16_t*>(dx), g, b, s);
+}
+
+moe_status moe_trace_events(int which, void* const* events, int n) {
+  if ((which != 0 && which != 1) || n < 0 || n > kMaxTrace || (n > 0 && !events)) return MOE_EINVAL;
+  for (int i = 0; i < kMaxTrace; ++i) g_trace[which][i] = i < n ? events[i] : nullptr;
+  g_ntrace[which] = n;
+  return MOE_OK;
 }
 
 moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, int64_t cols, void* dst,

@@ -296,3 +296,44 @@ class BackwardPlan:
 def layer_backward(dy, x, weights: Weights, routing, dims: Dims, prec: str, router_grad=True):
     plan = BackwardPlan(dims, prec, dy.device, router_grad)
     return plan.run(dy, x, weights, routing)
+
+
+FWD_STAGES = ("route", "schedule", "shared_ffn", "gate_up", "down", "combine")
+BWD_STAGES = ("prepare", "replay_gate_up", "down_dgrad_swiglu", "router_weight_grad", "gate_up_dgrad",
+              "shared_dgrad", "dx", "transposes", "wgrad_down", "wgrad_gate", "wgrad_up", "shared_wgrad",
+              "router_grad")
+
+
+class StageTimer:
+    """Per-stage device times of the fused forward (which=0) or backward
+    (which=1) from events the library records at its stage boundaries
+    (moe_trace_events): one event set per call, read after the calls."""
+
+    def __init__(self, which, calls):
+        self.which = which
+        self.names = FWD_STAGES if which == 0 else BWD_STAGES
+        self.sets = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+                     for _ in range(calls)]
+        for evs in self.sets:  # create the underlying HIP events
+            for e in evs:
+                e.record()
+        torch.cuda.synchronize()
+        self.used = 0
+
+    def arm(self, i):
+        """Record the next traced call into event set i."""
+        evs = self.sets[i]
+        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        call("moe_trace_events", self.which, arr, len(evs))
+        self.used = max(self.used, i + 1)
+
+    def disarm(self):
+        call("moe_trace_events", self.which, None, 0)
+
+    def mean_ms(self):
+        torch.cuda.synchronize()
+        out = dict.fromkeys(self.names, 0.0)
+        for evs in self.sets[:self.used]:
+            for k, n in enumerate(self.names):
+                out[n] += evs[k].elapsed_time(evs[k + 1]) / self.used
+        return out
