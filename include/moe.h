@@ -112,9 +112,10 @@ typedef struct {
   float* dw_router;       /* [E][d] fp32, or NULL */
 } moe_grads;
 
-/* Routing state of one forward pass (host struct of caller-owned device
- * pointers), kept for inspection or for a later backward.  Any field may be
- * NULL in moe_layer_forward (then it lives in the workspace). */
+/* Routing state of one forward pass and the activations kept for a later
+ * backward (host struct of caller-owned device pointers).  Any field may be
+ * NULL in moe_layer_forward (then it lives in the workspace, or for gu and
+ * gu_shared is not kept). */
 typedef struct {
   float* logits;          /* [T][E] fp32 */
   int32_t* topk_idx;      /* [T][k] ascending expert id */
@@ -123,6 +124,8 @@ typedef struct {
   int32_t* expert_offsets;/* [E+1] */
   int32_t* row_token;     /* [R] */
   int32_t* token_row;     /* [T][k] */
+  void* gu;               /* [R][2I] bf16: gate and up projections G | U of every routed row */
+  void* gu_shared;        /* [T][2I_s] bf16: G | U of the shared expert */
 } moe_routing;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -227,7 +230,8 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
  * backward, return the input gradients to token order, then the weight
  * gradients over each expert's whole token range) and "Router weight
  * gradient computation" (dL/dg of a route = <h, dY W_d>, fused into the
- * SwiGLU backward).  G and U are recomputed from x (the forward replay of
+ * SwiGLU backward).  G and U come from routing->gu / gu_shared when the
+ * forward kept them, else they are recomputed from x (the forward replay of
  * the blog post's "Reversed ring order" section).  Router chain, with the
  * selection held fixed: dl_j = g_j (dg_j - sum_i g_i dg_i) for the selected
  * experts, dW_router = dl^T x, dx += dl W_router.

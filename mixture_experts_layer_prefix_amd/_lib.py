@@ -41,7 +41,8 @@ class moe_grads(ctypes.Structure):
 
 class moe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "logits", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "row_token", "token_row")]
+        "logits", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "row_token", "token_row", "gu",
+        "gu_shared")]
 
 
 _P = ctypes.c_void_p

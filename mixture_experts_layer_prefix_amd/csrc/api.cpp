@@ -252,7 +252,7 @@ moe_status run_permute(const moe_dims* D, moe_prec prec, const int32_t* idx, con
 // Grouped gate/up GEMM with the SwiGLU epilogue into h.
 moe_status run_gateup(moe_prec prec, const void* A, const int32_t* a_rows, int64_t a_bytes, int64_t lda,
                       const int32_t* row_off, int64_t M, int G, const void* wg, const void* wu, int d, int I, void* h,
-                      int32_t* prefix, hipStream_t s) {
+                      int32_t* prefix, hipStream_t s, void* gu_out = nullptr) {
   GemmProblem q = {};
   q.mode = GEMM_GATEUP;
   q.A = A;
@@ -270,6 +270,7 @@ moe_status run_gateup(moe_prec prec, const void* A, const int32_t* a_rows, int64
   q.C = h;
   q.ldc = I;
   q.tile_prefix = prefix;
+  q.gu_out = gu_out;
   MOE_HIP(prec == MOE_F32 ? launch_gemm_f32(q, s) : launch_gemm_bf16(q, s));
   return MOE_OK;
 }
@@ -298,7 +299,7 @@ moe_status run_down(moe_prec prec, const int32_t* row_off, int64_t M, int G, con
 // MXFP8 grouped gate/up (h quantized along I in the epilogue) and down.
 moe_status run_gateup_mx(const moe_dims* D, const uint8_t* A, const uint8_t* A_scale, const int32_t* a_rows,
                          const int32_t* offsets, const moe_weights* w, uint8_t* h, uint8_t* h_scale, int32_t* prefix,
-                         hipStream_t s) {
+                         hipStream_t s, void* gu_out = nullptr) {
   GemmProblem q = {};
   q.mode = GEMM_GATEUP;
   q.A = A;
@@ -320,6 +321,7 @@ moe_status run_gateup_mx(const moe_dims* D, const uint8_t* A, const uint8_t* A_s
   q.C_scale = h_scale;
   q.ldc = D->I;
   q.tile_prefix = prefix;
+  q.gu_out = gu_out;
   MOE_HIP(launch_gemm_mxfp8(q, s));
   return MOE_OK;
 }
@@ -349,30 +351,30 @@ moe_status run_down_mx(const moe_dims* D, const uint8_t* h, const uint8_t* h_sca
 // One SwiGLU FFN over grouped rows: gate/up (+SwiGLU) into h, then down.
 moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, int64_t a_bytes, int64_t lda,
                            const int32_t* row_off, int64_t M, int G, const void* wg, const void* wu, const void* wd,
-                           int d, int I, void* h, void* out, int32_t* prefix, hipStream_t s) {
-  MOE_TRY(run_gateup(prec, A, a_rows, a_bytes, lda, row_off, M, G, wg, wu, d, I, h, prefix, s));
+                           int d, int I, void* h, void* out, int32_t* prefix, hipStream_t s, void* gu_out = nullptr) {
+  MOE_TRY(run_gateup(prec, A, a_rows, a_bytes, lda, row_off, M, G, wg, wu, d, I, h, prefix, s, gu_out));
   return run_down(prec, row_off, M, G, wd, d, I, h, out, prefix, s);
 }
 
 moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const uint8_t* A_scale,
                           const int32_t* a_rows, const int32_t* offsets, const moe_weights* w, void* o_perm,
-                          const FfnWs& ws, hipStream_t s, bool traced = false) {
+                          const FfnWs& ws, hipStream_t s, bool traced = false, void* gu_out = nullptr) {
   if (prec == MOE_MXFP8) {
     MOE_TRY(run_gateup_mx(D, static_cast<const uint8_t*>(A), A_scale, a_rows, offsets, w,
-                          static_cast<uint8_t*>(ws.h), ws.h_scale, ws.prefix, s));
+                          static_cast<uint8_t*>(ws.h), ws.h_scale, ws.prefix, s, gu_out));
     if (traced) trace(0, 4, s);
     return run_down_mx(D, static_cast<const uint8_t*>(ws.h), ws.h_scale, offsets, w, o_perm, ws.prefix, s);
   }
   const int64_t a_bytes = a_rows ? D->T * (int64_t)D->d * (int64_t)act_bytes(prec) : 0;
   const int64_t R = D->T * D->k;
   MOE_TRY(run_gateup(prec, A, a_rows, a_bytes, D->d, offsets, R, D->E, w->w_gate, w->w_up, D->d, D->I, ws.h,
-                     ws.prefix, s));
+                     ws.prefix, s, gu_out));
   if (traced) trace(0, 4, s);
   return run_down(prec, offsets, R, D->E, w->w_down, D->d, D->I, ws.h, o_perm, ws.prefix, s);
 }
 
 moe_status run_shared_ffn(const moe_dims* D, moe_prec prec, const void* x, const moe_weights* w, void* y_shared,
-                          void* hs, hipStream_t s) {
+                          void* hs, hipStream_t s, void* gu_out = nullptr) {
   if (D->T == 0) return MOE_OK;
   if (D->n_shared == 0) {
     MOE_HIP(launch_fill_zero(y_shared, (size_t)D->T * D->d * act_bytes(prec), s));
@@ -380,7 +382,7 @@ moe_status run_shared_ffn(const moe_dims* D, moe_prec prec, const void* x, const
   }
   const moe_prec p = prec == MOE_F32 ? MOE_F32 : MOE_BF16;  // shared expert stays bf16 under MXFP8
   return run_ffn_grouped(p, x, nullptr, 0, D->d, nullptr, D->T, 1, w->ws_gate, w->ws_up, w->ws_down, D->d,
-                         D->I_shared, hs, y_shared, nullptr, s);
+                         D->I_shared, hs, y_shared, nullptr, s, gu_out);
 }
 
 moe_status check_weights(const moe_dims* D, moe_prec prec, const moe_weights* w, bool routed, bool shared,
@@ -494,8 +496,11 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   }
   trace(1, 1, s);
 
-  // Forward replay up to the SwiGLU input: [G | U] of every routed row.
-  GemmProblem q = gemm(GEMM_GU, mx ? (const void*)b.xq : x, d, rt->expert_offsets, R, E,
+  // G | U of every routed row: kept by the forward, or replayed here.
+  const void* gu = rt->gu ? rt->gu : b.gu;
+  GemmProblem q;
+  if (!rt->gu) {
+  q = gemm(GEMM_GU, mx ? (const void*)b.xq : x, d, rt->expert_offsets, R, E,
                        mx ? (const void*)w->q_gate : w->w_gate, mx ? (const void*)w->q_up : w->w_up, (int64_t)I * d,
                        I, d, b.gu, 2 * I, b.prefix);
   q.a_rows = rt->row_token;
@@ -506,6 +511,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q.B1_scale = w->q_up_scale;
   }
   MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
+  }
   trace(1, 2, s);
   // Reverse combine + down-projection input gradient dH' = dY_perm W_d with
   // the SwiGLU backward and the router-weight partials in the epilogue.
@@ -513,7 +519,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
            mx ? (const void*)w->qt_down : w->wt_down, nullptr, (int64_t)I * d, I, d, b.dgu, 2 * I, b.prefix);
   q.a_rows = rt->row_token;
   q.a_bytes = T * (int64_t)d * (mx ? 1 : 2);
-  q.gu = b.gu;
+  q.gu = gu;
   q.w_row = b.w_row;
   q.dgu = b.dgu;
   q.h_out = b.gh;
@@ -543,10 +549,12 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
 
   const int Is = D->n_shared ? D->I_shared : 0;
   if (Is) {
-    q = gemm(GEMM_GU, x, d, nullptr, T, 1, w->ws_gate, w->ws_up, 0, Is, d, b.gus, 2 * Is, nullptr);
-    MOE_HIP(launch_gemm_bf16(q, s));
+    if (!rt->gu_shared) {
+      q = gemm(GEMM_GU, x, d, nullptr, T, 1, w->ws_gate, w->ws_up, 0, Is, d, b.gus, 2 * Is, nullptr);
+      MOE_HIP(launch_gemm_bf16(q, s));
+    }
     q = gemm(GEMM_SWIGLU_BWD, dy, d, nullptr, T, 1, w->wst_down, nullptr, 0, Is, d, b.dgus, 2 * Is, nullptr);
-    q.gu = b.gus;
+    q.gu = rt->gu_shared ? rt->gu_shared : b.gus;
     q.dgu = b.dgus;
     q.h_out = b.hs;
     MOE_HIP(launch_gemm_bf16(q, s));
@@ -755,7 +763,8 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
   if (!opt_ok(logit_bias)) return MOE_EINVAL;
   if (routing) {
     const void* f[] = {routing->logits, routing->topk_idx, routing->topk_w, routing->expert_counts,
-                       routing->expert_offsets, routing->row_token, routing->token_row};
+                       routing->expert_offsets, routing->row_token, routing->token_row, routing->gu,
+                       routing->gu_shared};
     for (const void* p : f)
       if (!opt_ok(p)) return MOE_EINVAL;
   }
@@ -784,12 +793,17 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
     MOE_HIP(launch_quantize_mx(static_cast<const bf16_t*>(x), dims->T, dims->d, 0, static_cast<uint8_t*>(f.x_perm),
                                f.x_perm_scale, s));
   trace(0, 2, s);
-  if (dims->n_shared > 0) MOE_TRY(run_shared_ffn(dims, prec, x, w, f.y_shared, f.hs, s));
+  // G | U kept for a later backward when the caller provides the buffers
+  // (bf16 and MXFP8: their backward consumes them).
+  void* keep_gu = routing && prec != MOE_F32 ? routing->gu : nullptr;
+  void* keep_gus = routing && prec != MOE_F32 ? routing->gu_shared : nullptr;
+  if (dims->n_shared > 0) MOE_TRY(run_shared_ffn(dims, prec, x, w, f.y_shared, f.hs, s, keep_gus));
   trace(0, 3, s);
   if (prec == MOE_MXFP8)
-    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, f.x_perm_scale, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true));
+    MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, f.x_perm_scale, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true,
+                           keep_gu));
   else if (fused_gather)
-    MOE_TRY(run_expert_ffn(dims, prec, x, nullptr, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true));
+    MOE_TRY(run_expert_ffn(dims, prec, x, nullptr, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true, keep_gu));
   else
     MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, nullptr, nullptr, f.offsets, w, f.o_perm, f.ffn, s, true));
   trace(0, 5, s);
@@ -815,6 +829,7 @@ moe_status moe_layer_backward(const moe_dims* dims, moe_prec prec, const void* d
     for (const void* p : f)
       if (!ptr_ok(p)) return MOE_EINVAL;
   }
+  if (!opt_ok(routing->gu) || !opt_ok(routing->gu_shared)) return MOE_EINVAL;
   const size_t need = workspace_size(dims, prec, 4);
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
   if (!aligned16(ws)) return MOE_EINVAL;

@@ -182,6 +182,7 @@ struct GemmProblem {
   void* dgu;                // [rows][2N] out: dG | dU
   void* h_out;              // [rows][N] out: w_row * h (nullptr: skip)
   float* dg_part;           // [rows][N/32] out: partial <dH', h> per 32 columns (nullptr: skip)
+  void* gu_out;              // gate/up: optional [rows][2N] bf16 G | U (kept for the backward)
   uint8_t* dgu_q;           // MX: [rows][2N] dG | dU quantized along the columns
   uint8_t* dgu_scale;       // MX: [rows][2N/32]
   // K-grouped (weight gradient) mode

@@ -46,8 +46,11 @@ constexpr int kPad = 8;     // bf16 elements of padding per LDS row (16 bytes)
 constexpr int kBK = 64;     // K slab
 constexpr int kLdsK = kBK + kPad;
 constexpr int kBigM = 256, kSmallM = 64, kBN = 256;
-constexpr int kWavesM = 2, kWavesN = 4;           // 8 waves: 2 per SIMD
-constexpr int kThreads = 64 * kWavesM * kWavesN;  // 512
+#ifndef MOE_GEMM_WAVES_N
+#define MOE_GEMM_WAVES_N 4
+#endif
+constexpr int kWavesM = 2, kWavesN = MOE_GEMM_WAVES_N;  // 2 x 4: 8 waves, 2 per SIMD
+constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr size_t kSmemBytes = 2ull * (kBigM + kBN) * kBK * sizeof(bf16_t);  // 131,072 B
 
 // Tile counts of a group of `rows` rows.
@@ -129,6 +132,7 @@ struct KArgs {
   float* dg_part;
   const int32_t* k_off;
   int64_t c_group_stride;
+  bf16_t* gu_out;        // gate/up: optional [rows][2N] G | U output
 };
 
 // LDS swizzle of a 128-byte row: chunk position = logical chunk ^ swz(row).
@@ -237,9 +241,9 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   const bf16_t* b0 = p.B0 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb;
   const bf16_t* b1 = (PAIRED || MODE == GEMM_DUALK) ? p.B1 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb
                                                     : b0;
-  const __amdgpu_buffer_rsrc_t br0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(PAIRED && ((wave >> 2) & 1) ? b1 : b0), (short)0, (int)bbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t br1 = MODE == GEMM_DUALK
+  const __amdgpu_buffer_rsrc_t br0 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b0), (short)0, (int)bbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t br1 = (PAIRED || MODE == GEMM_DUALK)
       ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b1), (short)0, (int)bbytes, 0x00020000)
       : br0;
   const uint32_t boff = (uint32_t)((lane >> 3) * ldb * 2) + chunk * 16;
@@ -255,11 +259,15 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
     const int kb = MODE == GEMM_DUALK ? (second ? k0 - p.k_half : k0) : ka;
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
-      // first B row (within this N-tile) of this wave's 8 rows in round i
-      int r0 = PAIRED ? i * (RPR / 2) + (wave & 3) * 8 : i * RPR + wave * 8;
+      // LDS rows lr.. lr+7 of this wave in round i; paired modes fill 32-row
+      // LDS blocks alternately from the two matrices (block b: matrix b & 1,
+      // matrix rows (b >> 1) * 32 ..), so the matrix choice is wave-uniform.
+      const int lr = i * RPR + wave * 8;
+      const int blk = lr >> 5;
+      int r0 = PAIRED ? (blk >> 1) * 32 + (lr & 31) : lr;
       r0 = min(r0, p.N - first_row - 8);  // rows past N load valid rows; their outputs are not stored
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? br1 : br0,
-                                               (lds_void*)(Bs + (buf * BN + i * RPR + wave * 8) * kBK), 16, boff,
+      const bool use1 = PAIRED ? (blk & 1) != 0 : second;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(use1 ? br1 : br0, (lds_void*)(Bs + (buf * BN + lr) * kBK), 16, boff,
                                                (uint32_t)((r0 * ldb + kb) * 2), 0, 0);
     }
   };
@@ -401,7 +409,14 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
         for (int q = 0; q < FN / 2; ++q) {
           const float gv = acc[i][2 * q][v], uv = acc[i][2 * q + 1][v];
           const int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
-          if (col < p.N) Crow[col] = f32_to_bf16(silu_f32(gv) * uv);
+          if (col < p.N) {
+            Crow[col] = f32_to_bf16(silu_f32(gv) * uv);
+            if (p.gu_out) {  // G | U kept for the backward
+              bf16_t* srow = p.gu_out + (row0 + rl) * 2 * p.N;
+              srow[col] = f32_to_bf16(gv);
+              srow[p.N + col] = f32_to_bf16(uv);
+            }
+          }
         }
       } else if (MODE == GEMM_GU) {
 #pragma unroll
@@ -627,6 +642,7 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   a.dg_part = q.dg_part;
   a.k_off = q.k_off;
   a.c_group_stride = q.c_group_stride;
+  a.gu_out = static_cast<bf16_t*>(q.gu_out);
   a.C = q.C;
   a.ldc = q.ldc;
   a.bias = q.bias;

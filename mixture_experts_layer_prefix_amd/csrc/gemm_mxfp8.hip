@@ -139,6 +139,7 @@ struct MxArgs {
   // K-grouped weight-gradient mode
   const int32_t* k_off;
   int64_t c_group_stride;
+  bf16_t* gu_out;           // gate/up: optional [rows][2N] G | U output
 };
 
 __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) {
@@ -371,6 +372,10 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
           uint8_t* C = static_cast<uint8_t*>(p.C);
           C[grow * ldc + col] = (uint8_t)code;
           if ((lane & 31) == 0) p.Cs[grow * (ldc / 32) + col / 32] = (uint8_t)sc;
+          if (p.gu_out) {  // G | U kept for the backward
+            p.gu_out[grow * 2 * N + col] = f32_to_bf16(acc[i][0][v]);
+            p.gu_out[grow * 2 * N + N + col] = f32_to_bf16(acc[i][1][v]);
+          }
         }
       } else if constexpr (MODE == GEMM_GU) {
         const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
@@ -570,6 +575,7 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.dg_part = q.dg_part;
   a.k_off = q.k_off;
   a.c_group_stride = q.c_group_stride;
+  a.gu_out = static_cast<bf16_t*>(q.gu_out);
   a.spread_small = MODE == GEMM_DOWN ? 1 : 0;
   if (MODE == GEMM_WGRAD) {
     a.big = a.small = nullptr;

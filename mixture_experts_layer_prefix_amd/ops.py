@@ -178,7 +178,9 @@ class ForwardPlan:
     """Pre-allocated output, routing buffers and workspace of one forward
     configuration, so that repeated calls allocate nothing."""
 
-    def __init__(self, dims: Dims, prec: str, device="cuda", keep_routing=True):
+    def __init__(self, dims: Dims, prec: str, device="cuda", keep_routing=True, keep_gu=False):
+        """keep_gu: also keep the gate/up projections G | U (routed and shared)
+        for a later backward, which then skips their recomputation."""
         self.dims, self.prec = dims, prec
         T, E, k = dims.T, dims.E, dims.k
         self.y = torch.empty(T, dims.d, dtype=_act_dtype(prec), device=device)
@@ -193,6 +195,10 @@ class ForwardPlan:
                 expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
                 row_token=torch.empty(max(dims.R, 1), dtype=torch.int32, device=device),
                 token_row=torch.empty(T, k, dtype=torch.int32, device=device))
+            if keep_gu:
+                self.routing["gu"] = torch.empty(max(dims.R, 1), 2 * dims.I, dtype=torch.bfloat16, device=device)
+                if dims.S:
+                    self.routing["gu_shared"] = torch.empty(T, 2 * dims.Is, dtype=torch.bfloat16, device=device)
             self.rt = moe_routing(**{n: t.data_ptr() for n, t in self.routing.items()})
         self.ws, self.ws_bytes = _workspace(dims, prec, 0, device)
         self.cdims = dims.c()
@@ -205,8 +211,8 @@ class ForwardPlan:
         return self.y
 
 
-def layer_forward(x, weights: Weights, dims: Dims, prec: str, bias=None, keep_routing=True):
-    plan = ForwardPlan(dims, prec, x.device, keep_routing)
+def layer_forward(x, weights: Weights, dims: Dims, prec: str, bias=None, keep_routing=True, keep_gu=False):
+    plan = ForwardPlan(dims, prec, x.device, keep_routing, keep_gu)
     y = plan.run(x, weights, bias)
     return y, plan.routing
 

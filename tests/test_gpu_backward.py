@@ -96,6 +96,13 @@ def test_small_backward_full(name):
     assert torch.equal(dx3, dx)
     for n in grads:
         assert torch.equal(grads3[n], grads[n]), n
+    # G | U kept by the forward: the same bits as the backward's own replay
+    _, routing4 = M.layer_forward(t["x"], wb, md, D.prec, bias=t["bias"], keep_gu=True)
+    assert "gu" in routing4
+    dx4, grads4 = M.layer_backward(dy, t["x"], wb, routing4, md, D.prec, router_grad=True)
+    assert torch.equal(dx4, dx)
+    for n in grads:
+        assert torch.equal(grads4[n], grads[n]), n
 
 
 def test_backward_no_tokens():

@@ -193,6 +193,14 @@ def test_small_mxfp8_backward(name):
     assert np.array_equal(to_np(dx2), got["dx"])
     for n, v in grads2.items():
         assert np.array_equal(to_np(v), got[n]), n
+    # G | U kept by the forward: the same bits as the backward's own replay
+    import mixture_experts_layer_prefix_amd as M
+    _, routing3 = M.layer_forward(t["x"], wb, plan.dims, "mxfp8", bias=t["bias"], keep_gu=True)
+    dx3, grads3 = plan.run(dy, t["x"], wb, routing3)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(dx3), got["dx"])
+    for n, v in grads3.items():
+        assert np.array_equal(to_np(v), got[n]), n
 
 
 def test_c4_backward_sampled():
