@@ -333,12 +333,22 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
     wait_vmcnt<0>();
   }
   __syncthreads();
+  // Keep the first half-slab's MFMAs ahead of the slab barrier: they only feed
+  // later MFMAs, and without this pin the compiler sinks them below the
+  // barrier, leaving the LDS reads of every slab exposed.
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
+  };
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % NS;
     read_scales(st);
     read_frags(st, 0);
     mma(0);
     read_frags(st, 1);
+    pin_acc();
     mma(1);
     if (kt + NS - 1 < KT) {
       if (any_sc) wait_vmcnt<(NS - 2) * (LPS + 1)>(); else wait_vmcnt<(NS - 2) * LPS>();
