@@ -574,10 +574,14 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   const int32_t* off = rt->expert_offsets;
   if (mx) {
     const int64_t Rp = b.Rp, Rs = b.Rp / 32;
-    MOE_HIP(launch_transpose_quant(x, d, d, rt->row_token, off, b.pad_off, E, Rp, b.xTq, b.xTqs, Rp, s));
-    MOE_HIP(launch_transpose_quant(dy, d, d, rt->row_token, off, b.pad_off, E, Rp, b.dyTq, b.dyTqs, Rp, s));
-    MOE_HIP(launch_transpose_quant(gh, I, I, nullptr, off, b.pad_off, E, Rp, b.ghTq, b.ghTqs, Rp, s));
-    MOE_HIP(launch_transpose_quant(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, Rp, b.dguTq, b.dguTqs, Rp, s));
+    // Expert-blocked: dG^T and dU^T are separate transposes so each is a
+    // [I][Kp_e] block sequence of its own.
+    MOE_HIP(launch_transpose_quant(x, d, d, rt->row_token, off, b.pad_off, E, Rp, b.xTq, b.xTqs, s));
+    MOE_HIP(launch_transpose_quant(dy, d, d, rt->row_token, off, b.pad_off, E, Rp, b.dyTq, b.dyTqs, s));
+    MOE_HIP(launch_transpose_quant(gh, I, I, nullptr, off, b.pad_off, E, Rp, b.ghTq, b.ghTqs, s));
+    MOE_HIP(launch_transpose_quant(dgu, 2 * I, I, nullptr, off, b.pad_off, E, Rp, b.dguTq, b.dguTqs, s));
+    MOE_HIP(launch_transpose_quant(dgu + I, 2 * I, I, nullptr, off, b.pad_off, E, Rp, b.dguTq + (int64_t)I * Rp,
+                                   b.dguTqs + (int64_t)I * Rs, s));
     trace(1, 8, s);
     MOE_TRY(run_wgrad_mx(b.dyTq, b.dyTqs, d, b.ghTq, b.ghTqs, I, Rp, b.pad_off, E, g->dw_down, s));
     trace(1, 9, s);

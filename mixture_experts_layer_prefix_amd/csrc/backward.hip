@@ -166,15 +166,17 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
 
 // As transpose_rows_kernel, with the output quantized to MX E4M3 along its
 // rows (blocks of 32 consecutive padded positions p, i.e. 32 consecutive
-// routed rows of one expert; zero padding quantizes to zero codes): dst
-// [cols][ld_dst] bytes, dst_scale [cols][ld_dst/32].  The four threads of a
+// routed rows of one expert; zero padding quantizes to zero codes), and
+// stored expert-blocked: segment e is a dense [cols][Kp_e] block at byte
+// pad_off[e] * cols (Kp_e = pad_off[e+1] - pad_off[e]), its scales a
+// [cols][Kp_e / 32] block at pad_off[e] * cols / 32.  The four threads of a
 // block combine their maxima with lane shuffles.
 __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __restrict__ src, int64_t ld_src, int cols,
                                                               const int32_t* __restrict__ gather,
                                                               const int32_t* __restrict__ seg_off,
                                                               const int32_t* __restrict__ pad_off, int nseg,
-                                                              uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_scale,
-                                                              int64_t ld_dst) {
+                                                              uint8_t* __restrict__ dst,
+                                                              uint8_t* __restrict__ dst_scale) {
   __shared__ bf16_t tile[64][66];
   const int64_t p0 = (int64_t)blockIdx.x * 64;
   if (p0 >= pad_off[nseg]) return;
@@ -221,9 +223,10 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
       w1 |= e4m3_rne_sat(v[4 + q] * inv) << (8 * q);
     }
     if (c0 + c < cols) {
-      const int64_t row = c0 + c;
-      *reinterpret_cast<uint2*>(dst + row * ld_dst + p0 + ch * 8) = uint2{w0, w1};
-      if ((ch & 3) == 0) dst_scale[row * (ld_dst / 32) + (p0 + ch * 8) / 32] = (uint8_t)(ex + 127);
+      const int64_t kp = pad_off[e + 1] - pad_off[e];
+      const int64_t off = (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + ch * 8;
+      *reinterpret_cast<uint2*>(dst + off) = uint2{w0, w1};
+      if ((ch & 3) == 0) dst_scale[off / 32] = (uint8_t)(ex + 127);
     }
   }
 }
@@ -364,12 +367,11 @@ hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int pad, 
 
 hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
                                   const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
-                                  uint8_t* dst, uint8_t* dst_scale, int64_t ld_dst, hipStream_t s) {
+                                  uint8_t* dst, uint8_t* dst_scale, hipStream_t s) {
   if (p_cap == 0 || cols == 0) return hipSuccess;
-  if (p_cap % 64 || ld_dst % 32 || ld_src % 8) return hipErrorInvalidValue;
+  if (p_cap % 64 || ld_src % 8) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 63) / 64));
-  transpose_quant_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, dst_scale,
-                                              ld_dst);
+  transpose_quant_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, dst_scale);
   return hipGetLastError();
 }
 

@@ -16,18 +16,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even (finite values).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp; outputs are
+// rounded to bf16 or E4M3 afterwards).
+__device__ __forceinline__ float sigmoid_f32(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
 
 // ---------------------------------------------------------------------------
 // MX (OCP MX v1.0) E4M3 elements with one E8M0 scale per 32 values: the block
@@ -121,9 +124,10 @@ int64_t bwd_padded_rows(int64_t rows, int groups, int pad);
 // pad_off[E+1]: padded prefix of counts; single[4] = {0, round_up(T, pad), 0, T}.
 hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int pad, int32_t* pad_off, int32_t* single,
                               hipStream_t s);
+// Expert-blocked output: segment e is a [cols][Kp_e] block at pad_off[e] * cols.
 hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
                                   const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
-                                  uint8_t* dst, uint8_t* dst_scale, int64_t ld_dst, hipStream_t s);
+                                  uint8_t* dst, uint8_t* dst_scale, hipStream_t s);
 hipError_t launch_row_weight(const int32_t* token_row, const float* topk_w, int64_t R, float* w_row, hipStream_t s);
 hipError_t launch_dg(const float* dg_part, int nparts, const int32_t* token_row, const float* topk_w, int64_t T, int k,
                      float* dtopk_w, float* dl, float* dl_row, hipStream_t s);
@@ -186,7 +190,8 @@ struct GemmProblem {
   uint8_t* dgu_q;           // MX: [rows][2N] dG | dU quantized along the columns
   uint8_t* dgu_scale;       // MX: [rows][2N/32]
   // K-grouped (weight gradient) mode
-  const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups
+  const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups; MXFP8: the operands
+                            // are expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike)
   int64_t c_group_stride;   // elements between group outputs
 };
 

@@ -52,6 +52,11 @@ constexpr int kBigM = 256, kSmallM = 64, kBN = 256;
 constexpr int kWavesM = 2, kWavesN = MOE_GEMM_WAVES_N;  // 2 x 4: 8 waves, 2 per SIMD
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr size_t kSmemBytes = 2ull * (kBigM + kBN) * kBK * sizeof(bf16_t);  // 131,072 B
+// Group tables (tile prefixes and row offsets, or K offsets) are copied into
+// LDS after the slab ring, so each tile's group lookup is a short LDS binary
+// search instead of a chain of dependent global loads.
+constexpr int kMaxGroups = 1024;
+constexpr size_t kTabBytes = 3ull * (kMaxGroups + 1) * sizeof(int32_t);
 
 // Tile counts of a group of `rows` rows.
 __host__ __device__ __forceinline__ void tiles_of(int64_t rows, int& nb, int& ns) {
@@ -377,7 +382,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
           const int col = min(col0, N - 1);
           const float gv = bf16_to_f32(gurow[col]);
           const float uv = bf16_to_f32(gurow[N + col]);
-          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float sg = sigmoid_f32(gv);
           const float sl = gv * sg;
           const float h = sl * uv;
           const float dhp = acc[i][j][v];
@@ -454,9 +459,24 @@ __device__ __forceinline__ void zero_tile(const KArgs& p, int g, int64_t m0, int
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  int32_t* tab = reinterpret_cast<int32_t*>(smem + kSmemBytes / sizeof(bf16_t));
   const bool single = p.big == nullptr;
-  const int nbig = single ? p.single_big : p.big[p.G];
-  const int nsmall = single ? p.single_small : p.small[p.G];
+  const int32_t* t_big = tab;
+  const int32_t* t_small = tab + (p.G + 1);
+  const int32_t* t_row = tab + 2 * (p.G + 1);
+  if (MODE == GEMM_WGRAD) {
+    for (int i = threadIdx.x; i <= p.G; i += kThreads) tab[i] = p.k_off[i];
+    __syncthreads();
+  } else if (!single) {
+    for (int i = threadIdx.x; i <= p.G; i += kThreads) {
+      tab[i] = p.big[i];
+      tab[p.G + 1 + i] = p.small[i];
+      tab[2 * (p.G + 1) + i] = p.row_off[i];
+    }
+    __syncthreads();
+  }
+  const int nbig = single ? p.single_big : t_big[p.G];
+  const int nsmall = single ? p.single_small : t_small[p.G];
   const int tb = nbig * p.ntiles;
   const int total = tb + nsmall * p.ntiles;
   const int nwg = gridDim.x;
@@ -475,8 +495,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
       const int g = __builtin_amdgcn_readfirstlane(P / per_g);
       const int r = P - g * per_g;
       const int mt = r / p.ntiles, nt = r - mt * p.ntiles;
-      const int kb = __builtin_amdgcn_readfirstlane(p.k_off[g]);
-      const int kt = __builtin_amdgcn_readfirstlane((p.k_off[g + 1] - kb) / kBK);
+      const int kb = __builtin_amdgcn_readfirstlane(tab[g]);
+      const int kt = __builtin_amdgcn_readfirstlane((tab[g + 1] - kb) / kBK);
       if (kt == 0) {
         zero_tile(p, g, (int64_t)mt * kBigM, nt * kBN);
         continue;
@@ -516,11 +536,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
     if (single) {
       m0 = is_big ? (int64_t)mt * kBigM : (int64_t)p.single_big * kBigM + (int64_t)mt * kSmallM;
     } else {
-      const int32_t* pre = is_big ? p.big : p.small;
+      const int32_t* pre = is_big ? t_big : t_small;
       g = find_group(pre, p.G, mt);
-      row_begin = p.row_off[g];
-      n_g = p.row_off[g + 1] - p.row_off[g];
-      const int nb_g = p.big[g + 1] - p.big[g];
+      row_begin = t_row[g];
+      n_g = t_row[g + 1] - t_row[g];
+      const int nb_g = t_big[g + 1] - t_big[g];
       m0 = is_big ? (int64_t)(mt - pre[g]) * kBigM : (int64_t)nb_g * kBigM + (int64_t)(mt - pre[g]) * kSmallM;
     }
     g = __builtin_amdgcn_readfirstlane(g);
@@ -615,7 +635,8 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<MODE>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(kSmemBytes + kTabBytes));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -664,14 +685,14 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   }
   int wg = num_cus();
   wg = (wg + 7) / 8 * 8;
-  gemm_bf16_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes, s>>>(a);
+  gemm_bf16_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes + kTabBytes, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
-  if (q.K % kBK != 0) return hipErrorInvalidValue;
+  if (q.K % kBK != 0 || q.G > kMaxGroups) return hipErrorInvalidValue;
   switch (q.mode) {
     case GEMM_GATEUP:
       if (q.N % 8 != 0) return hipErrorInvalidValue;

@@ -35,6 +35,9 @@ constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int stage_bytes(int bm) { return bm * kBKB + kBN * kBKB + bm * 4 + kBN * 4; }
 constexpr size_t kSmemBytes = 2 * stage_bytes(kBigM) > 3 * stage_bytes(kSmallM) ? 2 * stage_bytes(kBigM)
                                                                                  : 3 * stage_bytes(kSmallM);
+// Group tables in LDS after the slab ring (see the bf16 kernel).
+constexpr int kMaxGroups = 1024;
+constexpr size_t kTabBytes = 3ull * (kMaxGroups + 1) * sizeof(int32_t);
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -163,48 +166,62 @@ __device__ __forceinline__ uint32_t mx_lane_quant(float v, uint32_t* scale) {
   return e4m3_rne_sat(v * mx_inv_scale(e));
 }
 
-template <int BM, int MODE, int NS>
-__device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, int64_t row_begin, int64_t n_g,
-                                        int64_t m0, int ntile, int k_begin, int KT) {
+// Load state of one output tile: buffer descriptors over its operands and
+// the per-lane byte offsets (the K position rides in the scalar offset).
+// Built once per tile, so the next tile's first slabs can be issued while the
+// current tile finishes.
+template <int BM>
+struct MxLoad {
+  __amdgpu_buffer_rsrc_t ar, asr, br0, br1, bsr0, bsr1;
+  uint32_t aoff[BM / (kThreads / 8)];
+  uint32_t scoff, boff;
+  int k_begin, brows, ldb;
+};
+
+template <int BM, int MODE>
+__device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, int64_t row_begin, int64_t n_g,
+                                         int64_t m0, int ntile, int k_begin, int kp = 0) {
   constexpr int BN = kBN;
-  constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int RPR = kThreads / 8;  // rows per data load round
-  constexpr int AR = BM / RPR, BR = BN / RPR;
-  constexpr int STG = stage_bytes(BM);
-  constexpr int LPS = AR + BR;       // data loads per slab per thread (+1 scale load on most waves)
+  constexpr int RPR = kThreads / 8;
+  constexpr int AR = BM / RPR;
   constexpr bool PAIRED = MODE == GEMM_GATEUP || MODE == GEMM_GU;
   constexpr bool DUAL = MODE == GEMM_DUALK;
-  static_assert(FN == 2, "wave tile");
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int lrow = wave * 8 + (lane >> 3);
   const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-  int64_t ldb = p.ldb;
-  asm volatile("" : "+s"(ldb));
-  const int64_t ldas = p.lda / 32, ldbs = ldb / 32;  // scale bytes per A / B row
+  // Weight-gradient operands are stored expert-blocked: group g's A rows are
+  // a contiguous [M][Kp] block at byte koff[g] * M (B alike with N rows), Kp
+  // its padded row count, so a tile's K slabs are dense (few pages per slab).
+  constexpr bool KGROUPED = MODE == GEMM_WGRAD;
+  int64_t lda = KGROUPED ? (int64_t)kp : p.lda;
+  int64_t ldb = KGROUPED ? (int64_t)kp : p.ldb;
+  asm volatile("" : "+s"(lda), "+s"(ldb));
+  const int64_t ldas = lda / 32, ldbs = ldb / 32;  // scale bytes per A / B row
+  const uint8_t* Ab = KGROUPED ? p.A + (int64_t)k_begin * p.M : p.A;
+  const uint8_t* Asb = KGROUPED ? p.As + (int64_t)k_begin * p.M / 32 : p.As;
+  const uint8_t* Bb0 = KGROUPED ? p.B0 + (int64_t)k_begin * p.N : p.B0;
+  const uint8_t* Bsb0 = KGROUPED ? p.B0s + (int64_t)k_begin * p.N / 32 : p.B0s;
+  L.k_begin = KGROUPED ? 0 : k_begin;
+  L.ldb = (int)ldb;
 
   // A data and scales: the tile's rows (or gathered token rows; then the
   // descriptors span the whole gather source).
   const bool gath = p.a_rows != nullptr;
   const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
-  const uint8_t* abase = uniform_ptr(gath ? p.A : p.A + (row_begin + m0) * p.lda);
-  const uint8_t* asbase = uniform_ptr(gath ? p.As : p.As + (row_begin + m0) * ldas);
-  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * p.lda));
+  const uint8_t* abase = uniform_ptr(gath ? p.A : Ab + (row_begin + m0) * lda);
+  const uint8_t* asbase = uniform_ptr(gath ? p.As : Asb + (row_begin + m0) * ldas);
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * lda));
   const uint32_t asbytes = __builtin_amdgcn_readfirstlane(gath ? p.as_bytes : (uint32_t)(tile_rows * ldas));
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t asr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
-  uint32_t aoff[AR];
+  L.ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
+  L.asr = __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < AR; ++i) {
     const int64_t lr0 = i * RPR + lrow;
     const int64_t lr = lr0 < tile_rows ? lr0 : 0;
     const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
-    aoff[i] = (uint32_t)(src * p.lda) + chunk * 16;
+    L.aoff[i] = (uint32_t)(src * lda) + chunk * 16;
   }
   // Scale loads: waves 0..BM/64-1 fetch 64 A-scale rows each, waves 4..7 fetch
   // 64 B-scale rows each (paired modes: G rows 0-63, 64-127, then U rows).
@@ -222,54 +239,92 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
   const int span = PAIRED ? BN / 2 : BN;
   const int first_row = ntile * span;          // first B row of this N-tile
   const int brows = min(span, p.N - first_row);
+  L.brows = brows;
   if (b_sc) {
     const int r = PAIRED ? (bi & 1) * 64 + lane : bi * 64 + lane;
     scoff = (uint32_t)(min(r, brows - 1) * ldbs);
   }
-  const uint8_t* bs0 = p.B0s + (int64_t)g * p.bs_stride + first_row * ldbs;
+  L.scoff = scoff;
+  const uint8_t* bs0 = Bsb0 + (int64_t)g * p.bs_stride + first_row * ldbs;
   const uint8_t* bs1 = (PAIRED || DUAL) ? p.B1s + (int64_t)g * p.bs_stride + first_row * ldbs : bs0;
   const uint32_t bsbytes = __builtin_amdgcn_readfirstlane((uint32_t)(brows * ldbs));
-  const __amdgpu_buffer_rsrc_t bsr0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(PAIRED && bi >= 2 ? bs1 : bs0), (short)0, (int)bsbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t bsr1 =
-      DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(bs1), (short)0, (int)bsbytes, 0x00020000) : bsr0;
+  L.bsr0 = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(PAIRED && bi >= 2 ? bs1 : bs0), (short)0,
+                                            (int)bsbytes, 0x00020000);
+  L.bsr1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(bs1), (short)0, (int)bsbytes, 0x00020000)
+                : L.bsr0;
   // B data
-  const uint8_t* b0 = p.B0 + (int64_t)g * p.b_stride + first_row * ldb;
+  const uint8_t* b0 = Bb0 + (int64_t)g * p.b_stride + first_row * ldb;
   const uint8_t* b1 = (PAIRED || DUAL) ? p.B1 + (int64_t)g * p.b_stride + first_row * ldb : b0;
   const uint32_t bbytes = __builtin_amdgcn_readfirstlane((uint32_t)(brows * ldb));
-  const __amdgpu_buffer_rsrc_t br0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(PAIRED && ((wave >> 2) & 1) ? b1 : b0), (short)0, (int)bbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t br1 =
-      DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b1), (short)0, (int)bbytes, 0x00020000) : br0;
-  const uint32_t boff = (uint32_t)((lane >> 3) * ldb) + chunk * 16;
+  L.br0 = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(PAIRED && ((wave >> 2) & 1) ? b1 : b0), (short)0,
+                                           (int)bbytes, 0x00020000);
+  L.br1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b1), (short)0, (int)bbytes, 0x00020000)
+               : L.br0;
+  L.boff = (uint32_t)((lane >> 3) * ldb) + chunk * 16;
+}
 
+// Issue the loads of slab k0 (relative to the tile's K start) into stage st.
+template <int BM, int MODE>
+__device__ __forceinline__ void mx_issue(const MxArgs& p, const MxLoad<BM>& L, uint8_t* smem, int st, int k0) {
+  constexpr int BN = kBN;
+  constexpr int RPR = kThreads / 8;
+  constexpr int AR = BM / RPR, BR = BN / RPR;
+  constexpr int STG = stage_bytes(BM);
+  constexpr bool PAIRED = MODE == GEMM_GATEUP || MODE == GEMM_GU;
+  constexpr bool DUAL = MODE == GEMM_DUALK;
   typedef __attribute__((address_space(3))) void lds_void;
-  auto issue = [&](int st, int k0) {
-    uint8_t* S = smem + st * STG;
-    const int ka = k_begin + k0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t ldb = L.ldb;
+  uint8_t* S = smem + st * STG;
+  const int ka = L.k_begin + k0;
 #pragma unroll
-    for (int i = 0; i < AR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(S + (i * RPR + wave * 8) * kBKB), 16, aoff[i], ka, 0,
-                                               0);
-    const bool second = DUAL && k0 >= p.k_half;
-    const int kb = DUAL ? (second ? k0 - p.k_half : k0) : ka;
+  for (int i = 0; i < AR; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ar, (lds_void*)(S + (i * RPR + wave * 8) * kBKB), 16, L.aoff[i], ka, 0,
+                                             0);
+  const bool second = DUAL && k0 >= p.k_half;
+  const int kb = DUAL ? (second ? k0 - p.k_half : k0) : ka;
 #pragma unroll
-    for (int i = 0; i < BR; ++i) {
-      int r0 = PAIRED ? i * (RPR / 2) + (wave & 3) * 8 : i * RPR + wave * 8;
-      r0 = min(r0, brows - 8);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? br1 : br0,
-                                               (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, boff,
-                                               (uint32_t)(r0 * ldb + kb), 0, 0);
-    }
-    if (a_sc)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, scoff, ka / 32,
-                                               0, 0);
-    if (b_sc)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? bsr1 : bsr0,
-                                               (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + bi * 256), 4, scoff,
-                                               kb / 32, 0, 0);
-  };
-  const bool any_sc = a_sc || b_sc;
+  for (int i = 0; i < BR; ++i) {
+    int r0 = PAIRED ? i * (RPR / 2) + (wave & 3) * 8 : i * RPR + wave * 8;
+    r0 = min(r0, L.brows - 8);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? L.br1 : L.br0,
+                                             (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, L.boff,
+                                             (uint32_t)(r0 * ldb + kb), 0, 0);
+  }
+  if (wave < BM / 64)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, L.scoff,
+                                             ka / 32, 0, 0);
+  if (wave >= 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? L.bsr1 : L.bsr0,
+                                             (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + (wave - 4) * 256), 4,
+                                             L.scoff, kb / 32, 0, 0);
+}
+
+// One BM x 256 output tile whose load state L is set up.  prefetched: its
+// first min(NS, KT) slabs were already issued (by the previous tile).  nxt:
+// the next tile of this workgroup (or nullptr), whose first slabs are issued
+// once this tile's last slab barrier has freed the LDS ring.
+template <int BM, int MODE, int NS>
+__device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const MxLoad<BM>& L, int g,
+                                        int64_t row_begin, int64_t n_g, int64_t m0, int ntile, int KT,
+                                        bool prefetched, bool has_next, const MxLoad<BM>& nxt, int nxt_KT) {
+  constexpr int BN = kBN;
+  constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int RPR = kThreads / 8;  // rows per data load round
+  constexpr int AR = BM / RPR, BR = BN / RPR;
+  constexpr int STG = stage_bytes(BM);
+  constexpr int LPS = AR + BR;       // data loads per slab per thread (+1 scale load on most waves)
+  constexpr bool PAIRED = MODE == GEMM_GATEUP || MODE == GEMM_GU;
+  static_assert(FN == 2, "wave tile");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
+  auto issue = [&](int st, int k0) { mx_issue<BM, MODE>(p, L, smem, st, k0); };
+  const bool any_sc = wave < BM / 64 || wave >= 4;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -323,10 +378,12 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
                                                                     (sa[i] >> sh) & 0xFF, 0, (sb[j] >> sh) & 0xFF);
   };
 
-  wait_vmcnt<0>();
+  if (!prefetched) {
+    wait_vmcnt<0>();
 #pragma unroll
-  for (int s0 = 0; s0 < NS; ++s0)
-    if (s0 < KT) issue(s0, s0 * kBKB);
+    for (int s0 = 0; s0 < NS; ++s0)
+      if (s0 < KT) issue(s0, s0 * kBKB);
+  }
   if (KT >= NS) {
     if (any_sc) wait_vmcnt<(NS - 1) * (LPS + 1)>(); else wait_vmcnt<(NS - 1) * LPS>();
   } else {
@@ -358,12 +415,49 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
     __syncthreads();
     if (kt + NS < KT) issue(st, (kt + NS) * kBKB);
   }
+  // The ring is free: start the next tile's loads under this epilogue.
+  if (has_next) {
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0)
+      if (s0 < nxt_KT) mx_issue<BM, MODE>(p, nxt, smem, s0, s0 * kBKB);
+  }
 
   // Epilogue (32x32 block layout: column lane & 31, rows 8*(v/4) + 4*(lane/32) + v%4).
   int64_t ldc = p.ldc;
   asm volatile("" : "+s"(ldc));
   const int rows_left = (int)tile_rows;
   const int N = p.N;
+  if constexpr (MODE == GEMM_DOWN || MODE == GEMM_DUALK || MODE == GEMM_WGRAD) {
+    // Plain bf16 output.  One per-lane base pointer; rows step by compile-time
+    // multiples of ldc, the two column blocks by an immediate offset.
+    bf16_t* Cb = static_cast<bf16_t*>(p.C) + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) +
+                 (row_begin + m0 + wm * WM + 4 * (lane >> 5)) * ldc + ntile * BN + wn * WN + (lane & 31);
+    if (tile_rows == BM && ntile * BN + BN <= N) {  // interior tile: no bounds checks
+#pragma clang loop unroll(full)
+      for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+        for (int v = 0; v < 16; ++v) {
+          bf16_t* Cr = Cb + (int64_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * ldc;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
+        }
+    } else {
+      const int rl0 = wm * WM + 4 * (lane >> 5);
+      const int col0 = ntile * BN + wn * WN + (lane & 31);
+#pragma clang loop unroll(full)
+      for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+        for (int v = 0; v < 16; ++v) {
+          const int r = i * 32 + 8 * (v >> 2) + (v & 3);
+          if (rl0 + r >= rows_left) continue;
+          bf16_t* Cr = Cb + (int64_t)r * ldc;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (col0 + j * 32 < N) Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
+        }
+    }
+    return;
+  }
 #pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
@@ -405,7 +499,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
           const int col = min(col0, N - 1);
           const float gv = bf16_to_f32(gurow[col]);
           const float uv = bf16_to_f32(gurow[N + col]);
-          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float sg = sigmoid_f32(gv);
           const float sl = gv * sg;
           const float h = sl * uv;
           const float dhp = acc[i][j][v];
@@ -434,14 +528,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, int g, i
             }
           }
         }
-      } else {
-        if (!row_ok) continue;
-        bf16_t* C = static_cast<bf16_t*>(p.C) + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) + grow * ldc;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
-          if (col < N) C[col] = f32_to_bf16(acc[i][j][v]);
-        }
       }
     }
   }
@@ -463,34 +549,78 @@ __device__ __forceinline__ void mx_zero_tile(const MxArgs& p, int g, int64_t m0,
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_mx[];
+  int32_t* tab = reinterpret_cast<int32_t*>(smem_mx + kSmemBytes);
+  const int32_t* t_big = tab;
+  const int32_t* t_small = tab + (p.G + 1);
+  const int32_t* t_row = tab + 2 * (p.G + 1);
+  if (MODE == GEMM_WGRAD) {
+    for (int i = threadIdx.x; i <= p.G; i += kThreads) tab[i] = p.k_off[i];
+  } else {
+    for (int i = threadIdx.x; i <= p.G; i += kThreads) {
+      tab[i] = p.big[i];
+      tab[p.G + 1 + i] = p.small[i];
+      tab[2 * (p.G + 1) + i] = p.row_off[i];
+    }
+  }
+  __syncthreads();
   const int nwg = gridDim.x;
   const int per_xcd = nwg >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   if constexpr (MODE == GEMM_WGRAD) {
     // One output per group, all in big tiles; K range of group g from k_off.
+    // Tiles of groups without rows are zero-filled; every other tile's first
+    // slabs are issued by the previous tile of this workgroup (lookahead).
     const int mtl = (int)((p.M + kBigM - 1) / kBigM);
     const int per_g = mtl * p.ntiles;
     const int tot = p.G * per_g;
-    for (int it = 0;; ++it) {
-      const int P = it * nwg + xcd * per_xcd + slot;
-      if (P >= tot) break;
-      const int g = __builtin_amdgcn_readfirstlane(P / per_g);
-      const int r = P - g * per_g;
-      const int mt = r / p.ntiles, nt = r - mt * p.ntiles;
-      const int kb = __builtin_amdgcn_readfirstlane(p.k_off[g]);
-      const int kt = __builtin_amdgcn_readfirstlane((p.k_off[g + 1] - kb) / kBKB);
-      if (kt == 0) {
-        mx_zero_tile(p, g, (int64_t)mt * kBigM, nt * kBN);
-        continue;
+    struct Job { int g, mt, nt, kb, kt; };
+    auto job = [&](int P) {
+      Job j;
+      j.g = __builtin_amdgcn_readfirstlane(P / per_g);
+      const int r = P - j.g * per_g;
+      j.mt = __builtin_amdgcn_readfirstlane(r / p.ntiles);
+      j.nt = __builtin_amdgcn_readfirstlane(r - j.mt * p.ntiles);
+      j.kb = __builtin_amdgcn_readfirstlane(tab[j.g]);
+      j.kt = __builtin_amdgcn_readfirstlane((tab[j.g + 1] - j.kb) / kBKB);
+      return j;
+    };
+    int P = xcd * per_xcd + slot;
+    Job cj = {0, 0, 0, 0, 0};
+    for (; P < tot; P += nwg) {
+      cj = job(P);
+      if (cj.kt) break;
+      mx_zero_tile(p, cj.g, (int64_t)cj.mt * kBigM, cj.nt * kBN);
+    }
+    if (P >= tot) return;
+    MxLoad<kBigM> cur;
+    mx_setup<kBigM, MODE>(p, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kb, cj.kt * kBKB);
+    bool pre = false;
+    for (;;) {
+      int Pn = P + nwg;
+      Job nj = {0, 0, 0, 0, 0};
+      for (; Pn < tot; Pn += nwg) {
+        nj = job(Pn);
+        if (nj.kt) break;
       }
-      mx_tile<kBigM, MODE, 2>(p, smem_mx, g, 0, p.M, uniform_i64((int64_t)mt * kBigM),
-                              __builtin_amdgcn_readfirstlane(nt), kb, kt);
-      __syncthreads();
+      const bool has = Pn < tot;
+      MxLoad<kBigM> nxt;
+      if (has) mx_setup<kBigM, MODE>(p, nxt, nj.g, 0, p.M, (int64_t)nj.mt * kBigM, nj.nt, nj.kb, nj.kt * kBKB);
+      mx_tile<kBigM, MODE, 2>(p, smem_mx, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kt, pre, has, nxt,
+                              nj.kt);
+      for (int Pz = P + nwg; Pz < Pn; Pz += nwg) {  // zero tiles between the two
+        const Job z = job(Pz);
+        mx_zero_tile(p, z.g, (int64_t)z.mt * kBigM, z.nt * kBN);
+      }
+      if (!has) break;
+      cur = nxt;
+      cj = nj;
+      P = Pn;
+      pre = true;
     }
     return;
   }
-  const int nbig = p.big[p.G];
-  const int nsmall = p.small[p.G];
+  const int nbig = t_big[p.G];
+  const int nsmall = t_small[p.G];
   const int tb = nbig * p.ntiles;
   const int total = tb + nsmall * p.ntiles;
   const int ts = total - tb;
@@ -515,17 +645,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
     const int gn = min(GN, p.ntiles - ng * GN);
     const int mt = r0 / gn;
     const int ntile = ng * GN + (r0 - mt * gn);
-    const int32_t* pre = is_big ? p.big : p.small;
+    const int32_t* pre = is_big ? t_big : t_small;
     const int g = __builtin_amdgcn_readfirstlane(find_group(pre, p.G, mt));
-    const int64_t row_begin = uniform_i64(p.row_off[g]);
-    const int64_t n_g = uniform_i64(p.row_off[g + 1] - p.row_off[g]);
-    const int nb_g = p.big[g + 1] - p.big[g];
+    const int64_t row_begin = uniform_i64(t_row[g]);
+    const int64_t n_g = uniform_i64(t_row[g + 1] - t_row[g]);
+    const int nb_g = t_big[g + 1] - t_big[g];
     const int64_t m0 = uniform_i64(is_big ? (int64_t)(mt - pre[g]) * kBigM
                                           : (int64_t)nb_g * kBigM + (int64_t)(mt - pre[g]) * kSmallM);
-    if (is_big)
-      mx_tile<kBigM, MODE, 2>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile), 0, KT);
-    else
-      mx_tile<kSmallM, MODE, 3>(p, smem_mx, g, row_begin, n_g, m0, __builtin_amdgcn_readfirstlane(ntile), 0, KT);
+    const int nt = __builtin_amdgcn_readfirstlane(ntile);
+    if (is_big) {
+      MxLoad<kBigM> L;
+      mx_setup<kBigM, MODE>(p, L, g, row_begin, n_g, m0, nt, 0);
+      mx_tile<kBigM, MODE, 2>(p, smem_mx, L, g, row_begin, n_g, m0, nt, KT, false, false, L, 0);
+    } else {
+      MxLoad<kSmallM> L;
+      mx_setup<kSmallM, MODE>(p, L, g, row_begin, n_g, m0, nt, 0);
+      mx_tile<kSmallM, MODE, 3>(p, smem_mx, L, g, row_begin, n_g, m0, nt, KT, false, false, L, 0);
+    }
     __syncthreads();
   }
 }
@@ -547,7 +683,8 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mxfp8_kernel<MODE>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(kSmemBytes + kTabBytes));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -596,7 +733,7 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   }
   int wg = num_cus_mx();
   wg = (wg + 7) / 8 * 8;
-  gemm_mxfp8_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes, s>>>(a);
+  gemm_mxfp8_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes + kTabBytes, s>>>(a);
   return hipGetLastError();
 }
 
@@ -606,9 +743,9 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
 // K-grouped weight-gradient mode (k_off instead); K (each half in DUALK) must
 // be whole 128-byte slabs and N whole 64-column blocks.
 hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
-  if (q.N % 64 != 0) return hipErrorInvalidValue;
+  if (q.N % 64 != 0 || q.G > kMaxGroups) return hipErrorInvalidValue;
   if (q.mode == GEMM_WGRAD) {
-    if (!q.k_off || q.G < 1 || q.ldb % 128 || q.lda % 128) return hipErrorInvalidValue;
+    if (!q.k_off || q.G < 1) return hipErrorInvalidValue;
     return run_mx<GEMM_WGRAD>(q, s);
   }
   if (!q.row_off || q.K % kBKB != 0) return hipErrorInvalidValue;
