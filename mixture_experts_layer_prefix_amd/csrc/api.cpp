@@ -591,13 +591,12 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
                          g->dw_up, s));
     trace(1, 11, s);
   } else {
-    MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.xT), b.Rp,
-                                  s));
-    MOE_HIP(launch_transpose_rows(dy, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dyT), b.Rp,
-                                  s));
-    MOE_HIP(launch_transpose_rows(gh, I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.ghT), b.Rp, s));
-    MOE_HIP(launch_transpose_rows(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT),
-                                  b.Rp, s));
+    MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.xT), s));
+    MOE_HIP(launch_transpose_rows(dy, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dyT), s));
+    MOE_HIP(launch_transpose_rows(gh, I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.ghT), s));
+    MOE_HIP(launch_transpose_rows(dgu, 2 * I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT), s));
+    MOE_HIP(launch_transpose_rows(dgu + I, 2 * I, I, nullptr, off, b.pad_off, E, b.Rp,
+                                  static_cast<bf16_t*>(b.dguT) + (int64_t)I * b.Rp, s));
     trace(1, 8, s);
     const bf16_t* dguT = static_cast<const bf16_t*>(b.dguT);
     MOE_TRY(run_wgrad(b.dyT, d, b.ghT, I, b.Rp, b.pad_off, E, g->dw_down, s));
@@ -609,12 +608,14 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   }
   if (Is) {
     const int32_t* seg = b.single + 2;
-    MOE_HIP(launch_transpose_rows(x, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.xTs), b.Tp, s));
-    MOE_HIP(launch_transpose_rows(dy, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.dyTs), b.Tp, s));
+    const bf16_t* dgus = static_cast<const bf16_t*>(b.dgus);
+    MOE_HIP(launch_transpose_rows(x, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.xTs), s));
+    MOE_HIP(launch_transpose_rows(dy, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.dyTs), s));
     MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.hs), Is, Is, nullptr, seg, b.single, 1, b.Tp,
-                                  static_cast<bf16_t*>(b.hsT), b.Tp, s));
-    MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.dgus), 2 * Is, 2 * Is, nullptr, seg, b.single, 1, b.Tp,
-                                  static_cast<bf16_t*>(b.dgusT), b.Tp, s));
+                                  static_cast<bf16_t*>(b.hsT), s));
+    MOE_HIP(launch_transpose_rows(dgus, 2 * Is, Is, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.dgusT), s));
+    MOE_HIP(launch_transpose_rows(dgus + Is, 2 * Is, Is, nullptr, seg, b.single, 1, b.Tp,
+                                  static_cast<bf16_t*>(b.dgusT) + (int64_t)Is * b.Tp, s));
     const bf16_t* dgusT = static_cast<const bf16_t*>(b.dgusT);
     MOE_TRY(run_wgrad(b.dyTs, d, b.hsT, Is, b.Tp, b.single, 1, g->dws_down, s));
     MOE_TRY(run_wgrad(dgusT, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_gate, s));

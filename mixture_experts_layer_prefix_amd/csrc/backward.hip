@@ -121,12 +121,14 @@ __device__ __forceinline__ int find_segment(const int32_t* pad_off, int nseg, in
 
 // dst[c][p] = src[row(p)][c] for the 64x64 tile (p0.., c0..), where padded
 // column p of segment e is row seg_off[e] + (p - pad_off[e]) (zero past the
-// segment's rows) and row r reads source row gather[r] (or r).
+// segment's rows) and row r reads source row gather[r] (or r).  The output is
+// expert-blocked: segment e is a dense [cols][Kp_e] block at element
+// pad_off[e] * cols, Kp_e = pad_off[e+1] - pad_off[e].
 __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __restrict__ src, int64_t ld_src, int cols,
                                                              const int32_t* __restrict__ gather,
                                                              const int32_t* __restrict__ seg_off,
                                                              const int32_t* __restrict__ pad_off, int nseg,
-                                                             bf16_t* __restrict__ dst, int64_t ld_dst) {
+                                                             bf16_t* __restrict__ dst) {
   __shared__ bf16_t tile[64][66];
   const int64_t p0 = (int64_t)blockIdx.x * 64;
   if (p0 >= pad_off[nseg]) return;
@@ -160,7 +162,9 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       o[q] = (uint32_t)tile[ch * 8 + 2 * q][c] | ((uint32_t)tile[ch * 8 + 2 * q + 1][c] << 16);
-    *reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + c) * ld_dst + p0 + ch * 8) = o;
+    const int64_t kp = pad_off[e + 1] - pad_off[e];
+    *reinterpret_cast<u32x4*>(dst + (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + ch * 8) =
+        o;
   }
 }
 
@@ -390,11 +394,11 @@ hipError_t launch_dg(const float* dg_part, int nparts, const int32_t* token_row,
 
 hipError_t launch_transpose_rows(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
                                  const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap, bf16_t* dst,
-                                 int64_t ld_dst, hipStream_t s) {
+                                 hipStream_t s) {
   if (p_cap == 0 || cols == 0) return hipSuccess;
-  if (p_cap % 64 || ld_dst % 8 || ld_src % 8) return hipErrorInvalidValue;
+  if (p_cap % 64 || ld_src % 8 || cols % 8) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 63) / 64));
-  transpose_rows_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, ld_dst);
+  transpose_rows_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst);
   return hipGetLastError();
 }
 

@@ -131,9 +131,11 @@ hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, c
 hipError_t launch_row_weight(const int32_t* token_row, const float* topk_w, int64_t R, float* w_row, hipStream_t s);
 hipError_t launch_dg(const float* dg_part, int nparts, const int32_t* token_row, const float* topk_w, int64_t T, int k,
                      float* dtopk_w, float* dl, float* dl_row, hipStream_t s);
+// [rows][cols] -> expert-blocked transposed operand (segment e: a [cols][Kp_e]
+// block at element pad_off[e] * cols), rows optionally gathered.
 hipError_t launch_transpose_rows(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
                                  const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap, bf16_t* dst,
-                                 int64_t ld_dst, hipStream_t s);
+                                 hipStream_t s);
 hipError_t launch_transpose_batched(const bf16_t* src, int64_t batch, int64_t rows, int64_t cols, bf16_t* dst,
                                     hipStream_t s);
 hipError_t launch_dx(const bf16_t* da_perm, const int32_t* token_row, const int32_t* topk_idx, const float* dl,
@@ -190,8 +192,8 @@ struct GemmProblem {
   uint8_t* dgu_q;           // MX: [rows][2N] dG | dU quantized along the columns
   uint8_t* dgu_scale;       // MX: [rows][2N/32]
   // K-grouped (weight gradient) mode
-  const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups; MXFP8: the operands
-                            // are expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike)
+  const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups; the operands are
+                            // expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike)
   int64_t c_group_stride;   // elements between group outputs
 };
 

@@ -216,15 +216,23 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   // global 16-byte chunk for this lane's LDS slot: slot (lane & 7) of row r
   // holds chunk slot ^ swz(r), r & 7 = lane >> 3 and (r >> 3) & 1 = wave & 1
   const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-  int64_t ldb = p.ldb;
-  asm volatile("" : "+s"(ldb));  // keep per-tile address arithmetic inside the tile
+  // Weight-gradient operands are expert-blocked: group g's A is a dense
+  // [M][Kp] block at element k_off[g] * M (B alike with N rows), Kp its
+  // padded row count, so a tile's K slabs are contiguous.
+  constexpr bool KGROUPED = MODE == GEMM_WGRAD;
+  int64_t lda = KGROUPED ? (int64_t)KT * kBK : p.lda;
+  int64_t ldb = KGROUPED ? (int64_t)KT * kBK : p.ldb;
+  asm volatile("" : "+s"(lda), "+s"(ldb));  // keep per-tile address arithmetic inside the tile
+  const bf16_t* Ag = KGROUPED ? p.A + (int64_t)k_begin * p.M : p.A;
+  const bf16_t* Bg0 = KGROUPED ? p.B0 + (int64_t)k_begin * p.N : p.B0;
+  if (KGROUPED) k_begin = 0;
 
   // A: this tile's rows of the group (or gathered token rows); descriptor over
   // the tile's rows, or over the whole gather source.
   const bool gath = p.a_rows != nullptr;
   const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
-  const bf16_t* abase = uniform_ptr(gath ? p.A : p.A + (row_begin + m0) * p.lda);
-  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * p.lda * 2));
+  const bf16_t* abase = uniform_ptr(gath ? p.A : Ag + (row_begin + m0) * lda);
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * lda * 2));
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
   uint32_t aoff[AR];
 #pragma unroll
@@ -232,7 +240,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
     const int64_t lr0 = i * RPR + lrow;           // row within the tile
     const int64_t lr = lr0 < tile_rows ? lr0 : 0;
     const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
-    aoff[i] = (uint32_t)(src * p.lda * 2) + chunk * 16;
+    aoff[i] = (uint32_t)(src * lda * 2) + chunk * 16;
   }
   // B: the group's [N][ldb] matrix, rebased at the first row this N-tile
   // reads.  Paired modes interleave 32-row blocks of two matrices (W_gate,
@@ -243,7 +251,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   const int first_row = ntile * span;
   const uint32_t bbytes =
       __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)min(span, p.N - first_row) * ldb * 2));
-  const bf16_t* b0 = p.B0 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb;
+  const bf16_t* b0 = Bg0 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb;
   const bf16_t* b1 = (PAIRED || MODE == GEMM_DUALK) ? p.B1 + (int64_t)g * p.b_group_stride + (int64_t)first_row * ldb
                                                     : b0;
   const __amdgpu_buffer_rsrc_t br0 =
@@ -402,44 +410,55 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
     }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (rl >= rows_left) continue;
-      bf16_t* Crow = C + (int64_t)rl * ldc;
-      if (MODE == GEMM_GATEUP) {
+  // One per-lane base pointer; rows step by compile-time multiples of ldc and
+  // column blocks by immediate offsets.  Interior tiles skip the bounds checks.
+  const int rl0 = wm * WM + 4 * (lane >> 5);  // tile row of (i = 0, v = 0)
+  const bool full_rows = rows_left == BM;
+  const int N = p.N;
+  if constexpr (PAIRED) {
+    const int colb = ntile * (BN / 2) + wn * (FN / 2) * 32 + (lane & 31);
+    const bool full_cols = ntile * (BN / 2) + BN / 2 <= N;
+    bf16_t* Cb = C + (int64_t)rl0 * ldc + colb;
+    bf16_t* Sb = p.gu_out ? p.gu_out + (row0 + rl0) * 2 * N + colb : nullptr;
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+      for (int v = 0; v < 16; ++v) {
+        const int r = i * 32 + 8 * (v >> 2) + (v & 3);
+        if (!full_rows && rl0 + r >= rows_left) continue;
+        bf16_t* Cr = Cb + (int64_t)r * ldc;
 #pragma unroll
         for (int q = 0; q < FN / 2; ++q) {
+          if (!full_cols && colb + q * 32 >= N) continue;
           const float gv = acc[i][2 * q][v], uv = acc[i][2 * q + 1][v];
-          const int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
-          if (col < p.N) {
-            Crow[col] = f32_to_bf16(silu_f32(gv) * uv);
-            if (p.gu_out) {  // G | U kept for the backward
-              bf16_t* srow = p.gu_out + (row0 + rl) * 2 * p.N;
-              srow[col] = f32_to_bf16(gv);
-              srow[p.N + col] = f32_to_bf16(uv);
+          if (MODE == GEMM_GATEUP) {
+            Cr[q * 32] = f32_to_bf16(silu_f32(gv) * uv);
+            if (Sb) {  // G | U kept for the backward
+              bf16_t* Sr = Sb + (int64_t)r * 2 * N;
+              Sr[q * 32] = f32_to_bf16(gv);
+              Sr[N + q * 32] = f32_to_bf16(uv);
             }
+          } else {
+            Cr[q * 32] = f32_to_bf16(gv);
+            Cr[N + q * 32] = f32_to_bf16(uv);
           }
-        }
-      } else if (MODE == GEMM_GU) {
-#pragma unroll
-        for (int q = 0; q < FN / 2; ++q) {
-          const int col = ntile * (BN / 2) + (wn * (FN / 2) + q) * 32 + (lane & 31);
-          if (col < p.N) {
-            Crow[col] = f32_to_bf16(acc[i][2 * q][v]);
-            Crow[p.N + col] = f32_to_bf16(acc[i][2 * q + 1][v]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
-          if (col < p.N) Crow[col] = f32_to_bf16(acc[i][j][v]);
         }
       }
-    }
+  } else {
+    const int colb = ntile * BN + wn * WN + (lane & 31);
+    const bool full_cols = ntile * BN + BN <= N;
+    bf16_t* Cb = C + (int64_t)rl0 * ldc + colb;
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+      for (int v = 0; v < 16; ++v) {
+        const int r = i * 32 + 8 * (v >> 2) + (v & 3);
+        if (!full_rows && rl0 + r >= rows_left) continue;
+        bf16_t* Cr = Cb + (int64_t)r * ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (full_cols || colb + j * 32 < N) Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
+      }
   }
 }
 
