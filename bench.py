@@ -47,6 +47,35 @@ def gemm_flops(D):
             "wgrad_down": r, "wgrad_gate": r, "wgrad_up": r}
 
 
+def gemm_bytes(D, eb, active):
+    """Algorithmic HBM bytes of each GEMM stage: every operand read once and
+    every output written once (eb: bytes per operand element, 1 + 1/32 for
+    E4M3 with its E8M0 scales, 2 for bf16; weights of the `active` experts
+    that have rows; outputs bf16; the forward also keeps G|U in bf16)."""
+    R, d, I, E = float(D.R), float(D.d), float(D.I), float(D.E)
+    w = active * I * d * eb  # one projection matrix of every active expert
+    return {"gate_up": R * d * eb + 2 * w + R * I * eb + R * 2 * I * 2,
+            "down": R * I * eb + w + R * d * 2,
+            "replay_gate_up": R * d * eb + 2 * w + R * 2 * I * 2,
+            "down_dgrad_swiglu": R * d * eb + w + R * 2 * I * 2 + R * 2 * I * (2 + (eb if eb < 2 else 0))
+            + R * I * 2 + R * I / 8,
+            "gate_up_dgrad": R * 2 * I * eb + 2 * w + R * d * 2,
+            "wgrad_down": (d + I) * R * eb + E * d * I * 2, "wgrad_gate": (d + I) * R * eb + E * d * I * 2,
+            "wgrad_up": (d + I) * R * eb + E * d * I * 2}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter passes, or
+    None when the kernel's source has changed since they were taken."""
+    import hashlib
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
+        src = open(os.path.join(ROOT, "mixture_experts_layer_prefix_amd", "csrc", "gemm_mxfp8.hip"), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    return t["bytes_per_launch"] if hashlib.sha256(src).hexdigest() == t["source_sha256"] else None
+
+
 def split_flops(D):
     """(routed, bf16-side) FLOPs of one forward+backward step."""
     routed = 18.0 * D.R * D.d * D.I
@@ -74,23 +103,31 @@ KERNEL_OF = {"gate_up": "gate/up with SwiGLU epilogue", "down": "down projection
              "wgrad_gate": "K-grouped weight gradient", "wgrad_up": "K-grouped weight gradient"}
 
 
-def roofline_of(stages, flops, peak, label):
-    """Roofline of the kernel with the largest total time in the step: its
-    algorithmic FLOPs per launch over its average event-timed launch."""
+def roofline_of(stages, flops, nbytes, peak, label, traffic_key=None):
+    """Roofline of the kernel with the largest total time in the step.  Its
+    bound is MFMA or HBM, whichever its algorithmic FLOPs or bytes per launch
+    take longer on at the peak rate; achieved = that work per launch over the
+    kernel's average event-timed launch."""
     per = {}
     for name, f in flops.items():
         ms = stages.get(name, 0.0)
         if ms < 0.01:  # stage skipped (e.g. no replay when G|U are kept)
             continue
         k = KERNEL_OF[name.split("_", 1)[1]]
-        tot, fl, n = per.get(k, (0.0, 0.0, 0))
-        per[k] = (tot + ms, fl + f, n + 1)
+        tot, fl, by, n = per.get(k, (0.0, 0.0, 0.0, 0))
+        per[k] = (tot + ms, fl + f, by + nbytes[name], n + 1)
     kern = max(per, key=lambda k: per[k][0])
-    tot, fl, n = per[kern]
-    achieved = fl / (tot / 1e3) / 1e12
-    return dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s", frac=round(achieved / peak, 4),
-                traffic=None, kernel="%s: %s" % (label, kern), flops_per_launch=fl / n, launches_per_step=n,
-                launch_ms=round(tot / n, 4))
+    tot, fl, by, n = per[kern]
+    t_launch = tot / n / 1e3
+    fl, by = fl / n, by / n
+    if by / (PEAK_HBM_GBS * 1e9) > fl / (peak * 1e12):
+        achieved, pk, unit, bound = by / t_launch / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    else:
+        achieved, pk, unit, bound = fl / t_launch / 1e12, peak, "TFLOP/s", "mfma"
+    traffic = measured_traffic(traffic_key) if traffic_key and kern == KERNEL_OF["wgrad_down"] else None
+    return dict(bound=bound, achieved=round(achieved, 2), peak=pk, unit=unit, frac=round(achieved / pk, 4),
+                traffic=traffic, kernel="%s: %s" % (label, kern), flops_per_launch=fl, bytes_per_launch=by,
+                mfma_frac=round(fl / t_launch / 1e12 / peak, 4), launches_per_step=n, launch_ms=round(t_launch * 1e3, 4))
 
 
 def cpu_baseline(D, rows_hot=8192, tokens=2048):
@@ -158,6 +195,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the CPU oracle sample (0: skip)")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 DeepSeek-V3 (T=8192) measurements")
+    ap.add_argument("--only-bf16", action="store_true",
+                    help="run only the bf16 DeepSeek-V3 (T=8192) measurements (for per-part profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -173,6 +212,25 @@ def main():
     p = gen.Problem(D)
     names = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
     w = M.Weights(**{n: p.device(n) for n in names})
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "data": "synthetic"}
+    if not args.only_bf16:
+        headline(args, D, p, w, out, torch, M)
+    if not args.no_bf16:
+        bf16_part(args, D, w, out, torch, gen, M)
+    if args.cpu_sample > 0 and not args.only_bf16:
+        log("[bench] cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(D, rows_hot=4 * args.cpu_sample, tokens=args.cpu_sample)
+        log("[bench] cpu baseline %.2f tokens/s on %d threads" % (out["cpu_baseline"]["value"],
+                                                                  out["cpu_baseline"]["cores"]))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def headline(args, D, p, w, out, torch, M):
+    """The MXFP8 forward+backward step: value, roofline, stage times."""
     x, dy, bias = p.device("x"), p.device("dy"), p.device_bias()
     md = M.Dims(D.T, D.d, D.E, D.k, D.I, D.S, D.Is)
     wq = M.prepare_mxfp8(w, md)
@@ -203,112 +261,109 @@ def main():
     t_roof = routed / (PEAK["mxfp8"] * 1e12) + other / (PEAK["bf16"] * 1e12)
     stages = {"fwd_" + k: v for k, v in fwd_st.items()}
     stages.update({"bwd_" + k: v for k, v in bwd_st.items()})
-    flops = {("fwd_" if n in ("gate_up", "down") else "bwd_") + n: f for n, f in gemm_flops(D).items()}
-    roofline = roofline_of(stages, flops, PEAK["mxfp8"], "MXFP8 grouped GEMM (gemm_mxfp8_kernel)")
+    pre = lambda n: ("fwd_" if n in ("gate_up", "down") else "bwd_") + n
+    flops = {pre(n): f for n, f in gemm_flops(D).items()}
+    active = int((fplan.routing["expert_counts"] > 0).sum().item())
+    nbytes = {pre(n): b for n, b in gemm_bytes(D, 1 + 1 / 32, active).items()}
+    roofline = roofline_of(stages, flops, nbytes, PEAK["mxfp8"], "MXFP8 grouped GEMM (gemm_mxfp8_kernel)",
+                           "gemm_mxfp8_kernel<6>")
     log("[bench] timed %d steps: %.3f ms/step (fwd %.3f, bwd %.3f), %.0f tokens/s, %.1f TFLOP/s"
         % (args.steps, ms, sum(fwd_st.values()), sum(bwd_st.values()), tokens_s, tflops))
     log("[bench] stages ms:", {k: round(v, 3) for k, v in stages.items()})
     del fplan, bplan, wb, wq
     torch.cuda.empty_cache()
-
-    out = {
-        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
+    out.update({
+        "value": round(tokens_s, 1), "ms_per_step": round(ms, 4), "dtype": "mxfp8",
         "config": {"workload": WORKLOAD, "T": D.T, "d": D.d, "E": D.E, "k": D.k, "I": D.I, "n_shared": D.S,
                    "I_shared": D.Is, "precision": "mxfp8 routed experts, bf16 shared expert and router",
                    "pass": "forward+backward", "parallelism": "1 GPU"},
         "tflops": round(tflops, 2), "roofline_step_frac": round(t_roof / (ms / 1e3), 4),
         "roofline": roofline, "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+    })
+
+
+def bf16_part(args, D, w, out, torch, gen, M):
+    """The bf16 DeepSeek-V3 layer at T=8192: forward, backward, permute/combine."""
+    D3 = gen.get_config("c3a")
+    assert (D3.d, D3.E, D3.I, D3.S, D3.Is, D3.seed) == (D.d, D.E, D.I, D.S, D.Is, D.seed)  # same weights
+    p3 = gen.Problem(D3)
+    x3, dy3, bias3 = p3.device("x"), p3.device("dy"), p3.device_bias()
+    md3 = M.Dims(D3.T, D3.d, D3.E, D3.k, D3.I, D3.S, D3.Is)
+    wb3 = M.prepare_backward(w)
+    f3, b3 = M.ForwardPlan(md3, "bf16", keep_gu=True), M.BackwardPlan(md3, "bf16")
+    for _ in range(args.warmup):
+        f3.run(x3, w, bias3)
+        b3.run(dy3, x3, wb3, f3.routing)
+    t3f, t3b = M.StageTimer(0, args.steps), M.StageTimer(1, args.steps)
+
+    def fstep(i):
+        t3f.arm(i)
+        f3.run(x3, w, bias3)
+
+    def bstep(i):
+        t3b.arm(i)
+        b3.run(dy3, x3, wb3, f3.routing)
+
+    ef = timed_steps(fstep, args.steps, torch)
+    eb = timed_steps(bstep, args.steps, torch)
+    t3f.disarm()
+    t3b.disarm()
+    fms, bms = ef / args.steps * 1e3, eb / args.steps * 1e3
+    fst, bst = t3f.mean_ms(), t3b.mean_ms()
+    ffl, bfl = D3.fwd_flops(), D3.bwd_flops()
+    st3 = {"fwd_" + k: v for k, v in fst.items()}
+    st3.update({"bwd_" + k: v for k, v in bst.items()})
+    pre = lambda n: ("fwd_" if n in ("gate_up", "down") else "bwd_") + n
+    fl3 = {pre(n): f for n, f in gemm_flops(D3).items()}
+    active3 = int((f3.routing["expert_counts"] > 0).sum().item())
+    by3 = {pre(n): b for n, b in gemm_bytes(D3, 2, active3).items()}
+    out["bf16_dsv3_t8192"] = {
+        "forward": {"ms": round(fms, 4), "tokens_s": round(D3.T / (fms / 1e3), 1),
+                    "tflops": round(ffl / (fms / 1e3) / 1e12, 2),
+                    "mfma_peak_frac": round(ffl / (fms / 1e3) / 1e12 / PEAK["bf16"], 4),
+                    "roofline": roofline_of({k: v for k, v in st3.items() if k.startswith("fwd_")},
+                                            {k: v for k, v in fl3.items() if k.startswith("fwd_")}, by3,
+                                            PEAK["bf16"], "bf16 grouped GEMM (gemm_bf16_kernel)")},
+        "backward": {"ms": round(bms, 4), "tokens_s": round(D3.T / (bms / 1e3), 1),
+                     "tflops": round(bfl / (bms / 1e3) / 1e12, 2),
+                     "mfma_peak_frac": round(bfl / (bms / 1e3) / 1e12 / PEAK["bf16"], 4),
+                     "roofline": roofline_of({k: v for k, v in st3.items() if k.startswith("bwd_")},
+                                             {k: v for k, v in fl3.items() if k.startswith("bwd_")}, by3,
+                                             PEAK["bf16"], "bf16 grouped GEMM (gemm_bf16_kernel)")},
+        "stages_ms": {k: round(v, 4) for k, v in st3.items()},
     }
+    log("[bench] bf16 T=8192: fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)"
+        % (fms, ffl / (fms / 1e3) / 1e12, bms, bfl / (bms / 1e3) / 1e12))
+    # standalone dispatch gather and weighted sum (algorithmic bytes)
+    r = f3.routing
+    perm = M.permute(r["topk_idx"], x3, md3, "bf16")
+    o_perm = torch.empty(D3.R, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
+    y_sh = torch.empty(D3.T, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
+    reps = 5
 
-    if not args.no_bf16:
-        D3 = gen.get_config("c3a")
-        assert (D3.d, D3.E, D3.I, D3.S, D3.Is, D3.seed) == (D.d, D.E, D.I, D.S, D.Is, D.seed)  # same weights
-        p3 = gen.Problem(D3)
-        x3, dy3, bias3 = p3.device("x"), p3.device("dy"), p3.device_bias()
-        md3 = M.Dims(D3.T, D3.d, D3.E, D3.k, D3.I, D3.S, D3.Is)
-        wb3 = M.prepare_backward(w)
-        f3, b3 = M.ForwardPlan(md3, "bf16", keep_gu=True), M.BackwardPlan(md3, "bf16")
-        for _ in range(args.warmup):
-            f3.run(x3, w, bias3)
-            b3.run(dy3, x3, wb3, f3.routing)
-        t3f, t3b = M.StageTimer(0, args.steps), M.StageTimer(1, args.steps)
-
-        def fstep(i):
-            t3f.arm(i)
-            f3.run(x3, w, bias3)
-
-        def bstep(i):
-            t3b.arm(i)
-            b3.run(dy3, x3, wb3, f3.routing)
-
-        ef = timed_steps(fstep, args.steps, torch)
-        eb = timed_steps(bstep, args.steps, torch)
-        t3f.disarm()
-        t3b.disarm()
-        fms, bms = ef / args.steps * 1e3, eb / args.steps * 1e3
-        fst, bst = t3f.mean_ms(), t3b.mean_ms()
-        ffl, bfl = D3.fwd_flops(), D3.bwd_flops()
-        st3 = {"fwd_" + k: v for k, v in fst.items()}
-        st3.update({"bwd_" + k: v for k, v in bst.items()})
-        fl3 = {("fwd_" if n in ("gate_up", "down") else "bwd_") + n: f for n, f in gemm_flops(D3).items()}
-        out["bf16_dsv3_t8192"] = {
-            "forward": {"ms": round(fms, 4), "tokens_s": round(D3.T / (fms / 1e3), 1),
-                        "tflops": round(ffl / (fms / 1e3) / 1e12, 2),
-                        "mfma_peak_frac": round(ffl / (fms / 1e3) / 1e12 / PEAK["bf16"], 4),
-                        "roofline": roofline_of({k: v for k, v in st3.items() if k.startswith("fwd_")},
-                                                {k: v for k, v in fl3.items() if k.startswith("fwd_")},
-                                                PEAK["bf16"], "bf16 grouped GEMM (gemm_bf16_kernel)")},
-            "backward": {"ms": round(bms, 4), "tokens_s": round(D3.T / (bms / 1e3), 1),
-                         "tflops": round(bfl / (bms / 1e3) / 1e12, 2),
-                         "mfma_peak_frac": round(bfl / (bms / 1e3) / 1e12 / PEAK["bf16"], 4),
-                         "roofline": roofline_of({k: v for k, v in st3.items() if k.startswith("bwd_")},
-                                                 {k: v for k, v in fl3.items() if k.startswith("bwd_")},
-                                                 PEAK["bf16"], "bf16 grouped GEMM (gemm_bf16_kernel)")},
-            "stages_ms": {k: round(v, 4) for k, v in st3.items()},
-        }
-        log("[bench] bf16 T=8192: fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)"
-            % (fms, ffl / (fms / 1e3) / 1e12, bms, bfl / (bms / 1e3) / 1e12))
-        # standalone dispatch gather and weighted sum (algorithmic bytes)
-        r = f3.routing
-        perm = M.permute(r["topk_idx"], x3, md3, "bf16")
-        o_perm = torch.empty(D3.R, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
-        y_sh = torch.empty(D3.T, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
-        reps = 5
-
-        def one(fn):
+    def one(fn):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
             fn()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            for _ in range(reps):
-                fn()
-            e.record()
-            e.synchronize()
-            return s.elapsed_time(e) / 1e3 / reps
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / 1e3 / reps
 
-        t_perm = one(lambda: M.permute(r["topk_idx"], x3, md3, "bf16"))
-        t_comb = one(lambda: M.combine(o_perm, perm[3], r["topk_w"], y_sh, md3, "bf16"))
-        perm_bytes = D3.T * D3.d * 2 + D3.R * D3.d * 2 + D3.R * 4 * 3
-        comb_bytes = D3.R * D3.d * 2 + 2 * D3.T * D3.d * 2 + D3.R * 8
-        out["hbm"] = {"permute_GBs": round(perm_bytes / t_perm / 1e9, 1),
-                      "permute_frac": round(perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS, 4),
-                      "combine_GBs": round(comb_bytes / t_comb / 1e9, 1),
-                      "combine_frac": round(comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS, 4),
-                      "workload": "bf16, T=8192, d=7168, k=8 (standalone moe_permute with gather, moe_combine)"}
-        hc = r["expert_counts"].cpu()
-        out["routing_skew_t8192"] = dict(max_rows=int(hc.max()), empty_experts=int((hc == 0).sum()),
-                                         under_32=int((hc < 32).sum()))
-        del f3, b3, wb3
-
-    if args.cpu_sample > 0:
-        log("[bench] cpu baseline")
-        out["cpu_baseline"] = cpu_baseline(D, rows_hot=4 * args.cpu_sample, tokens=args.cpu_sample)
-        log("[bench] cpu baseline %.2f tokens/s on %d threads" % (out["cpu_baseline"]["value"],
-                                                                  out["cpu_baseline"]["cores"]))
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    t_perm = one(lambda: M.permute(r["topk_idx"], x3, md3, "bf16"))
+    t_comb = one(lambda: M.combine(o_perm, perm[3], r["topk_w"], y_sh, md3, "bf16"))
+    perm_bytes = D3.T * D3.d * 2 + D3.R * D3.d * 2 + D3.R * 4 * 3
+    comb_bytes = D3.R * D3.d * 2 + 2 * D3.T * D3.d * 2 + D3.R * 8
+    out["hbm"] = {"permute_GBs": round(perm_bytes / t_perm / 1e9, 1),
+                  "permute_frac": round(perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS, 4),
+                  "combine_GBs": round(comb_bytes / t_comb / 1e9, 1),
+                  "combine_frac": round(comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS, 4),
+                  "workload": "bf16, T=8192, d=7168, k=8 (standalone moe_permute with gather, moe_combine)"}
+    hc = r["expert_counts"].cpu()
+    out["routing_skew_t8192"] = dict(max_rows=int(hc.max()), empty_experts=int((hc == 0).sum()),
+                                     under_32=int((hc < 32).sum()))
+    del f3, b3, wb3
 
 
 if __name__ == "__main__":
