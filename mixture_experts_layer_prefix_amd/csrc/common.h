@@ -83,6 +83,30 @@ __device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&
   return (uint32_t)(e + 127);
 }
 
+// Weight-gradient tile order.  Each group's mtl x ntl grid of output tiles is
+// cut into 8 rectangles, one per XCD: a parts along M times 8/a along N, with
+// a chosen so that a rectangle spans the fewest A plus B tile strips.  XCD x
+// works through rectangle x of group 0, then of group 1, and so on, so the
+// workgroups of one XCD stream the same token-axis slabs of A and B through
+// that XCD's L2 instead of every XCD reading all of them.
+struct WgradRect {
+  int mt0, nt0, bm, bn;
+};
+__device__ __forceinline__ WgradRect wgrad_rect(int mtl, int ntl, int xcd) {
+  int a = 1, best = 1 << 30;
+  for (int c = 1; c <= 8; c *= 2) {
+    const int cost = (mtl + c - 1) / c + (ntl + 8 / c - 1) / (8 / c);
+    if (cost < best) best = cost, a = c;
+  }
+  const int b = 8 / a, bi = xcd / b, bj = xcd - bi * b;
+  WgradRect r;
+  r.mt0 = bi * mtl / a;
+  r.bm = (bi + 1) * mtl / a - r.mt0;
+  r.nt0 = bj * ntl / b;
+  r.bn = (bj + 1) * ntl / b - r.nt0;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel launchers (each returns hipGetLastError() of its launches)
 // ---------------------------------------------------------------------------

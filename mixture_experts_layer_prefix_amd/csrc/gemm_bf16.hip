@@ -505,15 +505,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
 
   if (MODE == GEMM_WGRAD) {
     // One output per group, all of it in big tiles; K range from k_off.
-    const int mtl = (int)((p.M + kBigM - 1) / kBigM);
-    const int per_g = mtl * p.ntiles;
+    const WgradRect rc = wgrad_rect((int)((p.M + kBigM - 1) / kBigM), p.ntiles, xcd);
+    const int per_g = rc.bm * rc.bn;
     const int tot = p.G * per_g;
-    for (int it = 0;; ++it) {
-      const int P = it * nwg + xcd * per_xcd + slot;
-      if (P >= tot) break;
+    for (int P = slot; P < tot; P += per_xcd) {
       const int g = __builtin_amdgcn_readfirstlane(P / per_g);
       const int r = P - g * per_g;
-      const int mt = r / p.ntiles, nt = r - mt * p.ntiles;
+      const int mt = rc.mt0 + r / rc.bn, nt = rc.nt0 + r % rc.bn;
       const int kb = __builtin_amdgcn_readfirstlane(tab[g]);
       const int kt = __builtin_amdgcn_readfirstlane((tab[g + 1] - kb) / kBK);
       if (kt == 0) {

@@ -570,23 +570,24 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
     // One output per group, all in big tiles; K range of group g from k_off.
     // Tiles of groups without rows are zero-filled; every other tile's first
     // slabs are issued by the previous tile of this workgroup (lookahead).
-    const int mtl = (int)((p.M + kBigM - 1) / kBigM);
-    const int per_g = mtl * p.ntiles;
+    const WgradRect rc = wgrad_rect((int)((p.M + kBigM - 1) / kBigM), p.ntiles, xcd);
+    const int per_g = rc.bm * rc.bn;
     const int tot = p.G * per_g;
     struct Job { int g, mt, nt, kb, kt; };
     auto job = [&](int P) {
       Job j;
       j.g = __builtin_amdgcn_readfirstlane(P / per_g);
       const int r = P - j.g * per_g;
-      j.mt = __builtin_amdgcn_readfirstlane(r / p.ntiles);
-      j.nt = __builtin_amdgcn_readfirstlane(r - j.mt * p.ntiles);
+      const int rm = r / rc.bn;
+      j.mt = __builtin_amdgcn_readfirstlane(rc.mt0 + rm);
+      j.nt = __builtin_amdgcn_readfirstlane(rc.nt0 + r - rm * rc.bn);
       j.kb = __builtin_amdgcn_readfirstlane(tab[j.g]);
       j.kt = __builtin_amdgcn_readfirstlane((tab[j.g + 1] - j.kb) / kBKB);
       return j;
     };
-    int P = xcd * per_xcd + slot;
+    int P = slot;
     Job cj = {0, 0, 0, 0, 0};
-    for (; P < tot; P += nwg) {
+    for (; P < tot; P += per_xcd) {
       cj = job(P);
       if (cj.kt) break;
       mx_zero_tile(p, cj.g, (int64_t)cj.mt * kBigM, cj.nt * kBN);
@@ -596,9 +597,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
     mx_setup<kBigM, MODE>(p, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kb, cj.kt * kBKB);
     bool pre = false;
     for (;;) {
-      int Pn = P + nwg;
+      int Pn = P + per_xcd;
       Job nj = {0, 0, 0, 0, 0};
-      for (; Pn < tot; Pn += nwg) {
+      for (; Pn < tot; Pn += per_xcd) {
         nj = job(Pn);
         if (nj.kt) break;
       }
@@ -607,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
       if (has) mx_setup<kBigM, MODE>(p, nxt, nj.g, 0, p.M, (int64_t)nj.mt * kBigM, nj.nt, nj.kb, nj.kt * kBKB);
       mx_tile<kBigM, MODE, 2>(p, smem_mx, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kt, pre, has, nxt,
                               nj.kt);
-      for (int Pz = P + nwg; Pz < Pn; Pz += nwg) {  // zero tiles between the two
+      for (int Pz = P + per_xcd; Pz < Pn; Pz += per_xcd) {  // zero tiles between the two
         const Job z = job(Pz);
         mx_zero_tile(p, z.g, (int64_t)z.mt * kBigM, z.nt * kBN);
       }
