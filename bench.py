@@ -17,6 +17,11 @@ bounded sample of the headline workload.
 Prints ONE JSON line.  Stage times come from HIP events that the library
 records on its stream at fixed stage boundaries during the timed steps; the
 roofline object describes the dominant kernel of the step.
+
+--workloads NAME[,NAME...] (or "n3") instead measures the forward and the
+backward of other layer shapes (gen/configs.py: the Kimi K2.7 Code, GLM-5.2,
+Qwen3.5 and DeepSeek-V4-Pro layers whole on one GPU, and one GPU's share of
+an EP-64 run) and prints one JSON line with a result per workload.
 """
 import argparse
 import json
@@ -197,6 +202,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 DeepSeek-V3 (T=8192) measurements")
     ap.add_argument("--only-bf16", action="store_true",
                     help="run only the bf16 DeepSeek-V3 (T=8192) measurements (for per-part profiles)")
+    ap.add_argument("--workloads", default="",
+                    help='comma-separated config names, or "n3": measure these workloads instead')
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -206,6 +213,16 @@ def main():
     import torch
     import gen
     import mixture_experts_layer_prefix_amd as M
+
+    if args.workloads:
+        names = gen.configs.N3 if args.workloads == "n3" else args.workloads.split(",")
+        res = {}
+        for n in names:
+            res[n] = workload_part(args, gen.get_config(n), torch, gen, M)
+            torch.cuda.empty_cache()
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "data": "synthetic", "workloads": res}), flush=True)
+        return
 
     D = gen.get_config("c4")
     log("[bench] workload", D)
@@ -280,6 +297,43 @@ def headline(args, D, p, w, out, torch, M):
         "tflops": round(tflops, 2), "roofline_step_frac": round(t_roof / (ms / 1e3), 4),
         "roofline": roofline, "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     })
+
+
+def workload_part(args, D, torch, gen, M):
+    """Forward and backward of one workload (weights and inputs from the
+    seeded generator, MXFP8 weights quantized once outside the timing)."""
+    log("[bench] workload", D)
+    p = gen.Problem(D)
+    names = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+    w = M.Weights(**{n: (p.device(n) if (D.S or not n.startswith("ws_")) else None) for n in names})
+    x, dy, bias = p.device("x"), p.device("dy"), p.device_bias()
+    md = M.Dims(D.T, D.d, D.E, D.k, D.I, D.S, D.Is)
+    mx = D.prec == "mxfp8"
+    if mx:
+        w = M.prepare_mxfp8(w, md)
+    wb = M.prepare_backward(w, mxfp8=mx)
+    f, b = M.ForwardPlan(md, D.prec, keep_gu=True), M.BackwardPlan(md, D.prec)
+    for _ in range(args.warmup):
+        f.run(x, w, bias)
+        b.run(dy, x, wb, f.routing)
+    ef = timed_steps(lambda i: f.run(x, w, bias), args.steps, torch)
+    eb = timed_steps(lambda i: b.run(dy, x, wb, f.routing), args.steps, torch)
+    fms, bms = ef / args.steps * 1e3, eb / args.steps * 1e3
+    peak = PEAK["mxfp8"] if mx else PEAK["bf16"]
+    hc = f.routing["expert_counts"].cpu()
+    res = {"T": D.T, "d": D.d, "E": D.E, "k": D.k, "I": D.I, "n_shared": D.S, "I_shared": D.Is,
+           "precision": D.prec, "router_skew": "Zipf(%g)" % D.zipf if D.zipf else "none",
+           "fwd_ms": round(fms, 4), "fwd_tokens_s": round(D.T / (fms / 1e3), 1),
+           "fwd_tflops": round(D.fwd_flops() / (fms / 1e3) / 1e12, 2),
+           "bwd_ms": round(bms, 4), "bwd_tokens_s": round(D.T / (bms / 1e3), 1),
+           "bwd_tflops": round(D.bwd_flops() / (bms / 1e3) / 1e12, 2),
+           "step_tokens_s": round(D.T / ((fms + bms) / 1e3), 1),
+           "mfma_peak_frac_step": round((D.fwd_flops() + D.bwd_flops()) / ((fms + bms) / 1e3) / 1e12 / peak, 4),
+           "max_rows": int(hc.max()), "empty_experts": int((hc == 0).sum())}
+    log("[bench]   fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)"
+        % (fms, res["fwd_tflops"], bms, res["bwd_tflops"]))
+    del f, b, wb, w
+    return res
 
 
 def bf16_part(args, D, w, out, torch, gen, M):

@@ -50,6 +50,31 @@ CONFIGS = {
 }
 
 
+# The layer shapes the Mixture-of-Kittens blog post benchmarks ("MoE layer
+# benchmarks": experts, hidden size, expert intermediate size, top-k of the
+# Kimi K2.7 Code, GLM-5.2, Qwen3.5-397B-A17B and DeepSeek-V4-Pro layers), as
+# whole layers on one GPU at T=8192 (one shared expert of the routed
+# intermediate size, the DeepSeek-V3-style layer the post targets; the
+# router skew recipe of c3), and as one GPU's share of the post's runs (EP
+# degree 64, 2,048 tokens per GPU before routing): the E/64 local experts and
+# the 2,048·k rows they receive on average, each row routed to one local
+# expert (k = 1 over the local experts, no skew, no shared expert: the shared
+# expert runs on the source GPU's own 2,048 tokens).
+SHAPES = {  # name: (E, d, I, k)
+    "kimi_k27": (384, 7168, 2048, 8),
+    "glm52": (256, 6144, 2048, 8),
+    "qwen35": (512, 4096, 1024, 10),
+    "dsv4pro": (384, 7168, 3072, 6),
+    "dsv3": (256, 7168, 2048, 8),
+}
+for _n, (_E, _d, _I, _k) in SHAPES.items():
+    if _n != "dsv3":
+        CONFIGS[_n] = Dims(_n, 8192, _d, _E, _k, _I, 1, _I, "bf16", 1.2, backward=True)
+        CONFIGS[_n + "_mx"] = Dims(_n + "_mx", 8192, _d, _E, _k, _I, 1, _I, "mxfp8", 1.2, backward=True)
+    CONFIGS["ep64_" + _n] = Dims("ep64_" + _n, 2048 * _k, _d, _E // 64, 1, _I, 0, 0, "mxfp8", 0.0, backward=True)
+N3 = [n for n in CONFIGS if n.split("_mx")[0] in SHAPES or n.startswith("ep64_")]
+
+
 def get_config(name, **over):
     c = CONFIGS[name]
     if not over:

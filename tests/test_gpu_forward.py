@@ -120,10 +120,20 @@ def test_c1_full_oracle():
 @pytest.mark.parametrize("cfg,nsample", [("c2", 48), ("c3a", 24), ("c3b", 16)])
 def test_large_config_sampled(cfg, nsample):
     """Full routing and permutation; outputs on a seeded token sample."""
+    check_forward_sampled(gen.get_config(cfg), nsample)
+
+
+def check_forward_sampled(D, nsample):
+    """Routing and permutation bit-exact on every token, bitwise-deterministic
+    output, and the output of sampled tokens (plus every token of the
+    smallest non-empty expert) against the oracle.  MXFP8 layers are quantized
+    once before the two runs."""
     import mixture_experts_layer_prefix_amd as M
-    D = gen.get_config(cfg)
+    cfg = D.name
     say("[case] sampled", cfg, D)
     p, t, md, w = device_problem(D)
+    if D.prec == "mxfp8":
+        w = M.prepare_mxfp8(w, md)
     y, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
     y2, _ = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
     assert torch.equal(y, y2), "forward is not bitwise deterministic"
@@ -135,11 +145,13 @@ def test_large_config_sampled(cfg, nsample):
         assert np.array_equal(to_np(routing[n]), ref[r]), n
     rng = np.random.default_rng(1234)
     tokens = sorted(rng.choice(D.T, size=nsample, replace=False).tolist())
-    # include every token of the smallest non-empty expert (ragged tail)
+    # include every token of the smallest non-empty expert (ragged tail) when
+    # it is small
     nz = np.nonzero(ref["counts"])[0]
     e_small = int(nz[np.argmin(ref["counts"][nz])])
     lo, hi = ref["offsets"][e_small], ref["offsets"][e_small + 1]
-    tokens = sorted(set(tokens) | set(ref["row_token"][lo:hi].tolist()))
+    if hi - lo <= 64:
+        tokens = sorted(set(tokens) | set(ref["row_token"][lo:hi].tolist()))
     ys = hp.sampled_forward(tokens, ref["topk_idx"], ref["topk_w"])
     got = to_np(y[torch.tensor(tokens, device="cuda")])
     e = rel_err(got, ys)

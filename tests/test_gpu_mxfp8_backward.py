@@ -205,8 +205,15 @@ def test_small_mxfp8_backward(name):
 
 def test_c4_backward_sampled():
     """The DeepSeek-V3-shaped MXFP8 layer (T=16384, Zipf-skewed routing)."""
-    D = gen.get_config("c4")
-    say("[case] c4 backward sampled", D)
+    check_backward_sampled(gen.get_config("c4"))
+
+
+def check_backward_sampled(D, ntok=6):
+    """Sampled tokens' dx and dL/dg, and sampled intermediate columns of the
+    weight gradients of the largest, smallest and median non-empty experts
+    (every row of those experts), each against the oracle and the
+    quantization-aware model."""
+    say("[case] %s backward sampled" % D.name, D)
     got, (plan, dy, t, wb, routing) = run_backward(D)
     del plan, dy, t, wb
     hp = HostProblem(D)
@@ -215,7 +222,7 @@ def test_c4_backward_sampled():
     assert np.array_equal(to_np(routing["topk_idx"]), idx)
     from tests.moe_parity import sampled_backward
     rng = np.random.default_rng(12)
-    tokens = np.sort(rng.choice(D.T, size=6, replace=False))
+    tokens = np.sort(rng.choice(D.T, size=ntok, replace=False))
     dx_ref, dg_ref = sampled_backward(hp, tokens, idx, g)
     tk = torch.as_tensor(tokens, device=got["dx"].device)
     dx_got, dg_got = to_np(got["dx"][tk]), to_np(got["dtopk_w"][tk])
