@@ -198,7 +198,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens of the CPU oracle sample (0: skip)")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 DeepSeek-V3 (T=8192) measurements")
     ap.add_argument("--only-bf16", action="store_true",
                     help="run only the bf16 DeepSeek-V3 (T=8192) measurements (for per-part profiles)")
@@ -236,6 +236,9 @@ def main():
         headline(args, D, p, w, out, torch, M)
     if not args.no_bf16:
         bf16_part(args, D, w, out, torch, gen, M)
+    if not args.only_bf16:
+        out["vendor_dense_gemm"] = vendor_reference(D, torch)
+        log("[bench] vendor dense GEMM reference:", out["vendor_dense_gemm"])
     if args.cpu_sample > 0 and not args.only_bf16:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(D, rows_hot=4 * args.cpu_sample, tokens=args.cpu_sample)
@@ -297,6 +300,38 @@ def headline(args, D, p, w, out, torch, M):
         "tflops": round(tflops, 2), "roofline_step_frac": round(t_roof / (ms / 1e3), 4),
         "roofline": roofline, "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     })
+
+
+def vendor_reference(D, torch, M_rows=16384):
+    """Context, not the product path: the vendor GEMM library (torch.matmul and
+    torch._scaled_mm, i.e. hipBLASLt) on one dense GEMM of the gate/up shape
+    (M_rows x 2I x d), bf16 and per-tensor-scaled E4M3, on this GPU."""
+    N, K = 2 * D.I, D.d
+    a = torch.randn(M_rows, K, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+    res = {"shape": "%d x %d x %d (M x N x K)" % (M_rows, N, K), "library": "hipBLASLt via torch"}
+
+    def rate(fn):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(20):
+            fn()
+        e.record()
+        e.synchronize()
+        return round(2.0 * M_rows * N * K / (s.elapsed_time(e) / 20 / 1e3) / 1e12, 1)
+
+    res["bf16_tflops"] = rate(lambda: a @ b.t())
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        one = torch.ones((), device="cuda")
+        res["fp8_tflops"] = rate(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                                          out_dtype=torch.bfloat16))
+    except Exception as ex:  # the fp8 path of the library may be missing
+        res["fp8_tflops"] = None
+        res["fp8_error"] = str(ex)[:120]
+    return res
 
 
 def workload_part(args, D, torch, gen, M):
