@@ -170,8 +170,8 @@ def cpu_baseline(D, rows_hot=8192, tokens=2048):
     spent_rows, nrows = 0.0, 0
     for e, n in ((hot, rows_hot), (med, max(int(counts[med]), 1))):
         wg, wu, wd = (p.host_expert(nm, e) for nm in ("w_gate", "w_up", "w_down"))
-        xr = p.host_rows("x", rng.choice(D.T, size=n, replace=False))
-        dyr = p.host_rows("dy", rng.choice(D.T, size=n, replace=False))
+        xr = p.host_rows("x", rng.choice(D.T, size=n, replace=n > D.T))
+        dyr = p.host_rows("dy", rng.choice(D.T, size=n, replace=n > D.T))
         t0 = time.perf_counter()
         O.swiglu_ffn(xr, wg, wu, wd)
         O.ffn_backward(xr, wg, wu, wd, 0.3 * dyr)

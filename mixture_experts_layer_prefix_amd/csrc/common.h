@@ -92,6 +92,31 @@ __device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&
 struct WgradRect {
   int mt0, nt0, bm, bn;
 };
+
+// Weight-gradient groups in descending K length (ties: lower id) into
+// order[0..G), from the K offset table koff[0..G] (both in LDS; every thread
+// of the block takes part).  Tiles are then handed out longest first, each
+// XCD's workgroups taking positions in snake order (see wgrad_pos), so the
+// few long tiles of the busiest experts spread over the workgroups before
+// the many short ones fill in (longest-processing-time list scheduling).
+__device__ __forceinline__ void wgrad_order(const int32_t* koff, int G, int32_t* order) {
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int kg = koff[g + 1] - koff[g];
+    int r = 0;
+    for (int h = 0; h < G; ++h) {
+      const int kh = koff[h + 1] - koff[h];
+      r += (kh > kg) || (kh == kg && h < g);
+    }
+    order[r] = g;
+  }
+}
+
+// Position of round r of workgroup `slot` among the `per_xcd` workgroups of
+// its XCD: slot s takes r * per_xcd + s on even rounds and
+// r * per_xcd + per_xcd - 1 - s on odd ones.
+__device__ __forceinline__ int wgrad_pos(int r, int slot, int per_xcd) {
+  return r * per_xcd + ((r & 1) ? per_xcd - 1 - slot : slot);
+}
 __device__ __forceinline__ WgradRect wgrad_rect(int mtl, int ntl, int xcd) {
   int a = 1, best = 1 << 30;
   for (int c = 1; c <= 8; c *= 2) {

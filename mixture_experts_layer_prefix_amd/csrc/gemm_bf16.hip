@@ -508,9 +508,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
     const WgradRect rc = wgrad_rect((int)((p.M + kBigM - 1) / kBigM), p.ntiles, xcd);
     const int per_g = rc.bm * rc.bn;
     const int tot = p.G * per_g;
-    for (int P = slot; P < tot; P += per_xcd) {
-      const int g = __builtin_amdgcn_readfirstlane(P / per_g);
-      const int r = P - g * per_g;
+    int32_t* order = tab + (p.G + 1);
+    wgrad_order(tab, p.G, order);
+    __syncthreads();
+    for (int rd = 0;; ++rd) {
+      const int P = wgrad_pos(rd, slot, per_xcd);
+      if (P >= tot) break;
+      const int gi = P / per_g;
+      const int g = __builtin_amdgcn_readfirstlane(order[gi]);
+      const int r = P - gi * per_g;
       const int mt = rc.mt0 + r / rc.bn, nt = rc.nt0 + r % rc.bn;
       const int kb = __builtin_amdgcn_readfirstlane(tab[g]);
       const int kt = __builtin_amdgcn_readfirstlane((tab[g + 1] - kb) / kBK);

@@ -573,11 +573,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
     const WgradRect rc = wgrad_rect((int)((p.M + kBigM - 1) / kBigM), p.ntiles, xcd);
     const int per_g = rc.bm * rc.bn;
     const int tot = p.G * per_g;
+    int32_t* order = tab + (p.G + 1);
+    wgrad_order(tab, p.G, order);
+    __syncthreads();
     struct Job { int g, mt, nt, kb, kt; };
     auto job = [&](int P) {
       Job j;
-      j.g = __builtin_amdgcn_readfirstlane(P / per_g);
-      const int r = P - j.g * per_g;
+      const int gi = P / per_g;
+      j.g = __builtin_amdgcn_readfirstlane(order[gi]);
+      const int r = P - gi * per_g;
       const int rm = r / rc.bn;
       j.mt = __builtin_amdgcn_readfirstlane(rc.mt0 + rm);
       j.nt = __builtin_amdgcn_readfirstlane(rc.nt0 + r - rm * rc.bn);
@@ -585,37 +589,38 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
       j.kt = __builtin_amdgcn_readfirstlane((tab[j.g + 1] - j.kb) / kBKB);
       return j;
     };
-    int P = slot;
+    auto pos = [&](int r) { return wgrad_pos(r, slot, per_xcd); };
+    int r = 0;
     Job cj = {0, 0, 0, 0, 0};
-    for (; P < tot; P += per_xcd) {
-      cj = job(P);
+    for (; pos(r) < tot; ++r) {
+      cj = job(pos(r));
       if (cj.kt) break;
       mx_zero_tile(p, cj.g, (int64_t)cj.mt * kBigM, cj.nt * kBN);
     }
-    if (P >= tot) return;
+    if (pos(r) >= tot) return;
     MxLoad<kBigM> cur;
     mx_setup<kBigM, MODE>(p, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kb, cj.kt * kBKB);
     bool pre = false;
     for (;;) {
-      int Pn = P + per_xcd;
+      int rn = r + 1;
       Job nj = {0, 0, 0, 0, 0};
-      for (; Pn < tot; Pn += per_xcd) {
-        nj = job(Pn);
+      for (; pos(rn) < tot; ++rn) {
+        nj = job(pos(rn));
         if (nj.kt) break;
       }
-      const bool has = Pn < tot;
+      const bool has = pos(rn) < tot;
       MxLoad<kBigM> nxt;
       if (has) mx_setup<kBigM, MODE>(p, nxt, nj.g, 0, p.M, (int64_t)nj.mt * kBigM, nj.nt, nj.kb, nj.kt * kBKB);
       mx_tile<kBigM, MODE, 2>(p, smem_mx, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kt, pre, has, nxt,
                               nj.kt);
-      for (int Pz = P + per_xcd; Pz < Pn; Pz += per_xcd) {  // zero tiles between the two
-        const Job z = job(Pz);
+      for (int rz = r + 1; rz < rn; ++rz) {  // zero tiles between the two
+        const Job z = job(pos(rz));
         mx_zero_tile(p, z.g, (int64_t)z.mt * kBigM, z.nt * kBN);
       }
       if (!has) break;
       cur = nxt;
       cj = nj;
-      P = Pn;
+      r = rn;
       pre = true;
     }
     return;
