@@ -173,25 +173,28 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
 // routed rows of one expert; zero padding quantizes to zero codes), and
 // stored expert-blocked: segment e is a dense [cols][Kp_e] block at byte
 // pad_off[e] * cols (Kp_e = pad_off[e+1] - pad_off[e]), its scales a
-// [cols][Kp_e / 32] block at pad_off[e] * cols / 32.  The four threads of a
-// block combine their maxima with lane shuffles.
+// [cols][Kp_e / 32] block at pad_off[e] * cols / 32.  One workgroup
+// transposes 128 positions x 64 columns (segments are whole multiples of 128
+// positions), so each output row piece it writes is 128 bytes, whole cache
+// lines; each thread quantizes one 32-position block of one column.
 __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __restrict__ src, int64_t ld_src, int cols,
                                                               const int32_t* __restrict__ gather,
                                                               const int32_t* __restrict__ seg_off,
                                                               const int32_t* __restrict__ pad_off, int nseg,
                                                               uint8_t* __restrict__ dst,
                                                               uint8_t* __restrict__ dst_scale) {
-  __shared__ bf16_t tile[64][66];
-  const int64_t p0 = (int64_t)blockIdx.x * 64;
+  constexpr int TP = 128, TC = 64, LDT = TC + 8;  // LDS rows of 144 bytes: 16-byte aligned
+  __shared__ __attribute__((aligned(16))) bf16_t tile[TP][LDT];
+  const int64_t p0 = (int64_t)blockIdx.x * TP;
   if (p0 >= pad_off[nseg]) return;
-  const int c0 = blockIdx.y * 64;
+  const int c0 = blockIdx.y * TC;
   const int e = find_segment(pad_off, nseg, p0);
   const int64_t r0 = seg_off[e] + (p0 - pad_off[e]);
   const int64_t r_end = seg_off[e + 1];
   const int tid = threadIdx.x;
   const int ch = tid & 7;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < TP / 32; ++h) {
     const int i = (tid >> 3) + 32 * h;
     const int64_t r = r0 + i;
     u32x4 v = u32x4{0, 0, 0, 0};
@@ -199,39 +202,33 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
       const int64_t srow = gather ? (int64_t)gather[r] : r;
       v = *reinterpret_cast<const u32x4*>(src + srow * ld_src + c0 + ch * 8);
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[i][ch * 8 + 2 * q] = (bf16_t)(v[q] & 0xFFFFu);
-      tile[i][ch * 8 + 2 * q + 1] = (bf16_t)(v[q] >> 16);
-    }
+    *reinterpret_cast<u32x4*>(&tile[i][ch * 8]) = v;
   }
   __syncthreads();
+  const int c = tid & (TC - 1), blk = tid / TC;
+  float v[32];
+  float amax = 0.0f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = (tid >> 3) + 32 * h;
-    float v[8];
-    float amax = 0.0f;
+  for (int q = 0; q < 32; ++q) {
+    v[q] = bf16_to_f32(tile[blk * 32 + q][c]);
+    amax = fmaxf(amax, fabsf(v[q]));
+  }
+  const int ex = mx_block_exp(amax);
+  const float inv = mx_inv_scale(ex);
+  u32x4 w[2];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      v[q] = bf16_to_f32(tile[ch * 8 + q][c]);
-      amax = fmaxf(amax, fabsf(v[q]));
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int ex = mx_block_exp(amax);
-    const float inv = mx_inv_scale(ex);
-    uint32_t w0 = 0, w1 = 0;
+  for (int q = 0; q < 8; ++q) {
+    uint32_t word = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w0 |= e4m3_rne_sat(v[q] * inv) << (8 * q);
-      w1 |= e4m3_rne_sat(v[4 + q] * inv) << (8 * q);
-    }
-    if (c0 + c < cols) {
-      const int64_t kp = pad_off[e + 1] - pad_off[e];
-      const int64_t off = (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + ch * 8;
-      *reinterpret_cast<uint2*>(dst + off) = uint2{w0, w1};
-      if ((ch & 3) == 0) dst_scale[off / 32] = (uint8_t)(ex + 127);
-    }
+    for (int b = 0; b < 4; ++b) word |= e4m3_rne_sat(v[4 * q + b] * inv) << (8 * b);
+    w[q >> 2][q & 3] = word;
+  }
+  if (c0 + c < cols) {
+    const int64_t kp = pad_off[e + 1] - pad_off[e];
+    const int64_t off = (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + blk * 32;
+    *reinterpret_cast<u32x4*>(dst + off) = w[0];
+    *reinterpret_cast<u32x4*>(dst + off + 16) = w[1];
+    dst_scale[off / 32] = (uint8_t)(ex + 127);
   }
 }
 
@@ -373,8 +370,8 @@ hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, c
                                   const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
                                   uint8_t* dst, uint8_t* dst_scale, hipStream_t s) {
   if (p_cap == 0 || cols == 0) return hipSuccess;
-  if (p_cap % 64 || ld_src % 8) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 63) / 64));
+  if (p_cap % 128 || ld_src % 8 || cols % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p_cap / 128), (unsigned)((cols + 63) / 64));
   transpose_quant_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, dst_scale);
   return hipGetLastError();
 }

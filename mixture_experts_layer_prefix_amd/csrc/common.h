@@ -173,7 +173,8 @@ int64_t bwd_padded_rows(int64_t rows, int groups, int pad);
 // pad_off[E+1]: padded prefix of counts; single[4] = {0, round_up(T, pad), 0, T}.
 hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int pad, int32_t* pad_off, int32_t* single,
                               hipStream_t s);
-// Expert-blocked output: segment e is a [cols][Kp_e] block at pad_off[e] * cols.
+// Expert-blocked output: segment e is a [cols][Kp_e] block at pad_off[e] * cols
+// (segments whole multiples of 128 positions; p_cap, cols multiples of 128, 8).
 hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
                                   const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
                                   uint8_t* dst, uint8_t* dst_scale, hipStream_t s);
