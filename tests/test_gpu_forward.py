@@ -21,6 +21,8 @@ SMALL = {
     "bf16_k1": gen.Dims("bf16_k1", 77, 64, 4, 1, 64, 1, 64, "bf16", 0.0),
     "bf16_kE": gen.Dims("bf16_kE", 64, 128, 8, 8, 64, 0, 0, "bf16", 0.0),
     "f32_skew": gen.Dims("f32_skew", 200, 96, 12, 3, 40, 1, 24, "f32", 1.2),
+    # the ABI's limits: E = 1024 experts, k = 16
+    "bf16_max_E_k": gen.Dims("bf16_max_E_k", 300, 128, 1024, 16, 64, 1, 64, "bf16", 1.2),
 }
 
 
