@@ -217,12 +217,8 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
   const float inv = mx_inv_scale(ex);
   u32x4 w[2];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) word |= e4m3_rne_sat(v[4 * q + b] * inv) << (8 * b);
-    w[q >> 2][q & 3] = word;
-  }
+  for (int q = 0; q < 8; ++q)
+    w[q >> 2][q & 3] = e4m3x4_rne_sat(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
   if (c0 + c < cols) {
     const int64_t kp = pad_off[e + 1] - pad_off[e];
     const int64_t off = (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + blk * 32;

@@ -32,28 +32,57 @@ __device__ __forceinline__ float sigmoid_f32(float z) { return __builtin_amdgcn_
 
 __device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
 
+// Reductions over the 32 lanes of each wave half (lanes 0-31 and 32-63) with
+// the result in every lane of the half, without LDS round trips: four DPP
+// steps inside each 16-lane row (partner lane l^1, l^2, then the mirrored
+// 8-lane and 16-lane halves), then v_permlane16_swap, which hands every lane
+// both rows' values of its half.  Every lane combines the same operands in
+// the same order, so all 32 lanes hold bit-identical results.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Unsigned maximum (of magnitudes as bit patterns: no float canonicalization).
+__device__ __forceinline__ uint32_t half_max32_u(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+__device__ __forceinline__ float half_sum32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // MX (OCP MX v1.0) E4M3 elements with one E8M0 scale per 32 values: the block
 // exponent is floor(log2 max|v|) - 8 clamped to [-127, 127] (-127 for an
 // all-zero block); elements are v / 2^e rounded to nearest-even E4M3,
 // saturating at +-448, sign kept.
 // ---------------------------------------------------------------------------
-// |s| < 512 assumed (the block scale puts the block maximum below 2^9).
+// E4M3 code of s, round to nearest even, saturating at +-448: the clamp to
+// +-448 followed by gfx950's OCP E4M3 conversion, which rounds to nearest
+// even (bit-identical to that definition for every fp32 input of magnitude
+// below 512, checked exhaustively on the hardware; larger inputs saturate).
+__device__ __forceinline__ float e4m3_clamp(float s) { return __builtin_amdgcn_fmed3f(s, -448.0f, 448.0f); }
 __device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
-  const uint32_t bits = __float_as_uint(s);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(s);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7Eu;  // 448 itself, ties at 464 go to 448, larger values saturate
-  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
-    code = (u >> 20) - (120u << 3);     // rebias exponent 127 -> 7
-  }
-  return sign | code;
+  const float c = e4m3_clamp(s);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+// Four codes packed into one word, a in the lowest byte.
+__device__ __forceinline__ uint32_t e4m3x4_rne_sat(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
 }
 
 // Block exponent (unbiased) of a 32-value block from its max magnitude.
@@ -74,12 +103,8 @@ __device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&
   const int e = mx_block_exp(amax);
   const float inv = mx_inv_scale(e);
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) p |= e4m3_rne_sat(v[4 * w + b] * inv) << (8 * b);
-    packed[w] = p;
-  }
+  for (int w = 0; w < 8; ++w)
+    packed[w] = e4m3x4_rne_sat(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv, v[4 * w + 3] * inv);
   return (uint32_t)(e + 127);
 }
 

@@ -374,36 +374,55 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
     // dH' (unscaled by the router weight w) -> dG, dU, w h (the down
     // projection's weight-gradient operand) and the partial router-weight
     // gradient <dH', h> over these 32 columns (all lanes take part in the
-    // reduction).
+    // reduction).  The G, U and router-weight loads of a batch of VB rows are
+    // all issued before the first use: one memory round trip per batch
+    // instead of one per row.
+    constexpr int VB = 8;
     const int N = p.N;
 #pragma clang loop unroll(full)
     for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
-      for (int v = 0; v < 16; ++v) {
-        const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int64_t grow = row0 + min(rl, rows_left - 1);
-        const float wr = p.w_row ? p.w_row[grow] : 1.0f;
-        const bf16_t* gurow = p.gu + grow * 2 * N;
+      for (int vb = 0; vb < 16; vb += VB) {
+        float wrb[VB];
+        bf16_t gb[VB][FN], ub[VB][FN];
+#pragma clang loop unroll(full)
+        for (int u = 0; u < VB; ++u) {
+          const int rl = wm * WM + i * 32 + 8 * ((vb + u) >> 2) + 4 * (lane >> 5) + ((vb + u) & 3);
+          const int64_t grow = row0 + min(rl, rows_left - 1);
+          wrb[u] = p.w_row ? p.w_row[grow] : 1.0f;
+          const bf16_t* gurow = p.gu + grow * 2 * N;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
-          const int col = min(col0, N - 1);
-          const float gv = bf16_to_f32(gurow[col]);
-          const float uv = bf16_to_f32(gurow[N + col]);
-          const float sg = sigmoid_f32(gv);
-          const float sl = gv * sg;
-          const float h = sl * uv;
-          const float dhp = acc[i][j][v];
-          const float dh = wr * dhp;
-          float part = dhp * h;
+          for (int j = 0; j < FN; ++j) {
+            const int col = min(ntile * BN + wn * WN + j * 32 + (lane & 31), N - 1);
+            gb[u][j] = gurow[col];
+            ub[u][j] = gurow[N + col];
+          }
+        }
+#pragma clang loop unroll(full)
+        for (int u = 0; u < VB; ++u) {
+          const int v = vb + u;
+          const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int64_t grow = row0 + min(rl, rows_left - 1);
+          const float wr = wrb[u];
 #pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-          if (rl < rows_left && col0 < N) {
-            bf16_t* drow = p.dgu + grow * 2 * N;
-            drow[col] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
-            drow[N + col] = f32_to_bf16(dh * sl);
-            if (p.h_out) p.h_out[grow * N + col] = f32_to_bf16(wr * h);
-            if (p.dg_part && (lane & 31) == 0) p.dg_part[grow * (N / 32) + col / 32] = part;
+          for (int j = 0; j < FN; ++j) {
+            const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
+            const int col = min(col0, N - 1);
+            const float gv = bf16_to_f32(gb[u][j]);
+            const float uv = bf16_to_f32(ub[u][j]);
+            const float sg = sigmoid_f32(gv);
+            const float sl = gv * sg;
+            const float h = sl * uv;
+            const float dhp = acc[i][j][v];
+            const float dh = wr * dhp;
+            const float part = half_sum32(dhp * h);
+            if (rl < rows_left && col0 < N) {
+              bf16_t* drow = p.dgu + grow * 2 * N;
+              drow[col] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
+              drow[N + col] = f32_to_bf16(dh * sl);
+              if (p.h_out) p.h_out[grow * N + col] = f32_to_bf16(wr * h);
+              if (p.dg_part && (lane & 31) == 0) p.dg_part[grow * (N / 32) + col / 32] = part;
+            }
           }
         }
       }

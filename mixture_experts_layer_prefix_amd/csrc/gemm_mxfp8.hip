@@ -158,10 +158,10 @@ __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) 
 // (lane & 31) of a lane half: returns the E4M3 code of this lane's value and
 // the block's E8M0 byte in *scale (all lanes take part).
 __device__ __forceinline__ uint32_t mx_lane_quant(float v, uint32_t* scale) {
-  float amax = fabsf(v);
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = mx_block_exp(amax);
+  // Block maximum magnitude as a bit pattern; its exponent field gives the
+  // block exponent (zero and fp32 subnormals clamp to -127).
+  const uint32_t amax = half_max32_u(__float_as_uint(v) & 0x7FFFFFFFu);
+  const int e = max((int)(amax >> 23) - 135, -127);
   *scale = (uint32_t)(e + 127);
   return e4m3_rne_sat(v * mx_inv_scale(e));
 }
@@ -458,6 +458,76 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     }
     return;
   }
+  if constexpr (MODE == GEMM_SWIGLU_BWD) {
+    // dH' -> dG, dU (bf16 and quantized along the columns), w h and the
+    // partial router-weight gradient <dH', h> per 32-column block.  The G, U
+    // and router-weight loads of a batch of VB rows are all issued before the
+    // first use: one memory round trip per batch instead of one per row.
+    constexpr int VB = 8;
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FM; ++i) {
+#pragma clang loop unroll(full)
+      for (int vb = 0; vb < 16; vb += VB) {
+        float wrb[VB];
+        bf16_t gb[VB][FN], ub[VB][FN];
+#pragma clang loop unroll(full)
+        for (int u = 0; u < VB; ++u) {
+          const int rl = wm * WM + i * 32 + 8 * ((vb + u) >> 2) + 4 * (lane >> 5) + ((vb + u) & 3);
+          const int64_t grow = row_begin + m0 + min(rl, rows_left - 1);
+          wrb[u] = p.w_row ? p.w_row[grow] : 1.0f;
+          const bf16_t* gurow = p.gu + grow * 2 * N;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = min(ntile * BN + wn * WN + j * 32 + (lane & 31), N - 1);
+            gb[u][j] = gurow[col];
+            ub[u][j] = gurow[N + col];
+          }
+        }
+#pragma clang loop unroll(full)
+        for (int u = 0; u < VB; ++u) {
+          const int v = vb + u;
+          const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const bool row_ok = rl < rows_left;
+          const int64_t grow = row_begin + m0 + (row_ok ? rl : rows_left - 1);
+          const float wr = wrb[u];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
+            const int col = min(col0, N - 1);
+            const float gv = bf16_to_f32(gb[u][j]);
+            const float uv = bf16_to_f32(ub[u][j]);
+            const float sg = sigmoid_f32(gv);
+            const float sl = gv * sg;
+            const float h = sl * uv;
+            const float dhp = acc[i][j][v];
+            const float dh = wr * dhp;
+            const float dgv = dh * uv * sg * (1.0f + gv * (1.0f - sg));
+            const float duv = dh * sl;
+            const float part = half_sum32(dhp * h);
+            uint32_t sg_sc, su_sc;
+            const uint32_t cg = mx_lane_quant(dgv, &sg_sc);
+            const uint32_t cu = mx_lane_quant(duv, &su_sc);
+            if (row_ok && col0 < N) {
+              bf16_t* drow = p.dgu + grow * 2 * N;
+              drow[col] = f32_to_bf16(dgv);
+              drow[N + col] = f32_to_bf16(duv);
+              uint8_t* qrow = p.dguq + grow * 2 * N;
+              qrow[col] = (uint8_t)cg;
+              qrow[N + col] = (uint8_t)cu;
+              p.h_out[grow * N + col] = f32_to_bf16(wr * h);
+              if ((lane & 31) == 0) {
+                uint8_t* srow = p.dgus + grow * (2 * N / 32);
+                srow[col / 32] = (uint8_t)sg_sc;
+                srow[(N + col) / 32] = (uint8_t)su_sc;
+                if (p.dg_part) p.dg_part[grow * (N / 32) + col / 32] = part;
+              }
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
@@ -487,46 +557,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
           bf16_t* C = static_cast<bf16_t*>(p.C) + grow * ldc;
           C[col] = f32_to_bf16(acc[i][0][v]);
           C[N + col] = f32_to_bf16(acc[i][1][v]);
-        }
-      } else if constexpr (MODE == GEMM_SWIGLU_BWD) {
-        // dH' -> dG, dU (bf16 and quantized along the columns), w h and the
-        // partial router-weight gradient <dH', h> per 32-column block.
-        const float wr = p.w_row ? p.w_row[grow] : 1.0f;
-        const bf16_t* gurow = p.gu + grow * 2 * N;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
-          const int col = min(col0, N - 1);
-          const float gv = bf16_to_f32(gurow[col]);
-          const float uv = bf16_to_f32(gurow[N + col]);
-          const float sg = sigmoid_f32(gv);
-          const float sl = gv * sg;
-          const float h = sl * uv;
-          const float dhp = acc[i][j][v];
-          const float dh = wr * dhp;
-          const float dgv = dh * uv * sg * (1.0f + gv * (1.0f - sg));
-          const float duv = dh * sl;
-          float part = dhp * h;
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-          uint32_t sg_sc, su_sc;
-          const uint32_t cg = mx_lane_quant(dgv, &sg_sc);
-          const uint32_t cu = mx_lane_quant(duv, &su_sc);
-          if (row_ok && col0 < N) {
-            bf16_t* drow = p.dgu + grow * 2 * N;
-            drow[col] = f32_to_bf16(dgv);
-            drow[N + col] = f32_to_bf16(duv);
-            uint8_t* qrow = p.dguq + grow * 2 * N;
-            qrow[col] = (uint8_t)cg;
-            qrow[N + col] = (uint8_t)cu;
-            p.h_out[grow * N + col] = f32_to_bf16(wr * h);
-            if ((lane & 31) == 0) {
-              uint8_t* srow = p.dgus + grow * (2 * N / 32);
-              srow[col / 32] = (uint8_t)sg_sc;
-              srow[(N + col) / 32] = (uint8_t)su_sc;
-              if (p.dg_part) p.dg_part[grow * (N / 32) + col / 32] = part;
-            }
-          }
         }
       }
     }
