@@ -459,70 +459,112 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     return;
   }
   if constexpr (MODE == GEMM_SWIGLU_BWD) {
-    // dH' -> dG, dU (bf16 and quantized along the columns), w h and the
-    // partial router-weight gradient <dH', h> per 32-column block.  The G, U
-    // and router-weight loads of a batch of VB rows are all issued before the
-    // first use: one memory round trip per batch instead of one per row.
-    constexpr int VB = 8;
+    // dH' -> dG, dU (bf16, and E4M3 along the columns), w h and the partial
+    // router-weight gradient <dH', h> per 32-column block.  The accumulators
+    // pass through LDS (the slab ring is idle once the last slab is read), so
+    // that four lanes then share one row's 32-column block, eight columns
+    // each: block maxima and sums take two DPP steps, every global access is
+    // 8 or 16 bytes, and one access instruction touches 16 rows.  Staging is
+    // per wave, 32-row blocks two at a time: element (r, c) of a wave's
+    // [PR][64] fp32 region sits at r * 64 + 4 * ((c / 4) ^ key(r)) + c % 4;
+    // key(r) flips chunk bit 0 with r bit 0 and chunk bit 3 with r bits 1 xor
+    // 2, so the accumulator-layout writes (rows r, r + 4) and the row reads
+    // (rows 4m..4m+3, four lanes each) are both free of bank conflicts.
+    constexpr int PI = FM >= 2 ? 2 : 1;  // 32-row blocks per pass
+    constexpr int PR = PI * 32;          // rows per pass
+    constexpr int ITEMS = PR * FN * 4 / 64;  // (row, block, quarter) items per lane per pass
+    static_assert(8 * PR * 64 * 4 <= (int)kSmemBytes, "staging fits the slab ring");
+    // Lane-derived epilogue values are computed here, not hoisted above the
+    // K loop where they would hold registers the loop needs.
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    float* stage = reinterpret_cast<float*>(smem) + wave * (PR * 64);
+    auto skey = [](int r) { return (r & 1) | ((((r >> 2) ^ (r >> 1)) & 1) << 3); };
+    const int qt = el & 3;  // quarter of the block: columns 8 qt .. 8 qt + 7
 #pragma clang loop unroll(full)
-    for (int i = 0; i < FM; ++i) {
+    for (int i0 = 0; i0 < FM; i0 += PI) {
+      if (i0) __syncthreads();  // the previous pass's row reads are done
 #pragma clang loop unroll(full)
-      for (int vb = 0; vb < 16; vb += VB) {
-        float wrb[VB];
-        bf16_t gb[VB][FN], ub[VB][FN];
+      for (int ii = 0; ii < PI; ++ii)
 #pragma clang loop unroll(full)
-        for (int u = 0; u < VB; ++u) {
-          const int rl = wm * WM + i * 32 + 8 * ((vb + u) >> 2) + 4 * (lane >> 5) + ((vb + u) & 3);
-          const int64_t grow = row_begin + m0 + min(rl, rows_left - 1);
-          wrb[u] = p.w_row ? p.w_row[grow] : 1.0f;
-          const bf16_t* gurow = p.gu + grow * 2 * N;
+        for (int v = 0; v < 16; ++v)
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const int col = min(ntile * BN + wn * WN + j * 32 + (lane & 31), N - 1);
-            gb[u][j] = gurow[col];
-            ub[u][j] = gurow[N + col];
+            const int r = ii * 32 + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
+            const int c = j * 32 + (el & 31);
+            stage[r * 64 + (((c >> 2) ^ skey(r)) << 2) + (c & 3)] = acc[i0 + ii][j][v];
           }
+      __syncthreads();
+#pragma unroll 1
+      for (int k = 0; k < ITEMS; ++k) {
+        const int rb = (k * 64 + el) >> 2;
+        const int r = rb % PR, blk = rb / PR;
+        const int tr = wm * WM + i0 * 32 + r;                    // row in the tile
+        const int col = ntile * BN + wn * WN + blk * 32 + 8 * qt;  // first of this lane's 8 columns
+        // Rows past the tile end skip their memory accesses but keep the
+        // quad's reductions in step (all four lanes of a row agree).
+        const bool ok = tr < rows_left && col < N;
+        const int64_t grow = row_begin + m0 + min(tr, rows_left - 1);
+        const int64_t rowoff = grow * (int64_t)(2 * N);  // elements before row grow of the [rows][2N] arrays
+        float* s0 = stage + r * 64 + (((blk * 8 + 2 * qt) ^ skey(r)) << 2);
+        float* s1 = stage + r * 64 + (((blk * 8 + 2 * qt + 1) ^ skey(r)) << 2);
+        u32x4 gq = {0, 0, 0, 0}, uq = {0, 0, 0, 0};
+        float wr = 0.0f;
+        if (ok) {
+          gq = *reinterpret_cast<const u32x4*>(p.gu + rowoff + col);
+          uq = *reinterpret_cast<const u32x4*>(p.gu + rowoff + N + col);
+          wr = p.w_row ? p.w_row[grow] : 1.0f;
         }
-#pragma clang loop unroll(full)
-        for (int u = 0; u < VB; ++u) {
-          const int v = vb + u;
-          const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bool row_ok = rl < rows_left;
-          const int64_t grow = row_begin + m0 + (row_ok ? rl : rows_left - 1);
-          const float wr = wrb[u];
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(s0), d1 = *reinterpret_cast<const f32x4*>(s1);
+        float dg[8], du[8];
+        uint32_t hw[4];
+        float part = 0.0f;
+        uint32_t mg = 0, mu = 0;
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col0 = ntile * BN + wn * WN + j * 32 + (lane & 31);
-            const int col = min(col0, N - 1);
-            const float gv = bf16_to_f32(gb[u][j]);
-            const float uv = bf16_to_f32(ub[u][j]);
-            const float sg = sigmoid_f32(gv);
-            const float sl = gv * sg;
-            const float h = sl * uv;
-            const float dhp = acc[i][j][v];
-            const float dh = wr * dhp;
-            const float dgv = dh * uv * sg * (1.0f + gv * (1.0f - sg));
-            const float duv = dh * sl;
-            const float part = half_sum32(dhp * h);
-            uint32_t sg_sc, su_sc;
-            const uint32_t cg = mx_lane_quant(dgv, &sg_sc);
-            const uint32_t cu = mx_lane_quant(duv, &su_sc);
-            if (row_ok && col0 < N) {
-              bf16_t* drow = p.dgu + grow * 2 * N;
-              drow[col] = f32_to_bf16(dgv);
-              drow[N + col] = f32_to_bf16(duv);
-              uint8_t* qrow = p.dguq + grow * 2 * N;
-              qrow[col] = (uint8_t)cg;
-              qrow[N + col] = (uint8_t)cu;
-              p.h_out[grow * N + col] = f32_to_bf16(wr * h);
-              if ((lane & 31) == 0) {
-                uint8_t* srow = p.dgus + grow * (2 * N / 32);
-                srow[col / 32] = (uint8_t)sg_sc;
-                srow[(N + col) / 32] = (uint8_t)su_sc;
-                if (p.dg_part) p.dg_part[grow * (N / 32) + col / 32] = part;
-              }
-            }
-          }
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t gw = gq[e >> 1], uw = uq[e >> 1];
+          const float gv = __uint_as_float((e & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+          const float uv = __uint_as_float((e & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
+          const float sg = sigmoid_f32(gv);
+          const float sl = gv * sg;
+          const float h = sl * uv;
+          const float dhp = e < 4 ? d0[e] : d1[e - 4];
+          const float dh = wr * dhp;
+          dg[e] = dh * uv * sg * (1.0f + gv * (1.0f - sg));
+          du[e] = dh * sl;
+          part += dhp * h;
+          mg = max(mg, __float_as_uint(dg[e]) & 0x7FFFFFFFu);
+          mu = max(mu, __float_as_uint(du[e]) & 0x7FFFFFFFu);
+          const uint32_t wh = f32_to_bf16(wr * h);
+          if (e & 1) hw[e >> 1] |= wh << 16; else hw[e >> 1] = wh;
+        }
+        // Reductions over the quad (the row's 32 columns).
+        mg = max(mg, dpp_u32<0xB1>(mg));
+        mg = max(mg, dpp_u32<0x4E>(mg));
+        mu = max(mu, dpp_u32<0xB1>(mu));
+        mu = max(mu, dpp_u32<0x4E>(mu));
+        part += dpp_f32<0xB1>(part);
+        part += dpp_f32<0x4E>(part);
+        if (!ok) continue;
+        const int eg = max((int)(mg >> 23) - 135, -127), eu = max((int)(mu >> 23) - 135, -127);
+        const float ig = mx_inv_scale(eg), iu = mx_inv_scale(eu);
+        bf16_t* drow = p.dgu + rowoff + col;
+        *reinterpret_cast<u32x4*>(drow) = u32x4{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
+                                                pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
+        *reinterpret_cast<u32x4*>(drow + N) = u32x4{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                                                    pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
+        *reinterpret_cast<u32x4*>(p.h_out + (rowoff >> 1) + col) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        uint8_t* qrow = p.dguq + rowoff + col;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(qrow) = u32x2{e4m3x4_rne_sat(dg[0] * ig, dg[1] * ig, dg[2] * ig, dg[3] * ig),
+                                                e4m3x4_rne_sat(dg[4] * ig, dg[5] * ig, dg[6] * ig, dg[7] * ig)};
+        *reinterpret_cast<u32x2*>(qrow + N) = u32x2{e4m3x4_rne_sat(du[0] * iu, du[1] * iu, du[2] * iu, du[3] * iu),
+                                                    e4m3x4_rne_sat(du[4] * iu, du[5] * iu, du[6] * iu, du[7] * iu)};
+        if (qt == 0) {
+          uint8_t* srow = p.dgus + (rowoff >> 5);
+          srow[col / 32] = (uint8_t)(eg + 127);
+          srow[(N + col) / 32] = (uint8_t)(eu + 127);
+          if (p.dg_part) p.dg_part[(rowoff >> 6) + col / 32] = part;
         }
       }
     }
