@@ -175,8 +175,9 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
 // pad_off[e] * cols (Kp_e = pad_off[e+1] - pad_off[e]), its scales a
 // [cols][Kp_e / 32] block at pad_off[e] * cols / 32.  One workgroup
 // transposes 128 positions x 64 columns (segments are whole multiples of 128
-// positions), so each output row piece it writes is 128 bytes, whole cache
-// lines; each thread quantizes one 32-position block of one column.
+// positions); each thread quantizes one 32-position block of one column, and
+// the codes go back through LDS so that every output row piece (one column's
+// 128 positions, a whole cache line) leaves as 8 lanes x 16 bytes.
 __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __restrict__ src, int64_t ld_src, int cols,
                                                               const int32_t* __restrict__ gather,
                                                               const int32_t* __restrict__ seg_off,
@@ -185,6 +186,11 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
                                                               uint8_t* __restrict__ dst_scale) {
   constexpr int TP = 128, TC = 64, LDT = TC + 8;  // LDS rows of 144 bytes: 16-byte aligned
   __shared__ __attribute__((aligned(16))) bf16_t tile[TP][LDT];
+  // After the quantization the same LDS holds the codes, [column][8 x 16 bytes],
+  // and the scales, [column][4].
+  u32x4(*codes)[8] = reinterpret_cast<u32x4(*)[8]>(&tile[0][0]);
+  uint32_t* scales = reinterpret_cast<uint32_t*>(&tile[0][0]) + TC * 8 * 4;
+  static_assert(TC * 8 * 16 + TC * 4 <= TP * LDT * 2, "codes fit the tile");
   const int64_t p0 = (int64_t)blockIdx.x * TP;
   if (p0 >= pad_off[nseg]) return;
   const int c0 = blockIdx.y * TC;
@@ -219,12 +225,21 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     w[q >> 2][q & 3] = e4m3x4_rne_sat(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
-  if (c0 + c < cols) {
-    const int64_t kp = pad_off[e + 1] - pad_off[e];
-    const int64_t off = (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + blk * 32;
-    *reinterpret_cast<u32x4*>(dst + off) = w[0];
-    *reinterpret_cast<u32x4*>(dst + off + 16) = w[1];
-    dst_scale[off / 32] = (uint8_t)(ex + 127);
+  __syncthreads();  // every thread has read its tile column
+  codes[c][blk * 2] = w[0];
+  codes[c][blk * 2 + 1] = w[1];
+  reinterpret_cast<uint8_t*>(scales)[c * 4 + blk] = (uint8_t)(ex + 127);
+  __syncthreads();
+  const int64_t kp = pad_off[e + 1] - pad_off[e];
+  const int64_t base = (int64_t)pad_off[e] * cols + (p0 - pad_off[e]);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = tid + 256 * it, cc = q >> 3, part = q & 7;
+    if (c0 + cc < cols) {
+      const int64_t off = base + (int64_t)(c0 + cc) * kp;
+      *reinterpret_cast<u32x4*>(dst + off + part * 16) = codes[cc][part];
+      if (part == 0) *reinterpret_cast<uint32_t*>(dst_scale + off / 32) = scales[cc];
+    }
   }
 }
 
