@@ -161,7 +161,7 @@ BwdWs carve_backward(Carver& c, const moe_dims* D, moe_prec prec) {
   w.dl = static_cast<float*>(c.take((size_t)R * 4));
   w.dl_row = static_cast<float*>(c.take((size_t)R * 4));
   w.gu = c.take((size_t)R * 2 * I * 2);
-  w.dgu = c.take((size_t)R * 2 * I * 2);
+  w.dgu = mx ? nullptr : c.take((size_t)R * 2 * I * 2);  // MXFP8: dG, dU stay in the epilogue
   w.gh = c.take((size_t)R * I * 2);
   w.da = c.take((size_t)R * d * 2);
   w.dg_part = static_cast<float*>(c.take((size_t)R * (I / 32) * 4));
@@ -529,6 +529,10 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q.B0_scale = w->qt_down_scale;
     q.dgu_q = b.dguq;
     q.dgu_scale = b.dguqs;
+    q.dgu_t = b.dguTq;  // dG^T | dU^T for the weight gradients, quantized in the epilogue
+    q.dgu_t_scale = b.dguTqs;
+    q.pad_off = b.pad_off;
+    q.t_ld = b.Rp;
   }
   MOE_HIP(mx ? launch_gemm_mxfp8(q, s) : launch_gemm_bf16(q, s));
   trace(1, 3, s);
@@ -574,14 +578,11 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   const int32_t* off = rt->expert_offsets;
   if (mx) {
     const int64_t Rp = b.Rp, Rs = b.Rp / 32;
-    // Expert-blocked: dG^T and dU^T are separate transposes so each is a
-    // [I][Kp_e] block sequence of its own.
+    // Expert-blocked [cols][Kp_e] operands; dG^T and dU^T came from the
+    // down-dgrad epilogue.
     MOE_HIP(launch_transpose_quant(x, d, d, rt->row_token, off, b.pad_off, E, Rp, b.xTq, b.xTqs, s));
     MOE_HIP(launch_transpose_quant(dy, d, d, rt->row_token, off, b.pad_off, E, Rp, b.dyTq, b.dyTqs, s));
     MOE_HIP(launch_transpose_quant(gh, I, I, nullptr, off, b.pad_off, E, Rp, b.ghTq, b.ghTqs, s));
-    MOE_HIP(launch_transpose_quant(dgu, 2 * I, I, nullptr, off, b.pad_off, E, Rp, b.dguTq, b.dguTqs, s));
-    MOE_HIP(launch_transpose_quant(dgu + I, 2 * I, I, nullptr, off, b.pad_off, E, Rp, b.dguTq + (int64_t)I * Rp,
-                                   b.dguTqs + (int64_t)I * Rs, s));
     trace(1, 8, s);
     MOE_TRY(run_wgrad_mx(b.dyTq, b.dyTqs, d, b.ghTq, b.ghTqs, I, Rp, b.pad_off, E, g->dw_down, s));
     trace(1, 9, s);

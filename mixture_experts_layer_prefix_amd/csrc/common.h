@@ -266,6 +266,11 @@ struct GemmProblem {
   void* gu_out;              // gate/up: optional [rows][2N] bf16 G | U (kept for the backward)
   uint8_t* dgu_q;           // MX: [rows][2N] dG | dU quantized along the columns
   uint8_t* dgu_scale;       // MX: [rows][2N/32]
+  uint8_t* dgu_t;           // MX: dG^T then dU^T quantized along the routed rows, expert-blocked as
+                            // the weight-gradient operands ([N][Kp_g] at pad_off[g] * N; dU^T N * t_ld later)
+  uint8_t* dgu_t_scale;     // MX: their scales (a 32nd of each offset)
+  const int32_t* pad_off;   // MX: [G+1] padded group row offsets (multiples of 128)
+  int64_t t_ld;             // MX: total padded rows
   // K-grouped (weight gradient) mode
   const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups; the operands are
                             // expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike)

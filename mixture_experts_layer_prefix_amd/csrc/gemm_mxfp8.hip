@@ -137,6 +137,10 @@ struct MxArgs {
   bf16_t* dgu;              // [rows][2N] dG | dU (bf16)
   uint8_t* dguq;            // [rows][2N] dG | dU quantized along the columns
   uint8_t* dgus;            // [rows][2N/32] their scales
+  uint8_t* dgu_t;           // dG^T then dU^T, E4M3 along the routed rows, expert-blocked (see the epilogue)
+  uint8_t* dgu_ts;          // their scales
+  const int32_t* pad_off;   // [G+1] padded row offsets of the groups (multiples of 128)
+  int64_t t_ld;             // padded rows of all groups: dU^T starts N * t_ld bytes after dG^T
   bf16_t* h_out;            // [rows][N] w h
   float* dg_part;           // [rows][N/32]
   // K-grouped weight-gradient mode
@@ -459,17 +463,27 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     return;
   }
   if constexpr (MODE == GEMM_SWIGLU_BWD) {
-    // dH' -> dG, dU (bf16, and E4M3 along the columns), w h and the partial
-    // router-weight gradient <dH', h> per 32-column block.  The accumulators
-    // pass through LDS (the slab ring is idle once the last slab is read), so
-    // that four lanes then share one row's 32-column block, eight columns
-    // each: block maxima and sums take two DPP steps, every global access is
-    // 8 or 16 bytes, and one access instruction touches 16 rows.  Staging is
-    // per wave, 32-row blocks two at a time: element (r, c) of a wave's
-    // [PR][64] fp32 region sits at r * 64 + 4 * ((c / 4) ^ key(r)) + c % 4;
-    // key(r) flips chunk bit 0 with r bit 0 and chunk bit 3 with r bits 1 xor
-    // 2, so the accumulator-layout writes (rows r, r + 4) and the row reads
-    // (rows 4m..4m+3, four lanes each) are both free of bank conflicts.
+    // dH' -> dG, dU, w h and the partial router-weight gradient <dH', h> per
+    // 32-column block.  dG and dU leave in E4M3 twice: along the columns (the
+    // gate/up input-gradient GEMM's A operand) and along the routed rows in
+    // the expert-blocked transposed layout of the weight-gradient operands
+    // (group g: [N][Kp_g] codes at pad_off[g] * N, scales at a 32nd of that).
+    //
+    // The accumulators pass through LDS (the slab ring is idle once the last
+    // slab is read), per wave, 32-row blocks two at a time: element (r, c)
+    // of a wave's [PR][64] fp32 region sits at r * 64 + 4 * ((c / 4) ^
+    // key(r)) + c % 4; key(r) flips chunk bit 0 with r bit 0 and chunk bit 3
+    // with r bits 1 xor 2, which keeps the accumulator-layout writes (rows r,
+    // r + 4), the row phase (rows 4m..4m+3, four lanes each) and the column
+    // phase (one row, 64 lanes) free of bank conflicts.
+    //   Row phase: four lanes share one row's 32-column block, eight columns
+    // each (block maxima and sums in two DPP steps, 8- and 16-byte global
+    // accesses); each lane writes its eight dG and eight dU, rounded to bf16,
+    // back over its eight dH' values (the two 16-byte chunks).
+    //   Column phase: lane (q, pair) takes columns 2 pair, 2 pair + 1 of dG
+    // (q = 0) or dU (q = 1) down each 32-row block and writes both columns'
+    // 32 codes.  Rows past the group's end quantize as zeros; the padding
+    // rows past the group's last tile are zero-filled by that tile.
     constexpr int PI = FM >= 2 ? 2 : 1;  // 32-row blocks per pass
     constexpr int PR = PI * 32;          // rows per pass
     constexpr int ITEMS = PR * FN * 4 / 64;  // (row, block, quarter) items per lane per pass
@@ -479,11 +493,21 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     int el = lane;
     asm volatile("" : "+v"(el));
     float* stage = reinterpret_cast<float*>(smem) + wave * (PR * 64);
+    uint32_t* stage_w = reinterpret_cast<uint32_t*>(stage);
     auto skey = [](int r) { return (r & 1) | ((((r >> 2) ^ (r >> 1)) & 1) << 3); };
-    const int qt = el & 3;  // quarter of the block: columns 8 qt .. 8 qt + 7
+    const int qt = el & 3;  // row phase: quarter of the block, columns 8 qt .. 8 qt + 7
+    const int cq = el >> 5, cp = el & 31;  // column phase: dG / dU, column pair
+    const int64_t kp = p.pad_off[g + 1] - p.pad_off[g];
+    const int wcol = ntile * BN + wn * WN;  // first of the wave's 64 columns
+    const bool wave_cols = wcol < N;        // N is a multiple of 64: all 64 or none
+    // This lane's first column in the transposed output, at row 0 of the
+    // group (the second column is kp bytes further), codes and scales.
+    const int64_t toff = (cq ? (int64_t)N * p.t_ld : 0) + (int64_t)p.pad_off[g] * N + (int64_t)(wcol + 2 * cp) * kp;
+    uint8_t* tq = p.dgu_t + toff;
+    uint8_t* ts = p.dgu_ts + toff / 32;
 #pragma clang loop unroll(full)
     for (int i0 = 0; i0 < FM; i0 += PI) {
-      if (i0) __syncthreads();  // the previous pass's row reads are done
+      if (i0) __syncthreads();  // the previous pass's column reads are done
 #pragma clang loop unroll(full)
       for (int ii = 0; ii < PI; ++ii)
 #pragma clang loop unroll(full)
@@ -501,13 +525,13 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         const int r = rb % PR, blk = rb / PR;
         const int tr = wm * WM + i0 * 32 + r;                    // row in the tile
         const int col = ntile * BN + wn * WN + blk * 32 + 8 * qt;  // first of this lane's 8 columns
-        // Rows past the tile end skip their memory accesses but keep the
-        // quad's reductions in step (all four lanes of a row agree).
+        // Rows past the tile end skip their global accesses but keep the
+        // quad's reductions in step and stage zeros for the column phase.
         const bool ok = tr < rows_left && col < N;
         const int64_t grow = row_begin + m0 + min(tr, rows_left - 1);
         const int64_t rowoff = grow * (int64_t)(2 * N);  // elements before row grow of the [rows][2N] arrays
-        float* s0 = stage + r * 64 + (((blk * 8 + 2 * qt) ^ skey(r)) << 2);
-        float* s1 = stage + r * 64 + (((blk * 8 + 2 * qt + 1) ^ skey(r)) << 2);
+        uint32_t* s0 = stage_w + r * 64 + (((blk * 8 + 2 * qt) ^ skey(r)) << 2);
+        uint32_t* s1 = stage_w + r * 64 + (((blk * 8 + 2 * qt + 1) ^ skey(r)) << 2);
         u32x4 gq = {0, 0, 0, 0}, uq = {0, 0, 0, 0};
         float wr = 0.0f;
         if (ok) {
@@ -538,6 +562,11 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
           const uint32_t wh = f32_to_bf16(wr * h);
           if (e & 1) hw[e >> 1] |= wh << 16; else hw[e >> 1] = wh;
         }
+        // dG, dU in bf16 over this lane's dH' (zeros for rows past the end).
+        *reinterpret_cast<u32x4*>(s0) = u32x4{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
+                                              pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
+        *reinterpret_cast<u32x4*>(s1) = u32x4{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                                              pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
         // Reductions over the quad (the row's 32 columns).
         mg = max(mg, dpp_u32<0xB1>(mg));
         mg = max(mg, dpp_u32<0x4E>(mg));
@@ -548,11 +577,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         if (!ok) continue;
         const int eg = max((int)(mg >> 23) - 135, -127), eu = max((int)(mu >> 23) - 135, -127);
         const float ig = mx_inv_scale(eg), iu = mx_inv_scale(eu);
-        bf16_t* drow = p.dgu + rowoff + col;
-        *reinterpret_cast<u32x4*>(drow) = u32x4{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
-                                                pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
-        *reinterpret_cast<u32x4*>(drow + N) = u32x4{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
-                                                    pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
         *reinterpret_cast<u32x4*>(p.h_out + (rowoff >> 1) + col) = u32x4{hw[0], hw[1], hw[2], hw[3]};
         uint8_t* qrow = p.dguq + rowoff + col;
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -566,6 +590,57 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
           srow[(N + col) / 32] = (uint8_t)(eu + 127);
           if (p.dg_part) p.dg_part[(rowoff >> 6) + col / 32] = part;
         }
+      }
+      __syncthreads();  // dG, dU of the pass are staged
+      // Column phase: this pass's 32-row blocks along the routed rows.
+#pragma unroll
+      for (int b = 0; b < PI; ++b) {
+        const int rr0 = (int)m0 + wm * WM + i0 * 32 + 32 * b;  // group row of the block's first row
+        if (!wave_cols || rr0 >= kp) continue;
+        uint32_t x[32];
+        uint32_t m0b = 0, m1b = 0;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const int r = 32 * b + q;
+          const int chunk = ((cp >> 4) * 8 + 2 * ((cp & 15) >> 2) + cq) ^ skey(r);
+          x[q] = stage_w[r * 64 + (chunk << 2) + (cp & 3)];
+          m0b = max(m0b, (x[q] << 16) & 0x7FFFFFFFu);
+          m1b = max(m1b, x[q] & 0x7FFF0000u);
+        }
+        const int e0 = max((int)(m0b >> 23) - 135, -127), e1 = max((int)(m1b >> 23) - 135, -127);
+        const float i0s = mx_inv_scale(e0), i1s = mx_inv_scale(e1);
+        u32x4 c0[2], c1[2];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int q = 4 * w;
+          c0[w >> 2][w & 3] = e4m3x4_rne_sat(__uint_as_float(x[q] << 16) * i0s, __uint_as_float(x[q + 1] << 16) * i0s,
+                                             __uint_as_float(x[q + 2] << 16) * i0s, __uint_as_float(x[q + 3] << 16) * i0s);
+          c1[w >> 2][w & 3] = e4m3x4_rne_sat(__uint_as_float(x[q] & 0xFFFF0000u) * i1s,
+                                             __uint_as_float(x[q + 1] & 0xFFFF0000u) * i1s,
+                                             __uint_as_float(x[q + 2] & 0xFFFF0000u) * i1s,
+                                             __uint_as_float(x[q + 3] & 0xFFFF0000u) * i1s);
+        }
+        uint8_t* o0 = tq + rr0;
+        *reinterpret_cast<u32x4*>(o0) = c0[0];
+        *reinterpret_cast<u32x4*>(o0 + 16) = c0[1];
+        *reinterpret_cast<u32x4*>(o0 + kp) = c1[0];
+        *reinterpret_cast<u32x4*>(o0 + kp + 16) = c1[1];
+        ts[rr0 / 32] = (uint8_t)(e0 + 127);
+        ts[(rr0 + kp) / 32] = (uint8_t)(e1 + 127);
+      }
+    }
+    // Padding rows [m0 + BM, Kp_g) after the group's last tile (a single
+    // 64-row tile whose group's row count ends within its first 64 rows of a
+    // 128-row padding unit): zero codes and scales.
+    if (wm == 0 && wave_cols && m0 + BM < kp && m0 + BM >= n_g) {
+      for (int rr = (int)m0 + BM; rr < kp; rr += 32) {
+        uint8_t* o0 = tq + rr;
+        *reinterpret_cast<u32x4*>(o0) = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(o0 + 16) = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(o0 + kp) = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(o0 + kp + 16) = u32x4{0, 0, 0, 0};
+        ts[rr / 32] = 0;
+        ts[(rr + kp) / 32] = 0;
       }
     }
     return;
@@ -796,6 +871,10 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.dgu = static_cast<bf16_t*>(q.dgu);
   a.dguq = q.dgu_q;
   a.dgus = q.dgu_scale;
+  a.dgu_t = q.dgu_t;
+  a.dgu_ts = q.dgu_t_scale;
+  a.pad_off = q.pad_off;
+  a.t_ld = q.t_ld;
   a.h_out = static_cast<bf16_t*>(q.h_out);
   a.dg_part = q.dg_part;
   a.k_off = q.k_off;
@@ -832,7 +911,8 @@ hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
     case GEMM_DOWN: return run_mx<GEMM_DOWN>(q, s);
     case GEMM_GU: return run_mx<GEMM_GU>(q, s);
     case GEMM_SWIGLU_BWD:
-      if (!q.gu || !q.dgu || !q.dgu_q || !q.dgu_scale || !q.h_out) return hipErrorInvalidValue;
+      if (!q.gu || !q.dgu_q || !q.dgu_scale || !q.h_out || !q.dgu_t || !q.dgu_t_scale || !q.pad_off || q.t_ld % 128)
+        return hipErrorInvalidValue;
       return run_mx<GEMM_SWIGLU_BWD>(q, s);
     case GEMM_DUALK:
       if ((q.K / 2) % kBKB != 0) return hipErrorInvalidValue;

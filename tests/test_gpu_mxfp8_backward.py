@@ -33,6 +33,10 @@ SMALL = {
     "mxb_tiles": gen.Dims("mxb_tiles", 1100, 512, 8, 2, 384, 1, 192, "mxfp8", 0.0, backward=True),
     # the ABI's limits: E = 1024 experts, k = 16
     "mxb_max_E_k": gen.Dims("mxb_max_E_k", 300, 128, 1024, 16, 128, 1, 64, "mxfp8", 1.2, backward=True),
+    # about 40 rows per expert: each expert's last GEMM tile (64 rows) ends
+    # inside its 128-row padding unit, so the padding rows of the
+    # weight-gradient operands past that tile must still be written as zeros
+    "mxb_pad_gap": gen.Dims("mxb_pad_gap", 160, 128, 8, 2, 128, 0, 0, "mxfp8", 0.0, backward=True),
 }
 
 
@@ -155,6 +159,12 @@ def run_backward(D):
     wb = M.prepare_backward(wq, mxfp8=True)
     _, routing = M.layer_forward(t["x"], wq, md, "mxfp8", bias=t["bias"])
     plan = M.BackwardPlan(md, "mxfp8")
+    # Poison the workspace and the outputs: every byte the backward reads
+    # must have been written by it (E4M3 and E8M0 0xFF are NaN).
+    plan.ws.fill_(255)
+    plan.dx.fill_(float("nan"))
+    for v in plan.grads.values():
+        v.fill_(float("nan"))
     dx, grads = plan.run(dy, t["x"], wb, routing)
     torch.cuda.synchronize()
     out = {"dx": dx}
