@@ -443,7 +443,12 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         for (int v = 0; v < 16; ++v) {
           bf16_t* Cr = Cb + (int64_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * ldc;
 #pragma unroll
-          for (int j = 0; j < FN; ++j) Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
+          for (int j = 0; j < FN; ++j) {
+            // Weight gradients are not read again by this layer: streaming
+            // stores keep them from displacing operand slabs in L2.
+            if constexpr (MODE == GEMM_WGRAD) __builtin_nontemporal_store(f32_to_bf16(acc[i][j][v]), &Cr[j * 32]);
+            else Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
+          }
         }
     } else {
       const int rl0 = wm * WM + 4 * (lane >> 5);
@@ -689,7 +694,7 @@ __device__ __forceinline__ void mx_zero_tile(const MxArgs& p, int g, int64_t m0,
   const int cpr = cols / 8;
   for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
     const int r = c / cpr, q = c - r * cpr;
-    *reinterpret_cast<u32x4*>(C + (m0 + r) * p.ldc + n0 + q * 8) = u32x4{0, 0, 0, 0};
+    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, reinterpret_cast<u32x4*>(C + (m0 + r) * p.ldc + n0 + q * 8));
   }
 }
 
