@@ -347,16 +347,30 @@ __global__ void __launch_bounds__(256) router_partial_kernel(const bf16_t* __res
   out[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
-// dW_router[e][c] = sum of expert e's chunk partials in chunk order (0 when empty).
+// dW_router[e][c] = sum of expert e's chunk partials (0 when empty) in a
+// fixed order: lane l of a column's 8 lanes sums chunks l, l + 8, l + 16, ...
+// in ascending order, then the 8 lane sums are added in lane order.  One
+// workgroup covers 32 columns of one expert, so the long chunk lists of the
+// busiest experts are read by 8 lanes at once.
 __global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restrict__ partial,
                                                             const int32_t* __restrict__ pad_off, int E, int d,
                                                             float* __restrict__ dw) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)E * d) return;
-  const int e = (int)(i / d), c = (int)(i - (int64_t)e * d);
+  __shared__ float part[8][33];
+  const int e = blockIdx.y;
+  const int cl = threadIdx.x & 31, l = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
+  const int q0 = pad_off[e] / kPadRows, q1 = pad_off[e + 1] / kPadRows;
   float acc = 0.0f;
-  for (int q = pad_off[e] / kPadRows; q < pad_off[e + 1] / kPadRows; ++q) acc += partial[(int64_t)q * d + c];
-  dw[i] = acc;
+  if (c < d)
+    for (int q = q0 + l; q < q1; q += 8) acc += partial[(int64_t)q * d + c];
+  part[l][cl] = acc;
+  __syncthreads();
+  if (l == 0 && c < d) {
+    float s = part[0][cl];
+#pragma unroll
+    for (int m = 1; m < 8; ++m) s += part[m][cl];
+    dw[(int64_t)e * d + c] = s;
+  }
 }
 
 unsigned grid_for(int64_t work, int64_t cap) {
@@ -434,7 +448,7 @@ hipError_t launch_router_wgrad(const bf16_t* x, const int32_t* row_token, const 
     const dim3 grid((unsigned)(p_cap / kPadRows), (unsigned)((d / 8 + 255) / 256));
     router_partial_kernel<<<grid, 256, 0, s>>>(x, row_token, dl_row, offsets, pad_off, E, d, partial);
   }
-  router_reduce_kernel<<<grid_for((int64_t)E * d, 1 << 30), 256, 0, s>>>(partial, pad_off, E, d, dw);
+  router_reduce_kernel<<<dim3((unsigned)((d + 31) / 32), (unsigned)E), 256, 0, s>>>(partial, pad_off, E, d, dw);
   return hipGetLastError();
 }
 
