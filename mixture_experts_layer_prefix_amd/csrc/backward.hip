@@ -172,8 +172,11 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
 // rows (blocks of 32 consecutive padded positions p, i.e. 32 consecutive
 // routed rows of one expert; zero padding quantizes to zero codes), and
 // stored expert-blocked: segment e is a dense [cols][Kp_e] block at byte
-// pad_off[e] * cols (Kp_e = pad_off[e+1] - pad_off[e]), its scales a
-// [cols][Kp_e / 32] block at pad_off[e] * cols / 32.  One workgroup
+// pad_off[e] * cols (Kp_e = pad_off[e+1] - pad_off[e]).  Its scales are
+// slab-major, a [Kp_e / 128][cols][4] block at pad_off[e] * cols / 32: the
+// four E8M0 bytes of one column and one 128-position slab are one dword, and
+// a slab's dwords are contiguous over the columns (the weight-gradient GEMM
+// reads one slab's scales of 256 rows as 1 KB).  One workgroup
 // transposes 128 positions x 64 columns (segments are whole multiples of 128
 // positions); each thread quantizes one 32-position block of one column, and
 // the codes go back through LDS so that every output row piece (one column's
@@ -232,15 +235,17 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
   __syncthreads();
   const int64_t kp = pad_off[e + 1] - pad_off[e];
   const int64_t base = (int64_t)pad_off[e] * cols + (p0 - pad_off[e]);
+  uint32_t* sdst = reinterpret_cast<uint32_t*>(dst_scale + (int64_t)pad_off[e] * cols / 32) +
+                   (p0 - pad_off[e]) / TP * cols;
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int q = tid + 256 * it, cc = q >> 3, part = q & 7;
     if (c0 + cc < cols) {
       const int64_t off = base + (int64_t)(c0 + cc) * kp;
       *reinterpret_cast<u32x4*>(dst + off + part * 16) = codes[cc][part];
-      if (part == 0) *reinterpret_cast<uint32_t*>(dst_scale + off / 32) = scales[cc];
     }
   }
+  if (tid < TC && c0 + tid < cols) sdst[c0 + tid] = scales[tid];
 }
 
 // dst[b][c][r] = src[b][r][c], element-wise bounds (any rows, cols).

@@ -198,7 +198,8 @@ int64_t bwd_padded_rows(int64_t rows, int groups, int pad);
 // pad_off[E+1]: padded prefix of counts; single[4] = {0, round_up(T, pad), 0, T}.
 hipError_t launch_pad_offsets(const int32_t* counts, int E, int64_t T, int pad, int32_t* pad_off, int32_t* single,
                               hipStream_t s);
-// Expert-blocked output: segment e is a [cols][Kp_e] block at pad_off[e] * cols
+// Expert-blocked output: segment e is a [cols][Kp_e] block at pad_off[e] * cols,
+// its scales a slab-major [Kp_e/128][cols][4] block at pad_off[e] * cols / 32
 // (segments whole multiples of 128 positions; p_cap, cols multiples of 128, 8).
 hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, const int32_t* gather,
                                   const int32_t* seg_off, const int32_t* pad_off, int nseg, int64_t p_cap,
@@ -268,12 +269,13 @@ struct GemmProblem {
   uint8_t* dgu_scale;       // MX: [rows][2N/32]
   uint8_t* dgu_t;           // MX: dG^T then dU^T quantized along the routed rows, expert-blocked as
                             // the weight-gradient operands ([N][Kp_g] at pad_off[g] * N; dU^T N * t_ld later)
-  uint8_t* dgu_t_scale;     // MX: their scales (a 32nd of each offset)
+  uint8_t* dgu_t_scale;     // MX: their scales, slab-major ([Kp_g/128][N][4] at pad_off[g] * N / 32)
   const int32_t* pad_off;   // MX: [G+1] padded group row offsets (multiples of 128)
   int64_t t_ld;             // MX: total padded rows
   // K-grouped (weight gradient) mode
   const int32_t* k_off;     // [G+1] K ranges (multiples of 64) of the groups; the operands are
-                            // expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike)
+                            // expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike); MX scales
+                            // slab-major ([Kp_g/128][M][4] at k_off[g] * M / 32)
   int64_t c_group_stride;   // elements between group outputs
 };
 

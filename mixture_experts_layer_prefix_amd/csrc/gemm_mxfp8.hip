@@ -215,9 +215,13 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
   const bool gath = p.a_rows != nullptr;
   const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
   const uint8_t* abase = uniform_ptr(gath ? p.A : Ab + (row_begin + m0) * lda);
-  const uint8_t* asbase = uniform_ptr(gath ? p.As : Asb + (row_begin + m0) * ldas);
+  // Weight-gradient scales are slab-major per group, [kp / 128][M][4]: a
+  // row's dword of one slab at row * 4, slabs M * 4 bytes apart.
+  const uint8_t* asbase =
+      uniform_ptr(gath ? p.As : KGROUPED ? Asb + m0 * 4 : Asb + (row_begin + m0) * ldas);
   const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * lda));
-  const uint32_t asbytes = __builtin_amdgcn_readfirstlane(gath ? p.as_bytes : (uint32_t)(tile_rows * ldas));
+  const uint32_t asbytes = __builtin_amdgcn_readfirstlane(
+      gath ? p.as_bytes : KGROUPED ? (uint32_t)(ldas * p.M - m0 * 4) : (uint32_t)(tile_rows * ldas));
   L.ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
   L.asr = __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
 #pragma unroll
@@ -237,7 +241,7 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
     const int64_t lr0 = wave * 64 + lane;
     const int64_t lr = lr0 < tile_rows ? lr0 : 0;
     const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
-    scoff = (uint32_t)(src * ldas);
+    scoff = (uint32_t)(src * (KGROUPED ? 4 : ldas));
   }
   const int bi = wave - 4;  // B-scale round of this wave
   const int span = PAIRED ? BN / 2 : BN;
@@ -246,12 +250,13 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
   L.brows = brows;
   if (b_sc) {
     const int r = PAIRED ? (bi & 1) * 64 + lane : bi * 64 + lane;
-    scoff = (uint32_t)(min(r, brows - 1) * ldbs);
+    scoff = (uint32_t)(min(r, brows - 1) * (KGROUPED ? 4 : ldbs));
   }
   L.scoff = scoff;
-  const uint8_t* bs0 = Bsb0 + (int64_t)g * p.bs_stride + first_row * ldbs;
+  const uint8_t* bs0 = Bsb0 + (int64_t)g * p.bs_stride + first_row * (KGROUPED ? 4 : ldbs);
   const uint8_t* bs1 = (PAIRED || DUAL) ? p.B1s + (int64_t)g * p.bs_stride + first_row * ldbs : bs0;
-  const uint32_t bsbytes = __builtin_amdgcn_readfirstlane((uint32_t)(brows * ldbs));
+  const uint32_t bsbytes = __builtin_amdgcn_readfirstlane(
+      KGROUPED ? (uint32_t)(ldbs * p.N - first_row * 4) : (uint32_t)(brows * ldbs));
   L.bsr0 = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(PAIRED && bi >= 2 ? bs1 : bs0), (short)0,
                                             (int)bsbytes, 0x00020000);
   L.bsr1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(bs1), (short)0, (int)bsbytes, 0x00020000)
@@ -295,13 +300,18 @@ __device__ __forceinline__ void mx_issue(const MxArgs& p, const MxLoad<BM>& L, u
                                              (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, L.boff,
                                              (uint32_t)(r0 * ldb + kb), 0, 0);
   }
+  // Scale dwords: row-major operands at K / 32 in the row; the slab-major
+  // weight-gradient operands at slab * rows * 4.
+  constexpr bool KGROUPED = MODE == GEMM_WGRAD;
+  const uint32_t sa_off = KGROUPED ? (uint32_t)(ka >> 7) * (uint32_t)(p.M * 4) : (uint32_t)(ka / 32);
+  const uint32_t sb_off = KGROUPED ? (uint32_t)(kb >> 7) * (uint32_t)(p.N * 4) : (uint32_t)(kb / 32);
   if (wave < BM / 64)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, L.scoff,
-                                             ka / 32, 0, 0);
+                                             sa_off, 0, 0);
   if (wave >= 4)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? L.bsr1 : L.bsr0,
                                              (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + (wave - 4) * 256), 4,
-                                             L.scoff, kb / 32, 0, 0);
+                                             L.scoff, sb_off, 0, 0);
 }
 
 // One BM x 256 output tile whose load state L is set up.  prefetched: its
@@ -506,10 +516,13 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     const int wcol = ntile * BN + wn * WN;  // first of the wave's 64 columns
     const bool wave_cols = wcol < N;        // N is a multiple of 64: all 64 or none
     // This lane's first column in the transposed output, at row 0 of the
-    // group (the second column is kp bytes further), codes and scales.
+    // group (the second column is kp bytes further), and its scale bytes:
+    // slab-major, [kp / 128][N][4] per group, so row rr's block scale of
+    // column c sits at (rr / 128) N 4 + c 4 + (rr / 32) % 4.
     const int64_t toff = (cq ? (int64_t)N * p.t_ld : 0) + (int64_t)p.pad_off[g] * N + (int64_t)(wcol + 2 * cp) * kp;
     uint8_t* tq = p.dgu_t + toff;
-    uint8_t* ts = p.dgu_ts + toff / 32;
+    uint8_t* ts = p.dgu_ts + ((cq ? (int64_t)N * p.t_ld : 0) + (int64_t)p.pad_off[g] * N) / 32 + (wcol + 2 * cp) * 4;
+    auto ts_at = [&](int rr) { return ts + (int64_t)(rr >> 7) * N * 4 + ((rr >> 5) & 3); };
 #pragma clang loop unroll(full)
     for (int i0 = 0; i0 < FM; i0 += PI) {
       if (i0) __syncthreads();  // the previous pass's column reads are done
@@ -630,8 +643,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         *reinterpret_cast<u32x4*>(o0 + 16) = c0[1];
         *reinterpret_cast<u32x4*>(o0 + kp) = c1[0];
         *reinterpret_cast<u32x4*>(o0 + kp + 16) = c1[1];
-        ts[rr0 / 32] = (uint8_t)(e0 + 127);
-        ts[(rr0 + kp) / 32] = (uint8_t)(e1 + 127);
+        uint8_t* s0 = ts_at(rr0);
+        s0[0] = (uint8_t)(e0 + 127);
+        s0[4] = (uint8_t)(e1 + 127);
       }
     }
     // Padding rows [m0 + BM, Kp_g) after the group's last tile (a single
@@ -644,8 +658,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         *reinterpret_cast<u32x4*>(o0 + 16) = u32x4{0, 0, 0, 0};
         *reinterpret_cast<u32x4*>(o0 + kp) = u32x4{0, 0, 0, 0};
         *reinterpret_cast<u32x4*>(o0 + kp + 16) = u32x4{0, 0, 0, 0};
-        ts[rr / 32] = 0;
-        ts[(rr + kp) / 32] = 0;
+        uint8_t* s0 = ts_at(rr);
+        s0[0] = 0;
+        s0[4] = 0;
       }
     }
     return;
