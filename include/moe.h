@@ -68,8 +68,10 @@ typedef struct {
 /* Weights (host struct of device pointers).  Element type: fp32 in MOE_F32,
  * bf16 otherwise.  ws_* are NULL when n_shared == 0.  In MOE_MXFP8 the
  * routed experts are read only from the pre-quantized copies q_* (produced
- * by moe_quantize_mxfp8 along the GEMM's K axis, i.e. along d for gate/up
- * and along I for down); w_gate/w_up/w_down may then be NULL. */
+ * by moe_quantize_mxfp8(axis 2) of the stacked [E*rows][K] matrix along the
+ * GEMM's K axis, i.e. along d for gate/up and along I for down: codes
+ * [E][rows][K], scales slab-major [K/128][E*rows][4]); w_gate/w_up/w_down
+ * may then be NULL. */
 typedef struct {
   const void* w_router;                          /* [E][d] */
   const void* w_gate;                            /* [E][I][d] */
@@ -78,9 +80,9 @@ typedef struct {
   const void* ws_gate;                           /* [S][I_s][d] */
   const void* ws_up;                             /* [S][I_s][d] */
   const void* ws_down;                           /* [S][d][I_s] */
-  const uint8_t *q_gate, *q_gate_scale;          /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
-  const uint8_t *q_up, *q_up_scale;              /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
-  const uint8_t *q_down, *q_down_scale;          /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
+  const uint8_t *q_gate, *q_gate_scale;          /* E4M3 [E][I][d], E8M0 [d/128][E*I][4] */
+  const uint8_t *q_up, *q_up_scale;              /* E4M3 [E][I][d], E8M0 [d/128][E*I][4] */
+  const uint8_t *q_down, *q_down_scale;          /* E4M3 [E][d][I], E8M0 [I/128][E*d][4] */
   /* Backward only: transposed copies for the input-gradient GEMMs, made
    * once per weight update with moe_transpose_weights (bf16). */
   const void* wt_gate;                           /* [E][d][I] = W_gate[e]^T */
@@ -90,11 +92,11 @@ typedef struct {
   const void* wst_up;                            /* [S][d][I_s] */
   const void* wst_down;                          /* [S][I_s][d] */
   /* Backward in MOE_MXFP8 only: the transposed routed copies quantized along
-   * their rows (the input-gradient GEMMs' K): moe_quantize_mxfp8(axis 0) of
+   * their rows (the input-gradient GEMMs' K): moe_quantize_mxfp8(axis 2) of
    * wt_gate, wt_up (blocks along I) and wt_down (blocks along d). */
-  const uint8_t *qt_gate, *qt_gate_scale;        /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
-  const uint8_t *qt_up, *qt_up_scale;            /* E4M3 [E][d][I], E8M0 [E][d][I/32] */
-  const uint8_t *qt_down, *qt_down_scale;        /* E4M3 [E][I][d], E8M0 [E][I][d/32] */
+  const uint8_t *qt_gate, *qt_gate_scale;        /* E4M3 [E][d][I], E8M0 [I/128][E*d][4] */
+  const uint8_t *qt_up, *qt_up_scale;            /* E4M3 [E][d][I], E8M0 [I/128][E*d][4] */
+  const uint8_t *qt_down, *qt_down_scale;        /* E4M3 [E][I][d], E8M0 [d/128][E*I][4] */
 } moe_weights;
 
 /* Gradients written by moe_layer_backward (host struct of caller-owned device
@@ -277,6 +279,11 @@ moe_status moe_trace_events(int which, void* const* events, int n);
  *   dst [rows][cols] E4M3, scale [rows][cols/32] E8M0.
  * axis = 1: one block per 32 consecutive rows of a column (rows % 32 == 0):
  *   dst [rows][cols] E4M3, scale [rows/32][cols] E8M0.
+ * axis = 2: the blocks of axis 0 (cols % 128 == 0) with the scales stored
+ *   slab-major for the grouped GEMMs: scale [cols/128][rows][4], byte
+ *   (c/128, r, (c/32) % 4) for the block of row r holding column c (the four
+ *   block scales of one row's 128-column slab form one dword, and a slab's
+ *   dwords are contiguous over the rows).
  * Per block: e = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for
  * an all-zero block); element = v / 2^e rounded to nearest-even E4M3,
  * saturating at +-448, sign kept; scale byte = e + 127. */

@@ -879,11 +879,11 @@ moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, i
 
 moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t cols, int axis, uint8_t* dst, uint8_t* scale,
                               void* stream) {
-  if (rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return MOE_EINVAL;
-  if ((axis == 0 && cols % 32) || (axis == 1 && rows % 32)) return MOE_EINVAL;
+  if (rows < 0 || cols < 0 || axis < 0 || axis > 2) return MOE_EINVAL;
+  if ((axis == 0 && cols % 32) || (axis == 1 && rows % 32) || (axis == 2 && cols % 128)) return MOE_EINVAL;
   if (rows == 0 || cols == 0) return MOE_OK;
   if (!ptr_ok(src_bf16) || !ptr_ok(dst) || !scale) return MOE_EINVAL;
-  if (axis == 0 && cols > INT_MAX) return MOE_EUNSUPPORTED;
+  if (axis != 1 && cols > INT_MAX) return MOE_EUNSUPPORTED;
   MOE_HIP(launch_quantize_mx(static_cast<const bf16_t*>(src_bf16), rows, cols, axis, dst, scale,
                              static_cast<hipStream_t>(stream)));
   return MOE_OK;

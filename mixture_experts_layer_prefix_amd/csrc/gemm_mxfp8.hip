@@ -121,7 +121,7 @@ struct MxArgs {
   const uint8_t* B1;
   const uint8_t* B0s;
   const uint8_t* B1s;
-  int64_t b_stride, bs_stride;  // bytes between experts in B and in its scales
+  int64_t b_stride;         // bytes between experts in B
   int64_t ldb;              // bytes per B row
   int N, K, ntiles;
   int k_half;               // DUALK: K of the first matrix
@@ -179,6 +179,7 @@ struct MxLoad {
   __amdgpu_buffer_rsrc_t ar, asr, br0, br1, bsr0, bsr1;
   uint32_t aoff[BM / (kThreads / 8)];
   uint32_t scoff, boff;
+  uint32_t sa_slab, sb_slab;  // bytes between the scale dwords of consecutive slabs (0: row-major A scales)
   int k_begin, brows, ldb;
 };
 
@@ -215,13 +216,17 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
   const bool gath = p.a_rows != nullptr;
   const int64_t tile_rows = min<int64_t>(BM, n_g - m0);
   const uint8_t* abase = uniform_ptr(gath ? p.A : Ab + (row_begin + m0) * lda);
-  // Weight-gradient scales are slab-major per group, [kp / 128][M][4]: a
+  // A scales: row-major [rows][K/32] for token rows (gathered or permuted
+  // by the caller), slab-major [K/128][M][4] for the operands the layer
+  // writes itself (h, dG|dU, the weight-gradient operands per group): a
   // row's dword of one slab at row * 4, slabs M * 4 bytes apart.
+  const bool a_slab = KGROUPED || (!gath && (MODE == GEMM_DOWN || MODE == GEMM_DUALK));
   const uint8_t* asbase =
-      uniform_ptr(gath ? p.As : KGROUPED ? Asb + m0 * 4 : Asb + (row_begin + m0) * ldas);
+      uniform_ptr(gath ? p.As : a_slab ? Asb + (row_begin + m0) * 4 : Asb + (row_begin + m0) * ldas);
   const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * lda));
   const uint32_t asbytes = __builtin_amdgcn_readfirstlane(
-      gath ? p.as_bytes : KGROUPED ? (uint32_t)(ldas * p.M - m0 * 4) : (uint32_t)(tile_rows * ldas));
+      gath ? p.as_bytes : a_slab ? (uint32_t)(ldas * p.M - (row_begin + m0) * 4) : (uint32_t)(tile_rows * ldas));
+  L.sa_slab = a_slab ? (uint32_t)(p.M * 4) : 0;
   L.ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
   L.asr = __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
 #pragma unroll
@@ -241,7 +246,7 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
     const int64_t lr0 = wave * 64 + lane;
     const int64_t lr = lr0 < tile_rows ? lr0 : 0;
     const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
-    scoff = (uint32_t)(src * (KGROUPED ? 4 : ldas));
+    scoff = (uint32_t)(src * (a_slab ? 4 : ldas));
   }
   const int bi = wave - 4;  // B-scale round of this wave
   const int span = PAIRED ? BN / 2 : BN;
@@ -250,13 +255,18 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
   L.brows = brows;
   if (b_sc) {
     const int r = PAIRED ? (bi & 1) * 64 + lane : bi * 64 + lane;
-    scoff = (uint32_t)(min(r, brows - 1) * (KGROUPED ? 4 : ldbs));
+    scoff = (uint32_t)(min(r, brows - 1) * 4);
   }
   L.scoff = scoff;
-  const uint8_t* bs0 = Bsb0 + (int64_t)g * p.bs_stride + first_row * (KGROUPED ? 4 : ldbs);
-  const uint8_t* bs1 = (PAIRED || DUAL) ? p.B1s + (int64_t)g * p.bs_stride + first_row * ldbs : bs0;
-  const uint32_t bsbytes = __builtin_amdgcn_readfirstlane(
-      KGROUPED ? (uint32_t)(ldbs * p.N - first_row * 4) : (uint32_t)(brows * ldbs));
+  // B scales are slab-major: [K/128][G*N][4] for the stacked weights (one
+  // matrix of G*N rows; DUALK: each of the two), [Kp/128][N][4] per group for
+  // the weight-gradient operands.
+  const int gs = KGROUPED ? 1 : p.G;
+  const int64_t brow0 = (int64_t)(KGROUPED ? 0 : g) * p.N + first_row;
+  const uint8_t* bs0 = Bsb0 + brow0 * 4;
+  const uint8_t* bs1 = (PAIRED || DUAL) ? p.B1s + brow0 * 4 : bs0;
+  const uint32_t bsbytes = __builtin_amdgcn_readfirstlane((uint32_t)(ldbs * gs * p.N - brow0 * 4));
+  L.sb_slab = (uint32_t)(gs * p.N * 4);
   L.bsr0 = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(PAIRED && bi >= 2 ? bs1 : bs0), (short)0,
                                             (int)bsbytes, 0x00020000);
   L.bsr1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(bs1), (short)0, (int)bsbytes, 0x00020000)
@@ -300,11 +310,10 @@ __device__ __forceinline__ void mx_issue(const MxArgs& p, const MxLoad<BM>& L, u
                                              (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, L.boff,
                                              (uint32_t)(r0 * ldb + kb), 0, 0);
   }
-  // Scale dwords: row-major operands at K / 32 in the row; the slab-major
-  // weight-gradient operands at slab * rows * 4.
-  constexpr bool KGROUPED = MODE == GEMM_WGRAD;
-  const uint32_t sa_off = KGROUPED ? (uint32_t)(ka >> 7) * (uint32_t)(p.M * 4) : (uint32_t)(ka / 32);
-  const uint32_t sb_off = KGROUPED ? (uint32_t)(kb >> 7) * (uint32_t)(p.N * 4) : (uint32_t)(kb / 32);
+  // Scale dwords: row-major operands at K / 32 in the row, slab-major ones
+  // at slab * (bytes per slab).
+  const uint32_t sa_off = L.sa_slab ? (uint32_t)(ka >> 7) * L.sa_slab : (uint32_t)(ka / 32);
+  const uint32_t sb_off = (uint32_t)(kb >> 7) * L.sb_slab;
   if (wave < BM / 64)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, L.scoff,
                                              sa_off, 0, 0);
@@ -603,9 +612,10 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         *reinterpret_cast<u32x2*>(qrow + N) = u32x2{e4m3x4_rne_sat(du[0] * iu, du[1] * iu, du[2] * iu, du[3] * iu),
                                                     e4m3x4_rne_sat(du[4] * iu, du[5] * iu, du[6] * iu, du[7] * iu)};
         if (qt == 0) {
-          uint8_t* srow = p.dgus + (rowoff >> 5);
-          srow[col / 32] = (uint8_t)(eg + 127);
-          srow[(N + col) / 32] = (uint8_t)(eu + 127);
+          // dG | dU scales slab-major over the 2N columns, [2N/128][rows][4]
+          // (the gate/up input-gradient GEMM's A layout).
+          p.dgus[(((int64_t)(col >> 7) * p.M + grow) << 2) + ((col >> 5) & 3)] = (uint8_t)(eg + 127);
+          p.dgus[(((int64_t)((N + col) >> 7) * p.M + grow) << 2) + (((N + col) >> 5) & 3)] = (uint8_t)(eu + 127);
           if (p.dg_part) p.dg_part[(rowoff >> 6) + col / 32] = part;
         }
       }
@@ -682,7 +692,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         if (row_ok && col < N) {
           uint8_t* C = static_cast<uint8_t*>(p.C);
           C[grow * ldc + col] = (uint8_t)code;
-          if ((lane & 31) == 0) p.Cs[grow * (ldc / 32) + col / 32] = (uint8_t)sc;
+          // h scales slab-major [I/128][rows][4] (the down GEMM's A layout)
+          if ((lane & 31) == 0) p.Cs[(((int64_t)(col >> 7) * p.M + grow) << 2) + ((col >> 5) & 3)] = (uint8_t)sc;
           if (p.gu_out) {  // G | U kept for the backward
             p.gu_out[grow * 2 * N + col] = f32_to_bf16(acc[i][0][v]);
             p.gu_out[grow * 2 * N + N + col] = f32_to_bf16(acc[i][1][v]);
@@ -876,7 +887,6 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.B0s = q.B0_scale;
   a.B1s = q.B1_scale;
   a.b_stride = q.b_group_stride;
-  a.bs_stride = q.b_group_stride / 32;
   a.N = q.N;
   a.K = q.K;
   constexpr bool paired = MODE == GEMM_GATEUP || MODE == GEMM_GU;

@@ -124,10 +124,14 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
   }
 }
 
+// Row blocks of 32 columns, rows optionally gathered.  Scales row-major
+// [R][d/32], or with slab_major slab-major [d/128][R][4] (the four blocks of
+// a 128-column slab of one row form one dword; a slab's dwords are
+// contiguous over the rows).
 __global__ void __launch_bounds__(256) gather_quant_kernel(const bf16_t* __restrict__ x,
                                                            const int32_t* __restrict__ row_token,
                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
-                                                           int64_t R, int d) {
+                                                           int64_t R, int d, bool slab_major) {
   const int bpr = d / 32;
   const int64_t nblk = R * bpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -150,7 +154,7 @@ __global__ void __launch_bounds__(256) gather_quant_kernel(const bf16_t* __restr
     u32x4* out = reinterpret_cast<u32x4*>(q + r * d + c * 32);
     out[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
     out[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
-    scale[r * bpr + c] = (uint8_t)sc;
+    scale[slab_major ? ((c >> 2) * R + r) * 4 + (c & 3) : r * bpr + c] = (uint8_t)sc;
   }
 }
 
@@ -205,15 +209,16 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_p
 hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uint8_t* q, uint8_t* scale, int64_t R,
                                   int d, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  gather_quant_kernel<<<stream_grid(R * (d / 32)), 256, 0, s>>>(x, row_token, q, scale, R, d);
+  gather_quant_kernel<<<stream_grid(R * (d / 32)), 256, 0, s>>>(x, row_token, q, scale, R, d, false);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_mx(const bf16_t* src, int64_t rows, int64_t cols, int axis, uint8_t* dst, uint8_t* scale,
                               hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  if (axis == 0)
-    gather_quant_kernel<<<stream_grid(rows * (cols / 32)), 256, 0, s>>>(src, nullptr, dst, scale, rows, (int)cols);
+  if (axis == 0 || axis == 2)
+    gather_quant_kernel<<<stream_grid(rows * (cols / 32)), 256, 0, s>>>(src, nullptr, dst, scale, rows, (int)cols,
+                                                                        axis == 2);
   else
     quant_cols_kernel<<<stream_grid(rows / 32 * cols), 256, 0, s>>>(src, rows, cols, dst, scale);
   return hipGetLastError();

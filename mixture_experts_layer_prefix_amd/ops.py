@@ -222,6 +222,8 @@ def quantize_mxfp8(src, axis):
     dst = torch.empty(rows, cols, dtype=torch.uint8, device=src.device)
     if axis == 0:
         scale = torch.empty(rows, cols // 32, dtype=torch.uint8, device=src.device)
+    elif axis == 2:  # slab-major [cols/128][rows][4] (the grouped GEMMs' weight layout)
+        scale = torch.empty(cols // 128, rows, 4, dtype=torch.uint8, device=src.device)
     else:
         scale = torch.empty(rows // 32, cols, dtype=torch.uint8, device=src.device)
     call("moe_quantize_mxfp8", _p(src), rows, cols, axis, _p(dst), _p(scale), _stream())
@@ -232,9 +234,9 @@ def prepare_mxfp8(weights: Weights, dims: Dims) -> Weights:
     """Weights with the routed experts pre-quantized for MOE_MXFP8 (blocks
     along each GEMM's K: d for gate/up, I for down)."""
     E, d, I = dims.E, dims.d, dims.I
-    qg, sg = quantize_mxfp8(weights.w_gate.reshape(E * I, d), 0)
-    qu, su = quantize_mxfp8(weights.w_up.reshape(E * I, d), 0)
-    qd, sd = quantize_mxfp8(weights.w_down.reshape(E * d, I), 0)
+    qg, sg = quantize_mxfp8(weights.w_gate.reshape(E * I, d), 2)
+    qu, su = quantize_mxfp8(weights.w_up.reshape(E * I, d), 2)
+    qd, sd = quantize_mxfp8(weights.w_down.reshape(E * d, I), 2)
     return Weights(w_router=weights.w_router, w_gate=weights.w_gate, w_up=weights.w_up, w_down=weights.w_down,
                    ws_gate=weights.ws_gate, ws_up=weights.ws_up, ws_down=weights.ws_down,
                    q_gate=qg, q_gate_scale=sg, q_up=qu, q_up_scale=su, q_down=qd, q_down_scale=sd)
@@ -261,7 +263,7 @@ def prepare_backward(weights: Weights, mxfp8=False) -> Weights:
         q = {}
         for n in ("gate", "up", "down"):
             wt = getattr(out, "wt_" + n)
-            codes, scale = quantize_mxfp8(wt.reshape(-1, wt.shape[-1]), 0)
+            codes, scale = quantize_mxfp8(wt.reshape(-1, wt.shape[-1]), 2)
             q["qt_" + n] = codes.reshape(wt.shape)
             q["qt_%s_scale" % n] = scale
         out = dataclasses.replace(out, **q)

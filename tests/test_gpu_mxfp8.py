@@ -38,6 +38,22 @@ def test_quantizer_bit_exact(axis):
     assert np.array_equal(to_np(q), rq) and np.array_equal(to_np(s), rs)
 
 
+def test_quantizer_slab_major_bit_exact():
+    """axis 2: the blocks of axis 0 with the scales slab-major [cols/128][rows][4]
+    (the grouped GEMMs' weight layout): the same codes, and the oracle's
+    [rows][cols/32] scales regrouped by 128-column slab."""
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.Dims("q2", 64, 256, 8, 2, 128, 0, 0, "bf16", 0.0)
+    p = gen.Problem(D)
+    w = p.device("w_gate").reshape(-1, D.d)  # [E*I][d] = [1024][256]
+    q, s = M.quantize_mxfp8(w, 2)
+    rq, rs = O.mx_quantize(p.host("w_gate").reshape(-1, D.d), axis=1)
+    rows = rq.shape[0]
+    assert tuple(s.shape) == (D.d // 128, rows, 4)
+    assert np.array_equal(to_np(q), rq)
+    assert np.array_equal(to_np(s), rs.reshape(rows, D.d // 128, 4).transpose(1, 0, 2))
+
+
 def mx_round(v, axis=-1):
     """Values after an MX quantize/dequantize round trip (oracle quantizer)."""
     q, sc = O.mx_quantize(v, axis=axis)
