@@ -93,6 +93,7 @@ struct FwdWs {
   void* sched;
   void* x_perm;
   uint8_t* x_perm_scale;
+  uint8_t* xs_slab;  // MXFP8: the token scales of every routed row, slab-major (the gate/up GEMM's A scales)
   FfnWs ffn;
   void* o_perm;
   void* y_shared;
@@ -114,9 +115,11 @@ FwdWs carve_forward(Carver& c, const moe_dims* D, moe_prec prec, const moe_routi
   if (prec == MOE_MXFP8) {  // quantized tokens [T][d] (+ scales); rows are gathered by the GEMM
     w.x_perm = c.take((size_t)T * D->d);
     w.x_perm_scale = static_cast<uint8_t*>(c.take((size_t)T * (D->d / 32)));
+    w.xs_slab = static_cast<uint8_t*>(c.take((size_t)R * (D->d / 32)));
   } else {
     w.x_perm = c.take((size_t)R * D->d * act_bytes(prec));
     w.x_perm_scale = nullptr;
+    w.xs_slab = nullptr;
   }
   w.ffn = carve_ffn(c, D, prec);
   w.o_perm = c.take((size_t)R * D->d * act_bytes(prec));
@@ -142,6 +145,7 @@ struct BwdWs {
   // MXFP8: quantized tokens and output gradients (along d), dG|dU along I, and
   // the transposed operands quantized along the routed-row axis.
   uint8_t *xq, *xqs, *dyq, *dyqs, *dguq, *dguqs;
+  uint8_t *xs_slab, *dys_slab;  // token scales of every routed row, slab-major (gathered GEMM A operands)
   uint8_t *xTq, *xTqs, *dyTq, *dyTqs, *ghTq, *ghTqs, *dguTq, *dguTqs;
   void *gus, *dgus, *hs, *dxs, *xTs, *dyTs, *hsT, *dgusT;
 };
@@ -171,6 +175,8 @@ BwdWs carve_backward(Carver& c, const moe_dims* D, moe_prec prec) {
     w.xqs = u8((size_t)T * d / 32);
     w.dyq = u8((size_t)T * d);
     w.dyqs = u8((size_t)T * d / 32);
+    w.xs_slab = u8((size_t)R * d / 32);
+    w.dys_slab = u8((size_t)R * d / 32);
     w.dguq = u8((size_t)R * 2 * I);
     w.dguqs = u8((size_t)R * 2 * I / 32);
     w.xTq = u8((size_t)d * w.Rp);
@@ -299,12 +305,13 @@ moe_status run_down(moe_prec prec, const int32_t* row_off, int64_t M, int G, con
 // MXFP8 grouped gate/up (h quantized along I in the epilogue) and down.
 moe_status run_gateup_mx(const moe_dims* D, const uint8_t* A, const uint8_t* A_scale, const int32_t* a_rows,
                          const int32_t* offsets, const moe_weights* w, uint8_t* h, uint8_t* h_scale, int32_t* prefix,
-                         hipStream_t s, void* gu_out = nullptr) {
+                         hipStream_t s, void* gu_out = nullptr, const uint8_t* A_scale_slab = nullptr) {
   GemmProblem q = {};
   q.mode = GEMM_GATEUP;
   q.A = A;
   q.A_scale = A_scale;
   q.a_rows = a_rows;
+  q.A_scale_slab = A_scale_slab;
   q.a_bytes = a_rows ? D->T * (int64_t)D->d : 0;
   q.lda = D->d;
   q.row_off = offsets;
@@ -358,10 +365,11 @@ moe_status run_ffn_grouped(moe_prec prec, const void* A, const int32_t* a_rows, 
 
 moe_status run_expert_ffn(const moe_dims* D, moe_prec prec, const void* A, const uint8_t* A_scale,
                           const int32_t* a_rows, const int32_t* offsets, const moe_weights* w, void* o_perm,
-                          const FfnWs& ws, hipStream_t s, bool traced = false, void* gu_out = nullptr) {
+                          const FfnWs& ws, hipStream_t s, bool traced = false, void* gu_out = nullptr,
+                          const uint8_t* A_scale_slab = nullptr) {
   if (prec == MOE_MXFP8) {
     MOE_TRY(run_gateup_mx(D, static_cast<const uint8_t*>(A), A_scale, a_rows, offsets, w,
-                          static_cast<uint8_t*>(ws.h), ws.h_scale, ws.prefix, s, gu_out));
+                          static_cast<uint8_t*>(ws.h), ws.h_scale, ws.prefix, s, gu_out, A_scale_slab));
     if (traced) trace(0, 4, s);
     return run_down_mx(D, static_cast<const uint8_t*>(ws.h), ws.h_scale, offsets, w, o_perm, ws.prefix, s);
   }
@@ -493,6 +501,8 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   if (mx) {  // tokens and output gradients quantized once along d (row-wise: commutes with the gather)
     MOE_HIP(launch_quantize_mx(x, T, d, 0, b.xq, b.xqs, s));
     MOE_HIP(launch_quantize_mx(dy, T, d, 0, b.dyq, b.dyqs, s));
+    MOE_HIP(launch_gather_scales_slab(b.dyqs, rt->row_token, R, d, b.dys_slab, s));
+    if (!rt->gu) MOE_HIP(launch_gather_scales_slab(b.xqs, rt->row_token, R, d, b.xs_slab, s));
   }
   trace(1, 1, s);
 
@@ -507,6 +517,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   q.a_bytes = T * (int64_t)d * (mx ? 1 : 2);
   if (mx) {
     q.A_scale = b.xqs;
+    q.A_scale_slab = b.xs_slab;
     q.B0_scale = w->q_gate_scale;
     q.B1_scale = w->q_up_scale;
   }
@@ -526,6 +537,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   q.dg_part = b.dg_part;
   if (mx) {
     q.A_scale = b.dyqs;
+    q.A_scale_slab = b.dys_slab;
     q.B0_scale = w->qt_down_scale;
     q.dgu_q = b.dguq;
     q.dgu_scale = b.dguqs;
@@ -795,9 +807,11 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
   const bool fused_gather = prec != MOE_F32;
   MOE_TRY(run_permute(dims, prec, f.topk_idx, x, f.counts, f.offsets, f.row_token, f.token_row,
                       fused_gather ? nullptr : f.x_perm, f.x_perm_scale, f.sched, s));
-  if (prec == MOE_MXFP8)
+  if (prec == MOE_MXFP8) {
     MOE_HIP(launch_quantize_mx(static_cast<const bf16_t*>(x), dims->T, dims->d, 0, static_cast<uint8_t*>(f.x_perm),
                                f.x_perm_scale, s));
+    MOE_HIP(launch_gather_scales_slab(f.x_perm_scale, f.row_token, dims->T * dims->k, dims->d, f.xs_slab, s));
+  }
   trace(0, 2, s);
   // G | U kept for a later backward when the caller provides the buffers
   // (bf16 and MXFP8: their backward consumes them).
@@ -807,7 +821,7 @@ moe_status moe_layer_forward(const moe_dims* dims, moe_prec prec, const void* x,
   trace(0, 3, s);
   if (prec == MOE_MXFP8)
     MOE_TRY(run_expert_ffn(dims, prec, f.x_perm, f.x_perm_scale, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true,
-                           keep_gu));
+                           keep_gu, f.xs_slab));
   else if (fused_gather)
     MOE_TRY(run_expert_ffn(dims, prec, x, nullptr, f.row_token, f.offsets, w, f.o_perm, f.ffn, s, true, keep_gu));
   else

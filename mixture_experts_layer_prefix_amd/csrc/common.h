@@ -181,6 +181,11 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_p
 // Gather + MX quantization along d.
 hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uint8_t* q, uint8_t* scale,
                                   int64_t R, int d, hipStream_t s);
+// Slab-major [K/128][R][4] scales of the rows row_token[0..R) of a
+// row-major [rows][K/32] scale array (the grouped GEMMs' A-scale layout for
+// gathered token rows).
+hipError_t launch_gather_scales_slab(const uint8_t* scale_rows, const int32_t* row_token, int64_t R, int K,
+                                     uint8_t* dst, hipStream_t s);
 hipError_t launch_quantize_mx(const bf16_t* src, int64_t rows, int64_t cols, int axis, uint8_t* dst,
                               uint8_t* scale, hipStream_t s);
 
@@ -240,6 +245,8 @@ struct GemmProblem {
   const void* A;            // [rows][K] (bf16 / fp32 / e4m3)
   const uint8_t* A_scale;   // MX: [rows][K/32]
   const int32_t* a_rows;    // optional row gather: row r reads A row a_rows[r]
+  const uint8_t* A_scale_slab;  // MX, optional: the A scales of the (gathered) rows in row order,
+                                // slab-major [K/128][M][4]; A_scale is then unused
   int64_t a_bytes;          // size of A in bytes when a_rows is set
   int64_t lda;
   const int32_t* row_off;   // [G+1] or nullptr

@@ -111,7 +111,8 @@ __global__ void __launch_bounds__(1024) mx_tile_prefix_kernel(const int32_t* __r
 struct MxArgs {
   const uint8_t* A;
   const uint8_t* As;        // A scales [rows][lda/32]
-  const int32_t* a_rows;    // optional gather of A rows (and their scales)
+  const int32_t* a_rows;
+  const uint8_t* As_slab;   // optional slab-major A scales in row order (gathered rows)    // optional gather of A rows (and their scales)
   uint32_t a_bytes, as_bytes;  // sizes of A and its scales when gathered
   int64_t lda;              // bytes per A row
   const int32_t* row_off;
@@ -220,12 +221,16 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
   // by the caller), slab-major [K/128][M][4] for the operands the layer
   // writes itself (h, dG|dU, the weight-gradient operands per group): a
   // row's dword of one slab at row * 4, slabs M * 4 bytes apart.
-  const bool a_slab = KGROUPED || (!gath && (MODE == GEMM_DOWN || MODE == GEMM_DUALK));
+  // Gathered token rows may bring their scales already slab-major in row
+  // order (As_slab); the data rows are still gathered.
+  const bool a_slab = KGROUPED || p.As_slab != nullptr || (!gath && (MODE == GEMM_DOWN || MODE == GEMM_DUALK));
+  const bool sgath = gath && p.As_slab == nullptr;  // per-row gathered scale loads
+  const uint8_t* Asl = p.As_slab ? p.As_slab : Asb;
   const uint8_t* asbase =
-      uniform_ptr(gath ? p.As : a_slab ? Asb + (row_begin + m0) * 4 : Asb + (row_begin + m0) * ldas);
+      uniform_ptr(sgath ? p.As : a_slab ? Asl + (row_begin + m0) * 4 : Asb + (row_begin + m0) * ldas);
   const uint32_t abytes = __builtin_amdgcn_readfirstlane(gath ? p.a_bytes : (uint32_t)(tile_rows * lda));
   const uint32_t asbytes = __builtin_amdgcn_readfirstlane(
-      gath ? p.as_bytes : a_slab ? (uint32_t)(ldas * p.M - (row_begin + m0) * 4) : (uint32_t)(tile_rows * ldas));
+      sgath ? p.as_bytes : a_slab ? (uint32_t)(ldas * p.M - (row_begin + m0) * 4) : (uint32_t)(tile_rows * ldas));
   L.sa_slab = a_slab ? (uint32_t)(p.M * 4) : 0;
   L.ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)abytes, 0x00020000);
   L.asr = __builtin_amdgcn_make_buffer_rsrc((void*)asbase, (short)0, (int)asbytes, 0x00020000);
@@ -245,7 +250,7 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, MxLoad<BM>& L, int g, 
   if (a_sc) {
     const int64_t lr0 = wave * 64 + lane;
     const int64_t lr = lr0 < tile_rows ? lr0 : 0;
-    const int64_t src = gath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
+    const int64_t src = sgath ? (int64_t)p.a_rows[row_begin + m0 + lr] : lr;
     scoff = (uint32_t)(src * (a_slab ? 4 : ldas));
   }
   const int bi = wave - 4;  // B-scale round of this wave
@@ -876,6 +881,7 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.A = static_cast<const uint8_t*>(q.A);
   a.As = q.A_scale;
   a.a_rows = q.a_rows;
+  a.As_slab = q.A_scale_slab;
   a.a_bytes = (uint32_t)q.a_bytes;
   a.as_bytes = (uint32_t)(q.a_bytes / 32);
   a.lda = q.lda;

@@ -158,6 +158,20 @@ __global__ void __launch_bounds__(256) gather_quant_kernel(const bf16_t* __restr
   }
 }
 
+// Slab-major scales of gathered rows: dst[s][r] = the dword of slab s (four
+// 32-element block scales) of source row row_token[r], for row-major source
+// scales [rows][K/32] (K % 128 == 0).  Thread per (r, s), rows fastest.
+__global__ void __launch_bounds__(256) gather_scales_slab_kernel(const uint32_t* __restrict__ src,
+                                                                 const int32_t* __restrict__ row_token, int64_t R,
+                                                                 int slabs, uint32_t* __restrict__ dst) {
+  const int64_t n = R * slabs;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t sl = i / R, r = i - sl * R;
+    dst[i] = src[(int64_t)row_token[r] * slabs + sl];
+  }
+}
+
 // Blocks of 32 consecutive rows of one column: thread per (row block, column).
 __global__ void __launch_bounds__(256) quant_cols_kernel(const bf16_t* __restrict__ src, int64_t rows, int64_t cols,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
@@ -210,6 +224,15 @@ hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uin
                                   int d, hipStream_t s) {
   if (R == 0) return hipSuccess;
   gather_quant_kernel<<<stream_grid(R * (d / 32)), 256, 0, s>>>(x, row_token, q, scale, R, d, false);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_scales_slab(const uint8_t* scale_rows, const int32_t* row_token, int64_t R, int K,
+                                     uint8_t* dst, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  if (K % 128) return hipErrorInvalidValue;
+  gather_scales_slab_kernel<<<stream_grid(R * (K / 128)), 256, 0, s>>>(
+      reinterpret_cast<const uint32_t*>(scale_rows), row_token, R, K / 128, reinterpret_cast<uint32_t*>(dst));
   return hipGetLastError();
 }
 
