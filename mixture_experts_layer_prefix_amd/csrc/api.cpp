@@ -166,7 +166,7 @@ BwdWs carve_backward(Carver& c, const moe_dims* D, moe_prec prec) {
   w.dl_row = static_cast<float*>(c.take((size_t)R * 4));
   w.gu = c.take((size_t)R * 2 * I * 2);
   w.dgu = mx ? nullptr : c.take((size_t)R * 2 * I * 2);  // MXFP8: dG, dU stay in the epilogue
-  w.gh = c.take((size_t)R * I * 2);
+  w.gh = mx ? nullptr : c.take((size_t)R * I * 2);  // MXFP8: w h stays in the epilogue
   w.da = c.take((size_t)R * d * 2);
   w.dg_part = static_cast<float*>(c.take((size_t)R * (I / 32) * 4));
   w.router_partial = static_cast<float*>(c.take((size_t)(w.Rp / 64) * d * 4));
@@ -541,8 +541,10 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     q.B0_scale = w->qt_down_scale;
     q.dgu_q = b.dguq;
     q.dgu_scale = b.dguqs;
-    q.dgu_t = b.dguTq;  // dG^T | dU^T for the weight gradients, quantized in the epilogue
+    q.dgu_t = b.dguTq;  // dG^T | dU^T and (w h)^T for the weight gradients, quantized in the epilogue
     q.dgu_t_scale = b.dguTqs;
+    q.gh_t = b.ghTq;
+    q.gh_t_scale = b.ghTqs;
     q.pad_off = b.pad_off;
     q.t_ld = b.Rp;
   }
@@ -590,11 +592,10 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   const int32_t* off = rt->expert_offsets;
   if (mx) {
     const int64_t Rp = b.Rp, Rs = b.Rp / 32;
-    // Expert-blocked [cols][Kp_e] operands; dG^T and dU^T came from the
-    // down-dgrad epilogue.
+    // Expert-blocked [cols][Kp_e] operands; dG^T, dU^T and (w h)^T came from
+    // the down-dgrad epilogue.
     MOE_HIP(launch_transpose_quant(x, d, d, rt->row_token, off, b.pad_off, E, Rp, b.xTq, b.xTqs, s));
     MOE_HIP(launch_transpose_quant(dy, d, d, rt->row_token, off, b.pad_off, E, Rp, b.dyTq, b.dyTqs, s));
-    MOE_HIP(launch_transpose_quant(gh, I, I, nullptr, off, b.pad_off, E, Rp, b.ghTq, b.ghTqs, s));
     trace(1, 8, s);
     MOE_TRY(run_wgrad_mx(b.dyTq, b.dyTqs, d, b.ghTq, b.ghTqs, I, Rp, b.pad_off, E, g->dw_down, s));
     trace(1, 9, s);

@@ -277,6 +277,8 @@ struct GemmProblem {
   uint8_t* dgu_t;           // MX: dG^T then dU^T quantized along the routed rows, expert-blocked as
                             // the weight-gradient operands ([N][Kp_g] at pad_off[g] * N; dU^T N * t_ld later)
   uint8_t* dgu_t_scale;     // MX: their scales, slab-major ([Kp_g/128][N][4] at pad_off[g] * N / 32)
+  uint8_t* gh_t;            // MX: (w h)^T in the same layout ([N][Kp_g] at pad_off[g] * N)
+  uint8_t* gh_t_scale;      // MX: its scales, slab-major
   const int32_t* pad_off;   // MX: [G+1] padded group row offsets (multiples of 128)
   int64_t t_ld;             // MX: total padded rows
   // K-grouped (weight gradient) mode

@@ -140,9 +140,10 @@ struct MxArgs {
   uint8_t* dgus;            // [rows][2N/32] their scales
   uint8_t* dgu_t;           // dG^T then dU^T, E4M3 along the routed rows, expert-blocked (see the epilogue)
   uint8_t* dgu_ts;          // their scales
+  uint8_t* gh_t;            // (w h)^T, the same layout (N rows)
+  uint8_t* gh_ts;
   const int32_t* pad_off;   // [G+1] padded row offsets of the groups (multiples of 128)
   int64_t t_ld;             // padded rows of all groups: dU^T starts N * t_ld bytes after dG^T
-  bf16_t* h_out;            // [rows][N] w h
   float* dg_part;           // [rows][N/32]
   // K-grouped weight-gradient mode
   const int32_t* k_off;
@@ -496,10 +497,11 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     // 32-column block.  dG and dU leave in E4M3 twice: along the columns (the
     // gate/up input-gradient GEMM's A operand) and along the routed rows in
     // the expert-blocked transposed layout of the weight-gradient operands
-    // (group g: [N][Kp_g] codes at pad_off[g] * N, scales at a 32nd of that).
+    // (group g: [N][Kp_g] codes at pad_off[g] * N, scales slab-major); w h
+    // leaves along the routed rows only (the down weight gradient's operand).
     //
     // The accumulators pass through LDS (the slab ring is idle once the last
-    // slab is read), per wave, 32-row blocks two at a time: element (r, c)
+    // slab is read), per wave, one 32-row block at a time: element (r, c)
     // of a wave's [PR][64] fp32 region sits at r * 64 + 4 * ((c / 4) ^
     // key(r)) + c % 4; key(r) flips chunk bit 0 with r bit 0 and chunk bit 3
     // with r bits 1 xor 2, which keeps the accumulator-layout writes (rows r,
@@ -508,21 +510,27 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     //   Row phase: four lanes share one row's 32-column block, eight columns
     // each (block maxima and sums in two DPP steps, 8- and 16-byte global
     // accesses); each lane writes its eight dG and eight dU, rounded to bf16,
-    // back over its eight dH' values (the two 16-byte chunks).
+    // back over its eight dH' values (the two 16-byte chunks), and its eight
+    // w h in bf16 to a second per-wave [32][64] region (16-byte chunk c of row
+    // r at c ^ 4 (r / 2 % 2): rows r, r + 2 share banks).
     //   Column phase: lane (q, pair) takes columns 2 pair, 2 pair + 1 of dG
-    // (q = 0) or dU (q = 1) down each 32-row block and writes both columns'
-    // 32 codes.  Rows past the group's end quantize as zeros; the padding
-    // rows past the group's last tile are zero-filled by that tile.
-    constexpr int PI = FM >= 2 ? 2 : 1;  // 32-row blocks per pass
+    // (q = 0) or dU (q = 1) down the 32-row block and writes both columns'
+    // 32 codes; lanes 0-31 then do the same for w h.  Rows past the group's
+    // end quantize as zeros; the padding rows past the group's last tile are
+    // zero-filled by that tile.
+    constexpr int PI = 1;                // 32-row blocks per pass
     constexpr int PR = PI * 32;          // rows per pass
     constexpr int ITEMS = PR * FN * 4 / 64;  // (row, block, quarter) items per lane per pass
-    static_assert(8 * PR * 64 * 4 <= (int)kSmemBytes, "staging fits the slab ring");
+    constexpr int WREG = PR * 64 * 4 + PR * 64 * 2;  // bytes per wave: fp32 region, then the bf16 w h region
+    static_assert(8 * WREG <= (int)kSmemBytes, "staging fits the slab ring");
     // Lane-derived epilogue values are computed here, not hoisted above the
     // K loop where they would hold registers the loop needs.
     int el = lane;
     asm volatile("" : "+v"(el));
-    float* stage = reinterpret_cast<float*>(smem) + wave * (PR * 64);
+    float* stage = reinterpret_cast<float*>(smem + wave * WREG);
     uint32_t* stage_w = reinterpret_cast<uint32_t*>(stage);
+    uint32_t* stage_h = reinterpret_cast<uint32_t*>(smem + wave * WREG + PR * 64 * 4);  // [PR][32] dwords
+    auto hkey = [](int r) { return ((r >> 1) & 1) << 2; };
     auto skey = [](int r) { return (r & 1) | ((((r >> 2) ^ (r >> 1)) & 1) << 3); };
     const int qt = el & 3;  // row phase: quarter of the block, columns 8 qt .. 8 qt + 7
     const int cq = el >> 5, cp = el & 31;  // column phase: dG / dU, column pair
@@ -537,6 +545,10 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     uint8_t* tq = p.dgu_t + toff;
     uint8_t* ts = p.dgu_ts + ((cq ? (int64_t)N * p.t_ld : 0) + (int64_t)p.pad_off[g] * N) / 32 + (wcol + 2 * cp) * 4;
     auto ts_at = [&](int rr) { return ts + (int64_t)(rr >> 7) * N * 4 + ((rr >> 5) & 3); };
+    // The same for w h (lanes 0-31).
+    uint8_t* hq = p.gh_t + (int64_t)p.pad_off[g] * N + (int64_t)(wcol + 2 * cp) * kp;
+    uint8_t* hs = p.gh_ts + (int64_t)p.pad_off[g] * N / 32 + (wcol + 2 * cp) * 4;
+    auto hs_at = [&](int rr) { return hs + (int64_t)(rr >> 7) * N * 4 + ((rr >> 5) & 3); };
 #pragma clang loop unroll(full)
     for (int i0 = 0; i0 < FM; i0 += PI) {
       if (i0) __syncthreads();  // the previous pass's column reads are done
@@ -594,11 +606,14 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
           const uint32_t wh = f32_to_bf16(wr * h);
           if (e & 1) hw[e >> 1] |= wh << 16; else hw[e >> 1] = wh;
         }
-        // dG, dU in bf16 over this lane's dH' (zeros for rows past the end).
+        // dG, dU in bf16 over this lane's dH', w h to its region (zeros for
+        // rows past the end).
         *reinterpret_cast<u32x4*>(s0) = u32x4{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
                                               pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
         *reinterpret_cast<u32x4*>(s1) = u32x4{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
                                               pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
+        *reinterpret_cast<u32x4*>(stage_h + r * 32 + (((blk * 4 + qt) ^ hkey(r)) << 2)) =
+            u32x4{hw[0], hw[1], hw[2], hw[3]};
         // Reductions over the quad (the row's 32 columns).
         mg = max(mg, dpp_u32<0xB1>(mg));
         mg = max(mg, dpp_u32<0x4E>(mg));
@@ -609,7 +624,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         if (!ok) continue;
         const int eg = max((int)(mg >> 23) - 135, -127), eu = max((int)(mu >> 23) - 135, -127);
         const float ig = mx_inv_scale(eg), iu = mx_inv_scale(eu);
-        *reinterpret_cast<u32x4*>(p.h_out + (rowoff >> 1) + col) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+
         uint8_t* qrow = p.dguq + rowoff + col;
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         *reinterpret_cast<u32x2*>(qrow) = u32x2{e4m3x4_rne_sat(dg[0] * ig, dg[1] * ig, dg[2] * ig, dg[3] * ig),
@@ -661,6 +676,37 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         uint8_t* s0 = ts_at(rr0);
         s0[0] = (uint8_t)(e0 + 127);
         s0[4] = (uint8_t)(e1 + 127);
+        if (el < 32) {  // w h: columns 2 cp, 2 cp + 1
+          uint32_t hm0 = 0, hm1 = 0;
+#pragma unroll
+          for (int q = 0; q < 32; ++q) {
+            const int r = 32 * b + q;
+            x[q] = stage_h[r * 32 + (((cp >> 2) ^ hkey(r)) << 2) + (cp & 3)];
+            hm0 = max(hm0, (x[q] << 16) & 0x7FFFFFFFu);
+            hm1 = max(hm1, x[q] & 0x7FFF0000u);
+          }
+          const int f0 = max((int)(hm0 >> 23) - 135, -127), f1 = max((int)(hm1 >> 23) - 135, -127);
+          const float j0s = mx_inv_scale(f0), j1s = mx_inv_scale(f1);
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const int q = 4 * w;
+            c0[w >> 2][w & 3] =
+                e4m3x4_rne_sat(__uint_as_float(x[q] << 16) * j0s, __uint_as_float(x[q + 1] << 16) * j0s,
+                               __uint_as_float(x[q + 2] << 16) * j0s, __uint_as_float(x[q + 3] << 16) * j0s);
+            c1[w >> 2][w & 3] = e4m3x4_rne_sat(__uint_as_float(x[q] & 0xFFFF0000u) * j1s,
+                                               __uint_as_float(x[q + 1] & 0xFFFF0000u) * j1s,
+                                               __uint_as_float(x[q + 2] & 0xFFFF0000u) * j1s,
+                                               __uint_as_float(x[q + 3] & 0xFFFF0000u) * j1s);
+          }
+          uint8_t* h0 = hq + rr0;
+          *reinterpret_cast<u32x4*>(h0) = c0[0];
+          *reinterpret_cast<u32x4*>(h0 + 16) = c0[1];
+          *reinterpret_cast<u32x4*>(h0 + kp) = c1[0];
+          *reinterpret_cast<u32x4*>(h0 + kp + 16) = c1[1];
+          uint8_t* hs0 = hs_at(rr0);
+          hs0[0] = (uint8_t)(f0 + 127);
+          hs0[4] = (uint8_t)(f1 + 127);
+        }
       }
     }
     // Padding rows [m0 + BM, Kp_g) after the group's last tile (a single
@@ -676,6 +722,16 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         uint8_t* s0 = ts_at(rr);
         s0[0] = 0;
         s0[4] = 0;
+        if (el < 32) {
+          uint8_t* h0 = hq + rr;
+          *reinterpret_cast<u32x4*>(h0) = u32x4{0, 0, 0, 0};
+          *reinterpret_cast<u32x4*>(h0 + 16) = u32x4{0, 0, 0, 0};
+          *reinterpret_cast<u32x4*>(h0 + kp) = u32x4{0, 0, 0, 0};
+          *reinterpret_cast<u32x4*>(h0 + kp + 16) = u32x4{0, 0, 0, 0};
+          uint8_t* hs0 = hs_at(rr);
+          hs0[0] = 0;
+          hs0[4] = 0;
+        }
       }
     }
     return;
@@ -909,9 +965,10 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.dgus = q.dgu_scale;
   a.dgu_t = q.dgu_t;
   a.dgu_ts = q.dgu_t_scale;
+  a.gh_t = q.gh_t;
+  a.gh_ts = q.gh_t_scale;
   a.pad_off = q.pad_off;
   a.t_ld = q.t_ld;
-  a.h_out = static_cast<bf16_t*>(q.h_out);
   a.dg_part = q.dg_part;
   a.k_off = q.k_off;
   a.c_group_stride = q.c_group_stride;
@@ -947,7 +1004,8 @@ hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
     case GEMM_DOWN: return run_mx<GEMM_DOWN>(q, s);
     case GEMM_GU: return run_mx<GEMM_GU>(q, s);
     case GEMM_SWIGLU_BWD:
-      if (!q.gu || !q.dgu_q || !q.dgu_scale || !q.h_out || !q.dgu_t || !q.dgu_t_scale || !q.pad_off || q.t_ld % 128)
+      if (!q.gu || !q.dgu_q || !q.dgu_scale || !q.dgu_t || !q.dgu_t_scale || !q.gh_t || !q.gh_t_scale || !q.pad_off ||
+          q.t_ld % 128)
         return hipErrorInvalidValue;
       return run_mx<GEMM_SWIGLU_BWD>(q, s);
     case GEMM_DUALK:
