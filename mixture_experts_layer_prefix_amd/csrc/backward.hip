@@ -35,6 +35,12 @@ namespace {
 constexpr int kMaxK = 16;
 constexpr int kPadRows = 64;
 
+__device__ __forceinline__ int64_t uniform_i64_bk(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __restrict__ counts, int E, int64_t T,
                                                            int pad, int32_t* __restrict__ pad_off,
                                                            int32_t* __restrict__ single_off) {
@@ -270,52 +276,71 @@ __global__ void __launch_bounds__(256) transpose_batched_kernel(const bf16_t* __
 
 // dx[t] = sum_j (dA_perm[token_row[t][j]] + dl[t][j] W_r[idx[t][j]]) + dx_shared[t]
 // (j ascending = ascending expert id), fp32 accumulation, one bf16 rounding.
+// One wave per token (grid-stride over tokens): the token's k rows, expert
+// ids and router-term weights are wave-uniform (scalar loads), and each lane
+// sums 8-element vectors of the row in ascending-expert order with k row
+// reads in flight: dA_perm rows, then the router term dl_j W_router[e_j],
+// then the shared expert's dX; fp32 accumulation, one rounding.
+template <int K>
 __global__ void __launch_bounds__(256) dx_kernel(const bf16_t* __restrict__ da_perm, const int32_t* __restrict__ token_row,
                                                  const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
                                                  const bf16_t* __restrict__ w_router,
                                                  const bf16_t* __restrict__ dx_shared, bf16_t* __restrict__ dx,
-                                                 int64_t T, int d, int k) {
+                                                 int64_t T, int d) {
+  constexpr int k = K;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int vpr = d / 8;
-  const int64_t nvec = T * vpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    const int64_t t = v / vpr;
-    const int c = (int)(v - t * vpr) * 8;
-    float acc[8];
+  for (int64_t tw = wave0; tw < T; tw += nwaves) {
+    const int64_t t = uniform_i64_bk(tw);
+    int64_t rows[K];
+    int eids[K];
+    float g[K];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= k) break;
-      const int64_t row = token_row[t * k + j];
-      const u32x4 w = *reinterpret_cast<const u32x4*>(da_perm + row * d + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += __uint_as_float(w[i] << 16);
-        acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < K; ++j) {
+      eids[j] = 0, g[j] = 0.0f;
+      rows[j] = __builtin_amdgcn_readfirstlane(token_row[t * k + j]);
       if (dl) {
-        const float g = dl[t * k + j];
-        const u32x4 r = *reinterpret_cast<const u32x4*>(w_router + (int64_t)topk_idx[t * k + j] * d + c);
+        eids[j] = __builtin_amdgcn_readfirstlane(topk_idx[t * k + j]);
+        g[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, dl[t * k + j])));
+      }
+    }
+    for (int v = lane; v < vpr; v += 64) {
+      const int c = v * 8;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(da_perm + rows[j] * d + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(g, __uint_as_float(r[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(g, __uint_as_float(r[i] & 0xFFFF0000u), acc[2 * i + 1]);
+          acc[2 * i] += __uint_as_float(w[i] << 16);
+          acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        if (dl) {
+          const u32x4 r = *reinterpret_cast<const u32x4*>(w_router + (int64_t)eids[j] * d + c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(g[j], __uint_as_float(r[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(g[j], __uint_as_float(r[i] & 0xFFFF0000u), acc[2 * i + 1]);
+          }
         }
       }
-    }
-    if (dx_shared) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(dx_shared + t * d + c);
+      if (dx_shared) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(dx_shared + t * d + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += __uint_as_float(w[i] << 16);
-        acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += __uint_as_float(w[i] << 16);
+          acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+        }
       }
-    }
-    u32x4 o;
+      u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(dx + t * d + c) = o;
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      *reinterpret_cast<u32x4*>(dx + t * d + c) = o;
+    }
   }
 }
 
@@ -441,8 +466,17 @@ hipError_t launch_dx(const bf16_t* da_perm, const int32_t* token_row, const int3
                      const bf16_t* w_router, const bf16_t* dx_shared, bf16_t* dx, int64_t T, int d, int k,
                      hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dx_kernel<<<grid_for(T * (d / 8), 16384), 256, 0, s>>>(da_perm, token_row, topk_idx, dl, w_router, dx_shared, dx, T,
-                                                         d, k);
+  const int64_t blocks = (T + 3) / 4;  // one wave per token
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+#define MOE_DX_CASE(KK) \
+  case KK: dx_kernel<KK><<<grid, 256, 0, s>>>(da_perm, token_row, topk_idx, dl, w_router, dx_shared, dx, T, d); break;
+  switch (k) {
+    MOE_DX_CASE(1) MOE_DX_CASE(2) MOE_DX_CASE(3) MOE_DX_CASE(4) MOE_DX_CASE(5) MOE_DX_CASE(6) MOE_DX_CASE(7)
+    MOE_DX_CASE(8) MOE_DX_CASE(9) MOE_DX_CASE(10) MOE_DX_CASE(11) MOE_DX_CASE(12) MOE_DX_CASE(13) MOE_DX_CASE(14)
+    MOE_DX_CASE(15) MOE_DX_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DX_CASE
   return hipGetLastError();
 }
 
