@@ -22,6 +22,11 @@ roofline object describes the dominant kernel of the step.
 backward of other layer shapes (gen/configs.py: the Kimi K2.7 Code, GLM-5.2,
 Qwen3.5 and DeepSeek-V4-Pro layers whole on one GPU, and one GPU's share of
 an EP-64 run) and prints one JSON line with a result per workload.
+
+--workloads n2 instead measures, at the DSV3 MXFP8 shape, the backward with the
+gate/up projections kept by the forward against the backward that replays
+them, and a token-granularity sweep: 32,768 tokens run as layer calls of 512 to
+32,768 tokens each (one JSON line).
 """
 import argparse
 import json
@@ -214,6 +219,11 @@ def main():
     import gen
     import mixture_experts_layer_prefix_amd as M
 
+    if args.workloads == "n2":
+        res = n2_part(args, torch, gen, M)
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "data": "synthetic", "n2": res}), flush=True)
+        return
     if args.workloads:
         names = gen.configs.N3 if args.workloads == "n3" else args.workloads.split(",")
         res = {}
@@ -368,6 +378,119 @@ def workload_part(args, D, torch, gen, M):
     log("[bench]   fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)"
         % (fms, res["fwd_tflops"], bms, res["bwd_tflops"]))
     del f, b, wb, w
+    return res
+
+
+WGRAD_SIDE = ("transposes", "wgrad_down", "wgrad_gate", "wgrad_up", "shared_wgrad", "router_grad")
+
+
+def n2_part(args, torch, gen, M, total=32768, chunks=(512, 1024, 2048, 4096, 8192, 16384, 32768)):
+    """Replay against kept G|U, and the token-granularity sweep, at the DSV3
+    MXFP8 shape (the weights and router skew of the headline workload).
+
+    Replay: the forward keeps the gate/up projections G|U (routed R x 2I and
+    shared T x 2I_s, bf16) for the backward, or the backward recomputes them
+    (the blog post's "Reversed ring order" replays the forward up to the
+    SwiGLU); both give the same bits, and the replay trades one gate/up GEMM
+    for the memory of G|U.
+
+    Granularity: `total` tokens are run as layer calls of c tokens each
+    (forward, then backward with the forward's G|U, call after call).  Per c:
+    the forward time, the backward's input-gradient side and its
+    weight-gradient side (the token-axis transposes, the deferred weight
+    gradients and the router weight gradient), each summed over the calls.
+    Per-token results do not depend on c (tested); the weight gradients of a
+    call cover its own tokens, so a chunked pipeline defers them to one pass
+    over the whole token axis, as the blog post's backward does: the sweep
+    reports that step as forward + input-gradient side at c + the
+    weight-gradient side of the single whole-axis call."""
+    res = {}
+    D = gen.get_config("c4", T=total)
+    log("[bench] n2 workload", D)
+    p = gen.Problem(D)
+    names = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+    w = M.Weights(**{n: p.device(n) for n in names})
+    x, dy, bias = p.device("x"), p.device("dy"), p.device_bias()
+    md0 = M.Dims(D.T, D.d, D.E, D.k, D.I, D.S, D.Is)
+    wq = M.prepare_mxfp8(w, md0)
+    wb = M.prepare_backward(wq, mxfp8=True)
+    del w
+    torch.cuda.empty_cache()
+    # (a) kept G|U against replay, at the headline token count
+    T1 = 16384
+    md1 = M.Dims(T1, D.d, D.E, D.k, D.I, D.S, D.Is)
+    x1, dy1 = x[:T1], dy[:T1]
+    rep = {}
+    for keep in (True, False):
+        f, b = M.ForwardPlan(md1, "mxfp8", keep_gu=keep), M.BackwardPlan(md1, "mxfp8")
+        for _ in range(args.warmup):
+            f.run(x1, wq, bias)
+            b.run(dy1, x1, wb, f.routing)
+        tb = M.StageTimer(1, args.steps)
+        ef = timed_steps(lambda i: f.run(x1, wq, bias), args.steps, torch)
+
+        def bstep(i):
+            tb.arm(i)
+            b.run(dy1, x1, wb, f.routing)
+
+        eb = timed_steps(bstep, args.steps, torch)
+        tb.disarm()
+        fms, bms = ef / args.steps * 1e3, eb / args.steps * 1e3
+        kept = sum(t.numel() * t.element_size() for n, t in f.routing.items() if n.startswith("gu"))
+        rep["kept" if keep else "replayed"] = {
+            "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4), "step_ms": round(fms + bms, 4),
+            "step_tokens_s": round(T1 / ((fms + bms) / 1e3), 1),
+            "replay_gate_up_ms": round(tb.mean_ms()["replay_gate_up"], 4),
+            "gu_bytes_kept": kept, "fwd_workspace_bytes": f.ws_bytes, "bwd_workspace_bytes": b.ws_bytes}
+        log("[bench] n2 G|U %s: fwd %.3f ms, bwd %.3f ms" % ("kept" if keep else "replayed", fms, bms))
+        del f, b
+        torch.cuda.empty_cache()
+    rep["workload"] = "T=%d, d=%d, E=%d, k=%d, I=%d, 1 bf16 shared expert, MXFP8 routed experts" % (
+        T1, D.d, D.E, D.k, D.I)
+    res["replay_vs_kept"] = rep
+    # (b) granularity sweep
+    sweep = {}
+    steps = max(1, min(args.steps, 3))
+    for c in chunks:
+        n = total // c
+        mdc = M.Dims(c, D.d, D.E, D.k, D.I, D.S, D.Is)
+        f, b = M.ForwardPlan(mdc, "mxfp8", keep_gu=True), M.BackwardPlan(mdc, "mxfp8")
+
+        def one_pass(i, tf=None, tb=None):
+            for j in range(n):
+                xs, ds = x[j * c:(j + 1) * c], dy[j * c:(j + 1) * c]
+                if tf is not None:
+                    tf.arm(i * n + j)
+                f.run(xs, wq, bias)
+                if tb is not None:
+                    tb.arm(i * n + j)
+                b.run(ds, xs, wb, f.routing)
+
+        one_pass(0)
+        tf, tb = M.StageTimer(0, steps * n), M.StageTimer(1, steps * n)
+        el = timed_steps(lambda i: one_pass(i, tf, tb), steps, torch)
+        tf.disarm()
+        tb.disarm()
+        fst, bst = tf.mean_ms(), tb.mean_ms()
+        fwd = sum(fst.values()) * n
+        wside = sum(bst[k] for k in WGRAD_SIDE) * n
+        dside = sum(bst.values()) * n - wside
+        sweep[c] = {"calls": n, "pass_ms": round(el / steps * 1e3, 3), "fwd_ms": round(fwd, 3),
+                    "bwd_input_grad_side_ms": round(dside, 3), "bwd_weight_grad_side_ms": round(wside, 3),
+                    "tokens_s_per_call_wgrads": round(total / (el / steps), 1),
+                    "fwd_tokens_s": round(total / (fwd / 1e3), 1),
+                    "workspace_bytes": f.ws_bytes + b.ws_bytes}
+        log("[bench] n2 chunk %d: pass %.2f ms (fwd %.2f, input-grad side %.2f, weight-grad side %.2f)"
+            % (c, el / steps * 1e3, fwd, dside, wside))
+        del f, b, tf, tb
+        torch.cuda.empty_cache()
+    whole = sweep[chunks[-1]]["bwd_weight_grad_side_ms"]
+    for c, r in sweep.items():
+        r["tokens_s_deferred_wgrads"] = round(total / ((r["fwd_ms"] + r["bwd_input_grad_side_ms"] + whole) / 1e3), 1)
+    res["granularity"] = {"total_tokens": total, "steps": steps, "per_chunk_tokens": sweep,
+                          "workload": "T=%d tokens as layer calls of 512..%d tokens, d=%d, E=%d, k=%d, I=%d, "
+                                      "1 bf16 shared expert, MXFP8 routed experts, Zipf(1.2) router skew"
+                                      % (total, chunks[-1], D.d, D.E, D.k, D.I)}
     return res
 
 
