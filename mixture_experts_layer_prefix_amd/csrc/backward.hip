@@ -35,12 +35,6 @@ namespace {
 constexpr int kMaxK = 16;
 constexpr int kPadRows = 64;
 
-__device__ __forceinline__ int64_t uniform_i64_bk(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 __global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __restrict__ counts, int E, int64_t T,
                                                            int pad, int32_t* __restrict__ pad_off,
                                                            int32_t* __restrict__ single_off) {
@@ -293,7 +287,7 @@ __global__ void __launch_bounds__(256) dx_kernel(const bf16_t* __restrict__ da_p
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int vpr = d / 8;
   for (int64_t tw = wave0; tw < T; tw += nwaves) {
-    const int64_t t = uniform_i64_bk(tw);
+    const int64_t t = uniform_i64(tw);
     int64_t rows[K];
     int eids[K];
     float g[K];

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp; outputs are
 // rounded to bf16 or E4M3 afterwards).
+// A 64-bit value that is the same in every lane, held in scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float sigmoid_f32(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }

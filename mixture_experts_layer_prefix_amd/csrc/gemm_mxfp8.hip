@@ -49,12 +49,6 @@ __device__ __forceinline__ T* uniform_ptr(T* ptr) {
   return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

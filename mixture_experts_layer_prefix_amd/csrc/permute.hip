@@ -12,11 +12,11 @@
 //  1. block histograms: block b counts the routes of its kTokBlock tokens
 //     per expert (LDS integer atomics; counts do not depend on order);
 //  2. one workgroup scans them expert-major: offsets[e] = sum of earlier
-//     experts' totals and base[b][e] = offsets[e] + routes of e in blocks
-//     before b;
+//     experts' totals and before[b][e] = routes of e in blocks before b;
 //  3. block b re-walks its routes in (token, slot) order, 256 at a time; a
-//     route's row is base[b][e] plus the number of earlier routes of e in the
-//     block (rank among the 256 in flight plus a running LDS cursor).
+//     route's row is offsets[e] + before[b][e] plus the number of earlier
+//     routes of e in the block (rank among the 256 in flight plus a running
+//     LDS cursor).
 // The result is the unique expert-major, token-ascending layout.
 //
 // The gather copies rows with 16-byte loads and stores; the MXFP8 variant
@@ -45,16 +45,26 @@ __global__ void __launch_bounds__(256) hist_kernel(const int32_t* __restrict__ t
   for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
+// block_counts[b][e] becomes the number of expert-e routes in the blocks
+// before b (loads batched so that many are in flight); counts and offsets
+// (exclusive scan over the experts) are written once.  The scatter adds
+// offsets[e] to the block's running count.
 __global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ block_counts, int nb, int E,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  constexpr int kBatch = 16;
   __shared__ int32_t s[1024];
   const int e = threadIdx.x;
   int32_t total = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      int32_t c = block_counts[(int64_t)b * E + e];
-      block_counts[(int64_t)b * E + e] = total;
-      total += c;
+    for (int b0 = 0; b0 < nb; b0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < nb ? block_counts[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b0 + i < nb) block_counts[(int64_t)(b0 + i) * E + e] = total;
+        total += c[i];
+      }
     }
   }
   s[e] = total;
@@ -66,21 +76,20 @@ __global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ block_
     __syncthreads();
   }
   if (e < E) {
-    const int32_t excl = s[e] - total;
     counts[e] = total;
-    offsets[e] = excl;
+    offsets[e] = s[e] - total;
     if (e == E - 1) offsets[E] = s[e];
-    for (int b = 0; b < nb; ++b) block_counts[(int64_t)b * E + e] += excl;
   }
 }
 
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k,
                                                       const int32_t* __restrict__ block_base,
+                                                      const int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ row_token,
                                                       int32_t* __restrict__ token_row) {
   __shared__ int32_t cursor[1024];
   __shared__ int32_t s_e[256];
-  for (int e = threadIdx.x; e < E; e += 256) cursor[e] = block_base[(int64_t)blockIdx.x * E + e];
+  for (int e = threadIdx.x; e < E; e += 256) cursor[e] = block_base[(int64_t)blockIdx.x * E + e] + offsets[e];
   const int64_t r0 = (int64_t)blockIdx.x * kTokBlock * k;
   const int64_t r1 = min((int64_t)(blockIdx.x + 1) * kTokBlock, T) * k;
   for (int64_t c0 = r0; c0 < r1; c0 += 256) {
@@ -207,7 +216,7 @@ hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int
   int32_t* bc = static_cast<int32_t*>(scratch);
   if (nb > 0) hist_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc);
   scan_kernel<<<1, 1024, 0, s>>>(bc, nb, E, counts, offsets);
-  if (nb > 0) scatter_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc, row_token, token_row);
+  if (nb > 0) scatter_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc, offsets, row_token, token_row);
   return hipGetLastError();
 }
 

@@ -34,6 +34,18 @@ __device__ __forceinline__ void better(float& bv, int& bid, float ov, int oid) {
   }
 }
 
+// Key whose unsigned order is the order of the (finite) logits; -0 and +0
+// share a key so that, as in a float comparison, they tie.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b << 1) == 0) return 0x80000000u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// `rounds` rounds of a wave-wide arg-max over the not yet taken logits:
+// each lane's best candidate (larger value, then smaller id), the wave
+// maximum of their keys in DPP steps, then among the lanes holding that
+// value the smallest id (the lane of an id is id mod 64).
 template <int PER_LANE>
 __device__ __forceinline__ void select_rounds(const float (&v)[PER_LANE], int E, int rounds, int lane, float (&sel_v)[kMaxK + 1],
                                               int (&sel_id)[kMaxK + 1]) {
@@ -48,15 +60,20 @@ __device__ __forceinline__ void select_rounds(const float (&v)[PER_LANE], int E,
       int e = lane + 64 * i;
       if (e < E && !((taken >> i) & 1u)) better(bv, bid, v[i], e);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oid = __shfl_xor(bid, off);
-      better(bv, bid, ov, oid);
+    const bool has = bid != 0x7fffffff;
+    const uint32_t key = has ? order_key(bv) : 0u;
+    const uint32_t h = half_max32_u(key);
+    const uint32_t m = max((uint32_t)__builtin_amdgcn_readlane((int)h, 0), (uint32_t)__builtin_amdgcn_readlane((int)h, 32));
+    uint64_t tie = __ballot(has && key == m);
+    int id = __builtin_amdgcn_readlane(bid, __ffsll((unsigned long long)tie) - 1);
+    tie &= tie - 1;
+    while (tie) {  // equal values in several lanes: the smallest id
+      id = min(id, __builtin_amdgcn_readlane(bid, __ffsll((unsigned long long)tie) - 1));
+      tie &= tie - 1;
     }
-    sel_v[r] = bv;
-    sel_id[r] = bid;
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+    sel_v[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), id & 63));
+    sel_id[r] = id;
+    if ((id & 63) == lane) taken |= 1u << (id >> 6);
   }
 }
 
