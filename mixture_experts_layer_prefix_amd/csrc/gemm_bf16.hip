@@ -612,38 +612,49 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  u32x4 ra[2], rb[2];
+  // Slabs move global -> registers -> LDS; kPD slabs are in flight in
+  // registers (one K loop of a 64 x 64 tile is otherwise a chain of
+  // load-latency waits).
+  constexpr int kPD = 4;
+  u32x4 ra[kPD][2], rb[kPD][2];
   const int KT = p.K / kBK;
-  auto ld = [&](int k0) {
+  auto ld = [&](int slot, int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
-      rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+      ra[slot][i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+      rb[slot][i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
     }
   };
-  auto st = [&](int b) {
+  auto st = [&](int slot, int b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + i * 256;
-      *reinterpret_cast<u32x4*>(&As[b][v / KV][(v % KV) * 8]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[b][v / KV][(v % KV) * 8]) = rb[i];
+      *reinterpret_cast<u32x4*>(&As[b][v / KV][(v % KV) * 8]) = ra[slot][i];
+      *reinterpret_cast<u32x4*>(&Bs[b][v / KV][(v % KV) * 8]) = rb[slot][i];
     }
   };
-  ld(0);
-  st(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int b = kt & 1;
-    if (kt + 1 < KT) ld((kt + 1) * kBK);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int kof = kk * 16 + (lane >> 5) * 8;
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[b][wm * WM + (lane & 31)][kof]);
-      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[b][wn * WN + (lane & 31)][kof]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+  for (int j = 0; j < kPD; ++j)
+    if (j < KT) ld(j, j * kBK);
+  st(0, 0);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < KT; kt0 += kPD) {
+#pragma unroll
+    for (int u = 0; u < kPD; ++u) {
+      const int kt = kt0 + u;  // slab kt sits in LDS buffer u & 1 (kPD is even)
+      if (kt < KT) {
+        if (kt + kPD < KT) ld(u, (kt + kPD) * kBK);  // register slot u was stored at step kt - 1
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+          const int kof = kk * 16 + (lane >> 5) * 8;
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
+          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+        }
+        if (kt + 1 < KT) st((u + 1) % kPD, (u + 1) & 1);
+        __syncthreads();
+      }
     }
-    if (kt + 1 < KT) st(b ^ 1);
-    __syncthreads();
   }
   float* C = static_cast<float*>(p.C);
 #pragma unroll

@@ -52,7 +52,7 @@ __device__ __forceinline__ void select_rounds(const float (&v)[PER_LANE], int E,
   uint32_t taken = 0;
 #pragma unroll
   for (int r = 0; r < kMaxK + 1; ++r) {
-    if (r >= rounds) break;
+    if (r >= rounds) continue;  // (not break: the loop unrolls, sel_v and sel_id stay in registers)
     float bv = -INFINITY;
     int bid = 0x7fffffff;
 #pragma unroll
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         double acc = 0.0;
         // 8 consecutive elements per lane per step (d is a multiple of 8), so
         // the row streams with wide loads and many requests in flight.
-#pragma unroll 4
+#pragma unroll 1
         for (int c = lane * 8; c < d; c += 512) {
           double xv[8], wv[8];
           load8_f64(x, t * (int64_t)d + c, act_f32, xv);
