@@ -23,6 +23,8 @@ SMALL = {
     "bwd_ragged": gen.Dims("bwd_ragged", 300, 256, 16, 4, 192, 1, 128, "bf16", 0.0, backward=True),
     "bwd_skew_noshared": gen.Dims("bwd_skew_noshared", 513, 192, 32, 8, 128, 0, 0, "bf16", 1.2, backward=True),
     "bwd_k1": gen.Dims("bwd_k1", 77, 64, 4, 1, 64, 1, 64, "bf16", 0.0, backward=True),
+    "bwd_kE": gen.Dims("bwd_kE", 64, 128, 8, 8, 64, 1, 64, "bf16", 0.0, backward=True),
+    "bwd_E1": gen.Dims("bwd_E1", 130, 128, 1, 1, 64, 0, 0, "bf16", 0.0, backward=True),
     "bwd_tiles": gen.Dims("bwd_tiles", 1100, 512, 8, 2, 320, 1, 192, "bf16", 0.0, backward=True),
     # the ABI's limits: E = 1024 experts, k = 16
     "bwd_max_E_k": gen.Dims("bwd_max_E_k", 300, 128, 1024, 16, 64, 1, 64, "bf16", 1.2, backward=True),

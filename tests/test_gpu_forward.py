@@ -20,6 +20,8 @@ SMALL = {
     "bf16_skew_noshared": gen.Dims("bf16_skew_noshared", 513, 192, 32, 8, 128, 0, 0, "bf16", 1.2),
     "bf16_k1": gen.Dims("bf16_k1", 77, 64, 4, 1, 64, 1, 64, "bf16", 0.0),
     "bf16_kE": gen.Dims("bf16_kE", 64, 128, 8, 8, 64, 0, 0, "bf16", 0.0),
+    # one routed expert, k = 1, no shared expert: a plain SwiGLU FFN
+    "bf16_E1": gen.Dims("bf16_E1", 130, 128, 1, 1, 64, 0, 0, "bf16", 0.0),
     "f32_skew": gen.Dims("f32_skew", 200, 96, 12, 3, 40, 1, 24, "f32", 1.2),
     # the ABI's limits: E = 1024 experts, k = 16
     "bf16_max_E_k": gen.Dims("bf16_max_E_k", 300, 128, 1024, 16, 64, 1, 64, "bf16", 1.2),
@@ -81,6 +83,26 @@ def test_small_layer_every_entry_point(name):
         assert np.array_equal(to_np(routing[n]), r), n
     y2, _ = M.layer_forward(t["x"], w, md, prec, bias=t["bias"])
     assert torch.equal(y, y2), "forward is not bitwise deterministic"
+
+
+@pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
+def test_zero_down_projection_leaves_shared_ffn(prec):
+    """Routed W_down = 0: every routed expert output is exactly zero, so the
+    layer output is the shared expert's output bit for bit (paper summary,
+    section 2.1: the layer output is the shared experts' sum plus the
+    weighted routed outputs)."""
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.Dims("zero_down", 300, 256, 16, 4, 256, 1, 128, prec, 1.2)
+    say("[case] zero W_down", D)
+    p, t, md, w = device_problem(D)
+    t["w_down"].zero_()
+    if prec == "mxfp8":
+        w = M.prepare_mxfp8(w, md)
+    y, _ = M.layer_forward(t["x"], w, md, prec, bias=t["bias"])
+    y_sh = M.shared_ffn(t["x"], w, md, prec)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y_sh) > 0
+    assert torch.equal(y, y_sh)
 
 
 def test_generator_device_matches_host():

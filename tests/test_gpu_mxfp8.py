@@ -21,6 +21,8 @@ SMALL = {
     "mx_ragged": gen.Dims("mx_ragged", 300, 256, 16, 4, 256, 1, 128, "mxfp8", 0.0),
     "mx_skew_noshared": gen.Dims("mx_skew_noshared", 513, 384, 32, 8, 128, 0, 0, "mxfp8", 1.2),
     "mx_k1": gen.Dims("mx_k1", 77, 128, 4, 1, 128, 1, 64, "mxfp8", 0.0),
+    "mx_kE": gen.Dims("mx_kE", 64, 128, 8, 8, 128, 0, 0, "mxfp8", 0.0),
+    "mx_E1": gen.Dims("mx_E1", 130, 128, 1, 1, 128, 0, 0, "mxfp8", 0.0),
     # the ABI's limits: E = 1024 experts, k = 16
     "mx_max_E_k": gen.Dims("mx_max_E_k", 300, 128, 1024, 16, 128, 1, 64, "mxfp8", 1.2),
 }

@@ -30,6 +30,8 @@ SMALL = {
     "mxb_ragged": gen.Dims("mxb_ragged", 300, 256, 16, 4, 256, 1, 128, "mxfp8", 0.0, backward=True),
     "mxb_skew_noshared": gen.Dims("mxb_skew_noshared", 513, 384, 32, 8, 128, 0, 0, "mxfp8", 1.2, backward=True),
     "mxb_k1": gen.Dims("mxb_k1", 77, 128, 4, 1, 128, 1, 64, "mxfp8", 0.0, backward=True),
+    "mxb_kE": gen.Dims("mxb_kE", 64, 128, 8, 8, 128, 1, 64, "mxfp8", 0.0, backward=True),
+    "mxb_E1": gen.Dims("mxb_E1", 130, 128, 1, 1, 128, 0, 0, "mxfp8", 0.0, backward=True),
     "mxb_tiles": gen.Dims("mxb_tiles", 1100, 512, 8, 2, 384, 1, 192, "mxfp8", 0.0, backward=True),
     # the ABI's limits: E = 1024 experts, k = 16
     "mxb_max_E_k": gen.Dims("mxb_max_E_k", 300, 128, 1024, 16, 128, 1, 64, "mxfp8", 1.2, backward=True),
