@@ -514,7 +514,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
   const int nwg = gridDim.x;
   const int per_xcd = nwg >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  constexpr int GN = 4;  // N-tiles of one M-tile visited before the next M-tile
+  // N-tiles of one M-tile visited before the next M-tile: 8 for the modes
+  // whose B is a down projection, both dgrad weights or the SwiGLU backward's
+  // 8 N-tiles (each A strip is read fewer times; measured 1-2% faster), 4 for
+  // the paired gate/up (more B reuse).
+  constexpr int GN = (MODE == GEMM_DOWN || MODE == GEMM_DUALK || MODE == GEMM_SWIGLU_BWD) ? 8 : 4;
 
   if (MODE == GEMM_WGRAD) {
     // One output per group, all of it in big tiles; K range from k_off.
