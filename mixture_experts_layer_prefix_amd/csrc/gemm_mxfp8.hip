@@ -327,10 +327,32 @@ __device__ __forceinline__ void mx_issue(const MxArgs& p, const MxLoad<BM>& L, u
 // first min(NS, KT) slabs were already issued (by the previous tile).  nxt:
 // the next tile of this workgroup (or nullptr), whose first slabs are issued
 // once this tile's last slab barrier has freed the LDS ring.
+// Background zero fill of the weight gradients of experts without rows
+// (K-grouped mode).  The dense [M][N] outputs of those experts are cut into
+// 1 KiB chunks; every wave owns a contiguous run of them and stores
+// kZeroPerSlab chunks after each slab it issues inside a K loop, so the
+// stores drain under the MFMA work instead of queueing as zero tiles at the
+// end of the launch; the wave stores what is left once its tiles are done.
+constexpr int kZeroPerSlab = 2;
+struct ZeroRun {
+  const int32_t* empty;  // LDS: ids of the experts without rows
+  int slot, off, cpr;    // current expert (index into empty), chunk in it, chunks per expert
+  int64_t left;          // chunks still to store
+};
+__device__ __forceinline__ void zero_chunk(const MxArgs& p, ZeroRun& z, int lane) {
+  const int64_t e = z.empty[z.slot];
+  uint8_t* base = reinterpret_cast<uint8_t*>(static_cast<bf16_t*>(p.C) + e * p.c_group_stride);
+  __builtin_nontemporal_store(u32x4{0, 0, 0, 0},
+                              reinterpret_cast<u32x4*>(base + (int64_t)z.off * 1024 + lane * 16));
+  if (++z.off == z.cpr) z.off = 0, ++z.slot;
+  --z.left;
+}
+
 template <int BM, int MODE, int NS>
 __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const MxLoad<BM>& L, int g,
                                         int64_t row_begin, int64_t n_g, int64_t m0, int ntile, int KT,
-                                        bool prefetched, bool has_next, const MxLoad<BM>& nxt, int nxt_KT) {
+                                        bool prefetched, bool has_next, const MxLoad<BM>& nxt, int nxt_KT,
+                                        ZeroRun* zr = nullptr) {
   constexpr int BN = kBN;
   constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -422,6 +444,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
 #pragma unroll
       for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
   };
+  // background zero stores (K-grouped mode; the waits below assume one slab in flight)
+  constexpr bool ZB = MODE == GEMM_WGRAD && NS == 2;
+  bool zprev = false;  // this wave stored kZeroPerSlab zero chunks after its last slab issue
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % NS;
     read_scales(st);
@@ -431,12 +456,29 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     pin_acc();
     mma(1);
     if (kt + NS - 1 < KT) {
-      if (any_sc) wait_vmcnt<(NS - 2) * (LPS + 1)>(); else wait_vmcnt<(NS - 2) * LPS>();
+      if constexpr (ZB) {
+        // Loads and stores complete in issue order: the zero stores issued
+        // after slab kt + 1 may stay in flight.
+        if (zprev) wait_vmcnt<kZeroPerSlab>(); else wait_vmcnt<0>();
+      } else {
+        if (any_sc) wait_vmcnt<(NS - 2) * (LPS + 1)>(); else wait_vmcnt<(NS - 2) * LPS>();
+      }
     } else {
       wait_vmcnt<0>();
     }
     __syncthreads();
-    if (kt + NS < KT) issue(st, (kt + NS) * kBKB);
+    zprev = false;
+    if (kt + NS < KT) {
+      issue(st, (kt + NS) * kBKB);
+      if constexpr (ZB) {
+        // not after the tile's last slab, whose wait takes everything
+        if (kt + NS < KT - 1 && zr->left >= kZeroPerSlab) {
+#pragma unroll
+          for (int s = 0; s < kZeroPerSlab; ++s) zero_chunk(p, *zr, lane);
+          zprev = true;
+        }
+      }
+    }
   }
   // The ring is free: start the next tile's loads under this epilogue.
   if (has_next) {
@@ -766,18 +808,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
   }
 }
 
-// Zero one 256 x 256 output tile of group g (weight gradient of an expert
-// without rows) with 16-byte stores.
-__device__ __forceinline__ void mx_zero_tile(const MxArgs& p, int g, int64_t m0, int n0) {
-  bf16_t* C = static_cast<bf16_t*>(p.C) + (int64_t)g * p.c_group_stride;
-  const int rows = (int)min<int64_t>(kBigM, p.M - m0);
-  const int cols = min(kBN, p.N - n0);
-  const int cpr = cols / 8;
-  for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
-    const int r = c / cpr, q = c - r * cpr;
-    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, reinterpret_cast<u32x4*>(C + (m0 + r) * p.ldc + n0 + q * 8));
-  }
-}
 
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
@@ -801,14 +831,39 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   if constexpr (MODE == GEMM_WGRAD) {
     // One output per group, all in big tiles; K range of group g from k_off.
-    // Tiles of groups without rows are zero-filled; every other tile's first
-    // slabs are issued by the previous tile of this workgroup (lookahead).
+    // Groups without rows come last in the order and get no tiles: their
+    // outputs are zero-filled in the background (ZeroRun).  Every tile's
+    // first slabs are issued by the previous tile of this workgroup
+    // (lookahead).
     const WgradRect rc = wgrad_rect((int)((p.M + kBigM - 1) / kBigM), p.ntiles, xcd);
     const int per_g = rc.bm * rc.bn;
-    const int tot = p.G * per_g;
     int32_t* order = tab + (p.G + 1);
     wgrad_order(tab, p.G, order);
     __syncthreads();
+    int n_act = 0, hi = p.G;  // groups with rows: a prefix of the order
+    while (n_act < hi) {
+      const int mid = (n_act + hi) >> 1, g = order[mid];
+      if (tab[g + 1] > tab[g]) n_act = mid + 1; else hi = mid;
+    }
+    n_act = __builtin_amdgcn_readfirstlane(n_act);
+    const int tot = n_act * per_g;
+    ZeroRun zr;
+    {
+      const int64_t cpr = p.M * (int64_t)p.N * 2 / 1024;
+      const int64_t ztot = (p.G - n_act) * cpr;
+      const int64_t nw = (int64_t)nwg * (kThreads / 64);
+      const int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int64_t z0 = uniform_i64(ztot * w / nw), z1 = uniform_i64(ztot * (w + 1) / nw);
+      zr.empty = order + n_act;
+      zr.cpr = (int)cpr;
+      zr.slot = (int)(z0 / cpr);
+      zr.off = (int)(z0 - (int64_t)zr.slot * cpr);
+      zr.left = z1 - z0;
+    }
+    auto zero_rest = [&]() {
+      const int lane = threadIdx.x & 63;
+      while (zr.left > 0) zero_chunk(p, zr, lane);
+    };
     struct Job { int g, mt, nt, kb, kt; };
     auto job = [&](int P) {
       Job j;
@@ -824,38 +879,32 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mxfp8_kernel(MxArgs p) {
     };
     auto pos = [&](int r) { return wgrad_pos(r, slot, per_xcd); };
     int r = 0;
-    Job cj = {0, 0, 0, 0, 0};
-    for (; pos(r) < tot; ++r) {
-      cj = job(pos(r));
-      if (cj.kt) break;
-      mx_zero_tile(p, cj.g, (int64_t)cj.mt * kBigM, cj.nt * kBN);
+    if (pos(r) >= tot) {
+      zero_rest();
+      return;
     }
-    if (pos(r) >= tot) return;
+    Job cj = job(pos(r));
     MxLoad<kBigM> cur;
     mx_setup<kBigM, MODE>(p, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kb, cj.kt * kBKB);
     bool pre = false;
     for (;;) {
-      int rn = r + 1;
-      Job nj = {0, 0, 0, 0, 0};
-      for (; pos(rn) < tot; ++rn) {
-        nj = job(pos(rn));
-        if (nj.kt) break;
-      }
+      const int rn = r + 1;
       const bool has = pos(rn) < tot;
+      Job nj = {0, 0, 0, 0, 0};
       MxLoad<kBigM> nxt;
-      if (has) mx_setup<kBigM, MODE>(p, nxt, nj.g, 0, p.M, (int64_t)nj.mt * kBigM, nj.nt, nj.kb, nj.kt * kBKB);
-      mx_tile<kBigM, MODE, 2>(p, smem_mx, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kt, pre, has, nxt,
-                              nj.kt);
-      for (int rz = r + 1; rz < rn; ++rz) {  // zero tiles between the two
-        const Job z = job(pos(rz));
-        mx_zero_tile(p, z.g, (int64_t)z.mt * kBigM, z.nt * kBN);
+      if (has) {
+        nj = job(pos(rn));
+        mx_setup<kBigM, MODE>(p, nxt, nj.g, 0, p.M, (int64_t)nj.mt * kBigM, nj.nt, nj.kb, nj.kt * kBKB);
       }
+      mx_tile<kBigM, MODE, 2>(p, smem_mx, cur, cj.g, 0, p.M, (int64_t)cj.mt * kBigM, cj.nt, cj.kt, pre, has, nxt,
+                              nj.kt, &zr);
       if (!has) break;
       cur = nxt;
       cj = nj;
       r = rn;
       pre = true;
     }
+    zero_rest();
     return;
   }
   const int nbig = t_big[p.G];
@@ -995,7 +1044,11 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
 hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
   if (q.N % 64 != 0 || q.G > kMaxGroups) return hipErrorInvalidValue;
   if (q.mode == GEMM_WGRAD) {
-    if (!q.k_off || q.G < 1) return hipErrorInvalidValue;
+    // Outputs dense per group ([M][N] at g * M * N), cut into whole 1 KiB
+    // chunks for the background zero fill of groups without rows.
+    if (!q.k_off || q.G < 1 || q.ldc != q.N || q.c_group_stride != q.M * (int64_t)q.N ||
+        (q.M * (int64_t)q.N * 2) % 1024 != 0 || q.M * (int64_t)q.N * 2 / 1024 > INT32_MAX)
+      return hipErrorInvalidValue;
     return run_mx<GEMM_WGRAD>(q, s);
   }
   if (!q.row_off || q.K % kBKB != 0) return hipErrorInvalidValue;
