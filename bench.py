@@ -211,7 +211,7 @@ def main():
                     help='comma-separated config names, or "n3": measure these workloads instead')
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,        /* bad argument: dims, NULL or misaligned pointer */
-  MOE_EUNSUPPORTED = 2,  /* valid request that this build does not implement */
+  MOE_EUNSUPPORTED = 2,  /* valid request that the library does not implement */
   MOE_EWORKSPACE = 3,    /* workspace missing or smaller than required */
   MOE_EHIP = 4           /* a HIP launch or runtime call failed */
 } moe_status;

@@ -651,7 +651,7 @@ const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
-    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape or mode not supported by this build";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape or mode not supported by the library";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
     case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
   }
