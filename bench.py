@@ -203,7 +203,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens of the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=12288, help="tokens of the CPU oracle sample (0: skip)")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 DeepSeek-V3 (T=8192) measurements")
     ap.add_argument("--only-bf16", action="store_true",
                     help="run only the bf16 DeepSeek-V3 (T=8192) measurements (for per-part profiles)")
