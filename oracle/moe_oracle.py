@@ -26,7 +26,8 @@ Sources (the pages of the Mixture-of-Kittens paper and blog post):
   * blog post, "Other features / MXFP8 support": routed experts in MXFP8,
     shared expert stays BF16; block format from "Microscaling Data Formats for
     Deep Learning" (cited by the paper), read as OCP MX v1.0 E4M3 elements
-    with one E8M0 scale per 32 elements;
+    with one E8M0 scale per 32 elements; the scale is the smallest power of
+    two that keeps the block maximum unclipped (see mx_scale_exponent);
   * blog post, "Other features / Router weight gradient computation": the
     router-weight gradient is the inner product of the SwiGLU activation and
     the down-projection input gradient.
@@ -387,12 +388,25 @@ def e4m3_decode(bits):
 
 
 def mx_scale_exponent(amax):
-    """Shared block exponent: floor(log2 amax) - 8, clamped to [-127, 127];
-    an all-zero block takes -127 (E8M0 code 0)."""
+    """Shared block exponent: the smallest integer e with amax / 2^e <= 448,
+    i.e. the finest power-of-two scale at which the block's largest magnitude
+    is still an E4M3 value without clipping; clamped to [-127, 127] (the E8M0
+    range); an all-zero block takes -127 (E8M0 code 0).
+
+    Reading: the pages fix the format (E4M3 elements, one power-of-two E8M0
+    scale per 32 elements; blog post "MXFP8 support") but not how an encoder
+    picks the scale.  The MX paper's rule, floor(log2 amax) - 8, maps a block
+    maximum with mantissa above 1.75 past 448, where it is clipped by up to
+    12.5%; this rule never clips and is otherwise the same (it is one larger
+    exactly when that happens).
+    """
     amax = np.asarray(amax, F64)
-    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
-    e = np.clip(ex - 1 - E4M3_EMAX, -127, 127)
-    return np.where(amax > 0, e, -127).astype(np.int64)
+    pos = amax > 0
+    _, ex = np.frexp(np.where(pos, amax, 1.0))      # amax = m 2^ex, m in [0.5, 1)
+    e = ex - 1 - E4M3_EMAX                          # floor(log2 amax) - 8: amax / 2^e in [256, 512)
+    e = e + (np.where(pos, amax, 0.0) > E4M3_MAX * np.ldexp(1.0, e))   # past 448: one step coarser
+    e = np.clip(e, -127, 127)
+    return np.where(pos, e, -127).astype(np.int64)
 
 
 def mx_quantize(v, axis=-1):
@@ -400,7 +414,8 @@ def mx_quantize(v, axis=-1):
 
     Returns (codes uint8 E4M3 bits, same shape as v) and (scales uint8 E8M0
     codes, with the axis length divided by 32).  Elements are v / 2^e_s
-    rounded to E4M3 (ties to even, saturating).
+    rounded to E4M3 (ties to even; saturation is reached only where the
+    scale is clamped at the top of the E8M0 range).
     """
     v = np.moveaxis(np.asarray(v, F64), axis, -1)
     n = v.shape[-1]

@@ -18,20 +18,53 @@ def test_hand_cases():
     # all-zero block: scale code 0, zero elements
     c, s = O.mx_quantize(np.zeros((1, 32)))
     assert s.tolist() == [[0]] and np.all(c == 0)
-    # amax 1.0: e_s = 0 - 8 -> code 119; 1.0 -> 256 = 2^8 (field 15, mant 0) = 0x78
+    # amax 1.0: 1.0 / 2^-8 = 256 <= 448 and 1.0 / 2^-9 = 512 > 448, so e_s = -8
+    # (code 119); 1.0 -> 256 = 2^8 (field 15, mant 0) = 0x78
     c, s = O.mx_quantize(block([1.0, 0.5, -1.0])[None])
     assert s[0, 0] == 119 and c[0, 0] == 0x78 and c[0, 1] == 0x70 and c[0, 2] == 0xF8
-    # 1.9375 * 256 = 496 saturates to 448 (0x7E); 1.8125 * 256 = 464 ties to 448 (even)
+    # amax 1.75 is exactly 448 at e_s = -8: kept at code 119, element 0x7E
+    c, s = O.mx_quantize(block([1.75, -1.75])[None])
+    assert s[0, 0] == 119 and c[0, 0] == 0x7E and c[0, 1] == 0xFE
+    # amax 1.9375: 1.9375 * 256 = 496 > 448, so e_s = -7 (code 120) and nothing
+    # clips: 1.9375 * 128 = 248 is halfway between 240 (0x77, mant 7) and 256
+    # (0x78, mant 0) -> 256; 1.8125 * 128 = 232 halfway between 224 (0x76) and
+    # 240 (0x77) -> 224; 1.0625 * 128 = 136 halfway between 128 (0x70) and 144
+    # (0x71) -> 128
     c, s = O.mx_quantize(block([1.9375, 1.8125, 1.0625])[None])
-    assert s[0, 0] == 119 and c[0, 0] == 0x7E and c[0, 1] == 0x7E
-    # 1.0625 * 256 = 272: halfway between 256 (m=0) and 288 (m=1) -> 256
-    assert c[0, 2] == 0x78
-    # subnormal: 2^-8 relative to 2^e_s -> 2 * 2^-9 -> code 0x02
+    assert s[0, 0] == 120 and c[0, 0] == 0x78 and c[0, 1] == 0x76 and c[0, 2] == 0x70
+    # just above 1.75: one step coarser
+    c, s = O.mx_quantize(block([1.75 * (1 + 2.0 ** -20)])[None])
+    assert s[0, 0] == 120
+    # 1.0625 * 256 = 272 at e_s = -8: halfway between 256 (m=0) and 288 (m=1) -> 256
+    c, s = O.mx_quantize(block([1.0, 1.0625])[None])
+    assert s[0, 0] == 119 and c[0, 1] == 0x78
+    # subnormal: 2^-16 relative to 2^-8 is 2^-8 = 2 * 2^-9 -> code 0x02
     c, s = O.mx_quantize(block([1.0, 2.0 ** -16])[None])
     assert c[0, 1] == 0x02
     # scale clamp at the bottom of E8M0
     c, s = O.mx_quantize(block([2.0 ** -130])[None])
     assert s[0, 0] == 0
+    # scale clamp at the top of E8M0 (code 254): 2^140 / 2^127 = 8192 saturates at 448
+    c, s = O.mx_quantize(block([2.0 ** 140, -(2.0 ** 140)])[None])
+    assert s[0, 0] == 254 and c[0, 0] == 0x7E and c[0, 1] == 0xFE
+
+
+def test_scale_is_smallest_unclipped_power_of_two():
+    """The block exponent is the smallest integer e with amax / 2^e <= 448,
+    found here by a search over e, on magnitudes spread over the whole range,
+    exact powers of two, 448 times powers of two and their neighbours."""
+    rng = np.random.default_rng(3)
+    a = np.exp(rng.uniform(-80, 80, size=4000))
+    pw = np.ldexp(1.0, np.arange(-100, 100))
+    edge = np.concatenate([pw, 448 * pw, 1.75 * pw])
+    a = np.concatenate([a, edge, np.nextafter(edge, 0), np.nextafter(edge, np.inf)])
+    got = O.mx_scale_exponent(a)
+    for v, e in zip(a, got):
+        want = -200
+        while v / 2.0 ** want > 448.0:
+            want += 1
+        assert e == want, (v, e, want)
+        assert v / 2.0 ** e <= 448.0 and v / 2.0 ** (e - 1) > 448.0
 
 
 def test_exhaustive_bf16_against_torch_cast():
@@ -69,9 +102,8 @@ def test_round_trip_error_bound(axis):
     scaled = np.abs(v) / sc
     _, ex = np.frexp(np.maximum(scaled, 2.0 ** -6))
     half_q = np.ldexp(1.0, np.maximum(ex - 1, -6) - 4) * sc
-    sat = scaled > 448
-    assert np.all(np.abs(back - v)[~sat] <= half_q[~sat])
-    assert np.all(np.abs(back - v)[sat] <= 64 * sc[sat])
+    assert np.all(scaled <= 448)           # the block scale never clips
+    assert np.all(np.abs(back - v) <= half_q)
 
 
 def test_round_trip_from_primitives_matches_codes():
