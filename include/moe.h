@@ -185,10 +185,13 @@ moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_per
 /* The two halves of moe_expert_ffn, for callers that schedule or time them
  * separately (same contract, same workspace which=2):
  *   moe_expert_gate_up: h[r] = SiLU(a W_g[e]^T) * (a W_u[e]^T), h [R][I] in
- *     the activation type (MOE_MXFP8: E4M3 [R][I] with h_scale E8M0
- *     [R][I/32], quantized in the epilogue; blog post "MXFP8 support":
- *     activation quantization fused into the SwiGLU);
- *   moe_expert_down: o_perm[r] = h[r] W_d[e]^T.
+ *     the activation type (MOE_MXFP8: E4M3 [R][I] quantized in the epilogue
+ *     along I, blog post "MXFP8 support": activation quantization fused into
+ *     the SwiGLU; h_scale E8M0 slab-major [I/128][R][4], the layout of
+ *     moe_quantize_mxfp8 axis 2: byte (c/128, r, (c/32) % 4) is the scale of
+ *     the block of row r holding column c);
+ *   moe_expert_down: o_perm[r] = h[r] W_d[e]^T (MOE_MXFP8: h and h_scale in
+ *     exactly that layout, e.g. moe_quantize_mxfp8(axis 2) of a bf16 h).
  * Blog post, "Scheduling the overlaps": up/gate projections with SwiGLU,
  * then the down projection, per expert. */
 moe_status moe_expert_gate_up(const moe_dims* dims, moe_prec prec, const void* x_perm, const uint8_t* x_perm_scale,
@@ -284,9 +287,11 @@ moe_status moe_trace_events(int which, void* const* events, int n);
  *   (c/128, r, (c/32) % 4) for the block of row r holding column c (the four
  *   block scales of one row's 128-column slab form one dword, and a slab's
  *   dwords are contiguous over the rows).
- * Per block: e = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for
- * an all-zero block); element = v / 2^e rounded to nearest-even E4M3,
- * saturating at +-448, sign kept; scale byte = e + 127. */
+ * Per block: e = the smallest integer with max |v| / 2^e <= 448 (the finest
+ * power-of-two scale that leaves the block maximum unclipped), clamped to
+ * [-127, 127] (-127 for an all-zero block); element = v / 2^e rounded to
+ * nearest-even E4M3, sign kept; scale byte = e + 127.  Every MX operand the
+ * library quantizes itself (tokens, h, gradients) uses the same rule. */
 moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t cols, int axis, uint8_t* dst,
                               uint8_t* scale, void* stream);
 

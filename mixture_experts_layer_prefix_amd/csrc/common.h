@@ -26,8 +26,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-// 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp; outputs are
-// rounded to bf16 or E4M3 afterwards).
 // A 64-bit value that is the same in every lane, held in scalar registers.
 __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -35,6 +33,8 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp; outputs are
+// rounded to bf16 or E4M3 afterwards).
 __device__ __forceinline__ float sigmoid_f32(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
@@ -72,15 +72,17 @@ __device__ __forceinline__ float half_sum32(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// MX (OCP MX v1.0) E4M3 elements with one E8M0 scale per 32 values: the block
-// exponent is floor(log2 max|v|) - 8 clamped to [-127, 127] (-127 for an
-// all-zero block); elements are v / 2^e rounded to nearest-even E4M3,
-// saturating at +-448, sign kept.
+// MX (OCP MX v1.0 format) E4M3 elements with one E8M0 scale per 32 values:
+// the block exponent is the smallest e with max|v| / 2^e <= 448 (the finest
+// power-of-two scale at which the block maximum is an E4M3 value without
+// clipping), clamped to [-127, 127] (-127 for an all-zero block); elements
+// are v / 2^e rounded to nearest-even E4M3, sign kept.
 // ---------------------------------------------------------------------------
 // E4M3 code of s, round to nearest even, saturating at +-448: the clamp to
 // +-448 followed by gfx950's OCP E4M3 conversion, which rounds to nearest
 // even (bit-identical to that definition for every fp32 input of magnitude
-// below 512, checked exhaustively on the hardware; larger inputs saturate).
+// below 512, checked exhaustively on the hardware).  With the block scale
+// above every scaled element is at most 448, so the clamp never acts.
 __device__ __forceinline__ float e4m3_clamp(float s) { return __builtin_amdgcn_fmed3f(s, -448.0f, 448.0f); }
 __device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
   const float c = e4m3_clamp(s);
@@ -92,11 +94,20 @@ __device__ __forceinline__ uint32_t e4m3x4_rne_sat(float a, float b, float c, fl
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
 }
 
-// Block exponent (unbiased) of a 32-value block from its max magnitude.
+// Block exponent (unbiased) from the fp32 bit pattern of the block's largest
+// magnitude (sign bit clear).  floor(log2 amax) - 8 places amax / 2^e in
+// [256, 512); a mantissa above 1.75 (field above 0x600000) would land past
+// 448, so the exponent is one larger there.  Zero and fp32 subnormals clamp
+// to -127; finite fp32 values never reach the upper clamp.
+__device__ __forceinline__ int mx_block_exp_bits(uint32_t abits) {
+  const int e = (int)(abits >> 23) - 135 + ((abits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(e, -127);
+}
+
+// Block exponent of a 32-value block from its max magnitude.
 __device__ __forceinline__ int mx_block_exp(float amax) {
   if (!(amax > 0.0f)) return -127;
-  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-  return max(ef - 127 - 8, -127);
+  return mx_block_exp_bits(__float_as_uint(amax));
 }
 
 // 2^-e as an fp32 (exact for e in [-127, 126]).

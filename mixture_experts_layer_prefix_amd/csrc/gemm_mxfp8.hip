@@ -158,10 +158,10 @@ __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) 
 // (lane & 31) of a lane half: returns the E4M3 code of this lane's value and
 // the block's E8M0 byte in *scale (all lanes take part).
 __device__ __forceinline__ uint32_t mx_lane_quant(float v, uint32_t* scale) {
-  // Block maximum magnitude as a bit pattern; its exponent field gives the
-  // block exponent (zero and fp32 subnormals clamp to -127).
+  // Block maximum magnitude as a bit pattern; its exponent and mantissa
+  // fields give the block exponent (zero and fp32 subnormals clamp to -127).
   const uint32_t amax = half_max32_u(__float_as_uint(v) & 0x7FFFFFFFu);
-  const int e = max((int)(amax >> 23) - 135, -127);
+  const int e = mx_block_exp_bits(amax);
   *scale = (uint32_t)(e + 127);
   return e4m3_rne_sat(v * mx_inv_scale(e));
 }
@@ -658,7 +658,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         part += dpp_f32<0xB1>(part);
         part += dpp_f32<0x4E>(part);
         if (!ok) continue;
-        const int eg = max((int)(mg >> 23) - 135, -127), eu = max((int)(mu >> 23) - 135, -127);
+        const int eg = mx_block_exp_bits(mg), eu = mx_block_exp_bits(mu);
         const float ig = mx_inv_scale(eg), iu = mx_inv_scale(eu);
 
         uint8_t* qrow = p.dguq + rowoff + col;
@@ -691,7 +691,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
           m0b = max(m0b, (x[q] << 16) & 0x7FFFFFFFu);
           m1b = max(m1b, x[q] & 0x7FFF0000u);
         }
-        const int e0 = max((int)(m0b >> 23) - 135, -127), e1 = max((int)(m1b >> 23) - 135, -127);
+        const int e0 = mx_block_exp_bits(m0b), e1 = mx_block_exp_bits(m1b);
         const float i0s = mx_inv_scale(e0), i1s = mx_inv_scale(e1);
         u32x4 c0[2], c1[2];
 #pragma unroll
@@ -721,7 +721,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
             hm0 = max(hm0, (x[q] << 16) & 0x7FFFFFFFu);
             hm1 = max(hm1, x[q] & 0x7FFF0000u);
           }
-          const int f0 = max((int)(hm0 >> 23) - 135, -127), f1 = max((int)(hm1 >> 23) - 135, -127);
+          const int f0 = mx_block_exp_bits(hm0), f1 = mx_block_exp_bits(hm1);
           const float j0s = mx_inv_scale(f0), j1s = mx_inv_scale(f1);
 #pragma unroll
           for (int w = 0; w < 8; ++w) {

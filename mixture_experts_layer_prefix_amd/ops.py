@@ -131,7 +131,8 @@ def expert_gate_up(x_perm, x_perm_scale, offsets, weights: Weights, dims: Dims, 
     dev = offsets.device
     if prec == "mxfp8":
         h = torch.empty(dims.R, dims.I, dtype=torch.uint8, device=dev)
-        h_scale = torch.empty(dims.R, dims.I // 32, dtype=torch.uint8, device=dev)
+        # slab-major scales [I/128][R][4] (moe_quantize_mxfp8 axis 2 layout)
+        h_scale = torch.empty(dims.I // 128, dims.R, 4, dtype=torch.uint8, device=dev)
     else:
         h = torch.empty(dims.R, dims.I, dtype=_act_dtype(prec), device=dev)
         h_scale = None

@@ -5,9 +5,10 @@ gradient.  Bars: max|d|/max|ref| <= 2e-2 per tensor; experts without rows
 get exact zero gradients; repeated runs are bitwise identical.
 
 Small shapes are checked in full against the oracle's layer backward; the
-DeepSeek-V3-shaped layer on sampled tokens (dx, dg) and on sampled
-intermediate columns of three experts' weight gradients (every row of those
-experts), each sample exact per-element math."""
+DeepSeek-V3-shaped layer on sampled tokens (dx, dg), on the router weight
+gradient rows of two ragged experts, and on sampled intermediate columns of
+every expert's weight gradients (every row of each expert) and of the shared
+expert's, each sample exact per-element math."""
 import numpy as np
 import pytest
 
@@ -135,52 +136,61 @@ def test_dsv3_backward_sampled():
     check_backward_sampled(gen.get_config("c3a"))
 
 
-def check_backward_sampled(D):
-    """Sampled tokens' dx and dL/dg, sampled intermediate columns of three
-    experts' weight gradients (every row of those experts) and of the shared
-    expert's, each exact per-element oracle math."""
+def check_backward_sampled(D, ntok=128, seed=11):
+    """Two backward runs bitwise equal; dx and dL/dg of ntok seeded tokens
+    plus every token of the smallest non-empty expert and of one expert with
+    64 to 256 rows; the router weight gradient rows of those experts; the
+    weight gradients of every non-empty expert on 16 seeded intermediate
+    columns each (all of the expert's rows), one error per tensor; the shared
+    expert's weight gradients on sampled columns (all tokens).  Each sample is
+    exact per-element oracle math."""
+    import mixture_experts_layer_prefix_amd as M
+    from tests.moe_parity import gather_wgrad, pick_tokens, router_wgrad_rows, sampled_eval, wgrad_columns
     say("[case] %s backward sampled" % D.name, D)
     p, t, md, wb, dy, routing, dx, grads = forward_and_backward(D)
+    dx2, grads2 = M.layer_backward(dy, t["x"], wb, routing, md, D.prec, router_grad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dx2, dx)
+    for n in grads:
+        assert torch.equal(grads2[n], grads[n]), n
+    del dx2, grads2
     hp = HostProblem(D)
     ref_rt = hp.routing()
     idx, g = ref_rt["topk_idx"], ref_rt["topk_w"]
     assert np.array_equal(to_np(routing["topk_idx"]), idx)
-    rng = np.random.default_rng(11)
-    tokens = np.sort(rng.choice(D.T, size=12, replace=False))
-    dx_ref, dg_ref = sampled_backward(hp, tokens, idx, g)
-    e_dx = rel_err(to_np(dx[torch.as_tensor(tokens)]), dx_ref)
-    e_dg = rel_err(to_np(grads["dtopk_w"][torch.as_tensor(tokens)]), dg_ref)
-    say("   sampled tokens: dx %.3e dg %.3e" % (e_dx, e_dg))
-    assert e_dx <= TOL["bf16"] and e_dg <= TOL["bf16"]
-    counts, offsets, row_token = ref_rt["counts"], ref_rt["offsets"], ref_rt["row_token"]
-    nz = np.nonzero(counts)[0]
-    picks = sorted({int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
-                    int(nz[np.argsort(counts[nz])[len(nz) // 2]])})
-    for e in picks:
-        rows = np.arange(offsets[e], offsets[e + 1])
-        toks = row_token[rows]
-        gr = np.array([g[tk][list(idx[tk]).index(e)] for tk in toks])
-        cols = np.sort(rng.choice(D.I, size=16, replace=False))
-        dWg, dWu, dWd = expert_wgrad_columns(hp, e, toks, gr, cols)
-        c = torch.as_tensor(cols)
-        eg = rel_err(to_np(grads["dw_gate"][e][c]), dWg)
-        eu = rel_err(to_np(grads["dw_up"][e][c]), dWu)
-        ed = rel_err(to_np(grads["dw_down"][e][:, c]), dWd)
-        say("   expert %d (%d rows): dw_gate %.3e dw_up %.3e dw_down %.3e" % (e, len(rows), eg, eu, ed))
-        assert max(eg, eu, ed) <= TOL["bf16"]
+    tokens, experts = pick_tokens(ref_rt, D.T, ntok, seed)
+    res = sampled_eval(hp, tokens, idx, g, backward=True)
+    tk = torch.as_tensor(tokens, device=dx.device)
+    errs = {"dx": rel_err(to_np(dx[tk]), res["dx"]), "dtopk_w": rel_err(to_np(grads["dtopk_w"][tk]), res["dg"])}
+    ex = router_wgrad_rows(hp, experts, tokens, idx, res["dl"])
+    errs["dw_router"] = rel_err(to_np(grads["dw_router"][torch.as_tensor(experts, device=dx.device)]), ex)
+    samples = wgrad_columns(hp, ref_rt, 16, seed)
+    gw = gather_wgrad(grads, samples)
+    for n, lst in samples.items():
+        errs[n] = rel_err(gw[n], np.concatenate([v[2].ravel() for v in lst]))
+        per = []
+        for e, cols, ev, _ in lst:
+            c = torch.as_tensor(cols, device=dx.device)
+            gv = to_np(grads[n][e][:, c] if n == "dw_down" else grads[n][e][c])
+            per.append((rel_err(gv, ev), e, int(ref_rt["counts"][e])))
+        say("   %s worst expert: %.3e (expert %d, %d rows)" % ((n,) + max(per)))
+    counts = ref_rt["counts"]
     empty = np.nonzero(counts == 0)[0]
     if len(empty):
-        assert torch.count_nonzero(grads["dw_down"][int(empty[0])]) == 0
-    if not D.S:
-        return
-    # shared-expert weight gradients on sampled intermediate columns (all tokens)
-    cols = np.sort(rng.choice(D.Is, size=4, replace=False))
-    wg, wu, wd = shared_weights(hp.p, D)
-    x_all = hp.p.host("x")
-    dy_all = hp.p.host("dy")
-    _, dWg, dWu, dWd, _, _ = O.ffn_backward(x_all, wg[cols], wu[cols], wd[:, cols], dy_all)
-    c = torch.as_tensor(cols)
-    es = max(rel_err(to_np(grads["dws_gate"][0][c]), dWg), rel_err(to_np(grads["dws_up"][0][c]), dWu),
-             rel_err(to_np(grads["dws_down"][0][:, c]), dWd))
-    say("   shared expert columns %s: %.3e" % (cols, es))
-    assert es <= TOL["bf16"]
+        sel = torch.as_tensor(empty, device=dx.device)
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            assert torch.count_nonzero(grads[n][sel]) == 0, n
+    if D.S:
+        # shared-expert weight gradients on sampled intermediate columns (all tokens)
+        rng = np.random.default_rng(seed + 1)
+        cols = np.sort(rng.choice(D.Is, size=4, replace=False))
+        wg, wu, wd = shared_weights(hp.p, D)
+        _, dWg, dWu, dWd, _, _ = O.ffn_backward(hp.p.host("x"), wg[cols], wu[cols], wd[:, cols], hp.p.host("dy"))
+        c = torch.as_tensor(cols, device=dx.device)
+        errs["dws_gate"] = rel_err(to_np(grads["dws_gate"][0][c]), dWg)
+        errs["dws_up"] = rel_err(to_np(grads["dws_up"][0][c]), dWu)
+        errs["dws_down"] = rel_err(to_np(grads["dws_down"][0][:, c]), dWd)
+    say("   %d sampled tokens (experts %s with %s rows): %s" % (
+        len(tokens), experts, [int(counts[e]) for e in experts], ", ".join("%s %.2e" % kv for kv in errs.items())))
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)

@@ -141,18 +141,22 @@ def test_c1_full_oracle():
     assert e <= TOL[D.prec]
 
 
-@pytest.mark.parametrize("cfg,nsample", [("c2", 48), ("c3a", 24), ("c3b", 16)])
+@pytest.mark.parametrize("cfg,nsample", [("c2", 512), ("c3a", 512), ("c3b", 512)])
 def test_large_config_sampled(cfg, nsample):
     """Full routing and permutation; outputs on a seeded token sample."""
     check_forward_sampled(gen.get_config(cfg), nsample)
 
 
-def check_forward_sampled(D, nsample):
+def check_forward_sampled(D, nsample, seed=1234):
     """Routing and permutation bit-exact on every token, bitwise-deterministic
-    output, and the output of sampled tokens (plus every token of the
-    smallest non-empty expert) against the oracle.  MXFP8 layers are quantized
-    once before the two runs."""
+    output, and the output of sampled tokens against the oracle: nsample
+    seeded tokens plus every token of the smallest non-empty expert and of
+    one expert with 64 to 256 rows.  MXFP8 layers are quantized once before
+    the two runs; their sample is also held against the quantization-aware
+    model (3e-2: the kernels' own error) and the stated 6e-2 bound against
+    the oracle."""
     import mixture_experts_layer_prefix_amd as M
+    from tests.moe_parity import check_mx_bound, pick_tokens, sampled_eval
     cfg = D.name
     say("[case] sampled", cfg, D)
     p, t, md, w = device_problem(D)
@@ -161,24 +165,25 @@ def check_forward_sampled(D, nsample):
     y, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
     y2, _ = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
     assert torch.equal(y, y2), "forward is not bitwise deterministic"
+    del y2
     hp = HostProblem(D)
     ref = hp.routing()
     check_routing(to_np(routing["logits"]), to_np(routing["topk_idx"]), to_np(routing["topk_w"]), ref, D.k)
     for n, r in (("expert_counts", "counts"), ("expert_offsets", "offsets"), ("row_token", "row_token"),
                  ("token_row", "token_row")):
         assert np.array_equal(to_np(routing[n]), ref[r]), n
-    rng = np.random.default_rng(1234)
-    tokens = sorted(rng.choice(D.T, size=nsample, replace=False).tolist())
-    # include every token of the smallest non-empty expert (ragged tail) when
-    # it is small
-    nz = np.nonzero(ref["counts"])[0]
-    e_small = int(nz[np.argmin(ref["counts"][nz])])
-    lo, hi = ref["offsets"][e_small], ref["offsets"][e_small + 1]
-    if hi - lo <= 64:
-        tokens = sorted(set(tokens) | set(ref["row_token"][lo:hi].tolist()))
-    ys = hp.sampled_forward(tokens, ref["topk_idx"], ref["topk_w"])
-    got = to_np(y[torch.tensor(tokens, device="cuda")])
-    e = rel_err(got, ys)
-    say("   %s sampled %d tokens: rel err %.3e rms %.3e; experts empty %d, max rows %d" % (
-        cfg, len(tokens), e, rms_rel(got, ys), int(np.sum(ref["counts"] == 0)), int(ref["counts"].max())))
-    assert e <= TOL[D.prec]
+    tokens, experts = pick_tokens(ref, D.T, nsample, seed)
+    mx = D.prec == "mxfp8"
+    res = sampled_eval(hp, tokens, ref["topk_idx"], ref["topk_w"], backward=False, mx=mx)
+    got = to_np(y[torch.as_tensor(tokens, device=y.device)])
+    e = rel_err(got, res["y"])
+    say("   %s sampled %d tokens (experts %s with %s rows): rel err %.3e rms %.3e; experts empty %d, max rows %d" % (
+        cfg, len(tokens), experts, [int(ref["counts"][x]) for x in experts], e, rms_rel(got, res["y"]),
+        int(np.sum(ref["counts"] == 0)), int(ref["counts"].max())))
+    if not mx:
+        assert e <= TOL[D.prec]
+        return
+    e_q, e_fmt = rel_err(got, res["y_q"]), rel_err(res["y_q"], res["y"])
+    say("   vs quantization-aware model %.3e (model vs oracle %.3e)" % (e_q, e_fmt))
+    assert e_q <= 3e-2
+    check_mx_bound({"y": (e, e_fmt)}, cfg)

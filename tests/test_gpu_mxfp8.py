@@ -1,13 +1,16 @@
 """GPU parity of the MXFP8 forward: the quantizer and the quantizing
 dispatch bit-exact against the oracle's MX quantizer; routed-expert MXFP8
-GEMMs and the whole layer within 6e-2 (max|d|/max|ref|) of the float64
-oracle of the unquantized layer."""
+GEMMs and the whole layer within 3e-2 of a quantization-aware float64 model
+(the oracle's quantizer at the path's quantization points, exact arithmetic
+otherwise: the kernels' own error) and held to the stated 6e-2
+(max|d|/max|ref|) against the float64 oracle of the unquantized layer, an
+expected failure only where MX rounding alone exceeds it."""
 import numpy as np
 import pytest
 
 import gen
 from oracle import moe_oracle as O
-from tests.moe_parity import TOL, HostProblem, device_problem, rel_err, rms_rel, to_np
+from tests.moe_parity import TOL, HostProblem, check_mx_bound, device_problem, rel_err, rms_rel, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -110,32 +113,61 @@ def test_small_mxfp8_layer(name):
     say("   mxfp8 y vs exact %.3e (rms %.3e); vs MX-rounded operands: y %.3e, o_perm %.3e (o_perm vs exact %.3e)"
         % (e_y, rms_rel(to_np(y), ref["y"]), e_qy, e_qo, e_o))
     assert e_qo <= 3e-2 and e_qy <= 3e-2
-    # Against the exact layer: the stated 6e-2 bound, unless the MX rounding of
-    # the operands alone already exceeds it on this shape (E4M3 leaves ~8% RMS
-    # relative error on a routed-only output; the bf16 shared expert dilutes
-    # it on the DSV3 shape, where the bound holds, see test_c4_forward_sampled).
-    e_fmt = rel_err(yq, ref["y"])
-    assert e_y <= max(TOL["mxfp8"], e_fmt + 1e-2), (e_y, e_fmt)
     y2, _ = M.layer_forward(t["x"], wq, md, "mxfp8", bias=t["bias"])
     assert torch.equal(y, y2)
+    # Against the exact layer: the stated 6e-2 bound (an expected failure
+    # where MX rounding of the operands alone already exceeds it).
+    check_mx_bound({"y": (e_y, rel_err(yq, ref["y"])), "o_perm": (e_o, rel_err(oq, ref["o_perm"]))}, name)
+
+
+def test_expert_down_takes_quantizer_layout():
+    """moe_expert_down reads h and h_scale in the layout of
+    moe_quantize_mxfp8(axis 2) (scales slab-major [I/128][R][4]), the layout
+    moe_expert_gate_up writes: a bf16 h from the generator quantized by that
+    entry point gives the oracle's product of the dequantized operands to
+    fp32-accumulation accuracy; and the h_scale written by
+    moe_expert_gate_up, read in that layout, dequantizes h to within the
+    MX rounding of the exact SwiGLU output."""
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.Dims("mx_down_layout", 300, 256, 8, 2, 384, 0, 0, "mxfp8", 0.0)
+    say("[case] h layout", D)
+    ref = HostProblem(D).oracle_forward()
+    p, t, md, w = device_problem(D)
+    wq = M.prepare_mxfp8(w, md)
+    off = torch.as_tensor(ref["offsets"], device="cuda")
+    # h from the generator's dy stream ([T][d] reshaped to [R][I] rows)
+    hb = gen.Problem(gen.Dims("hsrc", D.R, D.I, 1, 1, 128, 0, 0, "bf16", 0.0)).device("dy")
+    hq, hs = M.quantize_mxfp8(hb, 2)
+    o = M.expert_down(hq, hs, off, wq, md, "mxfp8")
+    h_host = gen.Problem(gen.Dims("hsrc", D.R, D.I, 1, 1, 128, 0, 0, "bf16", 0.0)).host("dy")
+    hd = mx_round(h_host)
+    want = np.zeros((D.R, D.d))
+    for e in range(D.E):
+        lo, hi = ref["offsets"][e], ref["offsets"][e + 1]
+        want[lo:hi] = hd[lo:hi] @ mx_round(p.host_expert("w_down", e)).T
+    e_o = rel_err(to_np(o), want)
+    say("   down of quantizer-made h: %.3e" % e_o)
+    assert e_o <= 1e-2   # bf16 output rounding (2^-9) and fp32 accumulation only
+    # the gate/up epilogue's h and scales decode, in that layout, to the exact
+    # SwiGLU output within MX rounding
+    counts, offsets, row_token, token_row, xq, xs = M.permute(torch.as_tensor(ref["topk_idx"], device="cuda"),
+                                                              t["x"], md, "mxfp8")
+    h, h_scale = M.expert_gate_up(xq, xs, offsets, wq, md, "mxfp8")
+    assert tuple(h_scale.shape) == (D.I // 128, D.R, 4)
+    sc = to_np(h_scale).transpose(1, 0, 2).reshape(D.R, D.I // 32)
+    h_dec = O.mx_dequantize(to_np(h), sc, axis=-1)
+    a = p.host("x")[ref["row_token"]]
+    h_exact = np.zeros((D.R, D.I))
+    for e in range(D.E):
+        lo, hi = ref["offsets"][e], ref["offsets"][e + 1]
+        h_exact[lo:hi] = O.swiglu_ffn(a[lo:hi], *(p.host_expert(n, e) for n in ("w_gate", "w_up", "w_down")))[3]
+    e_h = rel_err(h_dec, h_exact)
+    say("   gate/up h decoded slab-major vs exact SwiGLU: %.3e" % e_h)
+    assert e_h <= 1e-1   # three MX roundings (x, weights, h); a wrong layout gives O(1)
 
 
 def test_c4_forward_sampled():
-    import mixture_experts_layer_prefix_amd as M
-    D = gen.get_config("c4")
-    say("[case] c4 forward sampled", D)
-    p, t, md, w = device_problem(D)
-    wq = M.prepare_mxfp8(w, md)
-    # bf16 weights no longer needed on the device
-    y, routing = M.layer_forward(t["x"], wq, md, "mxfp8", bias=t["bias"])
-    hp = HostProblem(D)
-    ref = hp.routing()
-    assert np.array_equal(to_np(routing["topk_idx"]), ref["topk_idx"])
-    assert np.array_equal(to_np(routing["row_token"]), ref["row_token"])
-    rng = np.random.default_rng(99)
-    tokens = sorted(rng.choice(D.T, size=16, replace=False).tolist())
-    ys = hp.sampled_forward(tokens, ref["topk_idx"], ref["topk_w"])
-    got = to_np(y[torch.tensor(tokens, device="cuda")])
-    e = rel_err(got, ys)
-    say("   c4 sampled %d tokens: rel err %.3e rms %.3e" % (len(tokens), e, rms_rel(got, ys)))
-    assert e <= TOL["mxfp8"]
+    """The DeepSeek-V3-shaped MXFP8 forward (T=16384, Zipf-skewed routing)
+    on 512 sampled tokens plus the ragged experts' tokens."""
+    from tests.test_gpu_forward import check_forward_sampled
+    check_forward_sampled(gen.get_config("c4"), 512, seed=99)

@@ -9,17 +9,21 @@ axis; the shared expert and the router stay bf16.  Two references:
     the routed-row axis in 32-row blocks of one expert) and the path's bf16
     storage of G, U and of the weight-gradient operands, exact arithmetic
     otherwise.
-Bars per tensor (max|d|/max|ref|): against the quantization-aware model
-3e-2; against the oracle the stated 6e-2 bound, or the format's own error
-(the quantization-aware model against the oracle) plus 1e-2 where MX
-rounding alone exceeds 6e-2 on a small shape.  Weight gradients of experts
-without rows are exactly zero and repeated runs are bitwise identical."""
+Bars per tensor (max|d|/max|ref|): 3e-2 against the quantization-aware model
+(the kernels' own error: fp32 accumulation and rounding decisions at
+boundaries); the stated 6e-2 against the oracle, where a tensor over it is
+an expected failure (reported, not passed) only if the quantization-aware
+model is itself over it, i.e. E4M3 rounding alone exceeds the bound.  Weight
+gradients of experts without rows are exactly zero and repeated runs are
+bitwise identical."""
 import numpy as np
 import pytest
 
 import gen
 from oracle import moe_oracle as O
-from tests.moe_parity import TOL, HostProblem, bf16r, device_problem, qd, qd_rows, rel_err, shared_weights, to_np
+from tests.moe_parity import (TOL, HostProblem, bf16r, check_mx_bound, device_problem, gather_wgrad, mx_model_expert,
+                              pick_tokens, qd, qd_rows, rel_err, router_wgrad_rows, sampled_eval, shared_weights,
+                              to_np, wgrad_columns)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -46,41 +50,6 @@ def say(*a):
     print(*a, flush=True)
 
 
-def token_grads_q(x, dy, gr, wg, wu, wd):
-    """Quantization-aware input gradients dA and router-weight gradients dg of
-    one expert's rows (x, dy rows, router weights gr)."""
-    G = bf16r(qd(x) @ qd(wg).T)
-    U = bf16r(qd(x) @ qd(wu).T)
-    dHp = qd(dy) @ qd(wd.T).T
-    h = O.silu(G) * U
-    dh = gr[:, None] * dHp
-    dG = dh * U * O.silu_grad(G)
-    dU = dh * O.silu(G)
-    return qd(dG) @ qd(wg.T).T + qd(dU) @ qd(wu.T).T, np.sum(dHp * h, axis=1)
-
-
-def expert_grads_q(x, dy, gr, wg, wu, wd, with_da=True):
-    """Quantization-aware gradients of one expert over its rows (x, dy rows,
-    router weights gr): dA rows (None unless with_da), dg per row, dW_gate,
-    dW_up, dW_down.  Without dA the weights may be restricted to a subset of
-    intermediate columns (every other step is per column)."""
-    G = bf16r(qd(x) @ qd(wg).T)
-    U = bf16r(qd(x) @ qd(wu).T)
-    dHp = qd(dy) @ qd(wd.T).T
-    h = O.silu(G) * U
-    dg = np.sum(dHp * h, axis=1)
-    dh = gr[:, None] * dHp
-    dG = dh * U * O.silu_grad(G)
-    dU = dh * O.silu(G)
-    dA = qd(dG) @ qd(wg.T).T + qd(dU) @ qd(wu.T).T if with_da else None
-    # the weight-gradient operands pass through bf16 storage before their
-    # token-axis quantization (w h, dG, dU; x and dY are bf16 already)
-    dWd = qd_rows(dy).T @ qd_rows(bf16r(gr[:, None] * h))
-    dWg = qd_rows(bf16r(dG)).T @ qd_rows(x)
-    dWu = qd_rows(bf16r(dU)).T @ qd_rows(x)
-    return dA, dg, dWg, dWu, dWd
-
-
 def backward_q(hp, fw):
     """Quantization-aware model of the whole MXFP8 backward (small shapes)."""
     D, p = hp.dims, hp.p
@@ -97,8 +66,11 @@ def backward_q(hp, fw):
         if hi == lo:
             continue
         toks = row_token[lo:hi]
-        r = expert_grads_q(x[toks], dy[toks], g_row[lo:hi], *hp.expert(e))
-        dA[lo:hi], dg_row[lo:hi], out["w_gate"][e], out["w_up"][e], out["w_down"][e] = r
+        wg, wu, wd = hp.expert(e)
+        m = mx_model_expert(x[toks], dy[toks], g_row[lo:hi], wg, wu, wd, wgrad=False)
+        w = mx_model_expert(x[toks], dy[toks], g_row[lo:hi], wg, wu, wd)
+        dA[lo:hi], dg_row[lo:hi] = m["dA"], m["dg"]
+        out["w_gate"][e], out["w_up"][e], out["w_down"][e] = w["dWg"], w["dWu"], w["dWd"]
     dx = np.zeros((D.T, D.d))
     for j in range(D.k):
         dx += dA[token_row[:, j]]
@@ -115,42 +87,6 @@ def backward_q(hp, fw):
     res["dtopk_w"] = dg
     res["dw_router"] = dl.T @ x
     return res
-
-
-def sampled_backward_q(hp, tokens, idx, g):
-    """Quantization-aware dx (with the shared expert and router terms) and dg
-    of selected tokens given their routing; experts in parallel threads
-    (numpy releases the interpreter lock inside its kernels)."""
-    from concurrent.futures import ThreadPoolExecutor
-    D, p = hp.dims, hp.p
-    x, dy = p.host_rows("x", tokens), p.host_rows("dy", tokens)
-    pairs = {}
-    for i, t in enumerate(tokens):
-        for j in range(D.k):
-            pairs.setdefault(int(idx[t, j]), []).append((i, j, float(g[t, j])))
-
-    def one(e):
-        rows = [i for i, _, _ in pairs[e]]
-        gr = np.array([gg for _, _, gg in pairs[e]])
-        wts = tuple(p.host_expert(n, e) for n in ("w_gate", "w_up", "w_down"))
-        return e, token_grads_q(x[rows], dy[rows], gr, *wts)
-
-    dx = np.zeros((len(tokens), D.d))
-    dg = np.zeros((len(tokens), D.k))
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        for e, (dA, dge) in ex.map(one, sorted(pairs)):
-            for q, (i, j, _) in enumerate(pairs[e]):
-                dx[i] += dA[q]
-                dg[i, j] = dge[q]
-    for s in range(D.S):
-        dx += O.ffn_backward(x, *shared_weights(p, D, s), dy)[0]
-    gt = np.asarray(g, np.float64)[tokens]
-    dl = gt * (dg - np.sum(gt * dg, axis=1, keepdims=True))
-    wr = p.host("w_router")
-    for i, t in enumerate(tokens):
-        for j in range(D.k):
-            dx[i] += dl[i, j] * wr[int(idx[t, j])]
-    return dx, dg
 
 
 def run_backward(D):
@@ -193,7 +129,7 @@ def test_small_mxfp8_backward(name):
     for n in names:
         errs[n] = (rel_err(got[n], qref[n]), rel_err(got[n], exact[n]), rel_err(qref[n], exact[n]))
         say("   %-9s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)" % ((n,) + errs[n]))
-    bad = [n for n, (e_q, e_x, e_fmt) in errs.items() if e_q > TOL_Q or e_x > max(TOL["mxfp8"], e_fmt + 1e-2)]
+    bad = [n for n, (e_q, e_x, e_fmt) in errs.items() if e_q > TOL_Q]
     for n in bad:
         if n.startswith("dw_") and n != "dw_router":
             per = [(rel_err(got[n][e], qref[n][e]), e, int(exact["fw"]["counts"][e])) for e in range(D.E)]
@@ -215,6 +151,11 @@ def test_small_mxfp8_backward(name):
     assert np.array_equal(to_np(dx3), got["dx"])
     for n, v in grads3.items():
         assert np.array_equal(to_np(v), got[n]), n
+    # the shared expert runs in bf16: its gradients hold the bf16 bound
+    for n in ("dws_gate", "dws_up", "dws_down"):
+        if n in errs:
+            assert errs[n][1] <= TOL["bf16"], (n, errs[n][1])
+    check_mx_bound({n: (e_x, e_fmt) for n, (e_q, e_x, e_fmt) in errs.items()}, name)
 
 
 def test_c4_backward_sampled():
@@ -222,54 +163,74 @@ def test_c4_backward_sampled():
     check_backward_sampled(gen.get_config("c4"))
 
 
-def check_backward_sampled(D, ntok=6):
-    """Sampled tokens' dx and dL/dg, and sampled intermediate columns of the
-    weight gradients of the largest, smallest and median non-empty experts
-    (every row of those experts), each against the oracle and the
-    quantization-aware model."""
+def check_backward_sampled(D, ntok=128, seed=12):
+    """Two backward runs bitwise equal; then, against the oracle and the
+    quantization-aware model: dx and dL/dg of ntok seeded tokens plus every
+    token of the smallest non-empty expert and of one expert with 64 to 256
+    rows; the router weight gradient rows of those experts; the weight
+    gradients of every non-empty expert on 16 seeded intermediate columns
+    each (all of the expert's rows), one error per tensor; the shared
+    expert's weight gradients on sampled columns (bf16 bound)."""
     say("[case] %s backward sampled" % D.name, D)
     got, (plan, dy, t, wb, routing) = run_backward(D)
-    del plan, dy, t, wb
+    dx2, grads2 = plan.run(dy, t["x"], wb, routing)
+    torch.cuda.synchronize()
+    assert torch.equal(dx2, got["dx"]), "dx differs between two runs"
+    for n, v in grads2.items():
+        assert torch.equal(v, got[n]), "%s differs between two runs" % n
+    del plan, dy, t, wb, dx2, grads2
     hp = HostProblem(D)
     ref_rt = hp.routing()
     idx, g = ref_rt["topk_idx"], ref_rt["topk_w"]
     assert np.array_equal(to_np(routing["topk_idx"]), idx)
-    from tests.moe_parity import sampled_backward
-    rng = np.random.default_rng(12)
-    tokens = np.sort(rng.choice(D.T, size=ntok, replace=False))
-    dx_ref, dg_ref = sampled_backward(hp, tokens, idx, g)
+    tokens, experts = pick_tokens(ref_rt, D.T, ntok, seed)
+    res = sampled_eval(hp, tokens, idx, g, backward=True, mx=True)
     tk = torch.as_tensor(tokens, device=got["dx"].device)
-    dx_got, dg_got = to_np(got["dx"][tk]), to_np(got["dtopk_w"][tk])
-    dx_q, dg_q = sampled_backward_q(hp, tokens, idx, g)
-    for n, gv, ex, qv in (("dx", dx_got, dx_ref, dx_q), ("dtopk_w", dg_got, dg_ref, dg_q)):
+    errs = {}
+    rep = []
+    for n, gv, ex, qv in (("dx", to_np(got["dx"][tk]), res["dx"], res["dx_q"]),
+                          ("dtopk_w", to_np(got["dtopk_w"][tk]), res["dg"], res["dg_q"])):
+        rep.append((n, gv, ex, qv))
+    if "dw_router" in got:
+        ex = router_wgrad_rows(hp, experts, tokens, idx, res["dl"])
+        qv = router_wgrad_rows(hp, experts, tokens, idx, res["dl_q"])
+        rep.append(("dw_router", to_np(got["dw_router"][torch.as_tensor(experts, device=tk.device)]), ex, qv))
+    say("   %d sampled tokens; experts %s hold %s rows" % (len(tokens), experts,
+                                                        [int(ref_rt["counts"][e]) for e in experts]))
+    samples = wgrad_columns(hp, ref_rt, 16, seed, mx=True)
+    gw = gather_wgrad(got, samples)
+    for n, lst in samples.items():
+        ex = np.concatenate([v[2].ravel() for v in lst])
+        qv = np.concatenate([v[3].ravel() for v in lst])
+        rep.append((n, gw[n], ex, qv))
+        per = []
+        for e, cols, ev, mv in lst:
+            c = torch.as_tensor(cols, device=tk.device)
+            gv = to_np(got[n][e][:, c] if n == "dw_down" else got[n][e][c])
+            per.append((rel_err(gv, ev), rel_err(gv, mv), e, int(ref_rt["counts"][e])))
+        worst = max(per)
+        say("   %s per expert: worst vs oracle %.3e (vs model %.3e; expert %d, %d rows); worst vs model %.3e"
+            % (n, worst[0], worst[1], worst[2], worst[3], max(r[1] for r in per)))
+    for n, gv, ex, qv in rep:
         e_q, e_x, e_fmt = rel_err(gv, qv), rel_err(gv, ex), rel_err(qv, ex)
-        say("   sampled tokens %-8s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)" % (n, e_q, e_x, e_fmt))
-        assert e_q <= TOL_Q and e_x <= max(TOL["mxfp8"], e_fmt + 1e-2), n
-    counts, offsets, row_token = ref_rt["counts"], ref_rt["offsets"], ref_rt["row_token"]
-    nz = np.nonzero(counts)[0]
-    picks = sorted({int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
-                    int(nz[np.argsort(counts[nz])[len(nz) // 2]])})
-    p = hp.p
-    for e in picks:
-        rows = np.arange(offsets[e], offsets[e + 1])
-        toks = row_token[rows]
-        gr = np.array([g[tk][list(idx[tk]).index(e)] for tk in toks], np.float64)
-        cols = np.sort(rng.choice(D.I, size=16, replace=False))
-        x, dyr = p.host_rows("x", toks), p.host_rows("dy", toks)
-        wg, wu = p.host_expert_rows("w_gate", e, cols), p.host_expert_rows("w_up", e, cols)
-        wd = p.host_expert("w_down", e)[:, cols]
-        # the FFN restricted to these intermediate columns has exactly these
-        # columns' weight gradients
-        _, dWg, dWu, dWd, _, _ = O.ffn_backward(x, wg, wu, wd, gr[:, None] * dyr)
-        _, _, qWg, qWu, qWd = expert_grads_q(x, dyr, gr, wg, wu, wd, with_da=False)
-        c = torch.as_tensor(cols, device=got["dx"].device)
-        for n, gv, ex, qv in (("dw_gate", to_np(got["dw_gate"][e][c]), dWg, qWg),
-                              ("dw_up", to_np(got["dw_up"][e][c]), dWu, qWu),
-                              ("dw_down", to_np(got["dw_down"][e][:, c]), dWd, qWd)):
-            e_q, e_x, e_fmt = rel_err(gv, qv), rel_err(gv, ex), rel_err(qv, ex)
-            say("   expert %d (%d rows) %-8s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)"
-                % (e, len(rows), n, e_q, e_x, e_fmt))
-            assert e_q <= TOL_Q and e_x <= max(TOL["mxfp8"], e_fmt + 1e-2), (e, n)
-    empty = np.nonzero(counts == 0)[0]
+        say("   %-9s vs quantized model %.2e | vs oracle %.2e (format alone %.2e)" % (n, e_q, e_x, e_fmt))
+        assert e_q <= TOL_Q, (n, e_q)
+        errs[n] = (e_x, e_fmt)
+    empty = np.nonzero(ref_rt["counts"] == 0)[0]
     if len(empty):
-        assert torch.count_nonzero(got["dw_down"][int(empty[0])]) == 0
+        sel = torch.as_tensor(empty, device=tk.device)
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            assert torch.count_nonzero(got[n][sel]) == 0, n
+    if D.S:
+        rng = np.random.default_rng(seed + 1)
+        cols = np.sort(rng.choice(D.Is, size=4, replace=False))
+        wg, wu, wd = shared_weights(hp.p, D)
+        _, dWg, dWu, dWd, _, _ = O.ffn_backward(hp.p.host("x"), wg[cols], wu[cols], wd[:, cols], hp.p.host("dy"))
+        c = torch.as_tensor(cols, device=tk.device)
+        es = {n: rel_err(to_np(v), r) for n, v, r in (("dws_gate", got["dws_gate"][0][c], dWg),
+                                                     ("dws_up", got["dws_up"][0][c], dWu),
+                                                     ("dws_down", got["dws_down"][0][:, c], dWd))}
+        say("   shared expert (bf16) columns %s: %s" % (cols, ", ".join("%s %.2e" % kv for kv in es.items())))
+        for n, e in es.items():
+            assert e <= TOL["bf16"], (n, e)
+    check_mx_bound(errs, D.name)

@@ -4,7 +4,8 @@ and DeepSeek-V4-Pro), through the C ABI, with the checks and bars of the
 DeepSeek-V3-shaped tests:
   * whole layers on one GPU (T=8192, Zipf-skewed routing, one shared expert):
     bf16 and MXFP8 forward on sampled tokens with bit-exact routing, bf16
-    backward on sampled tokens and weight-gradient columns for two shapes;
+    backward of all four and the MXFP8 backward of GLM-5.2 on sampled tokens
+    and weight-gradient columns of every expert;
   * one GPU's share of the post's EP-64 runs (the E/64 local experts and the
     2,048·k rows they receive, gen/configs.py): MXFP8 backward on sampled
     tokens and weight-gradient columns.
@@ -32,19 +33,25 @@ def release_cached_memory():
 @pytest.mark.parametrize("name", WHOLE)
 def test_whole_layer_bf16_forward_sampled(name):
     from tests.test_gpu_forward import check_forward_sampled
-    check_forward_sampled(gen.get_config(name), 16)
+    check_forward_sampled(gen.get_config(name), 128)
 
 
 @pytest.mark.parametrize("name", WHOLE)
 def test_whole_layer_mxfp8_forward_sampled(name):
     from tests.test_gpu_forward import check_forward_sampled
-    check_forward_sampled(gen.get_config(name + "_mx"), 12)
+    check_forward_sampled(gen.get_config(name + "_mx"), 128)
 
 
-@pytest.mark.parametrize("name", ["qwen35", "dsv4pro"])
+@pytest.mark.parametrize("name", WHOLE)
 def test_whole_layer_bf16_backward_sampled(name):
     from tests.test_gpu_backward import check_backward_sampled
-    check_backward_sampled(gen.get_config(name))
+    check_backward_sampled(gen.get_config(name), ntok=48)
+
+
+@pytest.mark.parametrize("name", ["glm52"])
+def test_whole_layer_mxfp8_backward_sampled(name):
+    from tests.test_gpu_mxfp8_backward import check_backward_sampled
+    check_backward_sampled(gen.get_config(name + "_mx"), ntok=48)
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
