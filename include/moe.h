@@ -171,6 +171,25 @@ moe_status moe_permute(const moe_dims* dims, moe_prec prec, const int32_t* topk_
                        int32_t* token_row, void* x_perm, uint8_t* x_perm_scale, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same outputs bit for bit, without a workspace argument.  Its scratch
+ * (the schedule's per-block expert histograms, ceil(T/128) * E * 4 bytes)
+ * lives in a static device array of moe_permute_noalloc_scratch_bytes()
+ * bytes (4 MiB) that each GPU holds from its first call until the process
+ * ends; larger requests (e.g. T above 131,072 tokens at E = 1024, or above
+ * 524,288 at E = 256) return MOE_EWORKSPACE with nothing enqueued.  The
+ * call allocates nothing, with no HIP or library allocation, but it looks
+ * up the array's device address once per device.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from several host threads) race and give undefined outputs;
+ * serialize them.  Nothing in the array needs clearing between calls: the
+ * schedule writes every entry it reads. */
+moe_status moe_permute_noalloc(const moe_dims* dims, moe_prec prec, const int32_t* topk_idx, const void* x,
+                               int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                               int32_t* token_row, void* x_perm, uint8_t* x_perm_scale, void* stream);
+size_t moe_permute_noalloc_scratch_bytes(void);
+
 /* Routed expert FFNs on the permuted rows, grouped by expert:
  *   o_perm[r] = (SiLU(a W_g[e]^T) * (a W_u[e]^T)) W_d[e]^T,  a = x_perm[r],
  * for r in [expert_offsets[e], expert_offsets[e+1]).

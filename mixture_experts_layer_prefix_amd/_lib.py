@@ -52,6 +52,8 @@ _SIGS = {
     "moe_workspace_bytes": ([_DIMS, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "moe_route": ([_DIMS, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_permute": ([_DIMS, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_permute_noalloc": ([_DIMS, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_permute_noalloc_scratch_bytes": ([], ctypes.c_size_t),
     "moe_expert_ffn": ([_DIMS, ctypes.c_int, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, ctypes.c_size_t, _P],
                        ctypes.c_int),
     "moe_expert_gate_up": ([_DIMS, ctypes.c_int, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P,

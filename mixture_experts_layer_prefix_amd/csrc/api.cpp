@@ -690,6 +690,23 @@ moe_status moe_permute(const moe_dims* dims, moe_prec prec, const int32_t* topk_
                      x_perm_scale, ws, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_permute_noalloc(const moe_dims* dims, moe_prec prec, const int32_t* topk_idx, const void* x,
+                               int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                               int32_t* token_row, void* x_perm, uint8_t* x_perm_scale, void* stream) {
+  MOE_TRY(check_dims(dims, prec));
+  if (!ptr_ok(expert_counts) || !ptr_ok(expert_offsets)) return MOE_EINVAL;
+  if (dims->T > 0 && (!ptr_ok(topk_idx) || !ptr_ok(row_token) || !ptr_ok(token_row))) return MOE_EINVAL;
+  if (x_perm && (!aligned16(x_perm) || !ptr_ok(x) || (prec == MOE_MXFP8 && !ptr_ok(x_perm_scale)))) return MOE_EINVAL;
+  if (prec == MOE_MXFP8 && x_perm && dims->d % 32) return MOE_EUNSUPPORTED;
+  if (permute_scratch_bytes(dims->T, dims->E) > noalloc_scratch_capacity()) return MOE_EWORKSPACE;
+  void* sc = nullptr;
+  if (dims->T > 0) MOE_HIP(noalloc_scratch(&sc));
+  return run_permute(dims, prec, topk_idx, x, expert_counts, expert_offsets, row_token, token_row, x_perm,
+                     x_perm_scale, sc, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_permute_noalloc_scratch_bytes(void) { return noalloc_scratch_capacity(); }
+
 moe_status moe_expert_ffn(const moe_dims* dims, moe_prec prec, const void* x_perm, const uint8_t* x_perm_scale,
                           const int32_t* expert_offsets, const moe_weights* w, void* o_perm, void* ws, size_t ws_bytes,
                           void* stream) {

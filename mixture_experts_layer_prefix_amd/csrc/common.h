@@ -190,6 +190,10 @@ hipError_t launch_topk(bool act_f32, const float* logits, const void* x, const v
 // Schedule: per-block histograms -> scan -> stable scatter.
 int permute_num_blocks(int64_t T);
 size_t permute_scratch_bytes(int64_t T, int E);
+// The static scratch of moe_permute_noalloc: its size, and its device address
+// on the current device (looked up once per device, then cached).
+size_t noalloc_scratch_capacity();
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
                            int32_t* offsets, int32_t* row_token, int32_t* token_row, void* scratch,
                            hipStream_t s);

@@ -22,7 +22,17 @@
 // The gather copies rows with 16-byte loads and stores; the MXFP8 variant
 // quantizes every 32-element block of a row on the way (blog post, "MXFP8
 // support": activation quantization fused into the dispatch).
+#include <mutex>
+
 #include "common.h"
+
+// Scratch of moe_permute_noalloc: the schedule's per-block expert histograms
+// in a file-scope device array, for callers that cannot allocate.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not a device address: the host
+// reaches the array only through the per-device address that
+// hipGetSymbolAddress returns (moe::noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[4u << 20];
 
 namespace moe {
 
@@ -205,6 +215,28 @@ unsigned stream_grid(int64_t work) {
 }
 
 }  // namespace
+
+size_t noalloc_scratch_capacity() { return sizeof(scratch); }
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current: this device's copy
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int permute_num_blocks(int64_t T) { return (int)((T + kTokBlock - 1) / kTokBlock); }
 

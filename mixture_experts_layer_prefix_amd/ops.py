@@ -117,6 +117,16 @@ def permute(topk_idx, x, dims: Dims, prec: str, gather=True):
     return counts, offsets, row_token[:dims.R], token_row, x_perm, scale
 
 
+def permute_noalloc(topk_idx, x, dims: Dims, prec: str, out):
+    """moe_permute_noalloc into caller-allocated outputs: out = (counts,
+    offsets, row_token, token_row, x_perm, x_perm_scale) as permute returns
+    them (x_perm and x_perm_scale may be None).  Allocates nothing."""
+    counts, offsets, row_token, token_row, x_perm, scale = out
+    call("moe_permute_noalloc", ctypes.byref(dims.c()), PREC[prec], _p(topk_idx), _p(x), _p(counts), _p(offsets),
+         _p(row_token), _p(token_row), _p(x_perm), _p(scale), _stream())
+    return out
+
+
 def expert_ffn(x_perm, x_perm_scale, offsets, weights: Weights, dims: Dims, prec: str):
     dev = offsets.device
     o_perm = torch.empty(dims.R, dims.d, dtype=_act_dtype(prec), device=dev)

@@ -116,3 +116,21 @@ def test_backward_validation_before_device_work():
     assert lib.moe_transpose_weights(fake, -1, 4, 4, fake, None) == L.MOE_EINVAL
     assert lib.moe_transpose_weights(None, 1, 4, 4, fake, None) == L.MOE_EINVAL
     assert lib.moe_transpose_weights(None, 0, 4, 4, None, None) == L.MOE_OK
+
+
+def test_permute_noalloc_rejects_beyond_its_scratch_on_the_host():
+    """moe_permute_noalloc refuses a schedule whose block histograms exceed
+    its static scratch (MOE_EWORKSPACE) before any device work: the pointers
+    here are never dereferenced."""
+    cap = L.lib().moe_permute_noalloc_scratch_bytes()
+    assert cap == 4 << 20
+    fake = 0x100000
+    for T, E in ((cap // (1024 * 4) * 128 + 1, 1024), (cap // (256 * 4) * 128 + 1, 256)):
+        d = M.Dims(T, 64, E, 2, 64)
+        st = L.lib().moe_permute_noalloc(ctypes.byref(d.c()), L.PREC["bf16"], fake, fake, fake, fake, fake, fake,
+                                        None, None, None)
+        assert st == L.MOE_EWORKSPACE, (T, E, st)
+    d = M.Dims(16, 64, 8, 2, 64)
+    st = L.lib().moe_permute_noalloc(ctypes.byref(d.c()), L.PREC["bf16"], fake, fake, None, fake, fake, fake,
+                                    None, None, None)
+    assert st == L.MOE_EINVAL
