@@ -54,7 +54,7 @@ def gemm_flops(D):
     """Algorithmic FLOPs of each single-kernel GEMM stage (routed rows R)."""
     r = 2.0 * D.R * D.d * D.I
     return {"gate_up": 2 * r, "down": r, "replay_gate_up": 2 * r, "down_dgrad_swiglu": r, "gate_up_dgrad": 2 * r,
-            "wgrad_down": r, "wgrad_gate": r, "wgrad_up": r}
+            "wgrad_down": r, "wgrad_gate_up": 2 * r}
 
 
 def gemm_bytes(D, eb, active):
@@ -70,20 +70,23 @@ def gemm_bytes(D, eb, active):
             "down_dgrad_swiglu": R * d * eb + w + R * 2 * I * 2 + R * 2 * I * (2 + (eb if eb < 2 else 0))
             + R * I * 2 + R * I / 8,
             "gate_up_dgrad": R * 2 * I * eb + 2 * w + R * d * 2,
-            "wgrad_down": (d + I) * R * eb + E * d * I * 2, "wgrad_gate": (d + I) * R * eb + E * d * I * 2,
-            "wgrad_up": (d + I) * R * eb + E * d * I * 2}
+            "wgrad_down": (d + I) * R * eb + E * d * I * 2,
+            "wgrad_gate_up": (d + 2 * I) * R * eb + 2 * E * d * I * 2}
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter passes, or
-    None when the kernel's source has changed since they were taken."""
+def measured_traffic(kernel, stage):
+    """HBM bytes of one launch of `stage` (run by `kernel`) from the committed
+    counter passes, or None when the kernel's source has changed since they
+    were taken or the stage was not measured."""
     import hashlib
     try:
         t = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
         src = open(os.path.join(ROOT, "mixture_experts_layer_prefix_amd", "csrc", "gemm_mxfp8.hip"), "rb").read()
     except (OSError, KeyError, ValueError):
         return None
-    return t["bytes_per_launch"] if hashlib.sha256(src).hexdigest() == t["source_sha256"] else None
+    if hashlib.sha256(src).hexdigest() != t.get("source_sha256"):
+        return None
+    return t.get("bytes_per_launch", {}).get(stage) if isinstance(t.get("bytes_per_launch"), dict) else None
 
 
 def split_flops(D):
@@ -109,35 +112,30 @@ def timed_steps(run, steps, torch):
 # GEMM stage -> kernel (template instantiation) that runs it
 KERNEL_OF = {"gate_up": "gate/up with SwiGLU epilogue", "down": "down projection",
              "replay_gate_up": "G|U replay", "down_dgrad_swiglu": "down dgrad with SwiGLU backward epilogue",
-             "gate_up_dgrad": "gate/up dgrad (two matrices along K)", "wgrad_down": "K-grouped weight gradient",
-             "wgrad_gate": "K-grouped weight gradient", "wgrad_up": "K-grouped weight gradient"}
+             "gate_up_dgrad": "gate/up dgrad (two matrices along K)",
+             "wgrad_down": "K-grouped weight gradient dW_down",
+             "wgrad_gate_up": "K-grouped weight gradient dW_gate and dW_up (one launch, M = 2I)"}
 
 
 def roofline_of(stages, flops, nbytes, peak, label, traffic_key=None):
-    """Roofline of the kernel with the largest total time in the step.  Its
-    bound is MFMA or HBM, whichever its algorithmic FLOPs or bytes per launch
-    take longer on at the peak rate; achieved = that work per launch over the
-    kernel's average event-timed launch."""
-    per = {}
-    for name, f in flops.items():
-        ms = stages.get(name, 0.0)
-        if ms < 0.01:  # stage skipped (e.g. no replay when G|U are kept)
-            continue
-        k = KERNEL_OF[name.split("_", 1)[1]]
-        tot, fl, by, n = per.get(k, (0.0, 0.0, 0.0, 0))
-        per[k] = (tot + ms, fl + f, by + nbytes[name], n + 1)
-    kern = max(per, key=lambda k: per[k][0])
-    tot, fl, by, n = per[kern]
-    t_launch = tot / n / 1e3
-    fl, by = fl / n, by / n
+    """Roofline of the launch with the largest time in the step (every GEMM
+    stage is one launch).  Its bound is MFMA or HBM, whichever its
+    algorithmic FLOPs or bytes take longer on at the peak rate; achieved =
+    that work over the launch's event-timed duration."""
+    cand = {n: ms for n, ms in stages.items() if n in flops and ms >= 0.01}
+    name = max(cand, key=cand.get)
+    t_launch = cand[name] / 1e3
+    fl, by = flops[name], nbytes[name]
     if by / (PEAK_HBM_GBS * 1e9) > fl / (peak * 1e12):
         achieved, pk, unit, bound = by / t_launch / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
     else:
         achieved, pk, unit, bound = fl / t_launch / 1e12, peak, "TFLOP/s", "mfma"
-    traffic = measured_traffic(traffic_key) if traffic_key and kern == KERNEL_OF["wgrad_down"] else None
+    stage = name.split("_", 1)[1]
+    traffic = measured_traffic(traffic_key, stage) if traffic_key else None
     return dict(bound=bound, achieved=round(achieved, 2), peak=pk, unit=unit, frac=round(achieved / pk, 4),
-                traffic=traffic, kernel="%s: %s" % (label, kern), flops_per_launch=fl, bytes_per_launch=by,
-                mfma_frac=round(fl / t_launch / 1e12 / peak, 4), launches_per_step=n, launch_ms=round(t_launch * 1e3, 4))
+                traffic=traffic, kernel="%s: %s" % (label, KERNEL_OF[stage]), flops_per_launch=fl,
+                bytes_per_launch=by, mfma_frac=round(fl / t_launch / 1e12 / peak, 4), launches_per_step=1,
+                launch_ms=round(t_launch * 1e3, 4))
 
 
 def cpu_baseline(D, rows_hot=8192, tokens=2048):
@@ -207,6 +205,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 DeepSeek-V3 (T=8192) measurements")
     ap.add_argument("--only-bf16", action="store_true",
                     help="run only the bf16 DeepSeek-V3 (T=8192) measurements (for per-part profiles)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the forward throughput of c0-c3b and the full CPU oracle on c0-c2")
     ap.add_argument("--workloads", default="",
                     help='comma-separated config names, or "n3": measure these workloads instead')
     args = ap.parse_args()
@@ -249,11 +249,19 @@ def main():
     if not args.only_bf16:
         out["vendor_dense_gemm"] = vendor_reference(D, torch)
         log("[bench] vendor dense GEMM reference:", out["vendor_dense_gemm"])
+    if not args.only_bf16 and not args.no_configs:
+        out["forward_configs"] = forward_configs_part(args, w, torch, gen, M)
+    del w
+    torch.cuda.empty_cache()
     if args.cpu_sample > 0 and not args.only_bf16:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(D, rows_hot=4 * args.cpu_sample, tokens=args.cpu_sample)
+        model, aff = host_info()
+        out["cpu_baseline"].update({"cpu_model": model, "affinity_cores": aff})
         log("[bench] cpu baseline %.2f tokens/s on %d threads" % (out["cpu_baseline"]["value"],
                                                                   out["cpu_baseline"]["cores"]))
+        if not args.no_configs:
+            out["cpu_baseline"]["configs"] = cpu_oracle_configs()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -381,7 +389,7 @@ def workload_part(args, D, torch, gen, M):
     return res
 
 
-WGRAD_SIDE = ("transposes", "wgrad_down", "wgrad_gate", "wgrad_up", "shared_wgrad", "router_grad")
+WGRAD_SIDE = ("transposes", "wgrad_down", "wgrad_gate_up", "shared_wgrad", "router_grad")
 
 
 def n2_part(args, torch, gen, M, total=32768, chunks=(512, 1024, 2048, 4096, 8192, 16384, 32768)):
@@ -546,36 +554,158 @@ def bf16_part(args, D, w, out, torch, gen, M):
     }
     log("[bench] bf16 T=8192: fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)"
         % (fms, ffl / (fms / 1e3) / 1e12, bms, bfl / (bms / 1e3) / 1e12))
-    # standalone dispatch gather and weighted sum (algorithmic bytes)
     r = f3.routing
-    perm = M.permute(r["topk_idx"], x3, md3, "bf16")
-    o_perm = torch.empty(D3.R, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
-    y_sh = torch.empty(D3.T, D3.d, dtype=torch.bfloat16, device="cuda").normal_()
-    reps = 5
-
-    def one(fn):
-        fn()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        e.synchronize()
-        return s.elapsed_time(e) / 1e3 / reps
-
-    t_perm = one(lambda: M.permute(r["topk_idx"], x3, md3, "bf16"))
-    t_comb = one(lambda: M.combine(o_perm, perm[3], r["topk_w"], y_sh, md3, "bf16"))
-    perm_bytes = D3.T * D3.d * 2 + D3.R * D3.d * 2 + D3.R * 4 * 3
-    comb_bytes = D3.R * D3.d * 2 + 2 * D3.T * D3.d * 2 + D3.R * 8
-    out["hbm"] = {"permute_GBs": round(perm_bytes / t_perm / 1e9, 1),
-                  "permute_frac": round(perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS, 4),
-                  "combine_GBs": round(comb_bytes / t_comb / 1e9, 1),
-                  "combine_frac": round(comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS, 4),
-                  "workload": "bf16, T=8192, d=7168, k=8 (standalone moe_permute with gather, moe_combine)"}
+    out["hbm"] = hbm_part(D3, r, x3, md3, torch, M)
     hc = r["expert_counts"].cpu()
     out["routing_skew_t8192"] = dict(max_rows=int(hc.max()), empty_experts=int((hc == 0).sum()),
                                      under_32=int((hc < 32).sum()))
     del f3, b3, wb3
+
+
+def flushed_times(fn, torch, reps=7, flush_bytes=1 << 30):
+    """Device time of fn() per call with the last-level cache (the 256 MB
+    Infinity Cache) flushed first: a 1 GiB fill runs before every timed call,
+    outside its events; the median of reps calls."""
+    junk = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        junk.fill_(1)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+    del junk
+    return t[len(t) // 2]
+
+
+def hbm_part(D3, r, x3, md3, torch, M):
+    """Standalone dispatch and weighted sum against HBM (algorithmic bytes
+    over the flushed device time): the permute (schedule, then the row copy,
+    pushed from token order; moe_permute's kernels through its no-allocation
+    entry point into preallocated outputs), the schedule alone, the MXFP8
+    quantizing dispatch of the same routing, moe_combine, and a plain device
+    copy of 1 GiB as the attainable-bandwidth reference."""
+    R, T, d, k = D3.R, D3.T, D3.d, D3.k
+    perm = M.permute(r["topk_idx"], x3, md3, "bf16")
+    o_perm = torch.empty(R, d, dtype=torch.bfloat16, device="cuda").normal_()
+    y_sh = torch.empty(T, d, dtype=torch.bfloat16, device="cuda").normal_()
+    out_bufs = tuple(None if v is None else torch.empty_like(v) for v in perm)
+    t_perm = flushed_times(lambda: M.permute_noalloc(r["topk_idx"], x3, md3, "bf16", out_bufs), torch)
+    sched_bufs = out_bufs[:4] + (None, None)
+    t_sched = flushed_times(lambda: M.permute_noalloc(r["topk_idx"], x3, md3, "bf16", sched_bufs), torch)
+    y_out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    t_comb = flushed_times(lambda: M.combine_into(o_perm, perm[3], r["topk_w"], y_sh, md3, "bf16", y_out), torch)
+    xq = torch.empty(R, d, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(R, d // 32, dtype=torch.uint8, device="cuda")
+    mx_bufs = out_bufs[:4] + (xq, xs)
+    t_perm_mx = flushed_times(lambda: M.permute_noalloc(r["topk_idx"], x3, md3, "mxfp8", mx_bufs), torch)
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = flushed_times(lambda: dst.copy_(src), torch)
+    perm_bytes = T * d * 2 + R * d * 2 + T * k * 4 * 3      # x, x_perm, ids in, rows out
+    disp_bytes = T * d * 2 + R * d * 2 + T * k * 4          # the row copy: x once, every routed row, token_row
+    disp_mx_bytes = T * d * 2 + R * d * (1 + 1 / 32) + T * k * 4   # quantizing copy: E4M3 codes + E8M0 scales
+    comb_bytes = R * d * 2 + 2 * T * d * 2 + R * 8
+    gbs = lambda b, t: b / t / 1e9
+    res = {"permute_GBs": round(gbs(perm_bytes, t_perm), 1), "permute_frac": round(gbs(perm_bytes, t_perm) / PEAK_HBM_GBS, 4),
+           "permute_ms": round(t_perm * 1e3, 4), "schedule_ms": round(t_sched * 1e3, 4),
+           "dispatch_GBs": round(gbs(disp_bytes, t_perm - t_sched), 1),
+           "dispatch_frac": round(gbs(disp_bytes, t_perm - t_sched) / PEAK_HBM_GBS, 4),
+           "combine_GBs": round(gbs(comb_bytes, t_comb), 1), "combine_frac": round(gbs(comb_bytes, t_comb) / PEAK_HBM_GBS, 4),
+           "combine_ms": round(t_comb * 1e3, 4),
+           "dispatch_mx_GBs": round(gbs(disp_mx_bytes, t_perm_mx - t_sched), 1),
+           "dispatch_mx_frac": round(gbs(disp_mx_bytes, t_perm_mx - t_sched) / PEAK_HBM_GBS, 4),
+           "copy_GBs": round(gbs(2 * src.numel() * 2, t_copy), 1),
+           "workload": "bf16, T=%d, d=%d, k=%d: moe_permute (schedule + row copy; dispatch = permute minus the "
+                       "schedule alone) and moe_combine, each timed with the 256 MB last-level cache flushed by a "
+                       "1 GiB fill before every call (median of 7); copy = torch copy of 1 GiB, same protocol" % (T, d, k)}
+    log("[bench] hbm:", res)
+    return res
+
+
+def forward_configs_part(args, w_dsv3, torch, gen, M, names=("c0", "c1", "c2", "c3a", "c3b")):
+    """Forward throughput of the other forward configurations on one GPU:
+    tokens/s, TFLOP/s and the fraction of the precision's dense MFMA peak
+    (c0 runs in fp32 and is launch-bound, reported only).  The DeepSeek-V3
+    shapes reuse the headline's weights (same generator streams)."""
+    res = {}
+    for n in names:
+        D = gen.get_config(n)
+        p = gen.Problem(D)
+        md = M.Dims(D.T, D.d, D.E, D.k, D.I, D.S, D.Is)
+        wn = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+        if (D.d, D.E, D.I) == (7168, 256, 2048):
+            w = w_dsv3
+        else:
+            w = M.Weights(**{k: (p.device(k) if (D.S or not k.startswith("ws_")) else None) for k in wn})
+        x, bias = p.device("x"), p.device_bias()
+        plan = M.ForwardPlan(md, D.prec, keep_routing=True)
+        for _ in range(max(args.warmup, 1)):
+            plan.run(x, w, bias)
+        el = timed_steps(lambda i: plan.run(x, w, bias), args.steps, torch)
+        ms = el / args.steps * 1e3
+        fl = D.fwd_flops()
+        peak = PEAK["bf16"] if D.prec == "bf16" else 157.3
+        res[n] = {"T": D.T, "d": D.d, "E": D.E, "k": D.k, "I": D.I, "S": D.S, "prec": D.prec, "ms": round(ms, 4),
+                  "tokens_s": round(D.T / (ms / 1e3), 1), "tflops": round(fl / (ms / 1e3) / 1e12, 2),
+                  "peak_frac": round(fl / (ms / 1e3) / 1e12 / peak, 4),
+                  "peak": "bf16 dense MFMA 2.5 PF" if D.prec == "bf16" else "fp32 vector 157.3 TF (launch-bound)"}
+        log("[bench] forward %s: %.3f ms, %.0f tokens/s, %.1f TFLOP/s (%.1f%% of peak)"
+            % (n, ms, res[n]["tokens_s"], res[n]["tflops"], 100 * res[n]["peak_frac"]))
+        del plan, x
+        if w is not w_dsv3:
+            del w
+        torch.cuda.empty_cache()
+    return res
+
+
+def host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_oracle_configs(names=("c0", "c1", "c2"), one_thread=("c0", "c1")):
+    """The oracle, as it stands, on the full forward of the small
+    configurations (inputs regenerated on the host, untimed), with all the
+    threads its BLAS uses and, for c0 and c1, with one thread."""
+    import numpy as np
+    import gen
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    res = {}
+    for n in names:
+        D = gen.get_config(n)
+        p = gen.Problem(D)
+        get = lambda nm: p.host(nm) if (D.S or not nm.startswith("ws_")) else None
+        a = [p.host("x"), p.host("w_router"), p.logit_bias()] + [get(nm) for nm in (
+            "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+
+        def run():
+            t0 = time.perf_counter()
+            O.layer_forward(*a, D.k)
+            return time.perf_counter() - t0
+
+        t_all = run()
+        r = {"tokens_s": round(D.T / t_all, 1), "seconds": round(t_all, 3), "threads": threads}
+        if n in one_thread:
+            with threadpool_limits(limits=1):
+                t1 = run()
+            r.update({"tokens_s_1thread": round(D.T / t1, 1), "seconds_1thread": round(t1, 3)})
+        res[n] = r
+        log("[bench] oracle forward %s: %s" % (n, r))
+        del a
+    return res
+
 
 
 if __name__ == "__main__":

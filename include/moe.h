@@ -174,10 +174,10 @@ moe_status moe_permute(const moe_dims* dims, moe_prec prec, const int32_t* topk_
 /* moe_permute for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same outputs bit for bit, without a workspace argument.  Its scratch
- * (the schedule's per-block expert histograms, ceil(T/128) * E * 4 bytes)
+ * (the schedule's per-block expert histograms, ceil(T/32) * E * 4 bytes)
  * lives in a static device array of moe_permute_noalloc_scratch_bytes()
- * bytes (4 MiB) that each GPU holds from its first call until the process
- * ends; larger requests (e.g. T above 131,072 tokens at E = 1024, or above
+ * bytes (16 MiB) that each GPU holds from its first call until the process
+ * ends; larger requests (T above 131,072 tokens at E = 1024, or above
  * 524,288 at E = 256) return MOE_EWORKSPACE with nothing enqueued.  The
  * call allocates nothing, with no HIP or library allocation, but it looks
  * up the array's device address once per device.  Every call on a GPU
@@ -291,8 +291,8 @@ moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, i
  *     weights, MXFP8 quantization of x and dY), 2 G|U replayed, 3 down dgrad
  *     + SwiGLU backward done, 4 router-weight gradients done, 5 gate/up dgrad
  *     done, 6 shared-expert input gradient done, 7 dx done, 8 transposes done,
- *     9 dW_down done, 10 dW_gate done, 11 dW_up done, 12 shared weight
- *     gradients done, 13 router gradient done. */
+ *     9 dW_down done, 10 dW_gate and dW_up done (one launch), 11 shared
+ *     weight gradients done, 12 router gradient done. */
 moe_status moe_trace_events(int which, void* const* events, int n);
 
 /* MX quantization of a bf16 matrix src [rows][cols] (OCP MX v1.0; blog post
@@ -313,6 +313,27 @@ moe_status moe_trace_events(int which, void* const* events, int n);
  * library quantizes itself (tokens, h, gradients) uses the same rule. */
 moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t cols, int axis, uint8_t* dst,
                               uint8_t* scale, void* stream);
+
+/* Routed-row-axis MX quantization of a weight-gradient operand (the K axis
+ * of the MXFP8 weight-gradient GEMMs is the routed rows; blog post, "MXFP8
+ * support": quantization fused into the grouped GEMMs).  For every group e in
+ * [0, nseg): rows r in [seg_off[e], seg_off[e+1]) of a bf16 matrix (row r is
+ * src row gather[r] when gather is not NULL, else src row r; ld_src elements
+ * between rows), transposed into a [cols][Kp_e] block of E4M3 codes at byte
+ * pad_off[e] * cols of dst, Kp_e = pad_off[e+1] - pad_off[e] (a multiple of
+ * 128, at least the group's row count; positions past the group's rows hold
+ * zeros), quantized in blocks of 32 consecutive positions of one column with
+ * the scale rule of moe_quantize_mxfp8.  Scales slab-major per group:
+ * [Kp_e/128][cols][4] at byte pad_off[e] * cols / 32, byte (p/128) * cols * 4
+ * + c * 4 + (p/32) % 4 of the block for position p of column c.  This is the
+ * layout moe_layer_backward builds for x and dY in MOE_MXFP8.
+ * seg_off, pad_off: device int32 [nseg+1]; gather: device int32 or NULL;
+ * p_cap: a multiple of 128, at least pad_off[nseg] (sizes the launch); cols
+ * a multiple of 8; dst and dst_scale hold p_cap * cols and p_cap * cols / 32
+ * bytes. */
+moe_status moe_quantize_mxfp8_rows_t(const void* src_bf16, int64_t ld_src, int32_t cols, const int32_t* gather,
+                                     const int32_t* seg_off, const int32_t* pad_off, int32_t nseg, int64_t p_cap,
+                                     uint8_t* dst, uint8_t* dst_scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,5 +6,5 @@ the current stream) into those calls.
 """
 from . import _lib  # noqa: F401
 from .ops import (Dims, Weights, ForwardPlan, route, permute, permute_noalloc, expert_ffn, expert_gate_up, expert_down,  # noqa: F401
-                  shared_ffn, combine, layer_forward, quantize_mxfp8, prepare_mxfp8, workspace_bytes,
+                  shared_ffn, combine, combine_into, layer_forward, quantize_mxfp8, quantize_mxfp8_rows_t, prepare_mxfp8, workspace_bytes,
                   BackwardPlan, layer_backward, transpose_weights, prepare_backward, StageTimer)

@@ -70,6 +70,8 @@ _SIGS = {
     "moe_trace_events": ([ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int], ctypes.c_int),
     "moe_transpose_weights": ([_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P], ctypes.c_int),
     "moe_quantize_mxfp8": ([_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P], ctypes.c_int),
+    "moe_quantize_mxfp8_rows_t": ([_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int64,
+                                   _P, _P, _P], ctypes.c_int),
 }
 
 _lib = None

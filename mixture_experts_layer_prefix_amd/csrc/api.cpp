@@ -243,14 +243,13 @@ moe_status run_route(const moe_dims* D, moe_prec prec, const void* x, const void
 moe_status run_permute(const moe_dims* D, moe_prec prec, const int32_t* idx, const void* x, int32_t* counts,
                        int32_t* offsets, int32_t* row_token, int32_t* token_row, void* x_perm, uint8_t* x_perm_scale,
                        void* sched, hipStream_t s) {
-  const int64_t R = D->T * D->k;
   MOE_HIP(launch_schedule(idx, D->T, D->E, D->k, counts, offsets, row_token, token_row, sched, s));
   if (x_perm) {
     if (prec == MOE_MXFP8)
-      MOE_HIP(launch_gather_quant_mx(static_cast<const bf16_t*>(x), row_token, static_cast<uint8_t*>(x_perm),
-                                     x_perm_scale, R, D->d, s));
+      MOE_HIP(launch_dispatch_quant_mx(static_cast<const bf16_t*>(x), token_row, static_cast<uint8_t*>(x_perm),
+                                       x_perm_scale, D->T, D->k, D->d, s));
     else
-      MOE_HIP(launch_gather_rows(x, row_token, x_perm, R, D->d, (int)act_bytes(prec), s));
+      MOE_HIP(launch_dispatch_rows(x, token_row, x_perm, D->T, D->k, D->d, (int)act_bytes(prec), s));
   }
   return MOE_OK;
 }
@@ -443,27 +442,34 @@ GemmProblem gemm(int mode, const void* A, int64_t lda, const int32_t* row_off, i
 }
 
 // Weight gradients C_g = A[:, K_g] B[:, K_g]^T of every group from the
-// transposed operands A [M][ldk], B [N][ldk] over the K ranges k_off.
+// transposed operands A [M][ldk], B [N][ldk] over the K ranges k_off.  With
+// C1, A stacks two operands of M/2 rows each and rows [M/2, M) of every
+// group's result go to C1 (dW_gate and dW_up from [dG^T; dU^T] in one launch,
+// reading B = x^T once).
 moe_status run_wgrad(const void* A, int64_t M, const void* B, int N, int64_t ldk, const int32_t* k_off, int G,
-                     void* C, hipStream_t s) {
+                     void* C, hipStream_t s, void* C1 = nullptr) {
   GemmProblem q = gemm(GEMM_WGRAD, A, ldk, nullptr, M, G, B, nullptr, 0, N, 64, C, N, nullptr);
   q.ldb = ldk;
   q.k_off = k_off;
-  q.c_group_stride = M * N;
+  q.c_group_stride = (C1 ? M / 2 : M) * N;
+  q.C1 = C1;
+  q.m_split = C1 ? M / 2 : 0;
   MOE_HIP(launch_gemm_bf16(q, s));
   return MOE_OK;
 }
 
 // MXFP8 weight gradients from the quantized transposed operands
-// (A [M][ldk] + scales [M][ldk/32], B [N][ldk] + scales).
+// (A [M][ldk] + scales [M][ldk/32], B [N][ldk] + scales); C1 as in run_wgrad.
 moe_status run_wgrad_mx(const uint8_t* A, const uint8_t* As, int64_t M, const uint8_t* B, const uint8_t* Bs, int N,
-                        int64_t ldk, const int32_t* k_off, int G, void* C, hipStream_t s) {
+                        int64_t ldk, const int32_t* k_off, int G, void* C, hipStream_t s, void* C1 = nullptr) {
   GemmProblem q = gemm(GEMM_WGRAD, A, ldk, nullptr, M, G, B, nullptr, 0, N, 128, C, N, nullptr);
   q.A_scale = As;
   q.B0_scale = Bs;
   q.ldb = ldk;
   q.k_off = k_off;
-  q.c_group_stride = M * N;
+  q.c_group_stride = (C1 ? M / 2 : M) * N;
+  q.C1 = C1;
+  q.m_split = C1 ? M / 2 : 0;
   MOE_HIP(launch_gemm_mxfp8(q, s));
   return MOE_OK;
 }
@@ -591,7 +597,7 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   const bf16_t* dgu = static_cast<const bf16_t*>(b.dgu);
   const int32_t* off = rt->expert_offsets;
   if (mx) {
-    const int64_t Rp = b.Rp, Rs = b.Rp / 32;
+    const int64_t Rp = b.Rp;
     // Expert-blocked [cols][Kp_e] operands; dG^T, dU^T and (w h)^T came from
     // the down-dgrad epilogue.
     MOE_HIP(launch_transpose_quant(x, d, d, rt->row_token, off, b.pad_off, E, Rp, b.xTq, b.xTqs, s));
@@ -599,26 +605,21 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     trace(1, 8, s);
     MOE_TRY(run_wgrad_mx(b.dyTq, b.dyTqs, d, b.ghTq, b.ghTqs, I, Rp, b.pad_off, E, g->dw_down, s));
     trace(1, 9, s);
-    MOE_TRY(run_wgrad_mx(b.dguTq, b.dguTqs, I, b.xTq, b.xTqs, d, Rp, b.pad_off, E, g->dw_gate, s));
+    // dW_gate and dW_up in one launch over [dG^T; dU^T] (2I rows per expert)
+    MOE_TRY(run_wgrad_mx(b.dguTq, b.dguTqs, 2 * I, b.xTq, b.xTqs, d, Rp, b.pad_off, E, g->dw_gate, s, g->dw_up));
     trace(1, 10, s);
-    MOE_TRY(run_wgrad_mx(b.dguTq + (int64_t)I * Rp, b.dguTqs + (int64_t)I * Rs, I, b.xTq, b.xTqs, d, Rp, b.pad_off, E,
-                         g->dw_up, s));
-    trace(1, 11, s);
   } else {
     MOE_HIP(launch_transpose_rows(x, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.xT), s));
     MOE_HIP(launch_transpose_rows(dy, d, d, rt->row_token, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dyT), s));
     MOE_HIP(launch_transpose_rows(gh, I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.ghT), s));
-    MOE_HIP(launch_transpose_rows(dgu, 2 * I, I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT), s));
-    MOE_HIP(launch_transpose_rows(dgu + I, 2 * I, I, nullptr, off, b.pad_off, E, b.Rp,
-                                  static_cast<bf16_t*>(b.dguT) + (int64_t)I * b.Rp, s));
+    // [dG | dU] rows -> one [2I][Kp_e] block per expert: dG^T over dU^T
+    MOE_HIP(launch_transpose_rows(dgu, 2 * I, 2 * I, nullptr, off, b.pad_off, E, b.Rp, static_cast<bf16_t*>(b.dguT),
+                                  s));
     trace(1, 8, s);
-    const bf16_t* dguT = static_cast<const bf16_t*>(b.dguT);
     MOE_TRY(run_wgrad(b.dyT, d, b.ghT, I, b.Rp, b.pad_off, E, g->dw_down, s));
     trace(1, 9, s);
-    MOE_TRY(run_wgrad(dguT, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_gate, s));
+    MOE_TRY(run_wgrad(b.dguT, 2 * I, b.xT, d, b.Rp, b.pad_off, E, g->dw_gate, s, g->dw_up));
     trace(1, 10, s);
-    MOE_TRY(run_wgrad(dguT + (int64_t)I * b.Rp, I, b.xT, d, b.Rp, b.pad_off, E, g->dw_up, s));
-    trace(1, 11, s);
   }
   if (Is) {
     const int32_t* seg = b.single + 2;
@@ -627,19 +628,16 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
     MOE_HIP(launch_transpose_rows(dy, d, d, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.dyTs), s));
     MOE_HIP(launch_transpose_rows(static_cast<const bf16_t*>(b.hs), Is, Is, nullptr, seg, b.single, 1, b.Tp,
                                   static_cast<bf16_t*>(b.hsT), s));
-    MOE_HIP(launch_transpose_rows(dgus, 2 * Is, Is, nullptr, seg, b.single, 1, b.Tp, static_cast<bf16_t*>(b.dgusT), s));
-    MOE_HIP(launch_transpose_rows(dgus + Is, 2 * Is, Is, nullptr, seg, b.single, 1, b.Tp,
-                                  static_cast<bf16_t*>(b.dgusT) + (int64_t)Is * b.Tp, s));
-    const bf16_t* dgusT = static_cast<const bf16_t*>(b.dgusT);
+    MOE_HIP(launch_transpose_rows(dgus, 2 * Is, 2 * Is, nullptr, seg, b.single, 1, b.Tp,
+                                  static_cast<bf16_t*>(b.dgusT), s));
     MOE_TRY(run_wgrad(b.dyTs, d, b.hsT, Is, b.Tp, b.single, 1, g->dws_down, s));
-    MOE_TRY(run_wgrad(dgusT, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_gate, s));
-    MOE_TRY(run_wgrad(dgusT + (int64_t)Is * b.Tp, Is, b.xTs, d, b.Tp, b.single, 1, g->dws_up, s));
+    MOE_TRY(run_wgrad(b.dgusT, 2 * Is, b.xTs, d, b.Tp, b.single, 1, g->dws_gate, s, g->dws_up));
   }
-  trace(1, 12, s);
+  trace(1, 11, s);
   if (router)
     MOE_HIP(launch_router_wgrad(x, rt->row_token, b.dl_row, rt->expert_offsets, b.pad_off, E, d, b.Rp,
                                 b.router_partial, g->dw_router, s));
-  trace(1, 13, s);
+  trace(1, 12, s);
   return MOE_OK;
 }
 
@@ -688,6 +686,21 @@ moe_status moe_permute(const moe_dims* dims, moe_prec prec, const int32_t* topk_
   if (ws && !aligned16(ws)) return MOE_EINVAL;
   return run_permute(dims, prec, topk_idx, x, expert_counts, expert_offsets, row_token, token_row, x_perm,
                      x_perm_scale, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_quantize_mxfp8_rows_t(const void* src_bf16, int64_t ld_src, int32_t cols, const int32_t* gather,
+                                     const int32_t* seg_off, const int32_t* pad_off, int32_t nseg, int64_t p_cap,
+                                     uint8_t* dst, uint8_t* dst_scale, void* stream) {
+  if (nseg < 1 || nseg > 1024 || cols < 0 || p_cap < 0 || ld_src < cols) return MOE_EINVAL;
+  if (cols % 8 || ld_src % 8 || p_cap % 128) return MOE_EUNSUPPORTED;
+  if (p_cap == 0 || cols == 0) return MOE_OK;
+  if (!ptr_ok(src_bf16) || !opt_ok(gather) || !ptr_ok(seg_off) || !ptr_ok(pad_off) || !ptr_ok(dst) ||
+      !ptr_ok(dst_scale))
+    return MOE_EINVAL;
+  if (p_cap * (int64_t)cols > INT32_MAX * 16ll) return MOE_EUNSUPPORTED;
+  MOE_HIP(launch_transpose_quant(static_cast<const bf16_t*>(src_bf16), ld_src, cols, gather, seg_off, pad_off, nseg,
+                                 p_cap, dst, dst_scale, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 moe_status moe_permute_noalloc(const moe_dims* dims, moe_prec prec, const int32_t* topk_idx, const void* x,

@@ -197,12 +197,13 @@ hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
                            int32_t* offsets, int32_t* row_token, int32_t* token_row, void* scratch,
                            hipStream_t s);
-// x_perm[r] = x[row_token[r]]; elem_bytes 2 or 4 (d elements per row).
-hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm, int64_t R, int d,
-                              int elem_bytes, hipStream_t s);
-// Gather + MX quantization along d.
-hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uint8_t* q, uint8_t* scale,
-                                  int64_t R, int d, hipStream_t s);
+// x_perm[r] = x[row_token[r]], pushed from token order through token_row
+// (T tokens, k routes each); elem_bytes 2 or 4 (d elements per row).
+hipError_t launch_dispatch_rows(const void* x, const int32_t* token_row, void* x_perm, int64_t T, int k, int d,
+                                int elem_bytes, hipStream_t s);
+// The same with MX quantization along d (codes [R][d], scales [R][d/32]).
+hipError_t launch_dispatch_quant_mx(const bf16_t* x, const int32_t* token_row, uint8_t* q, uint8_t* scale, int64_t T,
+                                    int k, int d, hipStream_t s);
 // Slab-major [K/128][R][4] scales of the rows row_token[0..R) of a
 // row-major [rows][K/32] scale array (the grouped GEMMs' A-scale layout for
 // gathered token rows).
@@ -296,9 +297,10 @@ struct GemmProblem {
   void* gu_out;              // gate/up: optional [rows][2N] bf16 G | U (kept for the backward)
   uint8_t* dgu_q;           // MX: [rows][2N] dG | dU quantized along the columns
   uint8_t* dgu_scale;       // MX: [rows][2N/32]
-  uint8_t* dgu_t;           // MX: dG^T then dU^T quantized along the routed rows, expert-blocked as
-                            // the weight-gradient operands ([N][Kp_g] at pad_off[g] * N; dU^T N * t_ld later)
-  uint8_t* dgu_t_scale;     // MX: their scales, slab-major ([Kp_g/128][N][4] at pad_off[g] * N / 32)
+  uint8_t* dgu_t;           // MX: [dG^T; dU^T] quantized along the routed rows, expert-blocked as the
+                            // weight-gradient operand of M = 2N rows ([2N][Kp_g] at pad_off[g] * 2N,
+                            // dG^T in rows [0, N), dU^T in rows [N, 2N))
+  uint8_t* dgu_t_scale;     // MX: their scales, slab-major ([Kp_g/128][2N][4] at pad_off[g] * 2N / 32)
   uint8_t* gh_t;            // MX: (w h)^T in the same layout ([N][Kp_g] at pad_off[g] * N)
   uint8_t* gh_t_scale;      // MX: its scales, slab-major
   const int32_t* pad_off;   // MX: [G+1] padded group row offsets (multiples of 128)
@@ -308,6 +310,9 @@ struct GemmProblem {
                             // expert-blocked ([M][Kp_g] block at k_off[g] * M, B alike); MX scales
                             // slab-major ([Kp_g/128][M][4] at k_off[g] * M / 32)
   int64_t c_group_stride;   // elements between group outputs
+  void* C1;                 // K-grouped mode, optional: rows [m_split, M) of every group's output go to
+  int64_t m_split;          // C1 (at row - m_split, same strides), rows [0, m_split) to C: two gradient
+                            // tensors from one launch (dW_gate and dW_up over [dG^T; dU^T])
 };
 
 hipError_t launch_gemm_bf16(const GemmProblem& p, hipStream_t s);

@@ -137,6 +137,8 @@ struct KArgs {
   float* dg_part;
   const int32_t* k_off;
   int64_t c_group_stride;
+  bf16_t* C1;               // optional second output: rows [m_split, M) of every group
+  int64_t m_split;
   bf16_t* gu_out;        // gate/up: optional [rows][2N] G | U output
 };
 
@@ -361,8 +363,20 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
   // 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
   int64_t ldc = p.ldc;
   asm volatile("" : "+s"(ldc));
-  const int64_t row0 = row_begin + m0;
-  bf16_t* C = static_cast<bf16_t*>(p.C) + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) + row0 * ldc;
+  int64_t row0 = row_begin + m0;
+  // Split K-grouped output: a tile wholly past m_split writes C1; a tile
+  // straddling m_split picks the tensor per row (bounds-checked path).
+  bf16_t* Cg = static_cast<bf16_t*>(p.C);
+  bool straddle = false;
+  if (MODE == GEMM_WGRAD && p.C1) {
+    if (row0 >= p.m_split) {
+      Cg = p.C1;
+      row0 -= p.m_split;
+    } else {
+      straddle = row0 + BM > p.m_split;
+    }
+  }
+  bf16_t* C = Cg + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) + row0 * ldc;
   const int rows_left = (int)tile_rows;
   if constexpr (MODE == GEMM_SWIGLU_BWD) {
     // dH' (unscaled by the router weight w) -> dG, dU, w h (the down
@@ -468,6 +482,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
         const int r = i * 32 + 8 * (v >> 2) + (v & 3);
         if (!full_rows && rl0 + r >= rows_left) continue;
         bf16_t* Cr = Cb + (int64_t)r * ldc;
+        if (MODE == GEMM_WGRAD && straddle && row0 + rl0 + r >= p.m_split)  // this row belongs to C1
+          Cr = p.C1 + (int64_t)g * p.c_group_stride + (row0 + rl0 + r - p.m_split) * ldc + colb;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           if (full_cols || colb + j * 32 < N) Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
@@ -478,13 +494,18 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
 // Zero rows [m0, m0 + 256) x columns [n0, n0 + 256) of one group's output
 // (a weight gradient of an expert without rows) with 16-byte stores.
 __device__ __forceinline__ void zero_tile(const KArgs& p, int g, int64_t m0, int n0) {
-  bf16_t* C = static_cast<bf16_t*>(p.C) + (int64_t)g * p.c_group_stride;
   const int rows = (int)min<int64_t>(kBigM, p.M - m0);
   const int cols = min(kBN, p.N - n0);
   const int cpr = cols / 8;  // 16-byte chunks per row
   for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
     const int r = c / cpr, q = c - r * cpr;
-    *reinterpret_cast<u32x4*>(C + (m0 + r) * p.ldc + n0 + q * 8) = u32x4{0, 0, 0, 0};
+    int64_t row = m0 + r;
+    bf16_t* C = static_cast<bf16_t*>(p.C);
+    if (p.C1 && row >= p.m_split) {  // split output: rows past m_split live in C1
+      C = p.C1;
+      row -= p.m_split;
+    }
+    *reinterpret_cast<u32x4*>(C + (int64_t)g * p.c_group_stride + row * p.ldc + n0 + q * 8) = u32x4{0, 0, 0, 0};
   }
 }
 
@@ -714,6 +735,8 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
   a.dg_part = q.dg_part;
   a.k_off = q.k_off;
   a.c_group_stride = q.c_group_stride;
+  a.C1 = static_cast<bf16_t*>(q.C1);
+  a.m_split = q.m_split;
   a.gu_out = static_cast<bf16_t*>(q.gu_out);
   a.C = q.C;
   a.ldc = q.ldc;
@@ -762,6 +785,8 @@ hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
       return run_grouped<GEMM_DUALK>(q, s);
     case GEMM_WGRAD:
       if (q.N % 8 != 0 || !q.k_off || q.G < 1) return hipErrorInvalidValue;
+      // with a second output: two halves of M/2 rows each, the group stride of both
+      if (q.C1 && (q.M != 2 * q.m_split || q.c_group_stride != q.m_split * (int64_t)q.N)) return hipErrorInvalidValue;
       return run_grouped<GEMM_WGRAD>(q, s);
     default: {
       if (q.row_off) return hipErrorInvalidValue;

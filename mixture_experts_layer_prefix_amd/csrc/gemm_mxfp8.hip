@@ -132,16 +132,18 @@ struct MxArgs {
   bf16_t* dgu;              // [rows][2N] dG | dU (bf16)
   uint8_t* dguq;            // [rows][2N] dG | dU quantized along the columns
   uint8_t* dgus;            // [rows][2N/32] their scales
-  uint8_t* dgu_t;           // dG^T then dU^T, E4M3 along the routed rows, expert-blocked (see the epilogue)
+  uint8_t* dgu_t;           // [dG^T; dU^T], E4M3 along the routed rows, expert-blocked (see the epilogue)
   uint8_t* dgu_ts;          // their scales
   uint8_t* gh_t;            // (w h)^T, the same layout (N rows)
   uint8_t* gh_ts;
   const int32_t* pad_off;   // [G+1] padded row offsets of the groups (multiples of 128)
-  int64_t t_ld;             // padded rows of all groups: dU^T starts N * t_ld bytes after dG^T
+  int64_t t_ld;             // padded rows of all groups
   float* dg_part;           // [rows][N/32]
   // K-grouped weight-gradient mode
   const int32_t* k_off;
   int64_t c_group_stride;
+  bf16_t* C1;               // optional second output: rows [m_split, M) of every group
+  int64_t m_split;
   bf16_t* gu_out;           // gate/up: optional [rows][2N] G | U output
 };
 
@@ -341,9 +343,14 @@ struct ZeroRun {
 };
 __device__ __forceinline__ void zero_chunk(const MxArgs& p, ZeroRun& z, int lane) {
   const int64_t e = z.empty[z.slot];
-  uint8_t* base = reinterpret_cast<uint8_t*>(static_cast<bf16_t*>(p.C) + e * p.c_group_stride);
-  __builtin_nontemporal_store(u32x4{0, 0, 0, 0},
-                              reinterpret_cast<u32x4*>(base + (int64_t)z.off * 1024 + lane * 16));
+  int64_t off = (int64_t)z.off * 1024;
+  bf16_t* Cg = static_cast<bf16_t*>(p.C);
+  if (p.C1 && off >= p.m_split * p.N * 2) {  // split output: chunks never straddle (host-checked)
+    Cg = p.C1;
+    off -= p.m_split * p.N * 2;
+  }
+  uint8_t* base = reinterpret_cast<uint8_t*>(Cg + e * p.c_group_stride);
+  __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, reinterpret_cast<u32x4*>(base + off + lane * 16));
   if (++z.off == z.cpr) z.off = 0, ++z.slot;
   --z.left;
 }
@@ -495,9 +502,22 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
   if constexpr (MODE == GEMM_DOWN || MODE == GEMM_DUALK || MODE == GEMM_WGRAD) {
     // Plain bf16 output.  One per-lane base pointer; rows step by compile-time
     // multiples of ldc, the two column blocks by an immediate offset.
-    bf16_t* Cb = static_cast<bf16_t*>(p.C) + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) +
-                 (row_begin + m0 + wm * WM + 4 * (lane >> 5)) * ldc + ntile * BN + wn * WN + (lane & 31);
-    if (tile_rows == BM && ntile * BN + BN <= N) {  // interior tile: no bounds checks
+    // Split K-grouped output: a tile wholly past m_split writes C1; a tile
+    // straddling m_split picks the tensor per row (bounds-checked path).
+    bf16_t* Cg = static_cast<bf16_t*>(p.C);
+    int64_t mrow = row_begin + m0;
+    bool straddle = false;
+    if (MODE == GEMM_WGRAD && p.C1) {
+      if (mrow >= p.m_split) {
+        Cg = p.C1;
+        mrow -= p.m_split;
+      } else {
+        straddle = mrow + BM > p.m_split;
+      }
+    }
+    bf16_t* Cb = Cg + (MODE == GEMM_WGRAD ? (int64_t)g * p.c_group_stride : 0) +
+                 (mrow + wm * WM + 4 * (lane >> 5)) * ldc + ntile * BN + wn * WN + (lane & 31);
+    if (tile_rows == BM && ntile * BN + BN <= N && !straddle) {  // interior tile: no bounds checks
 #pragma clang loop unroll(full)
       for (int i = 0; i < FM; ++i)
 #pragma clang loop unroll(full)
@@ -521,6 +541,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
           const int r = i * 32 + 8 * (v >> 2) + (v & 3);
           if (rl0 + r >= rows_left) continue;
           bf16_t* Cr = Cb + (int64_t)r * ldc;
+          if (straddle && mrow + rl0 + r >= p.m_split)  // this row belongs to C1
+            Cr = p.C1 + (int64_t)g * p.c_group_stride + (mrow + rl0 + r - p.m_split) * ldc + col0;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             if (col0 + j * 32 < N) Cr[j * 32] = f32_to_bf16(acc[i][j][v]);
@@ -574,13 +596,15 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     const int wcol = ntile * BN + wn * WN;  // first of the wave's 64 columns
     const bool wave_cols = wcol < N;        // N is a multiple of 64: all 64 or none
     // This lane's first column in the transposed output, at row 0 of the
-    // group (the second column is kp bytes further), and its scale bytes:
-    // slab-major, [kp / 128][N][4] per group, so row rr's block scale of
-    // column c sits at (rr / 128) N 4 + c 4 + (rr / 32) % 4.
-    const int64_t toff = (cq ? (int64_t)N * p.t_ld : 0) + (int64_t)p.pad_off[g] * N + (int64_t)(wcol + 2 * cp) * kp;
-    uint8_t* tq = p.dgu_t + toff;
-    uint8_t* ts = p.dgu_ts + ((cq ? (int64_t)N * p.t_ld : 0) + (int64_t)p.pad_off[g] * N) / 32 + (wcol + 2 * cp) * 4;
-    auto ts_at = [&](int rr) { return ts + (int64_t)(rr >> 7) * N * 4 + ((rr >> 5) & 3); };
+    // group (the second column is kp bytes further), and its scale bytes.
+    // Group g's block is [2N][kp] at pad_off[g] * 2N: dG^T in its rows
+    // [0, N), dU^T in rows [N, 2N) (one weight-gradient operand of 2N rows);
+    // scales slab-major, [kp / 128][2N][4] per group, so row rr's block scale
+    // of transposed row c sits at (rr / 128) 2N 4 + c 4 + (rr / 32) % 4.
+    const int trow = cq * N + wcol + 2 * cp;  // this lane's first row of [dG^T; dU^T]
+    uint8_t* tq = p.dgu_t + (int64_t)p.pad_off[g] * 2 * N + (int64_t)trow * kp;
+    uint8_t* ts = p.dgu_ts + (int64_t)p.pad_off[g] * 2 * N / 32 + trow * 4;
+    auto ts_at = [&](int rr) { return ts + (int64_t)(rr >> 7) * 2 * N * 4 + ((rr >> 5) & 3); };
     // The same for w h (lanes 0-31).
     uint8_t* hq = p.gh_t + (int64_t)p.pad_off[g] * N + (int64_t)(wcol + 2 * cp) * kp;
     uint8_t* hs = p.gh_ts + (int64_t)p.pad_off[g] * N / 32 + (wcol + 2 * cp) * 4;
@@ -1021,6 +1045,8 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
   a.dg_part = q.dg_part;
   a.k_off = q.k_off;
   a.c_group_stride = q.c_group_stride;
+  a.C1 = static_cast<bf16_t*>(q.C1);
+  a.m_split = q.m_split;
   a.gu_out = static_cast<bf16_t*>(q.gu_out);
   a.spread_small = MODE == GEMM_DOWN ? 1 : 0;
   if (MODE == GEMM_WGRAD) {
@@ -1044,11 +1070,14 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
 hipError_t launch_gemm_mxfp8(const GemmProblem& q, hipStream_t s) {
   if (q.N % 64 != 0 || q.G > kMaxGroups) return hipErrorInvalidValue;
   if (q.mode == GEMM_WGRAD) {
-    // Outputs dense per group ([M][N] at g * M * N), cut into whole 1 KiB
-    // chunks for the background zero fill of groups without rows.
-    if (!q.k_off || q.G < 1 || q.ldc != q.N || q.c_group_stride != q.M * (int64_t)q.N ||
+    // Outputs dense per group ([M][N] at g * M * N, or with C1 two [M/2][N]
+    // halves at g * M/2 * N), cut into whole 1 KiB chunks for the background
+    // zero fill of groups without rows (no chunk straddles the halves).
+    const int64_t rows_c = q.C1 ? q.m_split : q.M;
+    if (!q.k_off || q.G < 1 || q.ldc != q.N || q.c_group_stride != rows_c * (int64_t)q.N ||
         (q.M * (int64_t)q.N * 2) % 1024 != 0 || q.M * (int64_t)q.N * 2 / 1024 > INT32_MAX)
       return hipErrorInvalidValue;
+    if (q.C1 && (q.M != 2 * q.m_split || (q.m_split * (int64_t)q.N * 2) % 1024 != 0)) return hipErrorInvalidValue;
     return run_mx<GEMM_WGRAD>(q, s);
   }
   if (!q.row_off || q.K % kBKB != 0) return hipErrorInvalidValue;

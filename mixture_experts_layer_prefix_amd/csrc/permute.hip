@@ -19,9 +19,10 @@
 //     LDS cursor).
 // The result is the unique expert-major, token-ascending layout.
 //
-// The gather copies rows with 16-byte loads and stores; the MXFP8 variant
-// quantizes every 32-element block of a row on the way (blog post, "MXFP8
-// support": activation quantization fused into the dispatch).
+// The dispatch copy runs from token order: each token's row is read once and
+// stored to its k routed rows with 16-byte accesses; the MXFP8 variant
+// quantizes every 32-element block of the row once on the way (blog post,
+// "MXFP8 support": activation quantization fused into the dispatch).
 #include <mutex>
 
 #include "common.h"
@@ -32,13 +33,13 @@
 // code `scratch` names a host-side stand-in, not a device address: the host
 // reaches the array only through the per-device address that
 // hipGetSymbolAddress returns (moe::noalloc_scratch below).
-static __device__ __align__(256) uint8_t scratch[4u << 20];
+static __device__ __align__(256) uint8_t scratch[16u << 20];
 
 namespace moe {
 
 namespace {
 
-constexpr int kTokBlock = 128;
+constexpr int kTokBlock = 32;  // tokens per schedule block: many blocks even for a few thousand tokens
 
 __global__ void __launch_bounds__(256) hist_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k,
                                                    int32_t* __restrict__ block_counts) {
@@ -56,39 +57,63 @@ __global__ void __launch_bounds__(256) hist_kernel(const int32_t* __restrict__ t
 }
 
 // block_counts[b][e] becomes the number of expert-e routes in the blocks
-// before b (loads batched so that many are in flight); counts and offsets
-// (exclusive scan over the experts) are written once.  The scatter adds
-// offsets[e] to the block's running count.
+// before b; counts and offsets (exclusive scan over the experts) are written
+// once.  The 1024 threads split every expert's column of block counts into
+// 1024 / E contiguous parts: each part sums its blocks (loads batched so that
+// many are in flight), then rewrites them as prefixes starting from the
+// earlier parts' total.  The scatter adds offsets[e] to the block's running
+// count.
 __global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ block_counts, int nb, int E,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   constexpr int kBatch = 16;
+  __shared__ int32_t part_sum[1024];
   __shared__ int32_t s[1024];
-  const int e = threadIdx.x;
-  int32_t total = 0;
-  if (e < E) {
-    for (int b0 = 0; b0 < nb; b0 += kBatch) {
-      int32_t c[kBatch];
+  const int parts = 1024 / E;  // E <= 1024
+  const int tid = threadIdx.x;
+  const int e = tid % E, part = tid / E;
+  const bool on = part < parts;
+  const int b_lo = on ? (int)((int64_t)part * nb / parts) : 0;
+  const int b_hi = on ? (int)((int64_t)(part + 1) * nb / parts) : 0;
+  int32_t sum = 0;
+  for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+    int32_t c[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < nb ? block_counts[(int64_t)(b0 + i) * E + e] : 0;
+    for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < b_hi ? block_counts[(int64_t)(b0 + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        if (b0 + i < nb) block_counts[(int64_t)(b0 + i) * E + e] = total;
-        total += c[i];
-      }
+    for (int i = 0; i < kBatch; ++i) sum += c[i];
+  }
+  part_sum[tid] = sum;
+  __syncthreads();
+  int32_t run = 0, total = 0;
+  if (on) {
+    for (int q = 0; q < parts; ++q) {
+      const int32_t v = part_sum[q * E + e];
+      run += q < part ? v : 0;
+      total += v;
     }
   }
-  s[e] = total;
+  for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+    int32_t c[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < b_hi ? block_counts[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (b0 + i < b_hi) block_counts[(int64_t)(b0 + i) * E + e] = run;
+      run += c[i];
+    }
+  }
+  s[tid] = (on && part == 0) ? total : 0;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    int32_t v = e >= off ? s[e - off] : 0;
+    int32_t v = tid >= off ? s[tid - off] : 0;
     __syncthreads();
-    s[e] += v;
+    s[tid] += v;
     __syncthreads();
   }
-  if (e < E) {
-    counts[e] = total;
-    offsets[e] = s[e] - total;
-    if (e == E - 1) offsets[E] = s[e];
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = s[tid] - total;
+    if (tid == E - 1) offsets[E] = s[tid];
   }
 }
 
@@ -129,18 +154,71 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   }
 }
 
-template <int EB>
-__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ row_token,
-                                                     uint8_t* __restrict__ xp, int64_t R, int64_t vpr) {
-  // vpr: 16-byte vectors per row
-  const int64_t nvec = R * vpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    const int64_t r = v / vpr, c = v - r * vpr;
-    const int64_t src = row_token[r];
-    const u32x4 val = *reinterpret_cast<const u32x4*>(x + (src * vpr + c) * 16);
-    *reinterpret_cast<u32x4*>(xp + (r * vpr + c) * 16) = val;
+// Dispatch as a push from token order: one workgroup per token reads the
+// token's row of x once and stores it to each of its k routed rows
+// (token_row).  The permutation is a bijection, so every routed row is
+// written exactly once and x_perm[r] = x[row_token[r]].  The workgroup is
+// sized so that each thread holds two 16-byte vectors of the row (all of
+// it for rows up to 2048 vectors); the k destination rows are
+// workgroup-uniform (scalar loads).
+__global__ void __launch_bounds__(1024) dispatch_rows_kernel(const uint8_t* __restrict__ x,
+                                                             const int32_t* __restrict__ token_row,
+                                                             uint8_t* __restrict__ xp, int k, int vpr) {
+  const int64_t t = blockIdx.x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x) + t * vpr;
+  for (int v0 = threadIdx.x; v0 < vpr; v0 += 2 * blockDim.x) {
+    const int v1 = v0 + blockDim.x;
+    const bool two = v1 < vpr;
+    const u32x4 a = __builtin_nontemporal_load(src + v0);
+    const u32x4 b = two ? __builtin_nontemporal_load(src + v1) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      u32x4* dst = reinterpret_cast<u32x4*>(xp) + (int64_t)token_row[t * k + j] * vpr;
+      dst[v0] = a;
+      if (two) dst[v1] = b;
+    }
   }
+}
+
+// The MXFP8 dispatch, pushed the same way: one workgroup per token, one
+// 32-element block of its row per thread, quantized once (codes and the
+// E8M0 byte) and stored to each of the token's k routed rows; scales
+// row-major [R][d/32].
+__global__ void __launch_bounds__(1024) dispatch_quant_kernel(const bf16_t* __restrict__ x,
+                                                              const int32_t* __restrict__ token_row,
+                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
+                                                              int k, int d) {
+  const int64_t t = blockIdx.x;
+  const int bpr = d / 32;
+  for (int b = threadIdx.x; b < bpr; b += blockDim.x) {
+    float v[32];
+    uint32_t packed[8];
+    const u32x4* in = reinterpret_cast<const u32x4*>(x + t * d + b * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = __builtin_nontemporal_load(in + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    const uint32_t sc = mx_quant32(v, packed);
+    for (int j = 0; j < k; ++j) {
+      const int64_t row = token_row[t * k + j];
+      u32x4* out = reinterpret_cast<u32x4*>(q + row * d + b * 32);
+      out[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      out[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+      scale[row * bpr + b] = (uint8_t)sc;
+    }
+  }
+}
+
+// Threads of a per-token workgroup covering `items` items with `per` per
+// thread: a whole number of waves, at most 1024.
+unsigned token_block(int items, int per) {
+  int th = (items + per - 1) / per;
+  th = (th + 63) / 64 * 64;
+  return (unsigned)(th < 64 ? 64 : (th > 1024 ? 1024 : th));
 }
 
 // Row blocks of 32 columns, rows optionally gathered.  Scales row-major
@@ -252,19 +330,21 @@ hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm, int64_t R, int d, int elem_bytes,
-                              hipStream_t s) {
-  if (R == 0) return hipSuccess;
-  const int64_t vpr = (int64_t)d * elem_bytes / 16;
-  gather_kernel<16><<<stream_grid(R * vpr), 256, 0, s>>>(static_cast<const uint8_t*>(x), row_token,
-                                                          static_cast<uint8_t*>(x_perm), R, vpr);
+hipError_t launch_dispatch_rows(const void* x, const int32_t* token_row, void* x_perm, int64_t T, int k, int d,
+                                int elem_bytes, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (((int64_t)d * elem_bytes) % 16 || T > INT32_MAX) return hipErrorInvalidValue;
+  const int vpr = (int)((int64_t)d * elem_bytes / 16);
+  dispatch_rows_kernel<<<(unsigned)T, token_block(vpr, 2), 0, s>>>(static_cast<const uint8_t*>(x), token_row,
+                                                                   static_cast<uint8_t*>(x_perm), k, vpr);
   return hipGetLastError();
 }
 
-hipError_t launch_gather_quant_mx(const bf16_t* x, const int32_t* row_token, uint8_t* q, uint8_t* scale, int64_t R,
-                                  int d, hipStream_t s) {
-  if (R == 0) return hipSuccess;
-  gather_quant_kernel<<<stream_grid(R * (d / 32)), 256, 0, s>>>(x, row_token, q, scale, R, d, false);
+hipError_t launch_dispatch_quant_mx(const bf16_t* x, const int32_t* token_row, uint8_t* q, uint8_t* scale, int64_t T,
+                                    int k, int d, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (d % 32 || T > INT32_MAX) return hipErrorInvalidValue;
+  dispatch_quant_kernel<<<(unsigned)T, token_block(d / 32, 1), 0, s>>>(x, token_row, q, scale, k, d);
   return hipGetLastError();
 }
 

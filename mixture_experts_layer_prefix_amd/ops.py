@@ -185,6 +185,13 @@ def combine(o_perm, token_row, topk_w, y_shared, dims: Dims, prec: str):
     return y
 
 
+def combine_into(o_perm, token_row, topk_w, y_shared, dims: Dims, prec: str, y):
+    """moe_combine into a caller-allocated y."""
+    call("moe_combine", ctypes.byref(dims.c()), PREC[prec], _p(o_perm), _p(token_row), _p(topk_w), _p(y_shared), _p(y),
+         _stream())
+    return y
+
+
 class ForwardPlan:
     """Pre-allocated output, routing buffers and workspace of one forward
     configuration, so that repeated calls allocate nothing."""
@@ -239,6 +246,22 @@ def quantize_mxfp8(src, axis):
         scale = torch.empty(rows // 32, cols, dtype=torch.uint8, device=src.device)
     call("moe_quantize_mxfp8", _p(src), rows, cols, axis, _p(dst), _p(scale), _stream())
     return dst, scale
+
+
+def quantize_mxfp8_rows_t(src, seg_off, pad_off, gather=None):
+    """moe_quantize_mxfp8_rows_t: the routed-row-axis MX quantization of a
+    weight-gradient operand.  src [rows][cols] bf16; seg_off, pad_off int32
+    [nseg+1] device tensors (pad_off: multiples of 128).  Returns the codes
+    (p_cap * cols bytes) and scales (p_cap * cols / 32 bytes), p_cap =
+    pad_off's last entry rounded to 128, as flat uint8 tensors."""
+    cols = src.shape[1]
+    p_cap = int(pad_off[-1].item())
+    p_cap = (p_cap + 127) // 128 * 128
+    dst = torch.empty(max(p_cap * cols, 16), dtype=torch.uint8, device=src.device)
+    scale = torch.empty(max(p_cap * cols // 32, 16), dtype=torch.uint8, device=src.device)
+    call("moe_quantize_mxfp8_rows_t", _p(src), src.stride(0), cols, _p(gather), _p(seg_off), _p(pad_off),
+         seg_off.numel() - 1, p_cap, _p(dst), _p(scale), _stream())
+    return dst[:p_cap * cols], scale[:p_cap * cols // 32]
 
 
 def prepare_mxfp8(weights: Weights, dims: Dims) -> Weights:
@@ -319,8 +342,7 @@ def layer_backward(dy, x, weights: Weights, routing, dims: Dims, prec: str, rout
 
 FWD_STAGES = ("route", "schedule", "shared_ffn", "gate_up", "down", "combine")
 BWD_STAGES = ("prepare", "replay_gate_up", "down_dgrad_swiglu", "router_weight_grad", "gate_up_dgrad",
-              "shared_dgrad", "dx", "transposes", "wgrad_down", "wgrad_gate", "wgrad_up", "shared_wgrad",
-              "router_grad")
+              "shared_dgrad", "dx", "transposes", "wgrad_down", "wgrad_gate_up", "shared_wgrad", "router_grad")
 
 
 class StageTimer:

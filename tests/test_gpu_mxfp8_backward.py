@@ -234,3 +234,41 @@ def check_backward_sampled(D, ntok=128, seed=12):
         for n, e in es.items():
             assert e <= TOL["bf16"], (n, e)
     check_mx_bound(errs, D.name)
+
+
+@pytest.mark.parametrize("name", ["mxb_ragged", "mxb_pad_gap", "mxb_max_E_k"])
+def test_routed_row_quantization_bit_exact(name):
+    """The weight-gradient operands x^T and dY^T of the MXFP8 backward:
+    moe_quantize_mxfp8_rows_t (the kernel the backward runs on them) against
+    the oracle's quantizer along the routed rows, bit for bit: every expert's
+    rows (gathered tokens, expert-major order), zero-padded to a multiple of
+    128 and cut into blocks of 32 rows, one block scale per column and
+    block; codes [d][Kp_e] and slab-major scales per expert."""
+    import mixture_experts_layer_prefix_amd as M
+    D = SMALL[name]
+    say("[case] routed-row quantization", name, D)
+    hp = HostProblem(D)
+    rt = hp.routing()
+    counts, offsets, row_token = rt["counts"], rt["offsets"], rt["row_token"]
+    kp = (counts.astype(np.int64) + 127) // 128 * 128
+    pad = np.concatenate([[0], np.cumsum(kp)]).astype(np.int32)
+    dev = lambda a: torch.as_tensor(np.ascontiguousarray(a), device="cuda")
+    for tensor in ("x", "dy"):
+        src = hp.p.device(tensor)
+        codes, scales = M.quantize_mxfp8_rows_t(src, dev(offsets.astype(np.int32)), dev(pad), dev(row_token))
+        codes, scales = to_np(codes), to_np(scales)
+        host = hp.p.host(tensor)
+        d = D.d
+        for e in range(D.E):
+            n, k_e = int(counts[e]), int(kp[e])
+            if k_e == 0:
+                continue
+            rows = np.zeros((k_e, d))
+            rows[:n] = host[row_token[offsets[e]:offsets[e + 1]]]
+            rq, rs = O.mx_quantize(rows, axis=0)          # blocks of 32 rows of one column
+            got_c = codes[pad[e] * d:(pad[e] + k_e) * d].reshape(d, k_e)
+            assert np.array_equal(got_c, rq.T), (tensor, e)
+            got_s = scales[pad[e] * d // 32:(pad[e] + k_e) * d // 32].reshape(k_e // 128, d, 4)
+            want_s = rs.reshape(k_e // 128, 4, d).transpose(0, 2, 1)
+            assert np.array_equal(got_s, want_s), (tensor, e)
+    say("   x and dY: every expert's block equal to the oracle quantizer")

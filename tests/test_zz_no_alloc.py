@@ -52,10 +52,10 @@ def test_noalloc_matches_permute_on_consecutive_calls(prec):
 
 
 def test_noalloc_at_capacity_then_smaller():
-    """ceil(T/128) * E * 4 bytes equal to the 4 MiB array, then a small call."""
+    """ceil(T/32) * E * 4 bytes equal to the 16 MiB array, then a small call."""
     import mixture_experts_layer_prefix_amd as M
     cap = M._lib.lib().moe_permute_noalloc_scratch_bytes()
-    T = cap // (1024 * 4) * 128
+    T = cap // (1024 * 4) * 32
     compare(gen.Dims("na_cap", T, 64, 1024, 2, 64, 0, 0, "bf16", 1.2))
     compare(gen.Dims("na_after", 257, 64, 1024, 16, 64, 0, 0, "bf16", 0.0))
 
@@ -64,7 +64,7 @@ def test_noalloc_rejects_beyond_capacity():
     import mixture_experts_layer_prefix_amd as M
     from mixture_experts_layer_prefix_amd import _lib as L
     cap = L.lib().moe_permute_noalloc_scratch_bytes()
-    T = cap // (1024 * 4) * 128 + 1
+    T = cap // (1024 * 4) * 32 + 1
     d = M.Dims(T, 64, 1024, 2, 64)
     buf = torch.empty(16, dtype=torch.int32, device="cuda")
     p = buf.data_ptr()
