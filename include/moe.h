@@ -295,6 +295,15 @@ moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, i
  *     weight gradients done, 12 router gradient done. */
 moe_status moe_trace_events(int which, void* const* events, int n);
 
+/* Tuning knob (host state of the library, process-wide, not thread-safe):
+ * caps the persistent grids of the grouped GEMMs at n workgroups (rounded
+ * down to a multiple of 8, the XCD count, and at least 8), e.g. to leave
+ * compute units to other work; n = 0 restores one workgroup per compute
+ * unit.  Results are bitwise identical for every n: which workgroup runs a
+ * tile, and in which order, never changes a tile's arithmetic (blog post,
+ * "Determinism").  Takes effect for calls enqueued afterwards. */
+moe_status moe_set_max_workgroups(int n);
+
 /* MX quantization of a bf16 matrix src [rows][cols] (OCP MX v1.0; blog post
  * "MXFP8 support": a quantization kernel pre-quantizes the weights).
  * axis = 0: one block per 32 consecutive elements of a row (cols % 32 == 0):

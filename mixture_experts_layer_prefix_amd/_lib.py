@@ -67,6 +67,7 @@ _SIGS = {
                            ctypes.POINTER(moe_routing), _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_layer_backward": ([_DIMS, ctypes.c_int, _P, _P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing),
                             _P, ctypes.POINTER(moe_grads), _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_set_max_workgroups": ([ctypes.c_int], ctypes.c_int),
     "moe_trace_events": ([ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int], ctypes.c_int),
     "moe_transpose_weights": ([_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P], ctypes.c_int),
     "moe_quantize_mxfp8": ([_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P], ctypes.c_int),

@@ -22,6 +22,9 @@ void trace(int which, int i, hipStream_t s) {
   if (i < g_ntrace[which] && g_trace[which][i]) (void)hipEventRecord(static_cast<hipEvent_t>(g_trace[which][i]), s);
 }
 
+// Cap on the persistent GEMM grids (moe_set_max_workgroups); 0: none.
+int g_max_wg = 0;
+
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -643,7 +646,21 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
 
 }  // namespace
 
+namespace moe {
+int gemm_grid(int num_cus) {
+  int wg = (num_cus + 7) / 8 * 8;
+  if (g_max_wg > 0 && g_max_wg < wg) wg = g_max_wg / 8 * 8;
+  return wg < 8 ? 8 : wg;
+}
+}  // namespace moe
+
 extern "C" {
+
+moe_status moe_set_max_workgroups(int n) {
+  if (n < 0) return MOE_EINVAL;
+  g_max_wg = n;
+  return MOE_OK;
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {

@@ -39,6 +39,22 @@ __device__ __forceinline__ float sigmoid_f32(float z) { return __builtin_amdgcn_
 
 __device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
 
+// Direct global -> LDS load of BYTES per lane (buffer_load ... lds): the wave
+// writes 64 * BYTES contiguous bytes starting at lds_dst.  Only whole-dword
+// transfers are allowed: a 1- or 2-byte transfer still writes a full dword
+// per lane, which overruns the destination (it once corrupted the group
+// tables behind a slab ring).  The destination must be BYTES-aligned.
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst, uint32_t voffset,
+                                        uint32_t soffset) {
+  static_assert(BYTES == 4 || BYTES == 16, "LDS-DMA transfers whole dwords: 4 or 16 bytes per lane");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_dst, 16, voffset, soffset, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_dst, 4, voffset, soffset, 0, 0);
+}
+
 // Reductions over the 32 lanes of each wave half (lanes 0-31 and 32-63) with
 // the result in every lane of the half, without LDS round trips: four DPP
 // steps inside each 16-lane row (partner lane l^1, l^2, then the mirrored
@@ -315,6 +331,10 @@ struct GemmProblem {
                             // tensors from one launch (dW_gate and dW_up over [dG^T; dU^T])
 };
 
+// Workgroups of the persistent GEMM grids: all compute units, or at most
+// the cap set with moe_set_max_workgroups (rounded down to a multiple of 8,
+// at least 8).  Results do not depend on it.
+int gemm_grid(int num_cus);
 hipError_t launch_gemm_bf16(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_mxfp8(const GemmProblem& p, hipStream_t s);

@@ -7,11 +7,10 @@
 // "Scheduling": tokens of an expert land in contiguous rows so the
 // expert-grouped GEMMs start without reordering).
 //
-// Tiles.  One persistent grid; every workgroup (4 waves, 2 x 2) loops over
-// output tiles of two kinds:
-//  * big tiles, 256 x 256: each wave owns 128 x 128 as 4 x 4 MFMA blocks, so
-//    a 16-byte LDS fragment feeds 4 MFMAs and LDS traffic stays at half the
-//    CU's LDS bandwidth while the matrix cores run;
+// Tiles.  One persistent grid of one 512-thread workgroup per compute unit
+// (8 waves as 2 x 4, two per SIMD) loops over output tiles of two kinds:
+//  * big tiles, 256 x 256: each wave owns 128 x 64 as 4 x 2 MFMA blocks of
+//    32 x 32 (v_mfma_f32_32x32x16_bf16, fp32 accumulators);
 //  * small tiles, 64 x 256, for the last rows of an expert (a group of n
 //    rows gets floor(n / 256) big tiles, one more if the remainder exceeds
 //    128, and 64-row tiles for a smaller remainder).  Under skewed routing
@@ -21,10 +20,14 @@
 //    bound by memory latency.  In the down projection they are spread
 //    evenly through the tile order so they stream weights while other CUs
 //    run big tiles.
-// K advances 64 at a time through two LDS buffers: the next slab is fetched
-// from global memory into registers while the MFMAs consume the current one
-// (one barrier per slab).  LDS rows are padded by 16 bytes, so 16-byte
-// fragment reads of consecutive rows fall in distinct banks.
+// K advances 64 at a time through a ring of LDS slabs filled straight from
+// global memory by buffer_load ... lds (16 bytes per lane, no register
+// staging; 32-bit per-lane offsets with the K position in the scalar offset
+// and buffer descriptors bounding every access), one barrier per slab.  Each
+// 128-byte LDS row holds its eight 16-byte chunks XOR-swizzled by the row
+// index (swz), so the 16-byte fragment reads of 32 consecutive rows are free
+// of bank conflicts; the fragment reads of the next K step are interleaved
+// with the MFMAs of the current one.
 //
 // Order.  M-tile prefixes per group are built on the device (empty experts
 // cost nothing, the host never learns the counts).  Logical tiles are dealt
@@ -257,13 +260,11 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
       : br0;
   const uint32_t boff = (uint32_t)((lane >> 3) * ldb * 2) + chunk * 16;
 
-  typedef __attribute__((address_space(3))) void lds_void;
   auto issue = [&](int buf, int k0) {
     const int ka = k_begin + k0;
 #pragma unroll
     for (int i = 0; i < AR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(As + (buf * BM + i * RPR + wave * 8) * kBK), 16,
-                                               aoff[i], ka * 2, 0, 0);
+      lds_dma<16>(ar, As + (buf * BM + i * RPR + wave * 8) * kBK, aoff[i], ka * 2);
     const bool second = MODE == GEMM_DUALK && k0 >= p.k_half;
     const int kb = MODE == GEMM_DUALK ? (second ? k0 - p.k_half : k0) : ka;
 #pragma unroll
@@ -276,8 +277,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& p, bf16_t* smem, int g, i
       int r0 = PAIRED ? (blk >> 1) * 32 + (lr & 31) : lr;
       r0 = min(r0, p.N - first_row - 8);  // rows past N load valid rows; their outputs are not stored
       const bool use1 = PAIRED ? (blk & 1) != 0 : second;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(use1 ? br1 : br0, (lds_void*)(Bs + (buf * BN + lr) * kBK), 16, boff,
-                                               (uint32_t)((r0 * ldb + kb) * 2), 0, 0);
+      lds_dma<16>(use1 ? br1 : br0, Bs + (buf * BN + lr) * kBK, boff, (uint32_t)((r0 * ldb + kb) * 2));
     }
   };
 
@@ -757,8 +757,7 @@ hipError_t run_grouped(const GemmProblem& q, hipStream_t s) {
     a.G = 1;
     tiles_of(q.M, a.single_big, a.single_small);
   }
-  int wg = num_cus();
-  wg = (wg + 7) / 8 * 8;
+  const int wg = gemm_grid(num_cus());
   gemm_bf16_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes + kTabBytes, s>>>(a);
   return hipGetLastError();
 }

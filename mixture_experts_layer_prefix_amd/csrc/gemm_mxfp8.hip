@@ -33,6 +33,9 @@ constexpr int kBigM = 256, kSmallM = 64, kBN = 256;
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int stage_bytes(int bm) { return bm * kBKB + kBN * kBKB + bm * 4 + kBN * 4; }
+// Every LDS-DMA destination (16-byte data rows, 4-byte scale dwords) stays
+// aligned to its transfer size when the stages are laid out back to back.
+static_assert(stage_bytes(256) % 16 == 0 && stage_bytes(64) % 16 == 0 && kBKB % 16 == 0, "LDS-DMA alignment");
 constexpr size_t kSmemBytes = 2 * stage_bytes(kBigM) > 3 * stage_bytes(kSmallM) ? 2 * stage_bytes(kBigM)
                                                                                  : 3 * stage_bytes(kSmallM);
 // Group tables in LDS after the slab ring (see the bf16 kernel).
@@ -293,36 +296,29 @@ __device__ __forceinline__ void mx_issue(const MxArgs& p, const MxLoad<BM>& L, u
   constexpr int STG = stage_bytes(BM);
   constexpr bool PAIRED = MODE == GEMM_GATEUP || MODE == GEMM_GU;
   constexpr bool DUAL = MODE == GEMM_DUALK;
-  typedef __attribute__((address_space(3))) void lds_void;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t ldb = L.ldb;
   uint8_t* S = smem + st * STG;
   const int ka = L.k_begin + k0;
 #pragma unroll
   for (int i = 0; i < AR; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ar, (lds_void*)(S + (i * RPR + wave * 8) * kBKB), 16, L.aoff[i], ka, 0,
-                                             0);
+    lds_dma<16>(L.ar, S + (i * RPR + wave * 8) * kBKB, L.aoff[i], ka);
   const bool second = DUAL && k0 >= p.k_half;
   const int kb = DUAL ? (second ? k0 - p.k_half : k0) : ka;
 #pragma unroll
   for (int i = 0; i < BR; ++i) {
     int r0 = PAIRED ? i * (RPR / 2) + (wave & 3) * 8 : i * RPR + wave * 8;
     r0 = min(r0, L.brows - 8);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? L.br1 : L.br0,
-                                             (lds_void*)(S + BM * kBKB + (i * RPR + wave * 8) * kBKB), 16, L.boff,
-                                             (uint32_t)(r0 * ldb + kb), 0, 0);
+    lds_dma<16>(second ? L.br1 : L.br0, S + BM * kBKB + (i * RPR + wave * 8) * kBKB, L.boff, (uint32_t)(r0 * ldb + kb));
   }
   // Scale dwords: row-major operands at K / 32 in the row, slab-major ones
   // at slab * (bytes per slab).
   const uint32_t sa_off = L.sa_slab ? (uint32_t)(ka >> 7) * L.sa_slab : (uint32_t)(ka / 32);
   const uint32_t sb_off = (uint32_t)(kb >> 7) * L.sb_slab;
   if (wave < BM / 64)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.asr, (lds_void*)(S + (BM + BN) * kBKB + wave * 256), 4, L.scoff,
-                                             sa_off, 0, 0);
+    lds_dma<4>(L.asr, S + (BM + BN) * kBKB + wave * 256, L.scoff, sa_off);
   if (wave >= 4)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? L.bsr1 : L.bsr0,
-                                             (lds_void*)(S + (BM + BN) * kBKB + BM * 4 + (wave - 4) * 256), 4,
-                                             L.scoff, sb_off, 0, 0);
+    lds_dma<4>(second ? L.bsr1 : L.bsr0, S + (BM + BN) * kBKB + BM * 4 + (wave - 4) * 256, L.scoff, sb_off);
 }
 
 // One BM x 256 output tile whose load state L is set up.  prefetched: its
@@ -332,9 +328,10 @@ __device__ __forceinline__ void mx_issue(const MxArgs& p, const MxLoad<BM>& L, u
 // Background zero fill of the weight gradients of experts without rows
 // (K-grouped mode).  The dense [M][N] outputs of those experts are cut into
 // 1 KiB chunks; every wave owns a contiguous run of them and stores
-// kZeroPerSlab chunks after each slab it issues inside a K loop, so the
-// stores drain under the MFMA work instead of queueing as zero tiles at the
-// end of the launch; the wave stores what is left once its tiles are done.
+// kZeroPerSlab chunks just before each slab it issues inside a K loop, so
+// the stores drain under the MFMA work instead of queueing as zero tiles at
+// the end of the launch; the wave stores what is left once its tiles are
+// done.
 constexpr int kZeroPerSlab = 2;
 struct ZeroRun {
   const int32_t* empty;  // LDS: ids of the experts without rows
@@ -453,7 +450,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
   };
   // background zero stores (K-grouped mode; the waits below assume one slab in flight)
   constexpr bool ZB = MODE == GEMM_WGRAD && NS == 2;
-  bool zprev = false;  // this wave stored kZeroPerSlab zero chunks after its last slab issue
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % NS;
     read_scales(st);
@@ -464,9 +460,10 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     mma(1);
     if (kt + NS - 1 < KT) {
       if constexpr (ZB) {
-        // Loads and stores complete in issue order: the zero stores issued
-        // after slab kt + 1 may stay in flight.
-        if (zprev) wait_vmcnt<kZeroPerSlab>(); else wait_vmcnt<0>();
+        // The zero stores went out before slab kt + 1's loads, which are the
+        // youngest operations in flight: wait for everything (no assumption
+        // about the completion order of stores and loads).
+        wait_vmcnt<0>();
       } else {
         if (any_sc) wait_vmcnt<(NS - 2) * (LPS + 1)>(); else wait_vmcnt<(NS - 2) * LPS>();
       }
@@ -474,17 +471,15 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
       wait_vmcnt<0>();
     }
     __syncthreads();
-    zprev = false;
     if (kt + NS < KT) {
-      issue(st, (kt + NS) * kBKB);
       if constexpr (ZB) {
-        // not after the tile's last slab, whose wait takes everything
+        // background zero stores, issued ahead of the next slab's loads
         if (kt + NS < KT - 1 && zr->left >= kZeroPerSlab) {
 #pragma unroll
           for (int s = 0; s < kZeroPerSlab; ++s) zero_chunk(p, *zr, lane);
-          zprev = true;
         }
       }
+      issue(st, (kt + NS) * kBKB);
     }
   }
   // The ring is free: start the next tile's loads under this epilogue.
@@ -1056,8 +1051,7 @@ hipError_t run_mx(const GemmProblem& q, hipStream_t s) {
     a.small = q.tile_prefix + (q.G + 1);
     mx_tile_prefix_kernel<<<1, 1024, 0, s>>>(q.row_off, q.G, q.tile_prefix, q.tile_prefix + (q.G + 1));
   }
-  int wg = num_cus_mx();
-  wg = (wg + 7) / 8 * 8;
+  const int wg = gemm_grid(num_cus_mx());
   gemm_mxfp8_kernel<MODE><<<(unsigned)wg, kThreads, kSmemBytes + kTabBytes, s>>>(a);
   return hipGetLastError();
 }

@@ -115,6 +115,11 @@ def test_small_mxfp8_layer(name):
     assert e_qo <= 3e-2 and e_qy <= 3e-2
     y2, _ = M.layer_forward(t["x"], wq, md, "mxfp8", bias=t["bias"])
     assert torch.equal(y, y2)
+    # the layer forward equals the staged entry points bit for bit (expert
+    # FFNs, shared FFN, moe_combine)
+    y_sh = M.shared_ffn(t["x"], wq, md, "mxfp8") if D.S else None
+    y_st = M.combine(o_perm, token_row, tw, y_sh, md, "mxfp8")
+    assert torch.equal(y, y_st), "moe_layer_forward differs from the staged entry points"
     # Against the exact layer: the stated 6e-2 bound (an expected failure
     # where MX rounding of the operands alone already exceeds it).
     check_mx_bound({"y": (e_y, rel_err(yq, ref["y"])), "o_perm": (e_o, rel_err(oq, ref["o_perm"]))}, name)
