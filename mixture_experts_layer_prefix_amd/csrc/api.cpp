@@ -238,7 +238,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP
 moe_status run_route(const moe_dims* D, moe_prec prec, const void* x, const void* wr, const float* bias,
                      float* logits, int32_t* idx, float* w, hipStream_t s) {
   const bool f32 = prec == MOE_F32;
-  MOE_HIP(launch_router_logits(f32, x, wr, bias, logits, D->T, D->d, D->E, s));
+  MOE_HIP(launch_router_logits(f32, x, wr, bias, logits, w, D->T, D->d, D->E, D->k, s));
   MOE_HIP(launch_topk(f32, logits, x, wr, bias, idx, w, D->T, D->d, D->E, D->k, s));
   return MOE_OK;
 }

@@ -143,6 +143,8 @@ struct KArgs {
   bf16_t* C1;               // optional second output: rows [m_split, M) of every group
   int64_t m_split;
   bf16_t* gu_out;        // gate/up: optional [rows][2N] G | U output
+  float* rowabs;         // router GEMM, optional: rowabs[row * rowabs_stride] = max over the columns of
+  int rowabs_stride;     // sum_k |A[row][k]| |B[col][k]| (as fp32 bits, by atomic max; zeroed by the caller)
 };
 
 // LDS swizzle of a 128-byte row: chunk position = logical chunk ^ swz(row).
@@ -634,9 +636,16 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
     pa[i] = p.A + r * p.lda + kc;
     pb[i] = p.B0 + (int64_t)min(ntile * BN + row, p.N - 1) * p.K + kc;
   }
-  f32x16 acc;
+  f32x16 acc, aab;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int v = 0; v < 16; ++v) acc[v] = aab[v] = 0.0f;
+  const bool want_abs = p.rowabs != nullptr;
+  auto abs8 = [](bf16x8 v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] &= 0x7FFF7FFFu;
+    return __builtin_bit_cast(bf16x8, u);
+  };
   // Slabs move global -> registers -> LDS; kPD slabs are in flight in
   // registers (one K loop of a 64 x 64 tile is otherwise a chain of
   // load-latency waits).
@@ -675,6 +684,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
           const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
           const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+          if (want_abs) aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abs8(af), abs8(bf), aab, 0, 0, 0);
         }
         if (kt + 1 < KT) st((u + 1) % kPD, (u + 1) & 1);
         __syncthreads();
@@ -687,6 +697,18 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
     const int64_t row = m0 + wm * WM + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     const int col = ntile * BN + wn * WN + (lane & 31);
     if (row < p.M && col < p.N) C[row * p.ldc + col] = acc[v] + (p.bias ? p.bias[col] : 0.0f);
+  }
+  if (want_abs) {
+    // Largest sum of |x_k| |w_k| of each row over this tile's 64 columns:
+    // the 32 columns of a wave half in DPP steps, then an atomic maximum of
+    // the (non-negative) fp32 bits; order-independent, so deterministic.
+    // Columns past N repeat expert N-1 (clamped loads): a real expert's sum.
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + wm * WM + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const uint32_t m = half_max32_u(__float_as_uint(aab[v]) & 0x7FFFFFFFu);
+      if ((lane & 31) == 0 && row < p.M) atomicMax(reinterpret_cast<unsigned int*>(p.rowabs + row * p.rowabs_stride), m);
+    }
   }
 }
 
@@ -799,6 +821,8 @@ hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
       a.C = q.C;
       a.ldc = q.ldc;
       a.bias = q.bias;
+      a.rowabs = q.rowabs;
+      a.rowabs_stride = q.rowabs_stride;
       const dim3 grid((unsigned)((q.M + 63) / 64), (unsigned)((q.N + 63) / 64));
       gemm_bf16_small_n_kernel<<<grid, 256, 0, s>>>(a);
       return hipGetLastError();

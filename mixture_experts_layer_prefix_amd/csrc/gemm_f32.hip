@@ -26,14 +26,17 @@ __global__ void __launch_bounds__(1024) f32_tile_prefix(const int32_t* __restric
   }
 }
 
-template <int MODE>
+// ABS (router logits): also the largest sum of |a_k| |b_k| of each row over
+// the tile's columns, into rowabs[row * rowabs_stride] by atomic maximum.
+template <int MODE, bool ABS = false>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ a_rows,
                                                        int64_t lda, const int32_t* __restrict__ row_off, int64_t M,
                                                        int G, const float* __restrict__ B0,
                                                        const float* __restrict__ B1, int64_t bstride, int N, int K,
                                                        float* __restrict__ C, int64_t ldc,
                                                        const float* __restrict__ bias,
-                                                       const int32_t* __restrict__ prefix) {
+                                                       const int32_t* __restrict__ prefix, float* rowabs = nullptr,
+                                                       int rowabs_stride = 0) {
   constexpr bool GU = MODE == GEMM_GATEUP;
   __shared__ float As[TK][TM + 1];
   __shared__ float Bs[GU ? 2 : 1][TK][TN + 1];
@@ -53,6 +56,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
   const int n0 = blockIdx.y * TN;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[2][4][4] = {};
+  float aab[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += TK) {
     for (int i = threadIdx.x; i < TM * TK; i += 256) {
       int r = i / TK, kk = i % TK;
@@ -82,6 +86,8 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
         for (int j = 0; j < 4; ++j) {
           float b = Bs[m][kk][tx * 4 + j];
           for (int i = 0; i < 4; ++i) acc[m][i][j] = fmaf(a[i], b, acc[m][i][j]);
+          if (ABS)
+            for (int i = 0; i < 4; ++i) aab[i][j] = fmaf(fabsf(a[i]), fabsf(b), aab[i][j]);
         }
     }
     __syncthreads();
@@ -97,6 +103,16 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
       if (GU) v = silu_f32(acc[0][i][j]) * acc[1][i][j];
       else v = acc[0][i][j] + (bias ? bias[col] : 0.0f);
       C[grow * ldc + col] = v;
+    }
+  }
+  if (ABS) {
+    for (int i = 0; i < 4; ++i) {
+      int64_t lr = m0 + ty * 4 + i;
+      if (lr >= n_g) continue;
+      float mx = 0.0f;
+      for (int j = 0; j < 4; ++j)
+        if (n0 + tx * 4 + j < N) mx = fmaxf(mx, aab[i][j]);
+      atomicMax(reinterpret_cast<unsigned int*>(rowabs + (row_begin + lr) * rowabs_stride), __float_as_uint(mx));
     }
   }
 }
@@ -120,6 +136,10 @@ hipError_t launch_gemm_f32(const GemmProblem& q, hipStream_t s) {
   if (q.mode == GEMM_GATEUP)
     gemm_f32_kernel<GEMM_GATEUP><<<grid, 256, 0, s>>>(A, q.a_rows, q.lda, q.row_off, q.M, q.G, B0, B1,
                                                       q.b_group_stride, q.N, q.K, C, q.ldc, q.bias, prefix);
+  else if (q.rowabs)
+    gemm_f32_kernel<GEMM_DOWN, true><<<grid, 256, 0, s>>>(A, q.a_rows, q.lda, q.row_off, q.M, q.G, B0, B1,
+                                                          q.b_group_stride, q.N, q.K, C, q.ldc, q.bias, prefix,
+                                                          q.rowabs, q.rowabs_stride);
   else
     gemm_f32_kernel<GEMM_DOWN><<<grid, 256, 0, s>>>(A, q.a_rows, q.lda, q.row_off, q.M, q.G, B0, B1,
                                                     q.b_group_stride, q.N, q.K, C, q.ldc, q.bias, prefix);

@@ -5,17 +5,25 @@
 // and a router weight for each; paper summary section 2.1: the weights are
 // normalized over the selected experts (softmax of the selected logits).
 //
-// The logits are an MFMA GEMM (fp32 accumulation) followed by the top-k
-// kernel: one wavefront per token, ceil(E/64) logits per lane, rounds of a
-// wave-wide arg-max (larger value, then smaller id).  The fp32 accumulation
-// order of the GEMM differs from a correctly rounded dot product by far less
-// than kBand.  When the k-th and (k+1)-th logits lie within kBand, the
-// experts whose logits lie between the (k+1)-th minus kBand and the k-th
-// plus kBand/2 get their logits recomputed as fp64 dot products rounded once
-// to fp32 (plus the fp32 bias), and the selection is redone.  Experts above
-// that window are in the top-k and experts below it are out under any
-// rounding of that size, so the selected set is the one a selection on
-// correctly rounded logits makes.
+// The logits are a GEMM with fp32 accumulation (MFMA in bf16, FMA in fp32)
+// followed by the top-k kernel: one wavefront per token, ceil(E/64) logits
+// per lane, rounds of a wave-wide arg-max (larger value, then smaller id).
+//
+// Exact selection.  A sum of d products accumulated in fp32 lies within
+// gamma_d * sum_i |x_i w_i| of the exact dot product, gamma_d = d u / (1 - d
+// u), u = 2^-24 (Higham, "Accuracy and Stability of Numerical Algorithms",
+// 2nd ed., section 3.1); the logits GEMM also accumulates sum_i |x_i||w_i|
+// and keeps, per token, its largest value A over the experts.  So every GPU
+// logit lies within delta = 2 (gamma_{d+2} + 2u) A + 4u (|l_k| + |l_k+1|) of
+// the correctly rounded logit plus bias (the factor 2 covers accumulation
+// orders inside the matrix cores; the last term the roundings of the logit
+// and of the bias add).  When the k-th and (k+1)-th GPU logits are more than
+// 2 delta apart, the selection is the one on correctly rounded logits.
+// Otherwise every expert whose GPU logit lies in [l_k+1 - 2 delta, l_k +
+// 2 delta] gets its logit recomputed as an fp64 dot product rounded once to
+// fp32 (plus the fp32 bias) and the selection is redone: experts above that
+// window are in the top-k and experts below it are out under any error of
+// that size, so the result is the selection on correctly rounded logits.
 #include <math.h>
 
 #include "common.h"
@@ -24,7 +32,6 @@ namespace moe {
 
 namespace {
 
-constexpr float kBand = 1.0f / 4096.0f;
 constexpr int kMaxK = 16;
 
 __device__ __forceinline__ void better(float& bv, int& bid, float ov, int oid) {
@@ -101,10 +108,15 @@ template <int PER_LANE>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, const void* __restrict__ x,
                                                    const void* __restrict__ wr, const float* __restrict__ bias,
                                                    bool act_f32, int32_t* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w, int64_t T, int d, int E, int k) {
+                                                   float* __restrict__ topk_w, int64_t T, int d, int E, int k,
+                                                   float gamma) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront leaves; no block barrier below
+  // max_e sum_i |x_ti| |W_r[e][i]| left by the logits kernel in this token's
+  // first topk_w slot (read before this wave writes its weights there)
+  const float abs_sum = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                      __builtin_bit_cast(int, topk_w[t * k])));
   float v[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
@@ -115,12 +127,16 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   float lv[kMaxK + 1];
   int lid[kMaxK + 1];
   select_rounds<PER_LANE>(v, E, rounds, lane, lv, lid);
-  if (k < E && lv[k - 1] - lv[k] <= kBand) {
+  constexpr float u = 5.9604645e-8f;  // 2^-24
+  const float delta = 2.0f * (gamma + 2.0f * u) * abs_sum * (1.0f + 4.0f * u) +
+                      4.0f * u * (fabsf(lv[k - 1]) + (k < E ? fabsf(lv[k]) : 0.0f));
+  if (k < E && lv[k - 1] - lv[k] <= 2.0f * delta) {
     // Near tie at the selection boundary.  Experts above hi are in the top-k
-    // whatever the rounding (fewer than k logits exceed the k-th largest);
-    // experts below lo are out (at least k+1 logits lie above them).  Only
-    // the ones in between get exact logits before the selection is redone.
-    const float lo = lv[k] - kBand, hi = lv[k - 1] + 0.5f * kBand;
+    // under any logit error up to delta (fewer than k GPU logits exceed the
+    // k-th largest); experts below lo are out (at least k+1 lie above them).
+    // Only the ones in between get exact logits before the selection is
+    // redone.
+    const float lo = lv[k] - 2.0f * delta, hi = lv[k - 1] + 2.0f * delta;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
       int e0 = 64 * i;
@@ -130,8 +146,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         mask &= mask - 1;
         int e = e0 + b;
         double acc = 0.0;
-        // 8 consecutive elements per lane per step (d is a multiple of 8), so
-        // the row streams with wide loads and many requests in flight.
+        // 8 consecutive elements per lane per step (d is a multiple of 8).
 #pragma unroll 1
         for (int c = lane * 8; c < d; c += 512) {
           double xv[8], wv[8];
@@ -176,8 +191,17 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 
 }  // namespace
 
+namespace {
+// topk_w[t * k] = 0 for every token: the slot the logits kernel's |x||w|
+// maximum accumulates into.
+__global__ void __launch_bounds__(256) zero_slot_kernel(float* __restrict__ p, int64_t T, int k) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < T) p[t * k] = 0.0f;
+}
+}  // namespace
+
 hipError_t launch_router_logits(bool act_f32, const void* x, const void* w_router, const float* bias,
-                                float* logits, int64_t T, int d, int E, hipStream_t s) {
+                                float* logits, float* topk_w, int64_t T, int d, int E, int k, hipStream_t s) {
   GemmProblem q = {};
   q.mode = act_f32 ? GEMM_DOWN : GEMM_PLAIN_F32OUT;
   q.A = x;
@@ -190,7 +214,10 @@ hipError_t launch_router_logits(bool act_f32, const void* x, const void* w_route
   q.C = logits;
   q.ldc = E;
   q.bias = bias;
+  q.rowabs = topk_w;
+  q.rowabs_stride = k;
   if (T == 0) return hipSuccess;
+  zero_slot_kernel<<<(unsigned)((T + 255) / 256), 256, 0, s>>>(topk_w, T, k);
   return act_f32 ? launch_gemm_f32(q, s) : launch_gemm_bf16(q, s);
 }
 
@@ -199,8 +226,11 @@ hipError_t launch_topk(bool act_f32, const float* logits, const void* x, const v
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((T + 3) / 4));
   const int per_lane = (E + 63) / 64;
-#define MOE_TOPK(P)                                                                                         \
-  topk_kernel<P><<<grid, 256, 0, s>>>(logits, x, w_router, bias, act_f32, topk_idx, topk_w, T, d, E, k); \
+  // gamma_{d+2}: d products (rounded too in fp32) and d additions
+  const double du = (double)(d + 2) * 5.9604644775390625e-8;
+  const float gamma = (float)(du / (1.0 - du));
+#define MOE_TOPK(P)                                                                                                \
+  topk_kernel<P><<<grid, 256, 0, s>>>(logits, x, w_router, bias, act_f32, topk_idx, topk_w, T, d, E, k, gamma); \
   break;
   switch (per_lane) {
     case 1: MOE_TOPK(1)
