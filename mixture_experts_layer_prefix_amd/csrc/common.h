@@ -197,9 +197,14 @@ __device__ __forceinline__ WgradRect wgrad_rect(int mtl, int ntl, int xcd) {
 
 // Router: logits (fp32) from x and W_r; top-k + weights (with fp64 refinement
 // of near-tie tokens).  act_f32: x and W_r are fp32 instead of bf16.
-// The logits kernel also leaves, in topk_w[t * k] (zeroed first), the bits
-// of max_e sum_i |x_ti| |W_r[e][i]|, which bounds the fp32 accumulation error
-// of every logit of token t; the top-k kernel reads it before writing topk_w.
+// The logits kernel sums each logit as an fp64 sum of fp32 partial sums over
+// kLogitChunkBf16 (bf16 path) or kLogitChunkF32 (fp32 path) consecutive
+// products, rounded once to fp32 before the bias is added; it also leaves,
+// in topk_w[t * k] (zeroed first), the bits of max_e sum_i |x_ti| |W_r[e][i]|
+// (fp32), which bounds the partial sums' error for every logit of token t.
+// The top-k kernel reads it before writing topk_w.
+constexpr int kLogitChunkBf16 = 64;  // the bf16 GEMM's K slab
+constexpr int kLogitChunkF32 = 16;   // the fp32 GEMM's K step
 hipError_t launch_router_logits(bool act_f32, const void* x, const void* w_router, const float* bias,
                                 float* logits, float* topk_w, int64_t T, int d, int E, int k, hipStream_t s);
 hipError_t launch_topk(bool act_f32, const float* logits, const void* x, const void* w_router,
@@ -306,7 +311,8 @@ struct GemmProblem {
   int64_t ldc;
   const float* bias;        // [N] (plain mode)
   float* rowabs;            // router GEMM, optional: max over the columns of sum_k |A[r][k]| |B[c][k]|,
-  int rowabs_stride;        // at rowabs[r * rowabs_stride] (atomic max of fp32 bits; caller zeroes it)
+  int rowabs_stride;        // at rowabs[r * rowabs_stride] (atomic max of fp32 bits; caller zeroes it);
+                            // with it, C is an fp64 sum of fp32 partial sums per K chunk (router logits)
   int32_t* tile_prefix;     // scratch [2(G+1)] (device), M-tile prefixes per group
   int64_t ldb;              // B row stride in elements (0: K; DUALK: K/2 each)
   // SwiGLU backward epilogue

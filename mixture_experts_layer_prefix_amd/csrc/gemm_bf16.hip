@@ -618,6 +618,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
 
 // Router-sized GEMM with fp32 output and bias: 64 x 64 tiles (the output has
 // only E columns, so big tiles would leave most CUs idle).
+template <bool ABS>
 __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
   constexpr int BM = 64, BN = 64, WM = 32, WN = 32;
   constexpr int KV = kBK / 8;
@@ -636,10 +637,23 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
     pa[i] = p.A + r * p.lda + kc;
     pb[i] = p.B0 + (int64_t)min(ntile * BN + row, p.N - 1) * p.K + kc;
   }
-  f32x16 acc, aab;
+  // Router logits (rowabs set): each slab's 64 products are summed by the
+  // matrix cores into a fresh fp32 partial (two, alternating, so a slab's
+  // MFMAs do not wait for the previous partial's fold), and the partials are
+  // added in fp64 in slab order.
+  f32x16 acc, aab, part0, part1;
+  double acc64[ABS ? 16 : 1];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = aab[v] = 0.0f;
-  const bool want_abs = p.rowabs != nullptr;
+  for (int v = 0; v < 16; ++v) acc[v] = aab[v] = part0[v] = part1[v] = 0.0f;
+#pragma unroll
+  for (int v = 0; v < (ABS ? 16 : 1); ++v) acc64[v] = 0.0;
+  static_assert(kBK == kLogitChunkBf16, "logit chunk = K slab");
+  auto fold = [&](const f32x16 q) {
+    if constexpr (ABS) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc64[v] += (double)q[v];
+    }
+  };
   auto abs8 = [](bf16x8 v) {
     u32x4 u = __builtin_bit_cast(u32x4, v);
 #pragma unroll
@@ -649,7 +663,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
   // Slabs move global -> registers -> LDS; kPD slabs are in flight in
   // registers (one K loop of a 64 x 64 tile is otherwise a chain of
   // load-latency waits).
-  constexpr int kPD = 4;
+  constexpr int kPD = ABS ? 2 : 4;
   u32x4 ra[kPD][2], rb[kPD][2];
   const int KT = p.K / kBK;
   auto ld = [&](int slot, int k0) {
@@ -678,18 +692,36 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
       const int kt = kt0 + u;  // slab kt sits in LDS buffer u & 1 (kPD is even)
       if (kt < KT) {
         if (kt + kPD < KT) ld(u, (kt + kPD) * kBK);  // register slot u was stored at step kt - 1
+        if constexpr (ABS) {
+          f32x16& q = (u & 1) ? part1 : part0;
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-          const int kof = kk * 16 + (lane >> 5) * 8;
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
-          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
-          if (want_abs) aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abs8(af), abs8(bf), aab, 0, 0, 0);
+          for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int kof = kk * 16 + (lane >> 5) * 8;
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
+            const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
+            q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, kk == 0 ? f32x16{} : q, 0, 0, 0);
+            aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abs8(af), abs8(bf), aab, 0, 0, 0);
+          }
+          if (kt > 0) fold((u & 1) ? part0 : part1);  // the previous slab's partial
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int kof = kk * 16 + (lane >> 5) * 8;
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
+            const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+          }
         }
         if (kt + 1 < KT) st((u + 1) % kPD, (u + 1) & 1);
         __syncthreads();
       }
     }
+  }
+  if constexpr (ABS) {
+    if ((KT - 1) & 1) fold(part1);  // the last slab's partial
+    else fold(part0);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = (float)acc64[v];
   }
   float* C = static_cast<float*>(p.C);
 #pragma unroll
@@ -698,7 +730,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
     const int col = ntile * BN + wn * WN + (lane & 31);
     if (row < p.M && col < p.N) C[row * p.ldc + col] = acc[v] + (p.bias ? p.bias[col] : 0.0f);
   }
-  if (want_abs) {
+  if constexpr (ABS) {
     // Largest sum of |x_k| |w_k| of each row over this tile's 64 columns:
     // the 32 columns of a wave half in DPP steps, then an atomic maximum of
     // the (non-negative) fp32 bits; order-independent, so deterministic.
@@ -824,7 +856,8 @@ hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
       a.rowabs = q.rowabs;
       a.rowabs_stride = q.rowabs_stride;
       const dim3 grid((unsigned)((q.M + 63) / 64), (unsigned)((q.N + 63) / 64));
-      gemm_bf16_small_n_kernel<<<grid, 256, 0, s>>>(a);
+      if (a.rowabs) gemm_bf16_small_n_kernel<true><<<grid, 256, 0, s>>>(a);
+      else gemm_bf16_small_n_kernel<false><<<grid, 256, 0, s>>>(a);
       return hipGetLastError();
     }
   }

@@ -26,8 +26,10 @@ __global__ void __launch_bounds__(1024) f32_tile_prefix(const int32_t* __restric
   }
 }
 
-// ABS (router logits): also the largest sum of |a_k| |b_k| of each row over
-// the tile's columns, into rowabs[row * rowabs_stride] by atomic maximum.
+// ABS (router logits): each K step's 16 products are summed by fmaf into a
+// fresh fp32 partial and the partials added in fp64 in K order; also the
+// largest sum of |a_k| |b_k| of each row over the tile's columns, into
+// rowabs[row * rowabs_stride] by atomic maximum.
 template <int MODE, bool ABS = false>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ a_rows,
                                                        int64_t lda, const int32_t* __restrict__ row_off, int64_t M,
@@ -57,6 +59,8 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[2][4][4] = {};
   float aab[4][4] = {};
+  double acc64[ABS ? 4 : 1][4] = {};
+  static_assert(TK == kLogitChunkF32, "logit chunk = K step");
   for (int k0 = 0; k0 < K; k0 += TK) {
     for (int i = threadIdx.x; i < TM * TK; i += 256) {
       int r = i / TK, kk = i % TK;
@@ -90,8 +94,17 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
             for (int i = 0; i < 4; ++i) aab[i][j] = fmaf(fabsf(a[i]), fabsf(b), aab[i][j]);
         }
     }
+    if constexpr (ABS)
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+          acc64[i][j] += (double)acc[0][i][j];
+          acc[0][i][j] = 0.0f;
+        }
     __syncthreads();
   }
+  if constexpr (ABS)
+    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) acc[0][i][j] = (float)acc64[i][j];
   for (int i = 0; i < 4; ++i) {
     int64_t lr = m0 + ty * 4 + i;
     if (lr >= n_g) continue;

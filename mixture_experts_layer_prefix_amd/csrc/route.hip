@@ -9,21 +9,33 @@
 // followed by the top-k kernel: one wavefront per token, ceil(E/64) logits
 // per lane, rounds of a wave-wide arg-max (larger value, then smaller id).
 //
-// Exact selection.  A sum of d products accumulated in fp32 lies within
-// gamma_d * sum_i |x_i w_i| of the exact dot product, gamma_d = d u / (1 - d
-// u), u = 2^-24 (Higham, "Accuracy and Stability of Numerical Algorithms",
-// 2nd ed., section 3.1); the logits GEMM also accumulates sum_i |x_i||w_i|
-// and keeps, per token, its largest value A over the experts.  So every GPU
-// logit lies within delta = 2 (gamma_{d+2} + 2u) A + 4u (|l_k| + |l_k+1|) of
-// the correctly rounded logit plus bias (the factor 2 covers accumulation
-// orders inside the matrix cores; the last term the roundings of the logit
-// and of the bias add).  When the k-th and (k+1)-th GPU logits are more than
-// 2 delta apart, the selection is the one on correctly rounded logits.
+// Exact selection.  Each logit is an fp64 sum, in K order, of fp32 partial
+// sums of c consecutive products (c = 64 on the bf16 path, the K slab of the
+// matrix-core GEMM; 16 on the fp32 path), rounded once to fp32, plus the
+// fp32 bias.  A partial of c products accumulated in fp32 lies within
+// gamma_c * sum |x_i w_i| of its exact value, gamma_c = c u / (1 - c u),
+// u = 2^-24 (Higham, "Accuracy and Stability of Numerical Algorithms", 2nd
+// ed., section 3.1), taken twice over so that any accumulation order inside
+// the matrix cores with a relative error up to 2u per addition is covered;
+// the fp64 sum of the partials, and the fp64 recomputation below, add at
+// most 4 d 2^-53 sum |x_i w_i|.  The logits GEMM also accumulates sum_i
+// |x_i||w_i| in fp32 and keeps, per token, its largest value A over the
+// experts (an fp32 sum of non-negative terms: the true maximum is at most A
+// / (1 - 2 gamma_d)).  With the two fp32 roundings (before and after the
+// bias) on either side, every GPU logit lies within
+//   delta = gamma A + 4u (|l_k| + |l_k+1|) + eta
+// of the logit recomputed in fp64, gamma = (2 gamma_c + 2u + 4 d 2^-53) /
+// (1 - 2 gamma_d) and eta = d 2^-124 for products below the fp32 normal
+// range that may be flushed (operands in the bf16 subnormal range are
+// outside this statement).  When the k-th and (k+1)-th GPU logits are more
+// than 2 delta apart, the selection is the one on the recomputed logits.
 // Otherwise every expert whose GPU logit lies in [l_k+1 - 2 delta, l_k +
 // 2 delta] gets its logit recomputed as an fp64 dot product rounded once to
 // fp32 (plus the fp32 bias) and the selection is redone: experts above that
 // window are in the top-k and experts below it are out under any error of
-// that size, so the result is the selection on correctly rounded logits.
+// that size.  The fp64 recomputation is the oracle's definition of a logit
+// (an fp64 product rounded to fp32, plus the bias) up to the order of the
+// fp64 additions.
 #include <math.h>
 
 #include "common.h"
@@ -109,7 +121,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
                                                    const void* __restrict__ wr, const float* __restrict__ bias,
                                                    bool act_f32, int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w, int64_t T, int d, int E, int k,
-                                                   float gamma) {
+                                                   float gamma, float eta) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront leaves; no block barrier below
@@ -128,8 +140,9 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   int lid[kMaxK + 1];
   select_rounds<PER_LANE>(v, E, rounds, lane, lv, lid);
   constexpr float u = 5.9604645e-8f;  // 2^-24
-  const float delta = 2.0f * (gamma + 2.0f * u) * abs_sum * (1.0f + 4.0f * u) +
-                      4.0f * u * (fabsf(lv[k - 1]) + (k < E ? fabsf(lv[k]) : 0.0f));
+  // (1 + 2^-20): the few fp32 roundings of this expression
+  const float delta = (gamma * abs_sum + 4.0f * u * (fabsf(lv[k - 1]) + (k < E ? fabsf(lv[k]) : 0.0f)) + eta) *
+                      (1.0f + 9.5367432e-7f);
   if (k < E && lv[k - 1] - lv[k] <= 2.0f * delta) {
     // Near tie at the selection boundary.  Experts above hi are in the top-k
     // under any logit error up to delta (fewer than k GPU logits exceed the
@@ -226,11 +239,13 @@ hipError_t launch_topk(bool act_f32, const float* logits, const void* x, const v
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((T + 3) / 4));
   const int per_lane = (E + 63) / 64;
-  // gamma_{d+2}: d products (rounded too in fp32) and d additions
-  const double du = (double)(d + 2) * 5.9604644775390625e-8;
-  const float gamma = (float)(du / (1.0 - du));
+  // the bound's coefficients (see the top of this file), rounded up
+  const double u = 5.9604644775390625e-8, c = act_f32 ? kLogitChunkF32 : kLogitChunkBf16;
+  const double gamma_c = c * u / (1.0 - c * u), gamma_d = d * u / (1.0 - d * u);
+  const float gamma = (float)((2.0 * gamma_c + 2.0 * u + 4.0 * d * 0x1p-53) / (1.0 - 2.0 * gamma_d) * (1.0 + 0x1p-20));
+  const float eta = (float)(d * 0x1p-124);
 #define MOE_TOPK(P)                                                                                                \
-  topk_kernel<P><<<grid, 256, 0, s>>>(logits, x, w_router, bias, act_f32, topk_idx, topk_w, T, d, E, k, gamma); \
+  topk_kernel<P><<<grid, 256, 0, s>>>(logits, x, w_router, bias, act_f32, topk_idx, topk_w, T, d, E, k, gamma, eta); \
   break;
   switch (per_lane) {
     case 1: MOE_TOPK(1)
