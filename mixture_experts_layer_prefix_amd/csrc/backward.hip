@@ -270,71 +270,99 @@ __global__ void __launch_bounds__(256) transpose_batched_kernel(const bf16_t* __
 
 // dx[t] = sum_j (dA_perm[token_row[t][j]] + dl[t][j] W_r[idx[t][j]]) + dx_shared[t]
 // (j ascending = ascending expert id), fp32 accumulation, one bf16 rounding.
-// One wave per token (grid-stride over tokens): the token's k rows, expert
-// ids and router-term weights are wave-uniform (scalar loads), and each lane
-// sums 8-element vectors of the row in ascending-expert order with k row
-// reads in flight: dA_perm rows, then the router term dl_j W_router[e_j],
-// then the shared expert's dX; fp32 accumulation, one rounding.
-template <int K>
-__global__ void __launch_bounds__(256) dx_kernel(const bf16_t* __restrict__ da_perm, const int32_t* __restrict__ token_row,
-                                                 const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
-                                                 const bf16_t* __restrict__ w_router,
-                                                 const bf16_t* __restrict__ dx_shared, bf16_t* __restrict__ dx,
-                                                 int64_t T, int d) {
-  constexpr int k = K;
-  const int lane = threadIdx.x & 63;
-  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
+// One workgroup per token, sized so that each thread owns two 16-byte
+// vectors of the row (one for k > 8, whose rows and router rows would
+// spill; the whole row for rows up to 1024 vectors): the token's k rows,
+// expert ids and logit gradients are workgroup-uniform, and the 2k row
+// reads of a thread are in flight together (k a template parameter).  Per element and expert: the dA_perm row is added, then the
+// router term dl_j W_router[e_j] (ROUTER); the shared expert's dX last.  The
+// routed rows and the shared dX stream (nontemporal); W_router rows are
+// reread by every token and stay cached.
+// 16-byte vectors per thread: two while 2k rows stay in registers.
+constexpr int dx_vectors_per_thread(int k) { return k <= 8 ? 2 : 1; }
+
+template <int K, bool ROUTER>
+__global__ void __launch_bounds__(512) dx_kernel(const bf16_t* __restrict__ da_perm, const int32_t* __restrict__ token_row,
+                                                  const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
+                                                  const bf16_t* __restrict__ w_router,
+                                                  const bf16_t* __restrict__ dx_shared, bf16_t* __restrict__ dx, int d) {
+  constexpr bool TWO = dx_vectors_per_thread(K) == 2;
   const int vpr = d / 8;
-  for (int64_t tw = wave0; tw < T; tw += nwaves) {
-    const int64_t t = uniform_i64(tw);
-    int64_t rows[K];
-    int eids[K];
-    float g[K];
+  const int64_t t = blockIdx.x;
+  int64_t rows[K], er[K];
+  float g[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    rows[j] = (int64_t)token_row[t * K + j] * vpr;
+    er[j] = ROUTER ? (int64_t)topk_idx[t * K + j] * vpr : 0;
+    g[j] = ROUTER ? dl[t * K + j] : 0.0f;
+  }
+  const u32x4* A = reinterpret_cast<const u32x4*>(da_perm);
+  const u32x4* WR = reinterpret_cast<const u32x4*>(w_router);
+  const u32x4* XS = dx_shared ? reinterpret_cast<const u32x4*>(dx_shared) + t * vpr : nullptr;
+  u32x4* Y = reinterpret_cast<u32x4*>(dx) + t * vpr;
+  auto add_bf16 = [](float (&a)[8], const u32x4& w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] += __uint_as_float(w[i] << 16);
+      a[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  };
+  auto fma_bf16 = [](float (&a)[8], float s, const u32x4& w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] = fmaf(s, __uint_as_float(w[i] << 16), a[2 * i]);
+      a[2 * i + 1] = fmaf(s, __uint_as_float(w[i] & 0xFFFF0000u), a[2 * i + 1]);
+    }
+  };
+  for (int v0 = threadIdx.x; v0 < vpr; v0 += (TWO ? 2 : 1) * blockDim.x) {
+    const int v1 = v0 + blockDim.x;
+    const bool two = TWO && v1 < vpr;
+    float a0[8], a1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a0[i] = a1[i] = 0.0f;
+    u32x4 w0[K], w1[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      eids[j] = 0, g[j] = 0.0f;
-      rows[j] = __builtin_amdgcn_readfirstlane(token_row[t * k + j]);
-      if (dl) {
-        eids[j] = __builtin_amdgcn_readfirstlane(topk_idx[t * k + j]);
-        g[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, dl[t * k + j])));
+      w0[j] = __builtin_nontemporal_load(A + rows[j] + v0);
+      w1[j] = two ? __builtin_nontemporal_load(A + rows[j] + v1) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      add_bf16(a0, w0[j]);
+      add_bf16(a1, w1[j]);
+      if (ROUTER) {
+        fma_bf16(a0, g[j], WR[er[j] + v0]);
+        fma_bf16(a1, g[j], two ? WR[er[j] + v1] : u32x4{0, 0, 0, 0});
       }
     }
-    for (int v = lane; v < vpr; v += 64) {
-      const int c = v * 8;
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(da_perm + rows[j] * d + c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += __uint_as_float(w[i] << 16);
-          acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-        if (dl) {
-          const u32x4 r = *reinterpret_cast<const u32x4*>(w_router + (int64_t)eids[j] * d + c);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = fmaf(g[j], __uint_as_float(r[i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(g[j], __uint_as_float(r[i] & 0xFFFF0000u), acc[2 * i + 1]);
-          }
-        }
-      }
-      if (dx_shared) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(dx_shared + t * d + c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += __uint_as_float(w[i] << 16);
-          acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-      }
+    auto finish = [&](float (&a)[8], int v) {
+      if (XS) add_bf16(a, __builtin_nontemporal_load(XS + v));
       u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      *reinterpret_cast<u32x4*>(dx + t * d + c) = o;
-    }
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(a[2 * i], a[2 * i + 1]);
+      __builtin_nontemporal_store(o, Y + v);
+    };
+    finish(a0, v0);
+    if (two) finish(a1, v1);
+  }
+}
+
+// The instantiation for the runtime k (1..kMaxK).
+template <int K>
+void launch_dx_k(int k, const bf16_t* da_perm, const int32_t* token_row, const int32_t* topk_idx, const float* dl,
+                 const bf16_t* w_router, const bf16_t* dx_shared, bf16_t* dx, int64_t T, int d, hipStream_t s) {
+  if constexpr (K <= kMaxK) {
+    if (k != K) return launch_dx_k<K + 1>(k, da_perm, token_row, topk_idx, dl, w_router, dx_shared, dx, T, d, s);
+    const int vpr = d / 8, vpt = dx_vectors_per_thread(K);
+    int th = ((vpr + vpt - 1) / vpt + 63) / 64 * 64;
+    th = th > 512 ? 512 : th;
+    if (dl)
+      dx_kernel<K, true><<<(unsigned)T, (unsigned)th, 0, s>>>(da_perm, token_row, topk_idx, dl, w_router, dx_shared,
+                                                             dx, d);
+    else
+      dx_kernel<K, false><<<(unsigned)T, (unsigned)th, 0, s>>>(da_perm, token_row, topk_idx, dl, w_router,
+                                                              dx_shared, dx, d);
   }
 }
 
@@ -460,17 +488,8 @@ hipError_t launch_dx(const bf16_t* da_perm, const int32_t* token_row, const int3
                      const bf16_t* w_router, const bf16_t* dx_shared, bf16_t* dx, int64_t T, int d, int k,
                      hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int64_t blocks = (T + 3) / 4;  // one wave per token
-  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
-#define MOE_DX_CASE(KK) \
-  case KK: dx_kernel<KK><<<grid, 256, 0, s>>>(da_perm, token_row, topk_idx, dl, w_router, dx_shared, dx, T, d); break;
-  switch (k) {
-    MOE_DX_CASE(1) MOE_DX_CASE(2) MOE_DX_CASE(3) MOE_DX_CASE(4) MOE_DX_CASE(5) MOE_DX_CASE(6) MOE_DX_CASE(7)
-    MOE_DX_CASE(8) MOE_DX_CASE(9) MOE_DX_CASE(10) MOE_DX_CASE(11) MOE_DX_CASE(12) MOE_DX_CASE(13) MOE_DX_CASE(14)
-    MOE_DX_CASE(15) MOE_DX_CASE(16)
-    default: return hipErrorInvalidValue;
-  }
-#undef MOE_DX_CASE
+  if (k < 1 || k > kMaxK || d % 8 || T > INT32_MAX) return hipErrorInvalidValue;
+  launch_dx_k<1>(k, da_perm, token_row, topk_idx, dl, w_router, dx_shared, dx, T, d, s);
   return hipGetLastError();
 }
 

@@ -24,15 +24,17 @@ namespace {
 constexpr int kMaxK = 16;
 
 // One workgroup per token, sized so that each thread owns two 16-byte
-// vectors of the row (the whole row for rows up to 2048 vectors): the
-// token's K rows and router weights are workgroup-uniform (scalar loads, no
-// per-thread index arithmetic) and 2K row loads are in flight per thread (K
-// a template parameter: registers for exactly the token's routes).
+// vectors of the row (the whole row for rows up to 2048 vectors; one vector
+// for K > 12, whose 2K rows would spill): the token's K rows and router
+// weights are workgroup-uniform (scalar loads, no per-thread index
+// arithmetic) and 2K row loads are in flight per thread (K a template
+// parameter: registers for exactly the token's routes).
 template <bool F32, int K>
 __global__ void __launch_bounds__(1024) combine_kernel(const void* __restrict__ o_perm, const int32_t* __restrict__ token_row,
                                                       const float* __restrict__ topk_w, const void* __restrict__ y_shared,
                                                       void* __restrict__ y, int d) {
   constexpr int k = K;
+  constexpr bool TWO = K <= 12;     // two vectors per thread while 2K rows fit in registers
   constexpr int EPV = F32 ? 4 : 8;  // elements per 16-byte vector
   const int vpr = d / EPV;
   const int64_t t = blockIdx.x;
@@ -46,9 +48,9 @@ __global__ void __launch_bounds__(1024) combine_kernel(const void* __restrict__ 
   const u32x4* O = static_cast<const u32x4*>(o_perm);
   const u32x4* YS = y_shared ? static_cast<const u32x4*>(y_shared) + t * vpr : nullptr;
   u32x4* Y = static_cast<u32x4*>(y) + t * vpr;
-  for (int v0 = threadIdx.x; v0 < vpr; v0 += 2 * blockDim.x) {
+  for (int v0 = threadIdx.x; v0 < vpr; v0 += (TWO ? 2 : 1) * blockDim.x) {
     const int v1 = v0 + blockDim.x;
-    const bool two = v1 < vpr;
+    const bool two = TWO && v1 < vpr;
     float a0[8], a1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a0[i] = a1[i] = 0.0f;
@@ -116,8 +118,8 @@ void launch_combine_k(bool act_f32, int k, const void* o_perm, const int32_t* to
                       const void* y_shared, void* y, int64_t T, int d, hipStream_t s) {
   if constexpr (K <= kMaxK) {
     if (k != K) return launch_combine_k<K + 1>(act_f32, k, o_perm, token_row, topk_w, y_shared, y, T, d, s);
-    const int vpr = d / (act_f32 ? 4 : 8);
-    int th = ((vpr + 1) / 2 + 63) / 64 * 64;
+    const int vpr = d / (act_f32 ? 4 : 8), vpt = K <= 12 ? 2 : 1;
+    int th = ((vpr + vpt - 1) / vpt + 63) / 64 * 64;
     th = th > 1024 ? 1024 : th;
     if (act_f32)
       combine_kernel<true, K><<<(unsigned)T, (unsigned)th, 0, s>>>(o_perm, token_row, topk_w, y_shared, y, d);
