@@ -11,12 +11,14 @@
 // Three integer kernels, no floating point and no order-dependent atomics:
 //  1. block histograms: block b counts the routes of its kTokBlock tokens
 //     per expert (LDS integer atomics; counts do not depend on order);
-//  2. one workgroup scans them expert-major: offsets[e] = sum of earlier
-//     experts' totals and before[b][e] = routes of e in blocks before b;
-//  3. block b re-walks its routes in (token, slot) order, 256 at a time; a
-//     route's row is offsets[e] + before[b][e] plus the number of earlier
-//     routes of e in the block (rank among the 256 in flight plus a running
-//     LDS cursor).
+//  2. one workgroup per expert scans that expert's column of block counts
+//     (stored expert-major): before[e][b] = routes of e in blocks before b,
+//     and counts[e] = its total;
+//  3. block b takes offsets[e] = sum of earlier experts' counts (an LDS scan
+//     of the E counts; block 0 also stores them), then re-walks its routes in
+//     (token, slot) order, 256 at a time; a route's row is offsets[e] +
+//     before[e][b] plus the number of earlier routes of e in the block (rank
+//     among the 256 in flight plus a running LDS cursor).
 // The result is the unique expert-major, token-ascending layout.
 //
 // The dispatch copy runs from token order: each token's row is read once and
@@ -53,78 +55,89 @@ __global__ void __launch_bounds__(256) hist_kernel(const int32_t* __restrict__ t
     if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);  // ids outside [0, E) break the contract; skip them
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)blockIdx.x * E + e] = h[e];
+  const int nb = gridDim.x;
+  for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)e * nb + blockIdx.x] = h[e];  // expert-major
 }
 
-// block_counts[b][e] becomes the number of expert-e routes in the blocks
-// before b; counts and offsets (exclusive scan over the experts) are written
-// once.  The 1024 threads split every expert's column of block counts into
-// 1024 / E contiguous parts: each part sums its blocks (loads batched so that
-// many are in flight), then rewrites them as prefixes starting from the
-// earlier parts' total.  The scatter adds offsets[e] to the block's running
-// count.
-__global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ block_counts, int nb, int E,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  constexpr int kBatch = 16;
-  __shared__ int32_t part_sum[1024];
-  __shared__ int32_t s[1024];
-  const int parts = 1024 / E;  // E <= 1024
+// Exclusive scan of one expert's column of block counts (workgroup e): each
+// thread sums a contiguous run of blocks, a 256-wide LDS scan of the run
+// sums gives each run its start, and the run is rewritten as prefixes.
+// counts[e] = the column total.
+__global__ void __launch_bounds__(256) scan_cols_kernel(int32_t* __restrict__ block_counts, int nb,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int32_t s[256];
   const int tid = threadIdx.x;
-  const int e = tid % E, part = tid / E;
-  const bool on = part < parts;
-  const int b_lo = on ? (int)((int64_t)part * nb / parts) : 0;
-  const int b_hi = on ? (int)((int64_t)(part + 1) * nb / parts) : 0;
+  int32_t* col = block_counts + (int64_t)blockIdx.x * nb;
+  const int per = (nb + 255) / 256;
+  const int b0 = min(tid * per, nb), b1 = min(b0 + per, nb);
   int32_t sum = 0;
-  for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
-    int32_t c[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < b_hi ? block_counts[(int64_t)(b0 + i) * E + e] : 0;
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) sum += c[i];
-  }
-  part_sum[tid] = sum;
+  for (int b = b0; b < b1; ++b) sum += col[b];
+  s[tid] = sum;
   __syncthreads();
-  int32_t run = 0, total = 0;
-  if (on) {
-    for (int q = 0; q < parts; ++q) {
-      const int32_t v = part_sum[q * E + e];
-      run += q < part ? v : 0;
-      total += v;
-    }
-  }
-  for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
-    int32_t c[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < b_hi ? block_counts[(int64_t)(b0 + i) * E + e] : 0;
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (b0 + i < b_hi) block_counts[(int64_t)(b0 + i) * E + e] = run;
-      run += c[i];
-    }
-  }
-  s[tid] = (on && part == 0) ? total : 0;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t v = tid >= off ? s[tid - off] : 0;
+  for (int off = 1; off < 256; off <<= 1) {
+    const int32_t v = tid >= off ? s[tid - off] : 0;
     __syncthreads();
     s[tid] += v;
     __syncthreads();
   }
-  if (tid < E) {
-    counts[tid] = total;
-    offsets[tid] = s[tid] - total;
-    if (tid == E - 1) offsets[E] = s[tid];
+  int32_t run = s[tid] - sum;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t c = col[b];
+    col[b] = run;
+    run += c;
+  }
+  if (tid == 255) counts[blockIdx.x] = s[255];
+}
+
+// Zero counts and offsets of an empty batch.
+__global__ void __launch_bounds__(256) zero_schedule_kernel(int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets, int E) {
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    if (e < E) counts[e] = 0;
+    offsets[e] = 0;
   }
 }
 
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k,
                                                       const int32_t* __restrict__ block_base,
-                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ row_token,
                                                       int32_t* __restrict__ token_row) {
   __shared__ int32_t cursor[1024];
   __shared__ int32_t s_e[256];
-  for (int e = threadIdx.x; e < E; e += 256) cursor[e] = block_base[(int64_t)blockIdx.x * E + e] + offsets[e];
+  // offsets[e] = sum of the counts of experts before e: 4 consecutive experts
+  // per thread, a 256-wide LDS scan of their sums (s_e serves as its array)
+  {
+    const int tid = threadIdx.x, e0 = tid * 4;
+    int32_t c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = e0 + q < E ? counts[e0 + q] : 0;
+      sum += c[q];
+    }
+    s_e[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int32_t v = tid >= off ? s_e[tid - off] : 0;
+      __syncthreads();
+      s_e[tid] += v;
+      __syncthreads();
+    }
+    int32_t run = s_e[tid] - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (e0 + q < E) {
+        cursor[e0 + q] = run;
+        if (blockIdx.x == 0) offsets[e0 + q] = run;
+      }
+      run += c[q];
+    }
+    if (blockIdx.x == 0 && tid == 255) offsets[E] = s_e[255];
+    __syncthreads();
+  }
+  const int nb = gridDim.x;
+  for (int e = threadIdx.x; e < E; e += 256) cursor[e] += block_base[(int64_t)e * nb + blockIdx.x];
   const int64_t r0 = (int64_t)blockIdx.x * kTokBlock * k;
   const int64_t r1 = min((int64_t)(blockIdx.x + 1) * kTokBlock, T) * k;
   for (int64_t c0 = r0; c0 < r1; c0 += 256) {
@@ -324,9 +337,13 @@ hipError_t launch_schedule(const int32_t* topk_idx, int64_t T, int E, int k, int
                            int32_t* row_token, int32_t* token_row, void* scratch, hipStream_t s) {
   const int nb = permute_num_blocks(T);
   int32_t* bc = static_cast<int32_t*>(scratch);
-  if (nb > 0) hist_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc);
-  scan_kernel<<<1, 1024, 0, s>>>(bc, nb, E, counts, offsets);
-  if (nb > 0) scatter_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc, offsets, row_token, token_row);
+  if (nb == 0) {
+    zero_schedule_kernel<<<1, 256, 0, s>>>(counts, offsets, E);
+    return hipGetLastError();
+  }
+  hist_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc);
+  scan_cols_kernel<<<E, 256, 0, s>>>(bc, nb, counts);
+  scatter_kernel<<<nb, 256, 0, s>>>(topk_idx, T, E, k, bc, counts, offsets, row_token, token_row);
   return hipGetLastError();
 }
 
