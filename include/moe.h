@@ -142,14 +142,21 @@ moe_status moe_workspace_bytes(const moe_dims* dims, moe_prec prec, int which, s
  * Blog post, "Overlapping computation and communication in MoE" (router
  * projection, top-k, a router weight per chosen expert); paper summary
  * section 2.1 ("normalized router weights").
- *   logits[t][e] = fp32(x_t . W_r[e]) + bias[e] (bias optional, fp32 [E]);
+ *   logits[t][e] = fp32(x_t . W_r[e]) + bias[e] (bias optional, fp32 [E]),
+ *                  the dot product an fp64 sum of fp32 partial sums over
+ *                  64-element K chunks (16 in MOE_F32), rounded once;
  *   topk_idx[t]  = the k largest logits, ties to the smaller id, stored in
  *                  ascending id order;
  *   topk_w[t][j] = softmax of the selected logits.
- * Selection is exact with respect to correctly rounded fp32 logits: tokens
- * whose k-th/(k+1)-th logit gap is within the fp32 accumulation error bound
- * have their boundary logits recomputed in fp64 before the selection.
- * logits, topk_idx and topk_w are outputs owned by the caller. */
+ * Selection equals the selection on logits recomputed in fp64 (the dot
+ * product in fp64, rounded to fp32, plus the bias): a rigorous bound on the
+ * computed logits' error (Higham's gamma_64 times the token's largest
+ * sum_i |x_i| |W_r[e][i]|, which the logits kernel also accumulates) sets a
+ * window around the k-th/(k+1)-th boundary, and every expert inside it is
+ * recomputed in fp64 before the selection is redone.  Operands in the bf16
+ * subnormal range are outside that statement.  logits, topk_idx and topk_w
+ * are outputs owned by the caller; topk_w also carries the per-token bound
+ * from the logits kernel to the selection kernel. */
 moe_status moe_route(const moe_dims* dims, moe_prec prec, const void* x, const void* w_router,
                      const float* logit_bias, float* logits, int32_t* topk_idx, float* topk_w,
                      void* stream);
