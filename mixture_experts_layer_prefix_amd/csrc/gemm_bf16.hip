@@ -617,7 +617,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
 }
 
 // Router-sized GEMM with fp32 output and bias: 64 x 64 tiles (the output has
-// only E columns, so big tiles would leave most CUs idle).
+// only E columns, so big tiles would leave most CUs idle).  ABS (router
+// logits): C is an fp64 sum of per-slab fp32 partials and rowabs receives
+// the per-row maximum of sum_k |A| |B| (see KArgs::rowabs).
 template <bool ABS>
 __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
   constexpr int BM = 64, BN = 64, WM = 32, WN = 32;
@@ -662,7 +664,9 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
   };
   // Slabs move global -> registers -> LDS; kPD slabs are in flight in
   // registers (one K loop of a 64 x 64 tile is otherwise a chain of
-  // load-latency waits).
+  // load-latency waits).  Two for ABS, whose second accumulator chain, fp64
+  // sums and alternating partials need the registers (four would leave two
+  // waves per SIMD instead of three).
   constexpr int kPD = ABS ? 2 : 4;
   u32x4 ra[kPD][2], rb[kPD][2];
   const int KT = p.K / kBK;

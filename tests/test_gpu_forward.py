@@ -197,21 +197,23 @@ def bf16_round(v):
     return t.float().numpy().astype(np.float64), t
 
 
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
 @pytest.mark.parametrize("case", ["scaled", "near_tie"])
-def test_routing_exact_at_large_scale_and_near_ties(case):
-    """Selection exactness is derived from the fp32 accumulation bound, so it
-    holds at any logit scale and at engineered near ties:
-      * scaled: x times 2^7 and W_r times 2^6 (exact in bf16), logits of
-        order 10^4 where one fp32 ulp exceeds any fixed window;
-      * near_tie: W_r row 10 is row 3 with one element moved by one bf16
-        ulp and both rows biased far above the rest, so experts 3 and 10
-        differ by x_t[5] * ulp (about 1e-3 of the logits' spacing) and top-1
-        must pick the larger correctly rounded logit (ties: expert 3).
+def test_routing_exact_at_large_scale_and_near_ties(case, prec):
+    """Selection exactness is derived from a bound on the logits'
+    accumulation error, so it holds at any logit scale and at engineered near
+    ties, on the bf16 (matrix-core) and the fp32 (vector) logits paths:
+      * scaled: x times 2^7 and W_r times 2^6 (exact in either type), logits
+        of order 10^4 where one fp32 ulp exceeds any fixed window;
+      * near_tie: W_r row 10 is row 3 with one element moved by one ulp of
+        the operand type and both rows biased far above the rest, so experts
+        3 and 10 differ by x_t[5] * ulp and top-1 must pick the larger
+        recomputed logit (ties: expert 3).
     Routing ids must equal the oracle's on every token; the test also reports
     the tokens whose GPU fp32 logits alone would have chosen otherwise."""
     import mixture_experts_layer_prefix_amd as M
-    D = gen.Dims("tie_" + case, 4096, 1024, 64, 1 if case == "near_tie" else 4, 64, 0, 0, "bf16", 0.0)
-    say("[case] routing", case, D)
+    D = gen.Dims("tie_" + case, 4096, 1024, 64, 1 if case == "near_tie" else 4, 64, 0, 0, prec, 0.0)
+    say("[case] routing", case, prec, D)
     p = gen.Problem(D)
     x = p.host("x")
     wr = p.host("w_router")
@@ -221,18 +223,25 @@ def test_routing_exact_at_large_scale_and_near_ties(case):
     else:
         wr = wr.copy()
         wr[10] = wr[3]
-        w5 = np.float32(wr[3, 5])
-        up = (np.frombuffer(np.float32(w5).tobytes(), np.uint32)[0] >> 16) + 1  # next bf16 up in magnitude
-        wr[10, 5] = np.frombuffer(np.uint32(up << 16).tobytes(), np.float32)[0]
+        bits = np.frombuffer(np.float32(wr[3, 5]).tobytes(), np.uint32)[0]
+        if prec == "bf16":
+            bits = ((bits >> 16) + 1) << 16   # next bf16 up in magnitude
+        else:
+            bits = bits + 1                   # next fp32 up in magnitude
+        wr[10, 5] = np.frombuffer(np.uint32(bits).tobytes(), np.float32)[0]
         bias = np.zeros(D.E, np.float32)
         bias[3] = bias[10] = 50.0
-    xh, xt = bf16_round(x)
-    wh, wt = bf16_round(wr)
+    if prec == "bf16":
+        xh, xt = bf16_round(x)
+        wh, wt = bf16_round(wr)
+    else:
+        xt, wt = torch.as_tensor(np.asarray(x, np.float32)), torch.as_tensor(np.asarray(wr, np.float32))
+        xh, wh = xt.numpy().astype(np.float64), wt.numpy().astype(np.float64)
     logits = O.router_logits(xh, wh, bias)
     ref_idx = O.topk_route(logits, D.k)
     md = M.Dims(D.T, D.d, D.E, D.k, D.I)
     bdev = None if bias is None else torch.as_tensor(bias, device="cuda")
-    gl, idx, tw = M.route(xt.cuda(), wt.cuda(), md, "bf16", bias=bdev)
+    gl, idx, tw = M.route(xt.cuda(), wt.cuda(), md, prec, bias=bdev)
     torch.cuda.synchronize()
     got = to_np(idx)
     raw = O.topk_route(to_np(gl), D.k)   # the selection the GPU's fp32 logits alone make
