@@ -40,6 +40,22 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer fwd/bwd tokens/sec + MFMA TFLOPS (% peak), DSV3 shape, bf16 & MXFP8"
 PEAK = {"bf16": 2500.0, "mxfp8": 5000.0}   # MI355X dense MFMA TFLOP/s
 PEAK_HBM_GBS = 8000.0
+# Parity of this workload against the float64 oracle at the stated MXFP8 bound
+# (max|d|/max|ref| <= 6e-2), as tests/test_gpu_mxfp8.py::test_c4_forward_sampled
+# and tests/test_gpu_mxfp8_backward.py::test_c4_backward_sampled measure it on
+# sampled tokens and every expert's weight-gradient columns.  Reported, not
+# measured here: "over_bound" tensors are expected failures of those tests
+# because the quantization-aware model (exact arithmetic on the MX-rounded
+# operands) is itself over the bound by the same margin.
+MXFP8_BOUND_STATUS = {
+    "bound": 6e-2, "source": "pytest -m gpu -rx (tests/test_gpu_mxfp8*.py)",
+    "within_bound": {"y": 4.1e-2, "dx": 3.7e-2, "dw_router": 5.4e-2},
+    "over_bound": {"dtopk_w": {"gpu": 7.0e-2, "quantized_operands_alone": 7.0e-2},
+                   "dw_gate": {"gpu": 9.0e-2, "quantized_operands_alone": 9.1e-2},
+                   "dw_up": {"gpu": 6.4e-2, "quantized_operands_alone": 6.4e-2},
+                   "dw_down": {"gpu": 6.3e-2, "quantized_operands_alone": 6.2e-2}},
+    "kernels_vs_quantized_model_max": 8.0e-3,
+}
 
 WORKLOAD = ("DSV3-shaped MoE layer forward+backward, MXFP8 routed experts (E4M3, E8M0 per 32 along K) with bf16 "
             "shared expert and router: T=16384 tokens, d=7168, 256 routed experts top-8, I=2048, 1 shared expert "
@@ -317,6 +333,7 @@ def headline(args, D, p, w, out, torch, M):
                    "pass": "forward+backward", "parallelism": "1 GPU"},
         "tflops": round(tflops, 2), "roofline_step_frac": round(t_roof / (ms / 1e3), 4),
         "roofline": roofline, "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "mxfp8_bound_status": MXFP8_BOUND_STATUS,
     })
 
 
