@@ -12,7 +12,8 @@
 //
 // Kernels here:
 //  - pad_offsets_kernel: expert K ranges of the weight-gradient GEMMs, each
-//    expert's rows rounded up to a multiple of 64 (zero padded);
+//    expert's rows rounded up to a multiple of the K slab (64 rows in bf16,
+//    128 in MXFP8; zero padded);
 //  - row_weight_kernel: router weight of every routed row;
 //  - dg_kernel: router-weight gradients, and the logit gradients through the
 //    renormalized softmax when the router gradient is requested;

@@ -29,6 +29,7 @@ SMALL = {
     "bwd_tiles": gen.Dims("bwd_tiles", 1100, 512, 8, 2, 320, 1, 192, "bf16", 0.0, backward=True),
     # the ABI's limits: E = 1024 experts, k = 16
     "bwd_max_E_k": gen.Dims("bwd_max_E_k", 300, 128, 1024, 16, 64, 1, 64, "bf16", 1.2, backward=True),
+    "bwd_one_token": gen.Dims("bwd_one_token", 1, 256, 16, 4, 192, 1, 128, "bf16", 0.0, backward=True),
 }
 
 

@@ -25,6 +25,8 @@ SMALL = {
     "f32_skew": gen.Dims("f32_skew", 200, 96, 12, 3, 40, 1, 24, "f32", 1.2),
     # the ABI's limits: E = 1024 experts, k = 16
     "bf16_max_E_k": gen.Dims("bf16_max_E_k", 300, 128, 1024, 16, 64, 1, 64, "bf16", 1.2),
+    # a single token: one schedule block, every GEMM a 64-row tile with one row
+    "bf16_one_token": gen.Dims("bf16_one_token", 1, 256, 16, 4, 192, 1, 128, "bf16", 0.0),
 }
 
 

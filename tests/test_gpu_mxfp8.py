@@ -28,6 +28,7 @@ SMALL = {
     "mx_E1": gen.Dims("mx_E1", 130, 128, 1, 1, 128, 0, 0, "mxfp8", 0.0),
     # the ABI's limits: E = 1024 experts, k = 16
     "mx_max_E_k": gen.Dims("mx_max_E_k", 300, 128, 1024, 16, 128, 1, 64, "mxfp8", 1.2),
+    "mx_one_token": gen.Dims("mx_one_token", 1, 256, 16, 4, 256, 1, 128, "mxfp8", 0.0),
 }
 
 

@@ -39,6 +39,7 @@ SMALL = {
     "mxb_tiles": gen.Dims("mxb_tiles", 1100, 512, 8, 2, 384, 1, 192, "mxfp8", 0.0, backward=True),
     # the ABI's limits: E = 1024 experts, k = 16
     "mxb_max_E_k": gen.Dims("mxb_max_E_k", 300, 128, 1024, 16, 128, 1, 64, "mxfp8", 1.2, backward=True),
+    "mxb_one_token": gen.Dims("mxb_one_token", 1, 256, 16, 4, 256, 1, 128, "mxfp8", 0.0, backward=True),
     # about 40 rows per expert: each expert's last GEMM tile (64 rows) ends
     # inside its 128-row padding unit, so the padding rows of the
     # weight-gradient operands past that tile must still be written as zeros
@@ -236,7 +237,7 @@ def check_backward_sampled(D, ntok=128, seed=12):
     check_mx_bound(errs, D.name)
 
 
-@pytest.mark.parametrize("name", ["mxb_ragged", "mxb_pad_gap", "mxb_max_E_k"])
+@pytest.mark.parametrize("name", ["mxb_ragged", "mxb_pad_gap", "mxb_max_E_k", "mxb_one_token"])
 def test_routed_row_quantization_bit_exact(name):
     """The weight-gradient operands x^T and dY^T of the MXFP8 backward:
     moe_quantize_mxfp8_rows_t (the kernel the backward runs on them) against
