@@ -41,15 +41,16 @@ METRIC = "MoE layer fwd/bwd tokens/sec + MFMA TFLOPS (% peak), DSV3 shape, bf16 
 PEAK = {"bf16": 2500.0, "mxfp8": 5000.0}   # MI355X dense MFMA TFLOP/s
 PEAK_HBM_GBS = 8000.0
 # Parity of this workload against the float64 oracle at the stated MXFP8 bound
-# (max|d|/max|ref| <= 6e-2), as tests/test_gpu_mxfp8.py::test_c4_forward_sampled
-# and tests/test_gpu_mxfp8_backward.py::test_c4_backward_sampled measure it on
-# sampled tokens and every expert's weight-gradient columns.  Reported, not
+# (max|d|/max|ref| <= 6e-2), as the GPU parity tests measure it: y on every
+# token (tests/test_gpu_forward.py::test_full_size_forward_every_token), the
+# backward on sampled tokens and every expert's weight-gradient columns
+# (tests/test_gpu_mxfp8_backward.py::test_c4_backward_sampled).  Reported, not
 # measured here: "over_bound" tensors are expected failures of those tests
 # because the quantization-aware model (exact arithmetic on the MX-rounded
 # operands) is itself over the bound by the same margin.
 MXFP8_BOUND_STATUS = {
     "bound": 6e-2, "source": "pytest -m gpu -rx (tests/test_gpu_mxfp8*.py)",
-    "within_bound": {"y": 4.1e-2, "dx": 3.7e-2, "dw_router": 5.4e-2},
+    "within_bound": {"y": 4.4e-2, "dx": 3.7e-2, "dw_router": 5.4e-2},
     "over_bound": {"dtopk_w": {"gpu": 7.0e-2, "quantized_operands_alone": 7.0e-2},
                    "dw_gate": {"gpu": 9.0e-2, "quantized_operands_alone": 9.1e-2},
                    "dw_up": {"gpu": 6.4e-2, "quantized_operands_alone": 6.4e-2},
