@@ -617,10 +617,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(KArgs p) {
 }
 
 // Router-sized GEMM with fp32 output and bias: 64 x 64 tiles (the output has
-// only E columns, so big tiles would leave most CUs idle).  ABS (router
-// logits): C is an fp64 sum of per-slab fp32 partials and rowabs receives
-// the per-row maximum of sum_k |A| |B| (see KArgs::rowabs).
-template <bool ABS>
+// only E columns, so big tiles would leave most CUs idle).
 __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
   constexpr int BM = 64, BN = 64, WM = 32, WN = 32;
   constexpr int KV = kBK / 8;
@@ -639,35 +636,13 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
     pa[i] = p.A + r * p.lda + kc;
     pb[i] = p.B0 + (int64_t)min(ntile * BN + row, p.N - 1) * p.K + kc;
   }
-  // Router logits (rowabs set): each slab's 64 products are summed by the
-  // matrix cores into a fresh fp32 partial (two, alternating, so a slab's
-  // MFMAs do not wait for the previous partial's fold), and the partials are
-  // added in fp64 in slab order.
-  f32x16 acc, aab, part0, part1;
-  double acc64[ABS ? 16 : 1];
+  f32x16 acc;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = aab[v] = part0[v] = part1[v] = 0.0f;
-#pragma unroll
-  for (int v = 0; v < (ABS ? 16 : 1); ++v) acc64[v] = 0.0;
-  static_assert(kBK == kLogitChunkBf16, "logit chunk = K slab");
-  auto fold = [&](const f32x16 q) {
-    if constexpr (ABS) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc64[v] += (double)q[v];
-    }
-  };
-  auto abs8 = [](bf16x8 v) {
-    u32x4 u = __builtin_bit_cast(u32x4, v);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] &= 0x7FFF7FFFu;
-    return __builtin_bit_cast(bf16x8, u);
-  };
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
   // Slabs move global -> registers -> LDS; kPD slabs are in flight in
   // registers (one K loop of a 64 x 64 tile is otherwise a chain of
-  // load-latency waits).  Two for ABS, whose second accumulator chain, fp64
-  // sums and alternating partials need the registers (four would leave two
-  // waves per SIMD instead of three).
-  constexpr int kPD = ABS ? 2 : 4;
+  // load-latency waits).
+  constexpr int kPD = 4;
   u32x4 ra[kPD][2], rb[kPD][2];
   const int KT = p.K / kBK;
   auto ld = [&](int slot, int k0) {
@@ -696,36 +671,17 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
       const int kt = kt0 + u;  // slab kt sits in LDS buffer u & 1 (kPD is even)
       if (kt < KT) {
         if (kt + kPD < KT) ld(u, (kt + kPD) * kBK);  // register slot u was stored at step kt - 1
-        if constexpr (ABS) {
-          f32x16& q = (u & 1) ? part1 : part0;
 #pragma unroll
-          for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int kof = kk * 16 + (lane >> 5) * 8;
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
-            const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
-            q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, kk == 0 ? f32x16{} : q, 0, 0, 0);
-            aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abs8(af), abs8(bf), aab, 0, 0, 0);
-          }
-          if (kt > 0) fold((u & 1) ? part0 : part1);  // the previous slab's partial
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int kof = kk * 16 + (lane >> 5) * 8;
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
-            const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
-          }
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+          const int kof = kk * 16 + (lane >> 5) * 8;
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[u & 1][wm * WM + (lane & 31)][kof]);
+          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[u & 1][wn * WN + (lane & 31)][kof]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
         }
         if (kt + 1 < KT) st((u + 1) % kPD, (u + 1) & 1);
         __syncthreads();
       }
     }
-  }
-  if constexpr (ABS) {
-    if ((KT - 1) & 1) fold(part1);  // the last slab's partial
-    else fold(part0);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = (float)acc64[v];
   }
   float* C = static_cast<float*>(p.C);
 #pragma unroll
@@ -734,17 +690,101 @@ __global__ void __launch_bounds__(256) gemm_bf16_small_n_kernel(KArgs p) {
     const int col = ntile * BN + wn * WN + (lane & 31);
     if (row < p.M && col < p.N) C[row * p.ldc + col] = acc[v] + (p.bias ? p.bias[col] : 0.0f);
   }
-  if constexpr (ABS) {
-    // Largest sum of |x_k| |w_k| of each row over this tile's 64 columns:
-    // the 32 columns of a wave half in DPP steps, then an atomic maximum of
-    // the (non-negative) fp32 bits; order-independent, so deterministic.
-    // Columns past N repeat expert N-1 (clamped loads): a real expert's sum.
+}
+
+// Router logits (rowabs set): 64 x 64 tiles of C = A . B^T + bias, where each
+// logit is an fp64 sum, in K order, of fp32 partial sums of one 64-element
+// K slab (the matrix cores sum a slab into a fresh accumulator), rounded once
+// to fp32 before the bias; and rowabs[row * rowabs_stride] = the maximum over
+// the tile's columns of sum_k |A[row][k]| |B[col][k]| (fp32 bits, by atomic
+// maximum: order-independent).  Operands go global -> LDS by LDS DMA into a
+// two-slab ring of swizzled 128-byte rows (as the grouped GEMMs), so no
+// register staging competes with the fp64 sums: about 110 registers, four
+// waves per SIMD, and the workgroups of a 16,384-token launch all resident.
+__global__ void __launch_bounds__(256) gemm_bf16_logits_kernel(KArgs p) {
+  constexpr int BM = 64, BN = 64, WM = 32, WN = 32;
+  static_assert(kBK == kLogitChunkBf16, "logit chunk = K slab");
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * kBK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+  const int rows_a = (int)min<int64_t>(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+  // Descriptors over the tile's rows; rows past the end load the last row
+  // (their outputs are not stored).  Wave w fills LDS rows 16 w .. 16 w + 15
+  // of A and of B, 8 rows per load; slot (lane & 7) of row r holds the
+  // 16-byte chunk slot ^ swz(r), r & 7 = lane >> 3, (r >> 3) & 1 = j.
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(p.A + m0 * p.lda), (short)0, (int)(rows_a * p.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(p.B0 + (int64_t)n0 * p.K), (short)0, (int)(rows_b * p.K * 2), 0x00020000);
+  uint32_t aoff[2], boff[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = m0 + wm * WM + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const uint32_t m = half_max32_u(__float_as_uint(aab[v]) & 0x7FFFFFFFu);
-      if ((lane & 31) == 0 && row < p.M) atomicMax(reinterpret_cast<unsigned int*>(p.rowabs + row * p.rowabs_stride), m);
+  for (int j = 0; j < 2; ++j) {
+    const int r = wave * 16 + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ (lane >> 3) ^ j;
+    aoff[j] = (uint32_t)(min(r, rows_a - 1) * p.lda * 2) + chunk * 16;
+    boff[j] = (uint32_t)(min(r, rows_b - 1) * p.K * 2) + chunk * 16;
+  }
+  auto issue = [&](int buf, int k0) {  // 4 loads per wave
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lds_dma<16>(ar, &As[buf][(wave * 16 + 8 * j) * kBK], aoff[j], (uint32_t)k0 * 2);
+      lds_dma<16>(br, &Bs[buf][(wave * 16 + 8 * j) * kBK], boff[j], (uint32_t)k0 * 2);
     }
+  };
+  auto abs8 = [](bf16x8 v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] &= 0x7FFF7FFFu;
+    return __builtin_bit_cast(bf16x8, u);
+  };
+  f32x16 part, aab;
+  double acc64[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    part[v] = aab[v] = 0.0f;
+    acc64[v] = 0.0;
+  }
+  const int KT = p.K / kBK;
+  const int ra = wm * WM + (lane & 31), rb = wn * WN + (lane & 31);
+  issue(0, 0);
+  if (KT > 1) issue(1, kBK);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) wait_vmcnt<4>(); else wait_vmcnt<0>();  // this slab's loads (the next slab's may fly)
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[buf][ra * kBK + ((c ^ swz(ra)) << 3)]);
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[buf][rb * kBK + ((c ^ swz(rb)) << 3)]);
+      part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, kk == 0 ? f32x16{} : part, 0, 0, 0);
+      aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abs8(af), abs8(bf), aab, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc64[v] += (double)part[v];
+    __syncthreads();  // every wave is done with this buffer: slab kt + 2 goes there
+    if (kt + 2 < KT) issue(buf, (kt + 2) * kBK);
+  }
+  float* C = static_cast<float*>(p.C);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = m0 + wm * WM + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const int col = n0 + wn * WN + (lane & 31);
+    if (row < p.M && col < p.N) C[row * p.ldc + col] = (float)acc64[v] + (p.bias ? p.bias[col] : 0.0f);
+  }
+  // Largest sum of |a_k| |b_k| of each row over this tile's 64 columns: the
+  // 32 columns of a wave half in DPP steps, then an atomic maximum of the
+  // (non-negative) fp32 bits; order-independent, so deterministic.  Columns
+  // past N repeat expert N-1 (clamped loads): a real expert's sum.
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = m0 + wm * WM + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const uint32_t m = half_max32_u(__float_as_uint(aab[v]) & 0x7FFFFFFFu);
+    if ((lane & 31) == 0 && row < p.M) atomicMax(reinterpret_cast<unsigned int*>(p.rowabs + row * p.rowabs_stride), m);
   }
 }
 
@@ -860,8 +900,8 @@ hipError_t launch_gemm_bf16(const GemmProblem& q, hipStream_t s) {
       a.rowabs = q.rowabs;
       a.rowabs_stride = q.rowabs_stride;
       const dim3 grid((unsigned)((q.M + 63) / 64), (unsigned)((q.N + 63) / 64));
-      if (a.rowabs) gemm_bf16_small_n_kernel<true><<<grid, 256, 0, s>>>(a);
-      else gemm_bf16_small_n_kernel<false><<<grid, 256, 0, s>>>(a);
+      if (a.rowabs) gemm_bf16_logits_kernel<<<grid, 256, 0, s>>>(a);
+      else gemm_bf16_small_n_kernel<<<grid, 256, 0, s>>>(a);
       return hipGetLastError();
     }
   }
