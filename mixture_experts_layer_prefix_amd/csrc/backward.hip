@@ -269,16 +269,18 @@ __global__ void __launch_bounds__(256) transpose_batched_kernel(const bf16_t* __
   }
 }
 
-// dx[t] = sum_j (dA_perm[token_row[t][j]] + dl[t][j] W_r[idx[t][j]]) + dx_shared[t]
+// dx[t] = sum_j dA_perm[token_row[t][j]] + sum_j dl[t][j] W_r[idx[t][j]]
+//         + dx_shared[t]
 // (j ascending = ascending expert id), fp32 accumulation, one bf16 rounding.
 // One workgroup per token, sized so that each thread owns two 16-byte
 // vectors of the row (one for k > 8, whose rows and router rows would
 // spill; the whole row for rows up to 1024 vectors): the token's k rows,
 // expert ids and logit gradients are workgroup-uniform, and the 2k row
-// reads of a thread are in flight together (k a template parameter).  Per element and expert: the dA_perm row is added, then the
-// router term dl_j W_router[e_j] (ROUTER); the shared expert's dX last.  The
-// routed rows and the shared dX stream (nontemporal); W_router rows are
-// reread by every token and stay cached.
+// reads of a thread are in flight together (k a template parameter).  Per
+// element: the k dA_perm rows are added, then the k router terms
+// (ROUTER), then the shared expert's dX.  The routed rows and the shared
+// dX stream (nontemporal); W_router rows are reread by every token and
+// stay cached.
 // 16-byte vectors per thread: two while 2k rows stay in registers.
 constexpr int dx_vectors_per_thread(int k) { return k <= 8 ? 2 : 1; }
 
@@ -332,9 +334,24 @@ __global__ void __launch_bounds__(512) dx_kernel(const bf16_t* __restrict__ da_p
     for (int j = 0; j < K; ++j) {
       add_bf16(a0, w0[j]);
       add_bf16(a1, w1[j]);
-      if (ROUTER) {
-        fma_bf16(a0, g[j], WR[er[j] + v0]);
-        fma_bf16(a1, g[j], two ? WR[er[j] + v1] : u32x4{0, 0, 0, 0});
+    }
+    if (ROUTER) {
+      // The router rows are loaded once the routed rows' registers are
+      // free (the empty asm pins the sums above it and, as a memory
+      // clobber, the router loads below it), so the two sets of 2k vectors
+      // are never live together.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a0[i]), "+v"(a1[i])::"memory");
+      u32x4 r0[K], r1[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        r0[j] = WR[er[j] + v0];
+        r1[j] = two ? WR[er[j] + v1] : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        fma_bf16(a0, g[j], r0[j]);
+        fma_bf16(a1, g[j], r1[j]);
       }
     }
     auto finish = [&](float (&a)[8], int v) {
