@@ -507,11 +507,13 @@ moe_status run_backward(const moe_dims* D, const bf16_t* dy, const bf16_t* x, co
   trace(1, 0, s);
   MOE_HIP(launch_pad_offsets(rt->expert_counts, E, T, b.pad, b.pad_off, b.single, s));
   MOE_HIP(launch_row_weight(rt->token_row, rt->topk_w, R, b.w_row, s));
-  if (mx) {  // tokens and output gradients quantized once along d (row-wise: commutes with the gather)
-    MOE_HIP(launch_quantize_mx(x, T, d, 0, b.xq, b.xqs, s));
+  if (mx) {  // output gradients (and, for the replay, tokens) quantized once along d (row-wise: commutes with the gather)
     MOE_HIP(launch_quantize_mx(dy, T, d, 0, b.dyq, b.dyqs, s));
     MOE_HIP(launch_gather_scales_slab(b.dyqs, rt->row_token, R, d, b.dys_slab, s));
-    if (!rt->gu) MOE_HIP(launch_gather_scales_slab(b.xqs, rt->row_token, R, d, b.xs_slab, s));
+    if (!rt->gu) {
+      MOE_HIP(launch_quantize_mx(x, T, d, 0, b.xq, b.xqs, s));
+      MOE_HIP(launch_gather_scales_slab(b.xqs, rt->row_token, R, d, b.xs_slab, s));
+    }
   }
   trace(1, 1, s);
 

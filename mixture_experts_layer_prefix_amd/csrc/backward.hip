@@ -35,6 +35,8 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kPadRows = 64;
+constexpr int kTqChunks = 4;  // 64-column chunks per transpose-quantize workgroup
+constexpr int kTrChunks = 4;  // 64-column chunks per bf16 transpose workgroup
 
 __global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __restrict__ counts, int E, int64_t T,
                                                            int pad, int32_t* __restrict__ pad_off,
@@ -133,39 +135,57 @@ __global__ void __launch_bounds__(256) transpose_rows_kernel(const bf16_t* __res
   __shared__ bf16_t tile[64][66];
   const int64_t p0 = (int64_t)blockIdx.x * 64;
   if (p0 >= pad_off[nseg]) return;
-  const int c0 = blockIdx.y * 64;
   const int e = find_segment(pad_off, nseg, p0);
   const int64_t r0 = seg_off[e] + (p0 - pad_off[e]);
   const int64_t r_end = seg_off[e + 1];
+  const int64_t kp = pad_off[e + 1] - pad_off[e];
   const int tid = threadIdx.x;
   const int ch = tid & 7;
+  // This thread's two source rows, shared by the workgroup's column chunks.
+  int64_t srow[2];
+  bool rok[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int i = (tid >> 3) + 32 * h;
-    const int64_t r = r0 + i;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (r < r_end && c0 + ch * 8 < cols) {
-      const int64_t srow = gather ? (int64_t)gather[r] : r;
-      v = *reinterpret_cast<const u32x4*>(src + srow * ld_src + c0 + ch * 8);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[i][ch * 8 + 2 * q] = (bf16_t)(v[q] & 0xFFFFu);
-      tile[i][ch * 8 + 2 * q + 1] = (bf16_t)(v[q] >> 16);
-    }
+    const int64_t r = r0 + (tid >> 3) + 32 * h;
+    rok[h] = r < r_end;
+    srow[h] = rok[h] ? (gather ? (int64_t)gather[r] : r) : 0;
   }
-  __syncthreads();
+  auto load = [&](int cc0, u32x4 (&v)[2]) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = (tid >> 3) + 32 * h;
-    if (c0 + c >= cols) continue;
-    u32x4 o;
+    for (int h = 0; h < 2; ++h) {
+      v[h] = u32x4{0, 0, 0, 0};
+      if (rok[h] && cc0 + ch * 8 < cols) v[h] = *reinterpret_cast<const u32x4*>(src + srow[h] * ld_src + cc0 + ch * 8);
+    }
+  };
+  const int cbase = blockIdx.y * 64 * kTrChunks;
+  u32x4 v[2];
+  load(cbase, v);
+  for (int k = 0; k < kTrChunks; ++k) {
+    const int c0 = cbase + k * 64;
+    if (c0 >= cols) break;
+    if (k) __syncthreads();  // the previous chunk's columns have been read
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = (uint32_t)tile[ch * 8 + 2 * q][c] | ((uint32_t)tile[ch * 8 + 2 * q + 1][c] << 16);
-    const int64_t kp = pad_off[e + 1] - pad_off[e];
-    *reinterpret_cast<u32x4*>(dst + (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) + ch * 8) =
-        o;
+    for (int h = 0; h < 2; ++h) {
+      const int i = (tid >> 3) + 32 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        tile[i][ch * 8 + 2 * q] = (bf16_t)(v[h][q] & 0xFFFFu);
+        tile[i][ch * 8 + 2 * q + 1] = (bf16_t)(v[h][q] >> 16);
+      }
+    }
+    if (k + 1 < kTrChunks && c0 + 64 < cols) load(c0 + 64, v);  // the next chunk's rows in flight
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = (tid >> 3) + 32 * h;
+      if (c0 + c >= cols) continue;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)tile[ch * 8 + 2 * q][c] | ((uint32_t)tile[ch * 8 + 2 * q + 1][c] << 16);
+      *reinterpret_cast<u32x4*>(dst + (int64_t)pad_off[e] * cols + (int64_t)(c0 + c) * kp + (p0 - pad_off[e]) +
+                                ch * 8) = o;
+    }
   }
 }
 
@@ -197,56 +217,71 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(const bf16_t* __re
   static_assert(TC * 8 * 16 + TC * 4 <= TP * LDT * 2, "codes fit the tile");
   const int64_t p0 = (int64_t)blockIdx.x * TP;
   if (p0 >= pad_off[nseg]) return;
-  const int c0 = blockIdx.y * TC;
   const int e = find_segment(pad_off, nseg, p0);
   const int64_t r0 = seg_off[e] + (p0 - pad_off[e]);
   const int64_t r_end = seg_off[e + 1];
   const int tid = threadIdx.x;
   const int ch = tid & 7;
+  // This thread's four source rows, shared by the workgroup's column chunks.
+  int64_t srow[TP / 32];
+  bool rok[TP / 32];
 #pragma unroll
   for (int h = 0; h < TP / 32; ++h) {
-    const int i = (tid >> 3) + 32 * h;
-    const int64_t r = r0 + i;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (r < r_end && c0 + ch * 8 < cols) {
-      const int64_t srow = gather ? (int64_t)gather[r] : r;
-      v = *reinterpret_cast<const u32x4*>(src + srow * ld_src + c0 + ch * 8);
+    const int64_t r = r0 + (tid >> 3) + 32 * h;
+    rok[h] = r < r_end;
+    srow[h] = rok[h] ? (gather ? (int64_t)gather[r] : r) : 0;
+  }
+  auto load = [&](int cc0, u32x4 (&v)[TP / 32]) {
+#pragma unroll
+    for (int h = 0; h < TP / 32; ++h) {
+      v[h] = u32x4{0, 0, 0, 0};
+      if (rok[h] && cc0 + ch * 8 < cols) v[h] = *reinterpret_cast<const u32x4*>(src + srow[h] * ld_src + cc0 + ch * 8);
     }
-    *reinterpret_cast<u32x4*>(&tile[i][ch * 8]) = v;
-  }
-  __syncthreads();
-  const int c = tid & (TC - 1), blk = tid / TC;
-  float v[32];
-  float amax = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 32; ++q) {
-    v[q] = bf16_to_f32(tile[blk * 32 + q][c]);
-    amax = fmaxf(amax, fabsf(v[q]));
-  }
-  const int ex = mx_block_exp(amax);
-  const float inv = mx_inv_scale(ex);
-  u32x4 w[2];
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    w[q >> 2][q & 3] = e4m3x4_rne_sat(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
-  __syncthreads();  // every thread has read its tile column
-  codes[c][blk * 2] = w[0];
-  codes[c][blk * 2 + 1] = w[1];
-  reinterpret_cast<uint8_t*>(scales)[c * 4 + blk] = (uint8_t)(ex + 127);
-  __syncthreads();
+  };
   const int64_t kp = pad_off[e + 1] - pad_off[e];
   const int64_t base = (int64_t)pad_off[e] * cols + (p0 - pad_off[e]);
   uint32_t* sdst = reinterpret_cast<uint32_t*>(dst_scale + (int64_t)pad_off[e] * cols / 32) +
                    (p0 - pad_off[e]) / TP * cols;
+  const int cbase = blockIdx.y * TC * kTqChunks;
+  u32x4 v[TP / 32];
+  load(cbase, v);
+  for (int k = 0; k < kTqChunks; ++k) {
+    const int c0 = cbase + k * TC;
+    if (c0 >= cols) break;
+    if (k) __syncthreads();  // the previous chunk's codes have left the LDS
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = tid + 256 * it, cc = q >> 3, part = q & 7;
-    if (c0 + cc < cols) {
-      const int64_t off = base + (int64_t)(c0 + cc) * kp;
-      *reinterpret_cast<u32x4*>(dst + off + part * 16) = codes[cc][part];
+    for (int h = 0; h < TP / 32; ++h) *reinterpret_cast<u32x4*>(&tile[(tid >> 3) + 32 * h][ch * 8]) = v[h];
+    if (k + 1 < kTqChunks && c0 + TC < cols) load(c0 + TC, v);  // the next chunk's rows in flight
+    __syncthreads();
+    const int c = tid & (TC - 1), blk = tid / TC;
+    float f[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      f[q] = bf16_to_f32(tile[blk * 32 + q][c]);
+      amax = fmaxf(amax, fabsf(f[q]));
     }
+    const int ex = mx_block_exp(amax);
+    const float inv = mx_inv_scale(ex);
+    u32x4 w[2];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      w[q >> 2][q & 3] = e4m3x4_rne_sat(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv, f[4 * q + 3] * inv);
+    __syncthreads();  // every thread has read its tile column
+    codes[c][blk * 2] = w[0];
+    codes[c][blk * 2 + 1] = w[1];
+    reinterpret_cast<uint8_t*>(scales)[c * 4 + blk] = (uint8_t)(ex + 127);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int q = tid + 256 * it, cc = q >> 3, part = q & 7;
+      if (c0 + cc < cols) {
+        const int64_t off = base + (int64_t)(c0 + cc) * kp;
+        *reinterpret_cast<u32x4*>(dst + off + part * 16) = codes[cc][part];
+      }
+    }
+    if (tid < TC && c0 + tid < cols) sdst[c0 + tid] = scales[tid];
   }
-  if (tid < TC && c0 + tid < cols) sdst[c0 + tid] = scales[tid];
 }
 
 // dst[b][c][r] = src[b][r][c], element-wise bounds (any rows, cols).
@@ -466,7 +501,7 @@ hipError_t launch_transpose_quant(const bf16_t* src, int64_t ld_src, int cols, c
                                   uint8_t* dst, uint8_t* dst_scale, hipStream_t s) {
   if (p_cap == 0 || cols == 0) return hipSuccess;
   if (p_cap % 128 || ld_src % 8 || cols % 8) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(p_cap / 128), (unsigned)((cols + 63) / 64));
+  const dim3 grid((unsigned)(p_cap / 128), (unsigned)((cols + 64 * kTqChunks - 1) / (64 * kTqChunks)));
   transpose_quant_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst, dst_scale);
   return hipGetLastError();
 }
@@ -489,7 +524,7 @@ hipError_t launch_transpose_rows(const bf16_t* src, int64_t ld_src, int cols, co
                                  hipStream_t s) {
   if (p_cap == 0 || cols == 0) return hipSuccess;
   if (p_cap % 64 || ld_src % 8 || cols % 8) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 63) / 64));
+  const dim3 grid((unsigned)(p_cap / 64), (unsigned)((cols + 64 * kTrChunks - 1) / (64 * kTrChunks)));
   transpose_rows_kernel<<<grid, 256, 0, s>>>(src, ld_src, cols, gather, seg_off, pad_off, nseg, dst);
   return hipGetLastError();
 }
