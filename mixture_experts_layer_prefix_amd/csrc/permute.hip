@@ -192,36 +192,41 @@ __global__ void __launch_bounds__(1024) dispatch_rows_kernel(const uint8_t* __re
   }
 }
 
-// The MXFP8 dispatch, pushed the same way: one workgroup per token, one
-// 32-element block of its row per thread, quantized once (codes and the
-// E8M0 byte) and stored to each of the token's k routed rows; scales
-// row-major [R][d/32].
+// The MXFP8 dispatch, pushed the same way: one workgroup per token, four
+// lanes per 32-element block of its row (16 bytes each, contiguous across the
+// wave); the block maximum is a two-step DPP maximum over the lane quad, each
+// lane encodes its eight values once and stores them (8 bytes) to each of
+// the token's k routed rows, the quad's first lane the E8M0 byte; scales
+// row-major [R][d/32].  The workgroup size is a multiple of 64 and d / 8 a
+// multiple of 4, so quads never straddle blocks.
 __global__ void __launch_bounds__(1024) dispatch_quant_kernel(const bf16_t* __restrict__ x,
                                                               const int32_t* __restrict__ token_row,
                                                               uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
                                                               int k, int d) {
   const int64_t t = blockIdx.x;
-  const int bpr = d / 32;
-  for (int b = threadIdx.x; b < bpr; b += blockDim.x) {
-    float v[32];
-    uint32_t packed[8];
-    const u32x4* in = reinterpret_cast<const u32x4*>(x + t * d + b * 32);
+  const int cpr = d / 8, bpr = d / 32;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + t * d) + c);
+    float v[8];
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 w = __builtin_nontemporal_load(in + i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      m = max(m, (w[j] << 16) & 0x7FFFFFFFu);
+      m = max(m, w[j] & 0x7FFF0000u);
     }
-    const uint32_t sc = mx_quant32(v, packed);
+    m = max(m, dpp_u32<0xB1>(m));
+    m = max(m, dpp_u32<0x4E>(m));
+    const int e = mx_block_exp_bits(m);
+    const float inv = mx_inv_scale(e);
+    const u32x2 codes = u32x2{e4m3x4_rne_sat(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                              e4m3x4_rne_sat(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv)};
     for (int j = 0; j < k; ++j) {
       const int64_t row = token_row[t * k + j];
-      u32x4* out = reinterpret_cast<u32x4*>(q + row * d + b * 32);
-      out[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-      out[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
-      scale[row * bpr + b] = (uint8_t)sc;
+      *reinterpret_cast<u32x2*>(q + row * d + c * 8) = codes;
+      if ((c & 3) == 0) scale[row * bpr + (c >> 2)] = (uint8_t)(e + 127);
     }
   }
 }
@@ -234,37 +239,43 @@ unsigned token_block(int items, int per) {
   return (unsigned)(th < 64 ? 64 : (th > 1024 ? 1024 : th));
 }
 
-// Row blocks of 32 columns, rows optionally gathered.  Scales row-major
-// [R][d/32], or with slab_major slab-major [d/128][R][4] (the four blocks of
-// a 128-column slab of one row form one dword; a slab's dwords are
-// contiguous over the rows).
-__global__ void __launch_bounds__(256) gather_quant_kernel(const bf16_t* __restrict__ x,
-                                                           const int32_t* __restrict__ row_token,
-                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
-                                                           int64_t R, int d, bool slab_major) {
-  const int bpr = d / 32;
-  const int64_t nblk = R * bpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-    const int64_t r = b / bpr, c = b - r * bpr;
-    const int64_t src = row_token ? (int64_t)row_token[r] : r;
-    const u32x4* in = reinterpret_cast<const u32x4*>(x + src * d + c * 32);
-    float v[32];
+// Row blocks of 32 columns of a contiguous [R][d] array, four lanes per block
+// (16 bytes each, so a wave reads 1 KiB of a row at once): the block maximum
+// is a two-step DPP maximum over the lane quad (exact: the same scale as from
+// the whole block in one thread), then each lane encodes its eight values.
+// Scales row-major [R][d/32], or with slab_major slab-major [d/128][R][4] (the
+// four blocks of a 128-column slab of one row form one dword; a slab's dwords
+// are contiguous over the rows).
+__global__ void __launch_bounds__(256) quant_rows_kernel(const bf16_t* __restrict__ x, uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ scale, int64_t R, int d,
+                                                         bool slab_major) {
+  const int cpr = d / 8;  // 16-byte chunks per row, a multiple of 4: quads never straddle rows
+  const int64_t n = R * cpr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 4: quads stay aligned
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / cpr;
+    const int ck = (int)(i - r * cpr);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(x + i * 8);
+    float v[8];
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 w = in[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      m = max(m, (w[j] << 16) & 0x7FFFFFFFu);
+      m = max(m, w[j] & 0x7FFF0000u);
     }
-    uint32_t packed[8];
-    const uint32_t sc = mx_quant32(v, packed);
-    u32x4* out = reinterpret_cast<u32x4*>(q + r * d + c * 32);
-    out[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    out[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
-    scale[slab_major ? ((c >> 2) * R + r) * 4 + (c & 3) : r * bpr + c] = (uint8_t)sc;
+    m = max(m, dpp_u32<0xB1>(m));
+    m = max(m, dpp_u32<0x4E>(m));
+    const int e = mx_block_exp_bits(m);
+    const float inv = mx_inv_scale(e);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(q + i * 8) = u32x2{e4m3x4_rne_sat(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                                                 e4m3x4_rne_sat(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv)};
+    if ((ck & 3) == 0) {
+      const int c = ck >> 2;
+      scale[slab_major ? ((int64_t)(c >> 2) * R + r) * 4 + (c & 3) : r * (d / 32) + c] = (uint8_t)(e + 127);
+    }
   }
 }
 
@@ -361,7 +372,7 @@ hipError_t launch_dispatch_quant_mx(const bf16_t* x, const int32_t* token_row, u
                                     int k, int d, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (d % 32 || T > INT32_MAX) return hipErrorInvalidValue;
-  dispatch_quant_kernel<<<(unsigned)T, token_block(d / 32, 1), 0, s>>>(x, token_row, q, scale, k, d);
+  dispatch_quant_kernel<<<(unsigned)T, token_block(d / 8, 1), 0, s>>>(x, token_row, q, scale, k, d);
   return hipGetLastError();
 }
 
@@ -378,8 +389,7 @@ hipError_t launch_quantize_mx(const bf16_t* src, int64_t rows, int64_t cols, int
                               hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (axis == 0 || axis == 2)
-    gather_quant_kernel<<<stream_grid(rows * (cols / 32)), 256, 0, s>>>(src, nullptr, dst, scale, rows, (int)cols,
-                                                                        axis == 2);
+    quant_rows_kernel<<<stream_grid(rows * (cols / 8)), 256, 0, s>>>(src, dst, scale, rows, (int)cols, axis == 2);
   else
     quant_cols_kernel<<<stream_grid(rows / 32 * cols), 256, 0, s>>>(src, rows, cols, dst, scale);
   return hipGetLastError();
