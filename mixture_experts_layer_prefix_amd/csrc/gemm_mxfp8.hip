@@ -159,16 +159,31 @@ __device__ __forceinline__ int find_group(const int32_t* prefix, int G, int mt) 
   return lo;
 }
 
-// Quantize the 32 values of one row's 32-column block held by lanes
-// (lane & 31) of a lane half: returns the E4M3 code of this lane's value and
-// the block's E8M0 byte in *scale (all lanes take part).
-__device__ __forceinline__ uint32_t mx_lane_quant(float v, uint32_t* scale) {
-  // Block maximum magnitude as a bit pattern; its exponent and mantissa
-  // fields give the block exponent (zero and fp32 subnormals clamp to -127).
-  const uint32_t amax = half_max32_u(__float_as_uint(v) & 0x7FFFFFFFu);
-  const int e = mx_block_exp_bits(amax);
-  *scale = (uint32_t)(e + 127);
-  return e4m3_rne_sat(v * mx_inv_scale(e));
+// 4 x 4 transpose inside each lane quad: lane j of the quad enters with
+// v[k] = element (k, j) and leaves with v[k] = element (j, k).  Two exchange
+// steps (partner lane j ^ 1, then j ^ 2), each swapping the two elements whose
+// index bit differs from the lane's.
+__device__ __forceinline__ void quad_transpose4(float (&v)[4], int j) {
+  const bool odd = j & 1;
+  const float ra = dpp_f32<0xB1>(odd ? v[0] : v[1]);  // quad_perm [1, 0, 3, 2]
+  const float rb = dpp_f32<0xB1>(odd ? v[2] : v[3]);
+  if (odd) {
+    v[0] = ra;
+    v[2] = rb;
+  } else {
+    v[1] = ra;
+    v[3] = rb;
+  }
+  const bool hi = j & 2;
+  const float rc = dpp_f32<0x4E>(hi ? v[0] : v[2]);  // quad_perm [2, 3, 0, 1]
+  const float rd = dpp_f32<0x4E>(hi ? v[1] : v[3]);
+  if (hi) {
+    v[0] = rc;
+    v[1] = rd;
+  } else {
+    v[2] = rc;
+    v[3] = rd;
+  }
 }
 
 // Load state of one output tile: buffer descriptors over its operands and
@@ -791,6 +806,61 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
     }
     return;
   }
+  if constexpr (MODE == GEMM_GATEUP) {
+    // h = SiLU(G) * U of column block wn of this tile (lane & 31 the column;
+    // lanes 0-31 rows 8 (v / 4) + v % 4, lanes 32-63 four rows further),
+    // quantized per row over its 32 columns.  Each lane quad (four adjacent
+    // columns) transposes its 4 x 4 block of four consecutive rows, so that a
+    // lane holds four adjacent columns of one row: the row's block maximum is
+    // the maximum over those four values and over the eight quads of the
+    // half-wave that hold the same row (DPP rotations by 4 and 8 inside each
+    // 16-lane row, then the half's two rows swapped), and the four codes leave
+    // as one dword.  The codes and scales are those of one lane per element.
+    uint8_t* C = static_cast<uint8_t*>(p.C);
+    const int jq = lane & 3;
+    const int colq = ntile * (BN / 2) + wn * 32 + (lane & 28);  // the quad's first column
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FM; ++i) {
+#pragma clang loop unroll(full)
+      for (int a = 0; a < 4; ++a) {
+        float hv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) hv[k] = silu_f32(acc[i][0][4 * a + k]) * acc[i][1][4 * a + k];
+        if (p.gu_out) {  // G | U kept for the backward
+          const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int rl = wm * WM + i * 32 + 8 * a + 4 * (lane >> 5) + k;
+            if (rl < rows_left && col < N) {
+              const int64_t grow = row_begin + m0 + rl;
+              p.gu_out[grow * 2 * N + col] = f32_to_bf16(acc[i][0][4 * a + k]);
+              p.gu_out[grow * 2 * N + N + col] = f32_to_bf16(acc[i][1][4 * a + k]);
+            }
+          }
+        }
+        quad_transpose4(hv, jq);
+        uint32_t mb = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mb = max(mb, __float_as_uint(hv[k]) & 0x7FFFFFFFu);
+        mb = max(mb, dpp_u32<0x124>(mb));  // row_ror:4
+        mb = max(mb, dpp_u32<0x128>(mb));  // row_ror:8
+        const auto sw = __builtin_amdgcn_permlane16_swap(mb, mb, false, false);
+        mb = max((uint32_t)sw[0], (uint32_t)sw[1]);
+        const int e = mx_block_exp_bits(mb);
+        const float inv = mx_inv_scale(e);
+        const uint32_t code = e4m3x4_rne_sat(hv[0] * inv, hv[1] * inv, hv[2] * inv, hv[3] * inv);
+        const int rl = wm * WM + i * 32 + 8 * a + 4 * (lane >> 5) + jq;
+        if (rl < rows_left && colq < N) {
+          const int64_t grow = row_begin + m0 + rl;
+          *reinterpret_cast<uint32_t*>(C + grow * ldc + colq) = code;
+          // h scales slab-major [I/128][rows][4] (the down GEMM's A layout)
+          if ((lane & 28) == 0)
+            p.Cs[(((int64_t)(colq >> 7) * p.M + grow) << 2) + ((colq >> 5) & 3)] = (uint8_t)(e + 127);
+        }
+      }
+    }
+    return;
+  }
 #pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
@@ -798,24 +868,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
       const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       const bool row_ok = rl < rows_left;
       const int64_t grow = row_begin + m0 + (row_ok ? rl : rows_left - 1);
-      if constexpr (MODE == GEMM_GATEUP) {
-        // h = SiLU(G) * U for column block wn of this tile, quantized per row
-        // over its 32 columns (lanes 0-31 or 32-63 of the wave).
-        const float h = silu_f32(acc[i][0][v]) * acc[i][1][v];
-        uint32_t sc;
-        const uint32_t code = mx_lane_quant(h, &sc);
-        const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
-        if (row_ok && col < N) {
-          uint8_t* C = static_cast<uint8_t*>(p.C);
-          C[grow * ldc + col] = (uint8_t)code;
-          // h scales slab-major [I/128][rows][4] (the down GEMM's A layout)
-          if ((lane & 31) == 0) p.Cs[(((int64_t)(col >> 7) * p.M + grow) << 2) + ((col >> 5) & 3)] = (uint8_t)sc;
-          if (p.gu_out) {  // G | U kept for the backward
-            p.gu_out[grow * 2 * N + col] = f32_to_bf16(acc[i][0][v]);
-            p.gu_out[grow * 2 * N + N + col] = f32_to_bf16(acc[i][1][v]);
-          }
-        }
-      } else if constexpr (MODE == GEMM_GU) {
+      if constexpr (MODE == GEMM_GU) {
         const int col = ntile * (BN / 2) + wn * 32 + (lane & 31);
         if (row_ok && col < N) {
           bf16_t* C = static_cast<bf16_t*>(p.C) + grow * ldc;
