@@ -632,6 +632,27 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
             const int c = j * 32 + (el & 31);
             stage[r * 64 + (((c >> 2) ^ skey(r)) << 2) + (c & 3)] = acc[i0 + ii][j][v];
           }
+      // This pass's G | U and router weights: item k + 1's loads are in flight
+      // while item k is processed (the first issued once the pass's
+      // accumulators have left their registers).
+      u32x4 ngq, nuq;
+      float nwr;
+      auto load_item = [&](int k) {
+        const int rb = (k * 64 + el) >> 2;
+        const int r = rb % PR, blk = rb / PR;
+        const int tr = wm * WM + i0 * 32 + r;
+        const int col = ntile * BN + wn * WN + blk * 32 + 8 * qt;
+        ngq = nuq = u32x4{0, 0, 0, 0};
+        nwr = 0.0f;
+        if (tr < rows_left && col < N) {
+          const int64_t grow = row_begin + m0 + tr;
+          const int64_t rowoff = grow * (int64_t)(2 * N);
+          ngq = *reinterpret_cast<const u32x4*>(p.gu + rowoff + col);
+          nuq = *reinterpret_cast<const u32x4*>(p.gu + rowoff + N + col);
+          nwr = p.w_row ? p.w_row[grow] : 1.0f;
+        }
+      };
+      load_item(0);
       __syncthreads();
 #pragma unroll 1
       for (int k = 0; k < ITEMS; ++k) {
@@ -646,13 +667,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, uint8_t* smem, const Mx
         const int64_t rowoff = grow * (int64_t)(2 * N);  // elements before row grow of the [rows][2N] arrays
         uint32_t* s0 = stage_w + r * 64 + (((blk * 8 + 2 * qt) ^ skey(r)) << 2);
         uint32_t* s1 = stage_w + r * 64 + (((blk * 8 + 2 * qt + 1) ^ skey(r)) << 2);
-        u32x4 gq = {0, 0, 0, 0}, uq = {0, 0, 0, 0};
-        float wr = 0.0f;
-        if (ok) {
-          gq = *reinterpret_cast<const u32x4*>(p.gu + rowoff + col);
-          uq = *reinterpret_cast<const u32x4*>(p.gu + rowoff + N + col);
-          wr = p.w_row ? p.w_row[grow] : 1.0f;
-        }
+        const u32x4 gq = ngq, uq = nuq;
+        const float wr = nwr;
+        if (k + 1 < ITEMS) load_item(k + 1);
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(s0), d1 = *reinterpret_cast<const f32x4*>(s1);
         float dg[8], du[8];
         uint32_t hw[4];
