@@ -35,8 +35,8 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kPadRows = 64;
-constexpr int kTqChunks = 4;  // 64-column chunks per transpose-quantize workgroup
-constexpr int kTrChunks = 4;  // 64-column chunks per bf16 transpose workgroup
+constexpr int kTqChunks = 8;  // 64-column chunks per transpose-quantize workgroup
+constexpr int kTrChunks = 8;  // 64-column chunks per bf16 transpose workgroup
 
 __global__ void __launch_bounds__(1024) pad_offsets_kernel(const int32_t* __restrict__ counts, int E, int64_t T,
                                                            int pad, int32_t* __restrict__ pad_off,
