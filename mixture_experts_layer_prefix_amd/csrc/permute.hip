@@ -293,6 +293,21 @@ __global__ void __launch_bounds__(256) gather_scales_slab_kernel(const uint32_t*
   }
 }
 
+// The same for K % 512 == 0: thread per (r, four consecutive slabs), one
+// 16-byte load of the source row and four dword stores, rows fastest.
+__global__ void __launch_bounds__(256) gather_scales_slab4_kernel(const u32x4* __restrict__ src,
+                                                                  const int32_t* __restrict__ row_token, int64_t R,
+                                                                  int groups, uint32_t* __restrict__ dst) {
+  const int64_t n = R * groups;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t q = i / R, r = i - q * R;
+    const u32x4 v = src[(int64_t)row_token[r] * groups + q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[(4 * q + j) * R + r] = v[j];
+  }
+}
+
 // Blocks of 32 consecutive rows of one column: thread per (row block, column).
 __global__ void __launch_bounds__(256) quant_cols_kernel(const bf16_t* __restrict__ src, int64_t rows, int64_t cols,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
@@ -380,8 +395,12 @@ hipError_t launch_gather_scales_slab(const uint8_t* scale_rows, const int32_t* r
                                      uint8_t* dst, hipStream_t s) {
   if (R == 0) return hipSuccess;
   if (K % 128) return hipErrorInvalidValue;
-  gather_scales_slab_kernel<<<stream_grid(R * (K / 128)), 256, 0, s>>>(
-      reinterpret_cast<const uint32_t*>(scale_rows), row_token, R, K / 128, reinterpret_cast<uint32_t*>(dst));
+  if (K % 512 == 0 && (reinterpret_cast<uintptr_t>(scale_rows) & 15) == 0)
+    gather_scales_slab4_kernel<<<stream_grid(R * (K / 512)), 256, 0, s>>>(
+        reinterpret_cast<const u32x4*>(scale_rows), row_token, R, K / 512, reinterpret_cast<uint32_t*>(dst));
+  else
+    gather_scales_slab_kernel<<<stream_grid(R * (K / 128)), 256, 0, s>>>(
+        reinterpret_cast<const uint32_t*>(scale_rows), row_token, R, K / 128, reinterpret_cast<uint32_t*>(dst));
   return hipGetLastError();
 }
 
