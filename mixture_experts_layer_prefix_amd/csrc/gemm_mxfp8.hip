@@ -19,9 +19,12 @@
 // four blocks, per row and slab).
 //
 // Gate/up mode writes h = SiLU(G) * U quantized along I (the down GEMM's K):
-// the 32 values of one 32-column block of a row sit in 32 lanes of a wave, so
-// the block maximum is a 5-step lane reduction, then each lane encodes its
-// element (blog post, "MXFP8 support": quantization fused into the SwiGLU).
+// the 32 values of one 32-column block of a row sit in 32 lanes of a wave;
+// each lane quad transposes a 4 x 4 block so that a lane holds four adjacent
+// columns of one row, the block maximum is a local maximum of four values
+// plus three cross-lane steps, and each lane encodes and stores its four
+// codes as one dword (blog post, "MXFP8 support": quantization fused into the
+// SwiGLU).
 #include "common.h"
 
 namespace moe {
