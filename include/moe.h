@@ -295,7 +295,8 @@ moe_status moe_transpose_weights(const void* src, int64_t batch, int64_t rows, i
  *     2 scheduled (+ MXFP8 token quantization), 3 shared FFN done,
  *     4 routed gate/up done, 5 routed down done, 6 combine done;
  *   which = 1, moe_layer_backward: 0 start, 1 prepared (padded offsets, row
- *     weights, MXFP8 quantization of x and dY), 2 G|U replayed, 3 down dgrad
+ *     weights, MXFP8 quantization of dY, and of x for the replay), 2 G|U
+ *     replayed (when the forward did not keep them), 3 down dgrad
  *     + SwiGLU backward done, 4 router-weight gradients done, 5 gate/up dgrad
  *     done, 6 shared-expert input gradient done, 7 dx done, 8 transposes done,
  *     9 dW_down done, 10 dW_gate and dW_up done (one launch), 11 shared
