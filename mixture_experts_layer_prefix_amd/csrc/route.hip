@@ -159,14 +159,42 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         mask &= mask - 1;
         int e = e0 + b;
         double acc = 0.0;
-        // 8 consecutive elements per lane per step (d is a multiple of 8).
+        // 8 consecutive elements per lane per step (d is a multiple of 8),
+        // added in ascending order; bf16 rows: four steps' loads in flight.
+        if (act_f32) {
 #pragma unroll 1
-        for (int c = lane * 8; c < d; c += 512) {
-          double xv[8], wv[8];
-          load8_f64(x, t * (int64_t)d + c, act_f32, xv);
-          load8_f64(wr, (int64_t)e * d + c, act_f32, wv);
+          for (int c = lane * 8; c < d; c += 512) {
+            double xv[8], wv[8];
+            load8_f64(x, t * (int64_t)d + c, true, xv);
+            load8_f64(wr, (int64_t)e * d + c, true, wv);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc += xv[q] * wv[q];
+            for (int q = 0; q < 8; ++q) acc += xv[q] * wv[q];
+          }
+        } else {
+          constexpr int U = 4;
+          const bf16_t* xb = static_cast<const bf16_t*>(x) + t * (int64_t)d;
+          const bf16_t* wb = static_cast<const bf16_t*>(wr) + (int64_t)e * d;
+#pragma unroll 1
+          for (int c0 = lane * 8; c0 < d; c0 += U * 512) {
+            u32x4 xr[U], wq[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              const int c = c0 + u * 512;
+              if (c < d) {
+                xr[u] = *reinterpret_cast<const u32x4*>(xb + c);
+                wq[u] = *reinterpret_cast<const u32x4*>(wb + c);
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              if (c0 + u * 512 >= d) break;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                acc += (double)__uint_as_float(xr[u][j] << 16) * (double)__uint_as_float(wq[u][j] << 16);
+                acc += (double)__uint_as_float(xr[u][j] & 0xFFFF0000u) * (double)__uint_as_float(wq[u][j] & 0xFFFF0000u);
+              }
+            }
+          }
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
