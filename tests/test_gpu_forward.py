@@ -134,13 +134,17 @@ def test_empty_batch():
 def test_full_oracle(cfg):
     """Every token of c1 (T=4096, d=2048, 64 experts top-6, shared expert) and
     c2 (T=8192, d=4096, 128 experts top-8, no shared expert): routing,
-    schedule and every output element against the oracle."""
+    schedule and every output element against the oracle; two runs bitwise
+    equal."""
     import mixture_experts_layer_prefix_amd as M
     D = gen.get_config(cfg)
     say("[case] %s full" % cfg, D)
     ref = HostProblem(D).oracle_forward()
     p, t, md, w = device_problem(D)
     y, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
+    y2, _ = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"])
+    assert torch.equal(y, y2), "forward is not bitwise deterministic"
+    del y2
     check_routing(to_np(routing["logits"]), to_np(routing["topk_idx"]), to_np(routing["topk_w"]), ref, D.k)
     for n, r in (("expert_counts", "counts"), ("expert_offsets", "offsets"), ("row_token", "row_token"),
                  ("token_row", "token_row")):
@@ -148,12 +152,6 @@ def test_full_oracle(cfg):
     e = rel_err(to_np(y), ref["y"])
     say("   %s rel err y %.3e rms %.3e" % (cfg, e, rms_rel(to_np(y), ref["y"])))
     assert e <= TOL[D.prec]
-
-
-@pytest.mark.parametrize("cfg,nsample", [("c2", 512), ("c3a", 512), ("c3b", 512)])
-def test_large_config_sampled(cfg, nsample):
-    """Full routing and permutation; outputs on a seeded token sample."""
-    check_forward_sampled(gen.get_config(cfg), nsample)
 
 
 @pytest.mark.parametrize("cfg", ["c3a", "c3b", "c4"])

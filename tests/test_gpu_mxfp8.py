@@ -172,8 +172,3 @@ def test_expert_down_takes_quantizer_layout():
     assert e_h <= 1e-1   # three MX roundings (x, weights, h); a wrong layout gives O(1)
 
 
-def test_c4_forward_sampled():
-    """The DeepSeek-V3-shaped MXFP8 forward (T=16384, Zipf-skewed routing)
-    on 512 sampled tokens plus the ragged experts' tokens."""
-    from tests.test_gpu_forward import check_forward_sampled
-    check_forward_sampled(gen.get_config("c4"), 512, seed=99)
