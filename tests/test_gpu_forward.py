@@ -198,6 +198,24 @@ def check_forward_sampled(D, nsample, seed=1234):
     say("   %s sampled %d tokens (experts %s with %s rows): rel err %.3e rms %.3e; experts empty %d, max rows %d" % (
         cfg, len(tokens), experts, [int(ref["counts"][x]) for x in experts], e, rms_rel(got, res["y"]),
         int(np.sum(ref["counts"] == 0)), int(ref["counts"].max())))
+    if e > TOL[D.prec if not mx else "mxfp8"]:
+        # name what is off before failing: the tokens, their experts, and
+        # whether the device inputs of those tokens still match the generator
+        tok_err = np.max(np.abs(got - res["y"]), axis=1) / np.max(np.abs(res["y"]))
+        bad = tokens[tok_err > TOL[D.prec]]
+        ex = ref["topk_idx"][bad].ravel()
+        vals, cnt = np.unique(ex, return_counts=True)
+        top = sorted(zip(cnt.tolist(), vals.tolist()), reverse=True)[:8]
+        x_dev = to_np(t["x"][torch.as_tensor(bad[:64], device=y.device)])
+        x_ok = np.array_equal(x_dev, hp.p.host_rows("x", bad[:64]).astype(np.float32))
+        if top and not mx:
+            v = top[0][1]
+            for n in ("w_gate", "w_up", "w_down"):
+                say("   device %s of expert %d equals the generator: %s" % (
+                    n, v, np.array_equal(to_np(t[n][v]), hp.p.host_expert(n, v).astype(np.float32))))
+        say("   %d of %d tokens over the bound (first %s); most frequent experts (count, id) %s with rows %s; "
+            "device x of those tokens equals the generator: %s" % (len(bad), len(tokens), bad[:8].tolist(), top,
+                                                                    [int(ref["counts"][v]) for _, v in top], x_ok))
     if not mx:
         assert e <= TOL[D.prec]
         return
