@@ -352,6 +352,22 @@ moe_status moe_quantize_mxfp8_rows_t(const void* src_bf16, int64_t ld_src, int32
                                      const int32_t* seg_off, const int32_t* pad_off, int32_t nseg, int64_t p_cap,
                                      uint8_t* dst, uint8_t* dst_scale, void* stream);
 
+/* The matrix-core operation under every MXFP8 GEMM of the library, one per
+ * tile (blog post "MXFP8 support": the routed experts' GEMMs take E4M3
+ * operands with one E8M0 scale per 32 elements along K; OCP MX v1.0).  For
+ * each tile t in [0, n): d[t] = c[t] + A[t] B[t]^T, with A[t] and B[t]
+ * [32][64] E4M3 codes (row-major, K contiguous; a and b hold n * 2048 bytes,
+ * 16-byte aligned), a_scale[t] and b_scale[t] [32][2] E8M0 codes (the scale
+ * of K[32j, 32j+32) of row i at byte 64t + 2i + j), c[t] and d[t] [32][32]
+ * fp32 row-major (n * 4096 bytes each; d may alias c).  Each tile is one
+ * gfx950 v_mfma_scale_f32_32x32x64_f8f6f4 with its operands in the lanes
+ * where the grouped GEMMs put them, so the rounding of that instruction,
+ * which those GEMMs inherit, can be measured and tested.  Device pointers;
+ * n = 0 is a no-op; EINVAL for n < 0 or above INT32_MAX, a null pointer, or
+ * a or b not 16-byte aligned. */
+moe_status moe_mx_mma_tiles(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, const uint8_t* b_scale,
+                            const float* c, float* d, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

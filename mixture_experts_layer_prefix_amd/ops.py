@@ -264,6 +264,20 @@ def quantize_mxfp8_rows_t(src, seg_off, pad_off, gather=None):
     return dst[:p_cap * cols], scale[:p_cap * cols // 32]
 
 
+def mx_mma_tiles(a, a_scale, b, b_scale, c):
+    """moe_mx_mma_tiles: d[t] = c[t] + A[t] B[t]^T per tile through one
+    scaled matrix-core operation.  a, b uint8 [n][32][64] E4M3 codes; a_scale,
+    b_scale uint8 [n][32][2] E8M0 codes; c float32 [n][32][32].  Returns d."""
+    n = a.shape[0]
+    assert a.shape == (n, 32, 64) and b.shape == (n, 32, 64) and c.shape == (n, 32, 32)
+    assert a_scale.shape == (n, 32, 2) and b_scale.shape == (n, 32, 2)
+    assert a.dtype == b.dtype == a_scale.dtype == b_scale.dtype == torch.uint8 and c.dtype == torch.float32
+    a, b, a_scale, b_scale, c = (t.contiguous() for t in (a, b, a_scale, b_scale, c))
+    d = torch.empty_like(c)
+    call("moe_mx_mma_tiles", _p(a), _p(a_scale), _p(b), _p(b_scale), _p(c), _p(d), n, _stream())
+    return d
+
+
 def prepare_mxfp8(weights: Weights, dims: Dims) -> Weights:
     """Weights with the routed experts pre-quantized for MOE_MXFP8 (blocks
     along each GEMM's K: d for gate/up, I for down)."""

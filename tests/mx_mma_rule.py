@@ -1,0 +1,67 @@
+"""Error model of gfx950's scaled matrix-core operation
+(v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and E8M0 block scales),
+measured on the device through moe_mx_mma_tiles and pinned by
+tests/test_gpu_mx_mma.py:
+
+  * every product a_k b_k 2^(sa + sb) is exact (at most 8 significant bits);
+  * products are summed in groups of eight consecutive K (aligned to 8);
+    inside a group each product is truncated toward zero to a multiple of
+    2^(E - 13), where 2^E bounds the group's leading product from below
+    (the hardware takes E from the operands' exponents, at most the largest
+    product's own exponent), so a product loses less than one such quantum,
+    and nothing when |p| >= 2^(E - 6) (it already lies on the grid);
+  * the group sums and the accumulator input are combined and rounded to
+    fp32, not always to the nearest fp32 value of their exact sum; the
+    model allows one fp32 ulp of the result for that step.  Measured against
+    the exact sum over 57,344 random outputs the device stays within one
+    quantum per product cut in the groups plus that ulp (at most 0.83 of the
+    bound with half an ulp).
+
+So the matrix cores do not meet the textbook fp32 inner-product bound
+gamma_K sum|a_i b_i|: with heavy-tailed operands (h, whose products span
+many binades) the in-group truncation dominates.  Test infrastructure, not
+part of the product path: the MXFP8 forward checks bound each kernel output
+by mx_dot, instruction by instruction."""
+import numpy as np
+
+GROUP = 8
+ALIGN_BITS = 13
+U_F32 = 2.0 ** -24
+
+
+def instruction_bound(p):
+    """p [..., 64]: the exact products of one instruction (float64).
+    Returns the bound on what the in-group alignment can cut: for each group
+    of eight, one quantum 2^(E - 13) per product below 2^(E - 6), with 2^E the
+    leading product's binade."""
+    g = p.reshape(*p.shape[:-1], p.shape[-1] // GROUP, GROUP)
+    a = np.abs(g)
+    amax = np.max(a, axis=-1, keepdims=True)
+    _, ex = np.frexp(amax)                       # amax in [2^(ex-1), 2^ex)
+    E = ex - 1
+    cut = (a > 0) & (a < np.ldexp(1.0, E - 6))
+    return np.sum(np.where(amax > 0, np.ldexp(1.0, E - ALIGN_BITS), 0.0) * cut, axis=(-2, -1))
+
+
+def mx_dot(a, b, row_chunk=64):
+    """Rows of a [r][K] times rows of b [n][K] (exact float64 values of MX
+    operands; K a multiple of 64, in the order the kernel feeds it) as the
+    matrix cores accumulate them over K/64 instructions.  Returns (s, e): s the
+    exact product, e a bound on the kernel's fp32 deviation from s (the
+    in-group cuts of every instruction plus one fp32 ulp of each
+    instruction's result, with slack for the float64 evaluation)."""
+    r, K = a.shape
+    n = b.shape[0]
+    assert K % 64 == 0 and b.shape[1] == K
+    s = np.zeros((r, n))
+    e = np.zeros((r, n))
+    for r0 in range(0, r, row_chunk):
+        rs = slice(r0, min(r, r0 + row_chunk))
+        acc = np.zeros((rs.stop - r0, n))
+        err = np.zeros_like(acc)
+        for k0 in range(0, K, 64):
+            p = a[rs, None, k0:k0 + 64] * b[None, :, k0:k0 + 64]
+            acc = acc + p.sum(axis=-1)
+            err = err + instruction_bound(p) + 2 * U_F32 * (np.abs(acc) + err) + 2.0 ** -50 * np.abs(p).sum(axis=-1)
+        s[rs], e[rs] = acc, err
+    return s, e

@@ -116,6 +116,12 @@ def test_backward_validation_before_device_work():
     assert lib.moe_transpose_weights(fake, -1, 4, 4, fake, None) == L.MOE_EINVAL
     assert lib.moe_transpose_weights(None, 1, 4, 4, fake, None) == L.MOE_EINVAL
     assert lib.moe_transpose_weights(None, 0, 4, 4, None, None) == L.MOE_OK
+    # the matrix-core tile entry point: count, null and alignment checks on the host
+    assert lib.moe_mx_mma_tiles(fake, fake, fake, fake, fake, fake, -1, None) == L.MOE_EINVAL
+    assert lib.moe_mx_mma_tiles(fake, fake, fake, fake, fake, fake, 1 << 31, None) == L.MOE_EINVAL
+    assert lib.moe_mx_mma_tiles(fake, None, fake, fake, fake, fake, 1, None) == L.MOE_EINVAL
+    assert lib.moe_mx_mma_tiles(fake + 8, fake, fake, fake, fake, fake, 1, None) == L.MOE_EINVAL
+    assert lib.moe_mx_mma_tiles(None, None, None, None, None, None, 0, None) == L.MOE_OK
 
 
 def test_permute_noalloc_rejects_beyond_its_scratch_on_the_host():
