@@ -368,6 +368,18 @@ moe_status moe_quantize_mxfp8_rows_t(const void* src_bf16, int64_t ld_src, int32
 moe_status moe_mx_mma_tiles(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, const uint8_t* b_scale,
                             const float* c, float* d, int64_t n, void* stream);
 
+/* The bf16 matrix-core operation under the bf16 grouped GEMMs and the router
+ * logits (blog post "MoE layer benchmarks": the layers run in bf16; the
+ * router's exact selection relies on a bound of this instruction's
+ * accumulation error).  For each tile t in [0, n): d[t] = c[t] + A[t] B[t]^T,
+ * with A[t] and B[t] [32][16] bf16 (row-major, K contiguous; a and b hold
+ * n * 1024 bytes, 16-byte aligned), c[t] and d[t] [32][32] fp32 row-major
+ * (d may alias c).  Each tile is one gfx950 v_mfma_f32_32x32x16_bf16 with its
+ * operands in the lanes where the bf16 GEMMs put them.  Device pointers;
+ * n = 0 is a no-op; EINVAL for n < 0 or above INT32_MAX, a null pointer, or
+ * a or b not 16-byte aligned. */
+moe_status moe_bf16_mma_tiles(const void* a, const void* b, const float* c, float* d, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,7 @@ _SIGS = {
     "moe_quantize_mxfp8_rows_t": ([_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int64,
                                    _P, _P, _P], ctypes.c_int),
     "moe_mx_mma_tiles": ([_P, _P, _P, _P, _P, _P, ctypes.c_int64, _P], ctypes.c_int),
+    "moe_bf16_mma_tiles": ([_P, _P, _P, _P, ctypes.c_int64, _P], ctypes.c_int),
 }
 
 _lib = None

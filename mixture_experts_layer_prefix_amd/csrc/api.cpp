@@ -953,6 +953,15 @@ moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t cols, 
   return MOE_OK;
 }
 
+moe_status moe_bf16_mma_tiles(const void* a, const void* b, const float* c, float* d, int64_t n, void* stream) {
+  if (n < 0 || n > INT32_MAX) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (!ptr_ok(a) || !ptr_ok(b) || !c || !d) return MOE_EINVAL;
+  MOE_HIP(launch_bf16_mma_tiles(static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), c, d, n,
+                                static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_mx_mma_tiles(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, const uint8_t* b_scale,
                             const float* c, float* d, int64_t n, void* stream) {
   if (n < 0 || n > INT32_MAX) return MOE_EINVAL;

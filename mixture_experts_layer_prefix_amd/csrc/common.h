@@ -349,6 +349,9 @@ int gemm_grid(int num_cus);
 hipError_t launch_gemm_bf16(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_mxfp8(const GemmProblem& p, hipStream_t s);
+// One bf16 MFMA per tile (moe_bf16_mma_tiles).
+hipError_t launch_bf16_mma_tiles(const bf16_t* a, const bf16_t* b, const float* c, float* d, int64_t n,
+                                 hipStream_t s);
 // One scaled MFMA per tile (moe_mx_mma_tiles).
 hipError_t launch_mx_mma_tiles(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, const uint8_t* b_scale,
                                const float* c, float* d, int64_t n, hipStream_t s);

@@ -278,6 +278,19 @@ def mx_mma_tiles(a, a_scale, b, b_scale, c):
     return d
 
 
+def bf16_mma_tiles(a, b, c):
+    """moe_bf16_mma_tiles: d[t] = c[t] + A[t] B[t]^T per tile through one bf16
+    matrix-core operation.  a, b bfloat16 [n][32][16]; c float32 [n][32][32].
+    Returns d."""
+    n = a.shape[0]
+    assert a.shape == (n, 32, 16) and b.shape == (n, 32, 16) and c.shape == (n, 32, 32)
+    assert a.dtype == b.dtype == torch.bfloat16 and c.dtype == torch.float32
+    a, b, c = a.contiguous(), b.contiguous(), c.contiguous()
+    d = torch.empty_like(c)
+    call("moe_bf16_mma_tiles", _p(a), _p(b), _p(c), _p(d), n, _stream())
+    return d
+
+
 def prepare_mxfp8(weights: Weights, dims: Dims) -> Weights:
     """Weights with the routed experts pre-quantized for MOE_MXFP8 (blocks
     along each GEMM's K: d for gate/up, I for down)."""

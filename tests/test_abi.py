@@ -122,6 +122,10 @@ def test_backward_validation_before_device_work():
     assert lib.moe_mx_mma_tiles(fake, None, fake, fake, fake, fake, 1, None) == L.MOE_EINVAL
     assert lib.moe_mx_mma_tiles(fake + 8, fake, fake, fake, fake, fake, 1, None) == L.MOE_EINVAL
     assert lib.moe_mx_mma_tiles(None, None, None, None, None, None, 0, None) == L.MOE_OK
+    assert lib.moe_bf16_mma_tiles(fake, fake, fake, fake, -1, None) == L.MOE_EINVAL
+    assert lib.moe_bf16_mma_tiles(fake, None, fake, fake, 1, None) == L.MOE_EINVAL
+    assert lib.moe_bf16_mma_tiles(fake + 8, fake, fake, fake, 1, None) == L.MOE_EINVAL
+    assert lib.moe_bf16_mma_tiles(None, None, None, None, 0, None) == L.MOE_OK
 
 
 def test_permute_noalloc_rejects_beyond_its_scratch_on_the_host():

@@ -5,7 +5,7 @@ GEMMs and the whole layer within 3e-2 of a quantization-aware float64 model
 otherwise: the kernels' own error), and on the small shapes element by
 element: G and U, every scale and code of h, and the down projection each
 within a bound derived from the matrix cores' measured accumulation
-(tests/mx_mma_rule.py); held to the stated 6e-2
+(tests/mma_rules.py); held to the stated 6e-2
 (max|d|/max|ref|) against the float64 oracle of the unquantized layer, an
 expected failure only where MX rounding alone exceeds it."""
 import numpy as np
@@ -14,7 +14,7 @@ import pytest
 import gen
 from oracle import moe_oracle as O
 from tests.moe_parity import TOL, HostProblem, check_mx_bound, device_problem, rel_err, rms_rel, to_np
-from tests.mx_mma_rule import mx_dot
+from tests.mma_rules import mx_dot
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
