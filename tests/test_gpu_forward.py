@@ -10,6 +10,7 @@ import pytest
 import gen
 from oracle import moe_oracle as O
 from tests.moe_parity import TOL, HostProblem, boundary_gaps, device_problem, rel_err, rms_rel, to_np
+from tests.mma_rules import bf16_dot
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -32,6 +33,36 @@ SMALL = {
 
 def say(*a):
     print(*a, flush=True)
+
+
+def check_bf16_expert_elementwise(p, D, ref, gu, h, o_perm):
+    """The bf16 routed experts element by element against exact arithmetic on
+    the same bf16 operands, each within the bound the matrix cores' measured
+    accumulation gives (tests/mma_rules.py): G and U (kept in bf16) within
+    half a bf16 ulp plus bf16_dot's bound; h = silu(G) U (fp32 from the fp32
+    G, U, stored in bf16) within half an ulp plus the band those bounds give
+    (silu is 1.1-Lipschitz, 2^-16 relative covers its fp32 evaluation); the
+    down projection against the exact product of the kernel's own h."""
+    a = p.host("x")[ref["row_token"]]
+    off = ref["offsets"]
+    R, I, d = D.R, D.I, D.d
+    G, U, dG, dU, o, do = (np.zeros(sh) for sh in ((R, I),) * 4 + ((R, d),) * 2)
+    for e in range(D.E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        wg, wu, wd = (p.host_expert(n, e) for n in ("w_gate", "w_up", "w_down"))
+        G[lo:hi], dG[lo:hi] = bf16_dot(a[lo:hi], wg)
+        U[lo:hi], dU[lo:hi] = bf16_dot(a[lo:hi], wu)
+        o[lo:hi], do[lo:hi] = bf16_dot(h[lo:hi], wd)
+    half = lambda x, y: 2.0 ** -8 * np.maximum(np.abs(x), np.abs(y))
+    s = O.silu(G)
+    h64 = s * U
+    dh = 1.1 * dG * (np.abs(U) + dU) + (np.abs(s) + 1.1 * dG) * dU + 2.0 ** -16 * (np.abs(s) + 1.1 * dG) * (np.abs(U) + dU)
+    for name, k, m, dm in (("G", gu[:, :I], G, dG), ("U", gu[:, I:], U, dU), ("h", h, h64, dh), ("o_perm", o_perm, o, do)):
+        over = np.abs(k - m) - (half(k, m) + dm)
+        assert np.all(over <= 0), "%s off by %.3e beyond its bound at %s" % (
+            name, over.max(), np.unravel_index(np.argmax(over), over.shape))
 
 
 def check_routing(gpu_logits, gpu_idx, gpu_w, ref, k):
@@ -83,8 +114,17 @@ def test_small_layer_every_entry_point(name):
     for n in ("topk_idx", "expert_counts", "expert_offsets", "token_row"):
         r = ref[{"expert_counts": "counts", "expert_offsets": "offsets"}.get(n, n)]
         assert np.array_equal(to_np(routing[n]), r), n
-    y2, _ = M.layer_forward(t["x"], w, md, prec, bias=t["bias"])
+    y2, routing2 = M.layer_forward(t["x"], w, md, prec, bias=t["bias"], keep_gu=prec == "bf16")
     assert torch.equal(y, y2), "forward is not bitwise deterministic"
+    if prec == "bf16":
+        # the two routed GEMMs through their own entry points: the same bits as
+        # moe_expert_ffn, and each element within its derived bound
+        h, _ = M.expert_gate_up(x_perm, None, offsets, w, md, prec)
+        o2 = M.expert_down(h, None, offsets, w, md, prec)
+        assert torch.equal(o2, o_perm)
+        check_bf16_expert_elementwise(p, D, ref, to_np(routing2["gu"][:D.R]).astype(np.float64),
+                                      to_np(h).astype(np.float64), to_np(o_perm).astype(np.float64))
+        say("   element-wise bounds hold for G, U, h and o_perm")
     if D.S and prec != "f32":
         # the layer forward gives the staged entry points' result bit for bit
         assert torch.equal(y, y_c), "moe_layer_forward differs from the staged entry points"
