@@ -163,8 +163,18 @@ def quantized_expert_outputs(p, D, ref):
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_mxfp8_layer(name):
+    check_mxfp8_layer(SMALL[name], strict=True)
+
+
+def check_mxfp8_layer(D, strict):
+    """One small MXFP8 layer: routing, the quantizing dispatch and the
+    staged/fused equalities bit-exact; y within 3e-2 of the quantization-aware
+    model; G, U, every h scale and code and o_perm element by element; the
+    combine against a float64 sum.  strict: also the stated 6e-2 bound
+    against the float64 oracle (an expected failure where the quantized
+    operands alone exceed it)."""
     import mixture_experts_layer_prefix_amd as M
-    D = SMALL[name]
+    name = D.name
     say("[case]", name, D)
     ref = HostProblem(D).oracle_forward()
     p, t, md, w = device_problem(D)
@@ -191,7 +201,10 @@ def test_small_mxfp8_layer(name):
     e_qo, e_qy = rel_err(to_np(o_perm), oq), rel_err(to_np(y), yq)
     say("   mxfp8 y vs exact %.3e (rms %.3e); vs MX-rounded operands: y %.3e, o_perm %.3e (o_perm vs exact %.3e)"
         % (e_y, rms_rel(to_np(y), ref["y"]), e_qy, e_qo, e_o))
-    assert e_qo <= 3e-2 and e_qy <= 3e-2
+    # o_perm is held element by element below: a max-norm bar on it fails where
+    # one h code next to a rounding boundary legitimately went the other way
+    # (a 128-term row moved by a fifth of an E4M3 step)
+    assert e_qy <= 3e-2
     # a second run, keeping G | U: bitwise the same output
     y2, routing2 = M.layer_forward(t["x"], wq, md, "mxfp8", bias=t["bias"], keep_gu=True)
     assert torch.equal(y, y2)
@@ -212,7 +225,8 @@ def test_small_mxfp8_layer(name):
     assert rel_err(to_np(y_st), y_c_ref) <= 4e-3
     # Against the exact layer: the stated 6e-2 bound (an expected failure
     # where MX rounding of the operands alone already exceeds it).
-    check_mx_bound({"y": (e_y, rel_err(yq, ref["y"])), "o_perm": (e_o, rel_err(oq, ref["o_perm"]))}, name)
+    if strict:
+        check_mx_bound({"y": (e_y, rel_err(yq, ref["y"])), "o_perm": (e_o, rel_err(oq, ref["o_perm"]))}, name)
 
 
 def test_expert_down_takes_quantizer_layout():
