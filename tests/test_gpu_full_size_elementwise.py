@@ -1,0 +1,125 @@
+"""The routed experts of the full-size DeepSeek-V3-shaped layers element by
+element on samples, through the persistent grids at their real tile counts:
+the bf16 layer at T=8192 and the MXFP8 layer at T=16384.
+
+Sampled routed rows (the first and last rows of the busiest expert, the rows
+of the smallest non-empty expert, the last rows of an expert with 64-256
+rows, and seeded random rows), four whole 32-column blocks of G, U and h, and
+256 seeded columns of the expert output; each element against exact
+arithmetic on the same operands (the oracle's MX rounding for MXFP8), within
+the bound of the matrix cores' measured accumulation (tests/mma_rules.py),
+as on the small shapes.  The rows' experts and tokens come from the oracle's
+routing, which is first checked equal to the device's."""
+import numpy as np
+import pytest
+
+import gen
+from oracle import moe_oracle as O
+from tests.mma_rules import bf16_dot, mx_dot
+from tests.moe_parity import HostProblem, device_problem, to_np
+from tests.test_gpu_mxfp8 import check_mx_h, mx_round
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def sample_rows(ref, R, seed, n_random=24):
+    counts, off = ref["counts"], ref["offsets"]
+    rng = np.random.default_rng(seed)
+    hot = int(np.argmax(counts))
+    rows = set(range(off[hot], off[hot] + 4)) | set(range(off[hot + 1] - 4, off[hot + 1]))
+    nz = np.nonzero(counts)[0]
+    small = int(nz[np.argmin(counts[nz])])
+    rows |= set(range(off[small], min(off[small + 1], off[small] + 4)))
+    mid = [int(e) for e in nz if 64 <= counts[e] <= 256]
+    if mid:
+        e = min(mid, key=lambda e: abs(int(counts[e]) - 128))
+        rows |= set(range(off[e + 1] - 4, off[e + 1]))
+    rows |= set(rng.choice(R, size=n_random, replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg", ["c3a", "c4"])
+def test_full_size_experts_elementwise(cfg):
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.get_config(cfg)
+    mx = D.prec == "mxfp8"
+    say("[case] full-size element-wise", D)
+    p, t, md, w = device_problem(D)
+    if mx:
+        w = M.prepare_mxfp8(w, md)
+    hp = HostProblem(D)
+    ref = hp.routing()
+    _, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"], keep_gu=True)
+    assert np.array_equal(to_np(routing["topk_idx"]), ref["topk_idx"])
+    assert np.array_equal(to_np(routing["row_token"]), ref["row_token"])
+    counts, offsets, row_token, token_row, xp, xs = M.permute(routing["topk_idx"], t["x"], md, D.prec)
+    h, hs = M.expert_gate_up(xp, xs, offsets, w, md, D.prec)
+    o = M.expert_down(h, hs, offsets, w, md, D.prec)
+    torch.cuda.synchronize()
+
+    rows = sample_rows(ref, D.R, seed=7)
+    rng = np.random.default_rng(11)
+    blocks = np.sort(rng.choice(D.I // 32, size=4, replace=False))
+    icols = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    dcols = np.sort(rng.choice(D.d, size=256, replace=False))
+    rt = torch.as_tensor(rows, device="cuda")
+    gu = to_np(routing["gu"][rt]).astype(np.float64)
+    Gk, Uk = gu[:, icols], gu[:, D.I + icols]
+    ok = to_np(o[rt]).astype(np.float64)[:, dcols]
+    if mx:
+        codes = to_np(h[rt])                                        # [n][I] E4M3
+        sc = to_np(hs[:, rt, :]).transpose(1, 0, 2).reshape(len(rows), D.I // 32)
+    else:
+        hk = to_np(h[rt]).astype(np.float64)                        # [n][I] bf16 values
+
+    # exact operands of the sampled rows, by expert
+    xr = hp.p.host_rows("x", ref["row_token"][rows])
+    if mx:
+        xr = mx_round(xr)
+    dot = mx_dot if mx else bf16_dot
+    ex = np.searchsorted(ref["offsets"], rows, side="right") - 1
+    n = len(rows)
+    G, dG, U, dU = (np.zeros((n, len(icols))) for _ in range(4))
+    for e in np.unique(ex):
+        sel = ex == e
+        wg = hp.p.host_expert_rows("w_gate", int(e), icols)
+        wu = hp.p.host_expert_rows("w_up", int(e), icols)
+        if mx:
+            wg, wu = mx_round(wg), mx_round(wu)
+        G[sel], dG[sel] = dot(xr[sel], wg)
+        U[sel], dU[sel] = dot(xr[sel], wu)
+    half = lambda a, b: 2.0 ** -8 * np.maximum(np.abs(a), np.abs(b))
+    for name, k, m, dm in (("G", Gk, G, dG), ("U", Uk, U, dU)):
+        over = np.abs(k - m) - (half(k, m) + dm)
+        assert np.all(over <= 0), "%s off by %.3e beyond its bound at %s" % (
+            name, over.max(), np.unravel_index(np.argmax(over), over.shape))
+    if mx:
+        check_mx_h(G, U, dG, dU, codes[:, icols], sc[:, blocks])
+        h_rows = O.e4m3_decode(codes) * np.ldexp(1.0, np.repeat(sc.astype(np.int64) - 127, 32, axis=1))
+    else:
+        s = O.silu(G)
+        h64 = s * U
+        dh = 1.1 * dG * (np.abs(U) + dU) + (np.abs(s) + 1.1 * dG) * dU + \
+            2.0 ** -16 * (np.abs(s) + 1.1 * dG) * (np.abs(U) + dU)
+        over = np.abs(hk[:, icols] - h64) - (half(hk[:, icols], h64) + dh)
+        assert np.all(over <= 0), "h off by %.3e beyond its bound at %s" % (
+            over.max(), np.unravel_index(np.argmax(over), over.shape))
+        h_rows = hk
+    # the down projection of the kernel's own h rows
+    o_ref, do = np.zeros((n, len(dcols))), np.zeros((n, len(dcols)))
+    for e in np.unique(ex):
+        sel = ex == e
+        wd = hp.p.host_expert_rows("w_down", int(e), dcols)
+        if mx:
+            wd = mx_round(wd)
+        o_ref[sel], do[sel] = dot(h_rows[sel], wd)
+    over = np.abs(ok - o_ref) - (half(ok, o_ref) + do)
+    assert np.all(over <= 0), "o_perm off by %.3e beyond its bound at %s" % (
+        over.max(), np.unravel_index(np.argmax(over), over.shape))
+    say("   %d rows of %d experts (busiest %d rows), %d G/U/h columns, %d output columns: every element within its bound"
+        % (n, len(np.unique(ex)), int(ref["counts"].max()), len(icols), len(dcols)))

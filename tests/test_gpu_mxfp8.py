@@ -108,23 +108,36 @@ def check_gate_up_elementwise(p, D, ref, gu, h, h_scale):
         over = np.abs(k - m) - (2.0 ** -8 * np.maximum(np.abs(k), np.abs(m)) + dm)
         assert np.all(over <= 0), "%s off by %.3e beyond its bound at %s" % (
             name, over.max(), np.unravel_index(np.argmax(over), over.shape))
+    sc = h_scale.transpose(1, 0, 2).reshape(R, I // 32)
+    h_dec, h64 = check_mx_h(G, U, dG, dU, h, sc)
+    qm, sm = O.mx_quantize(h64)
+    return h_dec, int(np.sum(qm != h)), int(np.sum(sm != sc))
+
+
+def check_mx_h(G, U, dG, dU, codes, scales):
+    """h = silu(G) U quantized by the gate/up epilogue, on any [n][c] set of
+    rows and whole 32-column blocks: G, U (float64, exact from the MX-rounded
+    operands) and their accumulation bounds dG, dU, the kernel's E4M3 codes
+    [n][c] and E8M0 scales [n][c/32].  Each scale must be the block rule's
+    exponent for some block maximum within h's band, each code within half an
+    E4M3 step plus the band of h.  Returns the decoded h and the float64 h."""
+    n, c = G.shape
     s = O.silu(G)
     h64 = s * U
     dh = 1.1 * dG * (np.abs(U) + dU) + (np.abs(s) + 1.1 * dG) * dU + 2.0 ** -16 * (np.abs(s) + 1.1 * dG) * (np.abs(U) + dU)
-    sc = h_scale.transpose(1, 0, 2).reshape(R, I // 32).astype(np.int64)
-    blk = lambda v: v.reshape(R, I // 32, 32)
+    sc = np.asarray(scales).astype(np.int64)
+    blk = lambda v: v.reshape(n, c // 32, 32)
     e_lo = O.mx_scale_exponent(np.max(np.maximum(blk(np.abs(h64) - dh), 0.0), axis=-1)) + 127
     e_hi = O.mx_scale_exponent(np.max(blk(np.abs(h64) + dh), axis=-1)) + 127
     bad = (sc < e_lo) | (sc > e_hi)
     assert not bad.any(), "h scale outside the admissible range at %s" % (np.argwhere(bad)[:5],)
     step = np.ldexp(1.0, np.repeat(sc - 127, 32, axis=1))
-    h_dec = O.e4m3_decode(h) * step
+    h_dec = O.e4m3_decode(codes) * step
     half = 0.5 * e4m3_quantum(np.maximum(np.abs(h_dec), np.abs(h64) + dh) / step) * step
     over = np.abs(h_dec - h64) - (half + dh)
     assert np.all(over <= 0), "h code off by %.3e beyond half a step plus its band at %s" % (
         over.max(), np.unravel_index(np.argmax(over), over.shape))
-    qm, sm = O.mx_quantize(h64)
-    return h_dec, int(np.sum(qm != h)), int(np.sum(sm != h_scale.transpose(1, 0, 2).reshape(R, I // 32)))
+    return h_dec, h64
 
 
 def check_down_elementwise(p, D, ref, h_dec, o_perm):
