@@ -1,7 +1,7 @@
 """The routed experts of the full-size layers element by element on samples,
 through the persistent grids at their real tile counts: the DeepSeek-V3
-layers (bf16 at T=8192, MXFP8 at T=16384) and the pages' other layer shapes
-at T=8192 in both precisions.
+layers (bf16 at T=8192, MXFP8 at T=16384), the pages' other layer shapes at
+T=8192 in both precisions, and one GPU's EP-64 share of each (MXFP8).
 
 Sampled routed rows (the first and last rows of the busiest expert, the rows
 of the smallest non-empty expert, the last rows of an expert with 64-256
@@ -47,7 +47,8 @@ def sample_rows(ref, R, seed, n_random=24):
 # the DeepSeek-V3 layers and the pages' other layer shapes (Kimi K2.7 Code,
 # GLM-5.2, Qwen3.5-397B-A17B, DeepSeek-V4-Pro; whole layers at T=8192), both precisions
 N3 = ["kimi_k27", "glm52", "qwen35", "dsv4pro"]
-CONFIGS = ["c3a", "c4"] + N3 + [n + "_mx" for n in N3]
+# and one GPU's EP-64 share of each (E/64 local experts, 2,048 k rows, MXFP8)
+CONFIGS = ["c3a", "c4"] + N3 + [n + "_mx" for n in N3] + ["ep64_" + n for n in ["dsv3"] + N3]
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
