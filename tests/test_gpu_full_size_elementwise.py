@@ -131,3 +131,60 @@ def test_full_size_experts_elementwise(cfg):
         over.max(), np.unravel_index(np.argmax(over), over.shape))
     say("   %d rows of %d experts (busiest %d rows), %d G/U/h columns, %d output columns: every element within its bound"
         % (n, len(np.unique(ex)), int(ref["counts"].max()), len(icols), len(dcols)))
+
+
+@pytest.mark.parametrize("cfg", ["c3a", "c4"])
+def test_full_size_shared_expert_elementwise(cfg):
+    """The shared expert (one dense group over every token, bf16 in both
+    precisions) on 24 seeded tokens: its kept G and U on four whole 32-column
+    blocks within half a bf16 ulp plus the bf16 matrix cores' bound, and its
+    output on 256 columns within half a bf16 ulp plus the bound carried from
+    h's band (the kernel's h is not exposed: each of its values lies within
+    half a bf16 ulp plus dh of the exact silu(G) U) through the down
+    projection, plus the accumulation bound of that projection.  That output
+    bound is coarse (about 15% of |y| at the median: the half ulps of 2,048
+    h values against a cancelling sum), so it catches layout or operand
+    mistakes rather than rounding ones; G and U are held tightly."""
+    import mixture_experts_layer_prefix_amd as M
+    D = gen.get_config(cfg)
+    assert D.S == 1
+    say("[case] full-size shared expert element-wise", D)
+    p, t, md, w = device_problem(D)
+    if D.prec == "mxfp8":
+        w = M.prepare_mxfp8(w, md)
+    _, routing = M.layer_forward(t["x"], w, md, D.prec, bias=t["bias"], keep_gu=True)
+    y_sh = M.shared_ffn(t["x"], w, md, D.prec)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    toks = np.sort(rng.choice(D.T, size=24, replace=False))
+    blocks = np.sort(rng.choice(D.Is // 32, size=4, replace=False))
+    icols = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    dcols = np.sort(rng.choice(D.d, size=256, replace=False))
+    tt = torch.as_tensor(toks, device="cuda")
+    gus = to_np(routing["gu_shared"][tt]).astype(np.float64)
+    yk = to_np(y_sh[tt]).astype(np.float64)[:, dcols]
+    hp = HostProblem(D)
+    xr = hp.p.host_rows("x", toks)
+    wg = hp.p.host_flat("ws_gate", 0, D.Is * D.d).reshape(D.Is, D.d)
+    wu = hp.p.host_flat("ws_up", 0, D.Is * D.d).reshape(D.Is, D.d)
+    wd = hp.p.host_flat("ws_down", 0, D.d * D.Is).reshape(D.d, D.Is)[dcols]
+    G, dG = bf16_dot(xr, wg)
+    U, dU = bf16_dot(xr, wu)
+    half = lambda a, b: 2.0 ** -8 * np.maximum(np.abs(a), np.abs(b))
+    for name, k, m, dm in (("G", gus[:, icols], G[:, icols], dG[:, icols]),
+                           ("U", gus[:, D.Is + icols], U[:, icols], dU[:, icols])):
+        over = np.abs(k - m) - (half(k, m) + dm)
+        assert np.all(over <= 0), "shared %s off by %.3e beyond its bound at %s" % (
+            name, over.max(), np.unravel_index(np.argmax(over), over.shape))
+    s = O.silu(G)
+    h64 = s * U
+    dh = 1.1 * dG * (np.abs(U) + dU) + (np.abs(s) + 1.1 * dG) * dU + 2.0 ** -16 * (np.abs(s) + 1.1 * dG) * (np.abs(U) + dU)
+    dh_k = 2.0 ** -8 * (np.abs(h64) + dh) + dh          # the kernel's bf16 h against h64
+    y_ref = h64 @ wd.T
+    carried = dh_k @ np.abs(wd).T
+    _, acc = bf16_dot(np.abs(h64) + dh_k, np.abs(wd))   # accumulation bound on the kernel's operands
+    over = np.abs(yk - y_ref) - (half(yk, y_ref) + carried + acc)
+    assert np.all(over <= 0), "shared output off by %.3e beyond its bound at %s" % (
+        over.max(), np.unravel_index(np.argmax(over), over.shape))
+    say("   %d tokens, %d G/U columns, %d output columns: every element within its bound (output bound / |y| median %.2e)"
+        % (len(toks), len(icols), len(dcols), float(np.median((carried + acc) / np.maximum(np.abs(y_ref), 1e-30)))))
